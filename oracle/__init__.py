@@ -1,0 +1,296 @@
+"""fp64 CPU oracle for one tensor-parallel rank's linear share.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package. It shares no code
+with the HIP library (no kernels, headers, helpers or tables) and imports
+nothing from it.
+
+Sources (cited by page title and section):
+
+* "How do tensor parallelism (TP) and pipeline parallelism (PP) split large
+  model weights across multi-GPU nodes?" (iloveeagents.com), "Detail": a
+  4096 x 4096 matrix W cut column-wise gives each of two GPUs a 4096 x 2048
+  piece; "Example": a column-parallel linear keeps out_features / t output
+  features and computes the local product x @ W_r.
+* "Tensor vs Pipeline Parallelism" (xingyuzhitong.com), "Tensor parallelism:
+  split inside each layer": first feed-forward matrix by columns, second by
+  rows, attention heads distributed, partial results combined by a sum; the
+  head and key-value head counts must divide evenly. "Common mistakes": a
+  degree that does not divide the key-value heads is refused.
+* "AI Infrastructure series, Part 5" (drpranayjha.com), "How does tensor
+  parallelism split a layer?": 64 query heads split over 2, 4 or 8 ranks, not
+  3 or 6; beyond the 8 key-value heads a group repeats key-value heads.
+  "Short answers": same maths, only the order of additions differs.
+* "Tensor Parallelism" glossary (aidolsgroup.com), "Full definition":
+  activations broadcast, partial outputs summed.
+
+Readings where the pages are silent (the same list is in the design notes):
+
+* W is logical [K_in x N_out], row-major, Y = X W; "column" = output feature.
+* Column-shard outputs are concatenated; only row-shard partials are summed.
+* The feed-forward nonlinearity is SwiGLU, H = SiLU(G) * U with
+  SiLU(g) = g / (1 + e^-g) on the gate; the fused matrix is [Wg | Wu], gate
+  first; rank r takes the same column range of Wg and of Wu. No bias.
+* QKV is [Wq | Wk | Wv]; rank r takes Q heads [r n_q / t, (r+1) n_q / t);
+  key-value heads [r n_kv / t, (r+1) n_kv / t) when t <= n_kv, else the one
+  head floor(r n_kv / t), replicated. The O projection takes the rows of the
+  rank's Q dims.
+* A degree that does not divide is an error, never a ragged split.
+* Rounding points: a column output consumed in bf16 (Y_r, H_r, QKV_r) is
+  rounded to bf16 (nearest, ties to even) from the fp64 value; row partials
+  and their sum stay unrounded.
+
+Every function below is parity-pinned by ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.orc_bf16_to_f64.restype = ctypes.c_double
+        lib.orc_f64_to_bf16.argtypes = [ctypes.c_double]
+        lib.orc_f64_to_bf16.restype = ctypes.c_uint16
+        lib.orc_round_bf16.argtypes = [P, I64, P]
+        lib.orc_bf16_to_f64_array.argtypes = [P, I64, P]
+        lib.orc_shard_matmul.argtypes = [P, I64, I64, I64, P, I64, P, P, I64, P]
+        lib.orc_swiglu.argtypes = [P, P, I64, P]
+        lib.orc_sum_partials.argtypes = [P, I64, ctypes.c_int32, I64, P]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# --------------------------------------------------------------------------
+# Shard bookkeeping (independent of the HIP library's planner).
+# --------------------------------------------------------------------------
+
+KINDS = ("col", "row", "gateup_col", "qkv_col", "o_row")
+
+
+class PlanError(ValueError):
+    """Raised with ``code`` in {"shape", "indivisible", "rank", "kind"}."""
+
+    def __init__(self, code: str, msg: str):
+        super().__init__(f"{code}: {msg}")
+        self.code = code
+
+
+def _head_sets(t: int, rank: int, n_q: int, n_kv: int):
+    """Q-head range, KV-head range and replication flag of rank ``rank``."""
+    if n_q % t != 0:
+        raise PlanError("indivisible", f"{n_q} query heads over {t} ranks")
+    if t <= n_kv:
+        if n_kv % t != 0:
+            raise PlanError("indivisible", f"{n_kv} key-value heads over {t} ranks")
+        per = n_kv // t
+        kv = (rank * per, rank * per + per)
+        replicated = False
+    else:
+        if t % n_kv != 0:
+            raise PlanError("indivisible", f"{t} ranks do not repeat {n_kv} key-value heads evenly")
+        h = (rank * n_kv) // t
+        kv = (h, h + 1)
+        replicated = True
+    q_per = n_q // t
+    return (rank * q_per, rank * q_per + q_per), kv, replicated
+
+
+def plan(kind: str, K: int, N: int, t: int, rank: int, heads=None) -> dict:
+    """Which rows and columns of the full logical weight W [K x N] rank
+    ``rank`` of ``t`` uses, in shard order.
+
+    Returns a dict with ``rows`` and ``cols`` (int64 index arrays into W),
+    ``shard_k``/``shard_n``, and for the attention kinds the head sets.
+    """
+    if kind not in KINDS:
+        raise PlanError("kind", kind)
+    if K <= 0 or N <= 0 or t <= 0:
+        raise PlanError("shape", f"K={K} N={N} t={t}")
+    if not 0 <= rank < t:
+        raise PlanError("rank", f"rank {rank} of {t}")
+    out = dict(kind=kind, K=K, N=N, t=t, rank=rank, q_heads=None, kv_heads=None,
+               kv_replicated=False)
+    all_rows = np.arange(K, dtype=np.int64)
+    all_cols = np.arange(N, dtype=np.int64)
+    if kind == "col":
+        if N % t:
+            raise PlanError("indivisible", f"N={N} over {t}")
+        w = N // t
+        rows, cols = all_rows, np.arange(rank * w, rank * w + w, dtype=np.int64)
+    elif kind == "row":
+        if K % t:
+            raise PlanError("indivisible", f"K={K} over {t}")
+        h = K // t
+        rows, cols = np.arange(rank * h, rank * h + h, dtype=np.int64), all_cols
+    elif kind == "gateup_col":
+        if N % 2:
+            raise PlanError("shape", "fused gate/up width must be even")
+        inter = N // 2
+        if inter % t:
+            raise PlanError("indivisible", f"I={inter} over {t}")
+        w = inter // t
+        gate = np.arange(rank * w, rank * w + w, dtype=np.int64)
+        rows, cols = all_rows, np.concatenate([gate, gate + inter])
+    else:
+        if heads is None:
+            raise PlanError("shape", "attention kinds need heads")
+        n_q, n_kv, d = heads
+        if n_q <= 0 or n_kv <= 0 or d <= 0 or n_q % n_kv:
+            raise PlanError("shape", f"heads {heads}")
+        (q0, q1), (k0, k1), rep = _head_sets(t, rank, n_q, n_kv)
+        out.update(q_heads=(q0, q1), kv_heads=(k0, k1), kv_replicated=rep)
+        if kind == "qkv_col":
+            if N != (n_q + 2 * n_kv) * d:
+                raise PlanError("shape", f"N={N} != (n_q + 2 n_kv) d")
+            q = np.arange(q0 * d, q1 * d, dtype=np.int64)
+            k = np.arange(k0 * d, k1 * d, dtype=np.int64) + n_q * d
+            v = k + n_kv * d
+            rows, cols = all_rows, np.concatenate([q, k, v])
+        else:  # o_row
+            if K != n_q * d:
+                raise PlanError("shape", f"K={K} != n_q d")
+            rows, cols = np.arange(q0 * d, q1 * d, dtype=np.int64), all_cols
+    out.update(rows=rows, cols=cols, shard_k=len(rows), shard_n=len(cols))
+    return out
+
+
+# --------------------------------------------------------------------------
+# Arithmetic (C core, fp64).
+# --------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().orc_bf16_to_f64_array(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().orc_round_bf16(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def _rowmajor(a: np.ndarray) -> tuple[np.ndarray, int]:
+    """uint16 2-D array with unit column stride; returns (array, leading dim)."""
+    assert a.dtype == np.uint16 and a.ndim == 2
+    if a.strides[1] != 2 or a.strides[0] % 2:
+        a = np.ascontiguousarray(a)
+    return a, max(a.strides[0] // 2, a.shape[1])
+
+
+def shard_matmul(X: np.ndarray, W: np.ndarray, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """Y[m, j] = sum_kk X[m, kk] W[rows[kk], cols[j]] in fp64, kk ascending."""
+    X, ldx = _rowmajor(X)
+    W, ldw = _rowmajor(W)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    M, Kr = X.shape
+    assert Kr == len(rows), (Kr, len(rows))
+    assert len(rows) == 0 or (rows.min() >= 0 and rows.max() < W.shape[0])
+    assert len(cols) == 0 or (cols.min() >= 0 and cols.max() < W.shape[1])
+    Y = np.empty((M, len(cols)), dtype=np.float64)
+    if M and len(cols):
+        _load().orc_shard_matmul(_ptr(X), M, ldx, Kr, _ptr(W), ldw, _ptr(rows), _ptr(cols),
+                                 len(cols), _ptr(Y))
+    return Y
+
+
+def swiglu(G: np.ndarray, U: np.ndarray) -> np.ndarray:
+    """bf16 bits of SiLU(G) * U, rounded once from fp64."""
+    G = np.ascontiguousarray(G, dtype=np.float64)
+    U = np.ascontiguousarray(U, dtype=np.float64)
+    assert G.shape == U.shape
+    H = np.empty(G.shape, dtype=np.uint16)
+    _load().orc_swiglu(_ptr(G), _ptr(U), G.size, _ptr(H))
+    return H
+
+
+def sum_partials(P: np.ndarray) -> np.ndarray:
+    """Y = P[0] + P[1] + ... + P[t-1], added in rank order, fp64."""
+    P = np.ascontiguousarray(P, dtype=np.float64)
+    t = P.shape[0]
+    Y = np.empty(P.shape[1:], dtype=np.float64)
+    stride = int(np.prod(P.shape[1:]))
+    _load().orc_sum_partials(_ptr(P), stride, t, stride, _ptr(Y))
+    return Y
+
+
+# --------------------------------------------------------------------------
+# The rank share, step by step.
+# --------------------------------------------------------------------------
+
+def col_linear(X: np.ndarray, W: np.ndarray, p: dict) -> np.ndarray:
+    """Column-parallel product of rank p["rank"], fp64 [M x shard_n], unrounded."""
+    assert p["kind"] in ("col", "qkv_col")
+    return shard_matmul(X, W, p["rows"], p["cols"])
+
+
+def col_linear_bf16(X: np.ndarray, W: np.ndarray, p: dict) -> np.ndarray:
+    """The column output as its bf16 consumer sees it."""
+    return round_bf16(col_linear(X, W, p))
+
+
+def gateup_swiglu(X: np.ndarray, Wgu: np.ndarray, p: dict) -> np.ndarray:
+    """H_r = bf16(SiLU(X Wg[:, I_r]) * (X Wu[:, I_r])) for the fused [Wg | Wu]."""
+    assert p["kind"] == "gateup_col"
+    half = p["shard_n"] // 2
+    G = shard_matmul(X, Wgu, p["rows"], p["cols"][:half])
+    U = shard_matmul(X, Wgu, p["rows"], p["cols"][half:])
+    return swiglu(G, U)
+
+
+def row_linear(Z: np.ndarray, W: np.ndarray, p: dict) -> np.ndarray:
+    """Row-parallel partial P_r = Z_r W[rows_r, :], fp64 [M x N]. ``Z`` is the
+    rank's own input slice [M x shard_k]."""
+    assert p["kind"] in ("row", "o_row")
+    return shard_matmul(Z, W, p["rows"], p["cols"])
+
+
+def ffn_shard(X: np.ndarray, Wgu: np.ndarray, Wd: np.ndarray, p_gu: dict, p_d: dict):
+    """One rank's feed-forward share: (H_r bf16 bits, P_r fp64)."""
+    H = gateup_swiglu(X, Wgu, p_gu)
+    return H, row_linear(H, Wd, p_d)
+
+
+def ffn_unsharded(X: np.ndarray, Wgu: np.ndarray, Wd: np.ndarray) -> np.ndarray:
+    """The layer the shards must add up to: t = 1."""
+    K, N2 = Wgu.shape
+    p_gu = plan("gateup_col", K, N2, 1, 0)
+    p_d = plan("row", Wd.shape[0], Wd.shape[1], 1, 0)
+    return ffn_shard(X, Wgu, Wd, p_gu, p_d)[1]
+
+
+def compare(got: np.ndarray, ref: np.ndarray) -> dict:
+    """Relative Frobenius error and max element error against max |ref|."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = got - ref
+    nref = np.linalg.norm(ref)
+    amax = float(np.abs(ref).max()) if ref.size else 0.0
+    return dict(
+        rel_fro=float(np.linalg.norm(diff) / nref) if nref > 0 else float(np.linalg.norm(diff)),
+        max_err=float(np.abs(diff).max()) if diff.size else 0.0,
+        max_ref=amax,
+        max_rel=float(np.abs(diff).max() / amax) if amax > 0 else float(np.abs(diff).max() if diff.size else 0.0),
+    )

@@ -1,0 +1,456 @@
+"""Pins for the fp64 oracle: each test checks it against something other than
+itself -- values and rules the pages fix, closed forms, exact integer
+arithmetic, an independent rational or high-precision computation, a library
+routine for the t = 1 special case, or brute force on tiny shapes.
+
+Page citations name the page title and the section.
+"""
+from __future__ import annotations
+
+import decimal
+import math
+import struct
+import types
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+
+U53 = 2.0 ** -53
+
+
+# ---------------------------------------------------------------------------
+# Independent references (pure Python, no oracle code).
+# ---------------------------------------------------------------------------
+
+_BF16_MAX = Fraction(255) * Fraction(2) ** 120
+
+
+def exact_round_bf16(x: float) -> int:
+    """bf16 bits of x, round to nearest, ties to even, by exact rational
+    arithmetic: 8 significant bits, binary32 exponent range."""
+    if math.isnan(x):
+        return 0x7FC0
+    sign = 0x8000 if math.copysign(1.0, x) < 0 else 0
+    if math.isinf(x):
+        return sign | 0x7F80
+    a = Fraction(abs(x))
+    if a == 0:
+        return sign
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** max(e - 7, -133)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    v = fl * quantum
+    if v > _BF16_MAX:
+        return sign | 0x7F80
+    return sign | (struct.unpack(">I", struct.pack(">f", float(v)))[0] >> 16)
+
+
+def bits_to_float(b: int) -> float:
+    return struct.unpack(">f", struct.pack(">I", (b & 0xFFFF) << 16))[0]
+
+
+def decode(bits: np.ndarray) -> np.ndarray:
+    """bf16 bits -> float64 through torch's own bfloat16 type."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def reassoc_bound(Xf: np.ndarray, Wf: np.ndarray, terms: int) -> np.ndarray:
+    """Two fp64 sums of the same products in different association differ by
+    at most 2 * gamma_n * sum |x||w| (Higham, Accuracy and Stability, 3.1)."""
+    g = terms * U53 / (1 - terms * U53)
+    return 2 * g * (np.abs(Xf) @ np.abs(Wf))
+
+
+def normal(seed, shape, sigma=1.0):
+    return si.normal_bf16(seed, shape, sigma)
+
+
+# ---------------------------------------------------------------------------
+# bf16 conversions.
+# ---------------------------------------------------------------------------
+
+def test_bf16_decode_matches_torch():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    got = oracle.bf16_to_f64(bits[finite])
+    np.testing.assert_array_equal(got, decode(bits[finite]))
+
+
+def _rounding_cases():
+    rng = np.random.default_rng(123)
+    xs = list(rng.standard_normal(3000) * np.exp2(rng.integers(-140, 128, 3000)))
+    # exact ties between adjacent bf16 values, and one fp64 ulp on either side
+    for b in rng.integers(0, 0x7F7F, 400):
+        lo, hi = bits_to_float(int(b)), bits_to_float(int(b) + 1)
+        mid = (lo + hi) / 2  # exact: 9 significant bits
+        xs += [mid, -mid, math.nextafter(mid, math.inf), math.nextafter(mid, -math.inf)]
+    xs += [0.0, -0.0, 1e-45, 3e-40, -1.1e-38, 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135,
+           3.3895313892515355e38, 3.3961e38, 3.4e38, -3.5e38, 1e300, math.inf, -math.inf]
+    return xs
+
+
+def test_bf16_round_matches_exact_rational():
+    xs = _rounding_cases()
+    got = oracle.round_bf16(np.array(xs, dtype=np.float64))
+    want = np.array([exact_round_bf16(x) for x in xs], dtype=np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(xs[i], hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def test_bf16_round_matches_torch_from_binary32():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(1 << 16) * np.exp2(rng.integers(-120, 120, 1 << 16))).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.round_bf16(x.astype(np.float64)), want)
+
+
+# ---------------------------------------------------------------------------
+# The matmul core.
+# ---------------------------------------------------------------------------
+
+def test_exact_integers_match_int64_matmul():
+    # X, W in {-3..3}: every product and partial sum is an integer, exact in fp64
+    X = si.int_bf16(11, (7, 200), -3, 3)
+    W = si.int_bf16(12, (200, 48), -3, 3)
+    Xi = decode(X).astype(np.int64)
+    Wi = decode(W).astype(np.int64)
+    got = oracle.shard_matmul(X, W, np.arange(200), np.arange(48))
+    np.testing.assert_array_equal(got, (Xi @ Wi).astype(np.float64))
+    # a gathered shard: columns in a scrambled order, rows a sub-range
+    cols = np.array([5, 0, 47, 13, 13, 30])
+    rows = np.arange(50, 150)
+    got = oracle.shard_matmul(X[:, 50:150], W, rows, cols)
+    np.testing.assert_array_equal(got, (Xi[:, 50:150] @ Wi[50:150][:, cols]).astype(np.float64))
+
+
+def test_t1_matches_torch_fp64_matmul():
+    X, W = normal(0, (16, 300)), normal(1, (300, 200), 0.02)
+    got = oracle.shard_matmul(X, W, np.arange(300), np.arange(200))
+    want = (torch.from_numpy(decode(X)) @ torch.from_numpy(decode(W))).numpy()
+    assert np.linalg.norm(got - want) <= 1e-12 * np.linalg.norm(want)
+
+
+def _brute(Xf, Wf):
+    """Plain in-order dot products with Python floats (fp64)."""
+    M, K = len(Xf), len(Xf[0])
+    N = len(Wf[0])
+    out = []
+    for m in range(M):
+        row = []
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc = acc + Xf[m][k] * Wf[k][n]
+            row.append(acc)
+        out.append(row)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("K,N", [(k, n) for k in (1, 2, 3, 4, 6, 12) for n in (1, 2, 4, 6, 9, 12)])
+def test_brute_force_tiny_shapes(K, N):
+    X, W = normal(2, (3, K)), normal(3, (K, N), 0.5)
+    Xf, Wf = decode(X).tolist(), decode(W).tolist()
+    for t in range(1, 13):
+        if N % t == 0:  # column shards: the rank's slice of output columns
+            w = N // t
+            for r in range(t):
+                p = oracle.plan("col", K, N, t, r)
+                got = oracle.col_linear(X, W, p)
+                want = _brute(Xf, [row[r * w:(r + 1) * w] for row in Wf])
+                np.testing.assert_array_equal(got, want)
+        if K % t == 0:  # row shards: the rank's input slice times its rows of W
+            h = K // t
+            for r in range(t):
+                p = oracle.plan("row", K, N, t, r)
+                got = oracle.row_linear(X[:, r * h:(r + 1) * h], W, p)
+                want = _brute([row[r * h:(r + 1) * h] for row in Xf], Wf[r * h:(r + 1) * h])
+                np.testing.assert_array_equal(got, want)
+
+
+def test_identity_weight():
+    X = normal(4, (6, 64))
+    Xf = decode(X)
+    I = si.identity_bf16(64)
+    for t in (1, 2, 4, 8):
+        parts = []
+        for r in range(t):
+            pc = oracle.plan("col", 64, 64, t, r)
+            np.testing.assert_array_equal(oracle.col_linear_bf16(X, I, pc), X[:, pc["cols"]])
+            pr = oracle.plan("row", 64, 64, t, r)
+            parts.append(oracle.row_linear(X[:, pr["rows"]], I, pr))
+        np.testing.assert_array_equal(oracle.sum_partials(np.stack(parts)), Xf)
+
+
+def test_permutation_weight_selects_columns():
+    X = normal(5, (5, 96))
+    W, perm = si.permutation_bf16(9, 96)
+    p = oracle.plan("col", 96, 96, 1, 0)
+    np.testing.assert_array_equal(oracle.col_linear_bf16(X, W, p), X[:, perm])
+
+
+def test_sum_partials_in_rank_order():
+    # 1e16 + 1 loses the 1 in fp64, so only the rank order 0, 1, 2 gives 0
+    P = np.array([[1e16], [1.0], [-1e16]])
+    assert oracle.sum_partials(P)[0] == 0.0
+    assert oracle.sum_partials(P[[1, 0, 2]])[0] == 0.0
+    assert oracle.sum_partials(P[[0, 2, 1]])[0] == 1.0
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU.
+# ---------------------------------------------------------------------------
+
+def _silu_times_u_highprec(g: float, u: float) -> int:
+    with decimal.localcontext() as ctx:
+        ctx.prec = 60
+        G = decimal.Decimal(g)
+        s = G / (1 + (-G).exp()) * decimal.Decimal(u)
+    return exact_round_bf16(float(s)) if abs(s) < decimal.Decimal("1e300") else 0
+
+
+def test_swiglu_closed_forms():
+    G = np.array([0.0, 0.0, 1.5, -2.0, 3.0])
+    U = np.array([2.0, -7.0, 0.0, 0.0, 1.0])
+    H = decode(oracle.swiglu(G, U))
+    assert np.all(H[:4] == 0.0)
+    # large |g|: SiLU(g) -> g for g -> +inf and -> 0 for g -> -inf, no NaN
+    H = decode(oracle.swiglu(np.array([800.0, -800.0, -1e308]), np.array([0.5, 3.0, 1.0])))
+    assert H[0] == 400.0 and H[1] == 0.0 and H[2] == 0.0
+
+
+def test_swiglu_onehot_gate_against_high_precision():
+    """With one-hot gate and up columns, G and U equal chosen columns of X
+    exactly, so H[m, j] must be bf16(SiLU(x[m, a_j]) * x[m, b_j]) with SiLU
+    applied to the gate half (the first half of [Wg | Wu])."""
+    K, inter, M = 40, 24, 6
+    X = normal(6, (M, K), 2.0)
+    rng = np.random.default_rng(1)
+    a, b = rng.integers(0, K, inter), rng.integers(0, K, inter)
+    Wgu = np.zeros((K, 2 * inter), dtype=np.uint16)
+    Wgu[a, np.arange(inter)] = 0x3F80
+    Wgu[b, inter + np.arange(inter)] = 0x3F80
+    Xf = decode(X)
+    for t in (1, 2, 3, 4):
+        w = inter // t
+        for r in range(t):
+            p = oracle.plan("gateup_col", K, 2 * inter, t, r)
+            H = oracle.gateup_swiglu(X, Wgu, p)
+            js = range(r * w, (r + 1) * w)
+            want = np.array([[_silu_times_u_highprec(Xf[m, a[j]], Xf[m, b[j]]) for j in js]
+                             for m in range(M)], dtype=np.uint16)
+            np.testing.assert_array_equal(H, want)
+
+
+def test_swiglu_matches_torch_silu_fp64():
+    rng = np.random.default_rng(2)
+    G = rng.standard_normal(20000) * 4
+    U = rng.standard_normal(20000)
+    want = torch.nn.functional.silu(torch.from_numpy(G)) * torch.from_numpy(U)
+    want_bits = np.array([exact_round_bf16(v) for v in want.numpy()], dtype=np.uint16)
+    got = oracle.swiglu(G, U)
+    # both round once from an fp64 value; the two exp() may differ by an fp64
+    # ulp, which can flip a bf16 decision only next to an exact tie
+    assert np.count_nonzero(got != want_bits) <= 2
+
+
+# ---------------------------------------------------------------------------
+# Shard bookkeeping and the sharding invariants.
+# ---------------------------------------------------------------------------
+
+def test_worked_tp2_split_shapes(golden):
+    g = golden("tp2_worked_split.json")
+    K, N = g["W"]
+    for r in range(g["t"]):
+        p = oracle.plan("col", K, N, g["t"], r)
+        assert [p["shard_k"], p["shard_n"]] == g["column_shards"][r]
+        assert [int(p["cols"][0]), int(p["cols"][-1]) + 1] == g["column_ranges"][r]
+        q = oracle.plan("row", K, N, g["t"], r)
+        assert [q["shard_k"], q["shard_n"]] == g["row_shards"][r]
+        assert [int(q["rows"][0]), int(q["rows"][-1]) + 1] == g["row_ranges"][r]
+
+
+def test_head_tables(golden):
+    g = golden("heads_64q_8kv.json")
+    nq, nkv, d = g["n_q"], g["n_kv"], g["head_dim"]
+    assert g["layers"] * nkv * d * 2 * 2 == g["kv_bytes_per_token"]  # K and V, 2 bytes
+    N, K = (nq + 2 * nkv) * d, nq * d
+    for t in g["accepted_t"]:
+        rows = []
+        for r in range(t):
+            p = oracle.plan("qkv_col", 8192, N, t, r, heads=(nq, nkv, d))
+            rows.append([*p["q_heads"], *p["kv_heads"], p["kv_replicated"]])
+            o = oracle.plan("o_row", K, 8192, t, r, heads=(nq, nkv, d))
+            assert o["shard_k"] == (nq // t) * d and o["rows"][0] == p["q_heads"][0] * d
+            # every local query head finds its key-value head locally
+            group = nq // nkv
+            for q in range(*p["q_heads"]):
+                assert p["kv_heads"][0] <= q // group < p["kv_heads"][1]
+        assert rows == g["per_rank"][str(t)]
+    for t in g["refused_t"]:
+        for kind, KK, NN in (("qkv_col", 8192, N), ("o_row", K, 8192)):
+            with pytest.raises(oracle.PlanError) as e:
+                oracle.plan(kind, KK, NN, t, 0, heads=(nq, nkv, d))
+            assert e.value.code == "indivisible"
+
+
+def test_llama70b_rank_share_qkv_and_o():
+    p = oracle.plan("qkv_col", 8192, 10240, 8, 0, heads=(64, 8, 128))
+    assert p["shard_n"] == 1280  # 8 Q heads + 1 K + 1 V head of 128
+    assert list(p["cols"][[0, 1023, 1024, 1151, 1152, 1279]]) == [0, 1023, 8192, 8319, 9216, 9343]
+    o = oracle.plan("o_row", 8192, 8192, 8, 0, heads=(64, 8, 128))
+    assert (o["shard_k"], o["shard_n"]) == (1024, 8192)
+
+
+def test_plan_errors():
+    for args, code in [(("col", 64, 60, 8, 0), "indivisible"), (("row", 60, 64, 8, 0), "indivisible"),
+                       (("col", 64, 64, 4, 4), "rank"), (("col", 64, 64, 4, -1), "rank"),
+                       (("col", 0, 64, 1, 0), "shape"), (("gateup_col", 64, 63, 1, 0), "shape"),
+                       (("gateup_col", 64, 96, 32, 0), "indivisible"), (("foo", 8, 8, 1, 0), "kind")]:
+        with pytest.raises(oracle.PlanError) as e:
+            oracle.plan(*args)
+        assert e.value.code == code, args
+
+
+def test_size_closed_forms(golden):
+    g = golden("sizes.json")
+    for hidden, nbytes in g["reduce_message"]["cases"]:
+        assert oracle.plan("row", 28672, hidden, 8, 0)["shard_n"] * 2 == nbytes
+    pm = g["prefill_message"]
+    assert pm["tokens"] * oracle.plan("row", 1024, pm["hidden"], 8, 0)["shard_n"] * 2 == pm["bytes"]
+    s = g["per_rank_share"]["llama70b_ffn"]
+    H, I, t = s["hidden"], s["intermediate"], s["t"]
+    total = 0
+    for r in range(t):
+        gu = oracle.plan("gateup_col", H, 2 * I, t, r)
+        dn = oracle.plan("row", I, H, t, r)
+        share = (gu["shard_k"] * gu["shard_n"] + dn["shard_k"] * dn["shard_n"]) * 2
+        assert share == s["per_rank_bytes"]
+        total += share
+    assert total == s["total_bytes"] == 3 * H * I * 2
+
+
+def test_gateup_pairs_same_columns():
+    p = oracle.plan("gateup_col", 16, 16, 2, 1)
+    assert list(p["cols"]) == [4, 5, 6, 7, 12, 13, 14, 15]
+
+
+def _concat_invariant(orc, X, W, t):
+    K, N = W.shape
+    full = orc.col_linear(X, W, orc.plan("col", K, N, 1, 0))
+    parts = [orc.col_linear(X, W, orc.plan("col", K, N, t, r)) for r in range(t)]
+    np.testing.assert_array_equal(np.concatenate(parts, axis=1), full)
+
+
+def _row_sum_invariant(orc, Z, W, t):
+    K, N = W.shape
+    full = orc.row_linear(Z, W, orc.plan("row", K, N, 1, 0))
+    parts = []
+    for r in range(t):
+        p = orc.plan("row", K, N, t, r)
+        parts.append(orc.row_linear(Z[:, p["rows"]], W, p))
+    got = orc.sum_partials(np.stack(parts))
+    assert np.all(np.abs(got - full) <= reassoc_bound(decode(Z), decode(W), K + t))
+
+
+def _ffn_invariant(orc, X, Wgu, Wd, t):
+    K, N2 = Wgu.shape
+    I, H = Wd.shape
+    want = orc.ffn_unsharded(X, Wgu, Wd)
+    H_full = orc.gateup_swiglu(X, Wgu, orc.plan("gateup_col", K, N2, 1, 0))
+    parts = []
+    for r in range(t):
+        Hr, Pr = orc.ffn_shard(X, Wgu, Wd, orc.plan("gateup_col", K, N2, t, r),
+                               orc.plan("row", I, H, t, r))
+        # each element of H is the same in-order sum, so the shard is bit-exact
+        np.testing.assert_array_equal(Hr, H_full[:, r * (I // t):(r + 1) * (I // t)])
+        parts.append(Pr)
+    got = orc.sum_partials(np.stack(parts))
+    assert np.all(np.abs(got - want) <= reassoc_bound(decode(H_full), decode(Wd), I + t))
+
+
+def test_concat_invariant_small():
+    X, W = normal(7, (5, 72)), normal(8, (72, 96), 0.1)
+    for t in (1, 2, 3, 4, 6, 8, 12):
+        _concat_invariant(oracle, X, W, t)
+
+
+def test_row_sum_invariant_small():
+    Z, W = normal(9, (5, 96), 1.0), normal(10, (96, 40), 0.1)
+    for t in (2, 3, 4, 8, 12):
+        _row_sum_invariant(oracle, Z, W, t)
+
+
+def test_ffn_invariant_small():
+    X, Wgu, Wd = normal(0, (4, 64)), normal(1, (64, 2 * 48), 0.1), normal(3, (48, 64), 0.1)
+    for t in (1, 2, 3, 4, 8):
+        _ffn_invariant(oracle, X, Wgu, Wd, t)
+
+
+@pytest.mark.slow
+def test_worked_split_full_size_invariants():
+    """The worked TP=2 split at its own size: X [8 x 4096], W and W2 4096 x 4096."""
+    X = si.normal_bf16(0, (8, 4096), 1.0)
+    W = si.normal_bf16(1, (4096, 4096), 0.02)
+    W2 = si.normal_bf16(2, (4096, 4096), 0.02)
+    _concat_invariant(oracle, X, W, 2)
+    Y = oracle.col_linear_bf16(X, W, oracle.plan("col", 4096, 4096, 1, 0))
+    _row_sum_invariant(oracle, Y, W2, 2)
+
+
+# ---------------------------------------------------------------------------
+# The pins bite: a planted mistake in a copy of the oracle fails them.
+# ---------------------------------------------------------------------------
+
+def _mutant(**over):
+    ns = types.SimpleNamespace(**{k: getattr(oracle, k) for k in dir(oracle) if not k.startswith("__")})
+    for k, v in over.items():
+        setattr(ns, k, v)
+    return ns
+
+
+def test_planted_contiguous_gateup_cut_is_caught():
+    def bad_plan(kind, K, N, t, rank, heads=None):
+        p = oracle.plan(kind, K, N, t, rank, heads)
+        if kind == "gateup_col":  # a plain 1/t cut of [Wg | Wu]
+            w = N // t
+            p["cols"] = np.arange(rank * w, rank * w + w, dtype=np.int64)
+        return p
+
+    def ffn_shard(X, Wgu, Wd, pg, pd):
+        Hh = oracle.gateup_swiglu(X, Wgu, pg)
+        return Hh, oracle.row_linear(Hh, Wd, pd)
+
+    X, Wgu, Wd = normal(0, (4, 64)), normal(1, (64, 96), 0.1), normal(3, (48, 64), 0.1)
+    with pytest.raises(AssertionError):
+        _ffn_invariant(_mutant(plan=bad_plan, ffn_shard=ffn_shard), X, Wgu, Wd, 2)
+
+
+def test_planted_transposed_operand_is_caught():
+    def bad_matmul(X, W, rows, cols):  # W read transposed
+        return oracle.shard_matmul(X, np.ascontiguousarray(W.T), rows, cols)
+
+    X, W = si.int_bf16(11, (7, 48), -3, 3), si.int_bf16(12, (48, 48), -3, 3)
+    Xi, Wi = decode(X).astype(np.int64), decode(W).astype(np.int64)
+    assert not np.array_equal(bad_matmul(X, W, np.arange(48), np.arange(48)), Xi @ Wi)
+
+
+def test_planted_truncating_round_is_caught():
+    xs = _rounding_cases()
+    trunc = np.array([struct.unpack(">I", struct.pack(">f", x))[0] >> 16 if abs(x) < 3e38 else 0
+                      for x in xs], dtype=np.uint16)
+    want = np.array([exact_round_bf16(x) for x in xs], dtype=np.uint16)
+    assert np.count_nonzero(trunc != want) > 100
