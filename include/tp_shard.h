@@ -1,0 +1,224 @@
+/*
+ * tp_shard.h -- one tensor-parallel rank's linear share of a Megatron-style
+ * transformer layer on an MI355X (gfx950) GPU.
+ *
+ * The method, as the pages state it:
+ *   - "Tensor vs Pipeline Parallelism" (xingyuzhitong.com), section "Tensor
+ *     parallelism: split inside each layer": the first linear layer of the
+ *     feed-forward block is split by columns and the second by rows, attention
+ *     heads are distributed among GPUs, and the partial results are combined
+ *     by an all-reduce.
+ *   - "AI Infrastructure series, Part 5" (drpranayjha.com), section "How does
+ *     tensor parallelism split a layer?": the first matrix of each block by
+ *     columns, the second by rows; each GPU holds and reads 1/N of every
+ *     matrix; 64 query heads split over 2, 4 or 8 GPUs but not 3 or 6; past
+ *     the 8 key-value heads a group repeats key-value heads.
+ *   - "Tensor Parallelism" glossary (aidolsgroup.com), "Full definition":
+ *     activations are broadcast and partial outputs are summed.
+ *   - "How do tensor parallelism (TP) and pipeline parallelism (PP) split large
+ *     model weights ...?" (iloveeagents.com), "Detail" and "Example": a
+ *     4096 x 4096 W cut column-wise into two 4096 x 2048 pieces; a
+ *     column-parallel linear keeps out_features / t outputs and computes the
+ *     local product.
+ *
+ * On one GPU the t ranks run one after another, each with its own packed
+ * shard and its own fp32 partial, and tp_reduce_partials sums the partials in
+ * place of the cross-GPU all-reduce.
+ *
+ * Conventions for every entry point:
+ *   - A weight W is logical [K x N] row-major bf16 (raw uint16_t bits), and a
+ *     layer computes Y = X W. "Column" means an output feature.
+ *   - bf16 is bfloat16 as raw uint16_t bits. Rounding to bf16 is round to
+ *     nearest, ties to even.
+ *   - Pointers named "device" point to GPU memory the caller allocated; the
+ *     library never allocates, frees or keeps device memory and holds no
+ *     state between calls. The caller keeps every buffer alive until the work
+ *     queued on `stream` has finished.
+ *   - All device work is queued asynchronously on `stream` (a hipStream_t;
+ *     NULL means the default stream). No call waits for the GPU.
+ *   - Arguments are checked on the host before anything is queued; on any
+ *     error nothing is queued and an error code is returned. No C++ exception
+ *     crosses this interface. Every call is reentrant.
+ *   - Device pointers must be 16-byte aligned; leading dimensions of bf16
+ *     arrays must be multiples of 8 elements and those of fp32 arrays
+ *     multiples of 4 (TP_ERR_ALIGN otherwise). Inputs and outputs must not
+ *     overlap unless a call says otherwise.
+ */
+#ifndef TP_SHARD_H
+#define TP_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define TP_API __attribute__((visibility("default")))
+#else
+#define TP_API
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef int32_t tp_status;
+enum {
+  TP_OK = 0,
+  TP_ERR_NULL = -1,        /* a required pointer is NULL */
+  TP_ERR_SHAPE = -2,       /* a size <= 0 (M < 0), or descriptors that do not fit together */
+  TP_ERR_INDIVISIBLE = -3, /* t does not divide the split dimension or the heads */
+  TP_ERR_RANK = -4,        /* rank outside [0, t) */
+  TP_ERR_ALIGN = -5,       /* misaligned pointer, leading dimension or width */
+  TP_ERR_WORKSPACE = -6,   /* workspace smaller than tp_workspace_bytes() */
+  TP_ERR_HIP = -7,         /* the HIP runtime reported an error at launch */
+  TP_ERR_KIND = -8         /* unknown kind, or a kind the call does not take */
+};
+
+/* How a rank's shard is cut from the full weight. */
+typedef enum {
+  TP_COL = 0,        /* columns [r N/t, (r+1) N/t) of W [K x N] */
+  TP_ROW = 1,        /* rows    [r K/t, (r+1) K/t) of W [K x N] */
+  TP_GATEUP_COL = 2, /* W = [Wg | Wu], N = 2 I: columns [r I/t, (r+1) I/t) of Wg and of Wu */
+  TP_QKV_COL = 3,    /* W = [Wq | Wk | Wv], N = (n_q + 2 n_kv) d: the rank's Q, K and V heads */
+  TP_O_ROW = 4       /* W [n_q d x N]: the rows of the rank's Q heads */
+} tp_kind;
+
+/* Which kernel family runs a linear. AUTO picks DECODE for M <= 64. */
+typedef enum {
+  TP_PATH_AUTO = 0,
+  TP_PATH_DECODE = 1,  /* split-K MFMA GEMV, HBM-bound; needs M <= 64 */
+  TP_PATH_PREFILL = 2  /* LDS-tiled MFMA GEMM, compute-bound */
+} tp_path;
+
+/* Attention shape: query heads, key-value heads, head dimension. */
+typedef struct {
+  int32_t n_q, n_kv, head_dim;
+} tp_heads;
+
+/* A run of columns of the full W: columns [src_col, src_col + len) become
+ * shard columns [dst_col, dst_col + len). */
+typedef struct {
+  int64_t src_col, len, dst_col;
+} tp_col_range;
+
+/* One rank's shard (plain old data, filled by tp_shard_plan). */
+typedef struct {
+  int32_t kind, t, rank, n_col_ranges;
+  int64_t K, N;                 /* full logical weight [K x N] */
+  int64_t shard_k, shard_n;     /* logical shard [shard_k x shard_n] */
+  int64_t row_begin, row_end;   /* rows of W in the shard: [row_begin, row_end) */
+  tp_col_range col_ranges[3];   /* columns of W in the shard, in shard order */
+  int32_t q_head_begin, q_head_end;   /* attention kinds: the rank's Q heads */
+  int32_t kv_head_begin, kv_head_end; /* attention kinds: the rank's KV heads */
+  int32_t kv_replicated;        /* 1 if t > n_kv: the KV head is repeated on t / n_kv ranks */
+  int32_t path;                 /* tp_path; tp_shard_plan sets TP_PATH_AUTO, the caller may change it */
+  int64_t out_n;                /* width of the column output: shard_n, or shard_n / 2 (= I/t) for TP_GATEUP_COL */
+  int64_t packed_k, packed_n;   /* padded sizes of the packed layout */
+  int64_t packed_bytes;         /* bytes tp_shard_pack writes */
+} tp_shard_desc;
+
+/*
+ * Plans rank `rank` of `t` for a weight of kind `kind`, logical [K x N]
+ * (host only, integer, no GPU work). `heads` is required for TP_QKV_COL and
+ * TP_O_ROW and ignored otherwise.
+ *
+ * Rules ("Tensor vs Pipeline Parallelism", "Tensor parallelism: split inside
+ * each layer" and "Common mistakes"; "AI Infrastructure series, Part 5",
+ * "How does tensor parallelism split a layer?"): t must divide the split
+ * dimension exactly, never a ragged split (TP_ERR_INDIVISIBLE). For the
+ * attention kinds n_q % t == 0, and n_kv % t == 0 when t <= n_kv, else
+ * t % n_kv == 0 and rank r holds KV head floor(r n_kv / t), repeated.
+ * TP_QKV_COL needs N == (n_q + 2 n_kv) d, TP_O_ROW needs K == n_q d, and
+ * n_q % n_kv == 0 (TP_ERR_SHAPE). The kernels read 16-byte vectors, so the
+ * shard's k extent, its output width and d must be multiples of 8
+ * (TP_ERR_ALIGN).
+ */
+TP_API tp_status tp_shard_plan(tp_kind kind, int64_t K, int64_t N, int32_t t, int32_t rank,
+                        const tp_heads* heads, tp_shard_desc* out);
+
+/*
+ * Copies the rank's shard out of the full weight into the kernels' packed
+ * layout ("AI Infrastructure series, Part 5", "What does it look like in vLLM
+ * ...": the engine splits the weights as it loads them). Load-time work.
+ *   W        device, full logical [K x N] bf16, row-major, leading dim ldw >= N
+ *   W_packed device, desc->packed_bytes bytes, 16-byte aligned; its layout is
+ *            private to the library (tiles of 16 output columns x 32 k,
+ *            zero-padded to packed_n x packed_k, gate/up tiles interleaved).
+ */
+TP_API tp_status tp_shard_pack(const tp_shard_desc* desc, const uint16_t* W, int64_t ldw,
+                        void* W_packed, hipStream_t stream);
+
+/*
+ * Column-parallel linear of one rank ("How do tensor parallelism ... split
+ * ...", "Example": each GPU computes its share of the output features as the
+ * local product x W_r; "Tensor vs Pipeline Parallelism", "Tensor
+ * parallelism: split inside each layer").
+ *   X [M x K] bf16, leading dim ldx (every rank reads the same X)
+ *   TP_COL, TP_QKV_COL: Y [M x shard_n] = bf16(X W_r) (for QKV the columns
+ *     are [Q_r | K_r | V_r])
+ *   TP_GATEUP_COL: Y [M x I/t] = bf16(SiLU(X Wg_r) * (X Wu_r)), SiLU(g) =
+ *     g / (1 + e^-g): SwiGLU fused into the epilogue, G and U never leave the
+ *     GPU's registers
+ * Accumulation is fp32 from bf16 products; the result is rounded once to bf16.
+ * ldy lets Y be a column slice of a wider buffer. M == 0 queues nothing and
+ * returns TP_OK without looking at X, W_packed or Y (they may be NULL).
+ * ws may be NULL when tp_workspace_bytes(desc, M) == 0.
+ */
+TP_API tp_status tp_col_linear(const tp_shard_desc* desc, const uint16_t* X, int64_t M, int64_t ldx,
+                        const void* W_packed, uint16_t* Y, int64_t ldy, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Row-parallel linear of one rank: the fp32 partial P_r = Z_r W[rows_r, :]
+ * ("Tensor vs Pipeline Parallelism", "Tensor parallelism: split inside each
+ * layer": second matrix by rows; "Tensor Parallelism" glossary: partial
+ * outputs are summed). It never reduces.
+ *   Z [M x shard_k] bf16, leading dim ldz: the rank's own input slice (its
+ *     column output, or its heads' attention output for TP_O_ROW)
+ *   P [M x N] fp32, leading dim ldp
+ */
+TP_API tp_status tp_row_linear(const tp_shard_desc* desc, const uint16_t* Z, int64_t M, int64_t ldz,
+                        const void* W_packed, float* P, int64_t ldp, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One rank's feed-forward share: tp_col_linear(gateup) into H, then
+ * tp_row_linear(down) from H into the partial P ("AI Infrastructure series,
+ * Part 5", "How does tensor parallelism split a layer?": first matrix by
+ * columns, second by rows, so the first output slice is exactly the second's
+ * input slice and nothing is exchanged between them).
+ *   gateup: a TP_GATEUP_COL plan of [Wg | Wu] [H x 2I]; down: a TP_ROW plan of
+ *   Wd [I x H] with the same t and rank, and gateup->out_n == down->shard_k
+ *   (TP_ERR_SHAPE otherwise).
+ *   H_ws device [M x I/t] bf16 (contiguous), P [M x H] fp32 with leading dim ldp.
+ */
+TP_API tp_status tp_ffn_shard(const tp_shard_desc* gateup, const tp_shard_desc* down,
+                       const uint16_t* X, int64_t M, int64_t ldx, const void* Wgu_packed,
+                       const void* Wd_packed, uint16_t* H_ws, float* P, int64_t ldp,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The sum that replaces the all-reduce ("Tensor Parallelism" glossary:
+ * partial outputs are summed; "Tensor vs Pipeline Parallelism": two
+ * all-reduces per layer, after attention and after the feed-forward block):
+ *   Y[m][n] = P_0[m][n] + P_1[m][n] + ... + P_{t-1}[m][n], added in fp32 in
+ *   rank order, where P_r = P + r * stride_elems is [M x N] with leading dim
+ *   ldp. Y [M x N] fp32 with leading dim ldy may be P_0 itself (in place);
+ *   it must not overlap P_1 ... P_{t-1}.
+ */
+TP_API tp_status tp_reduce_partials(const float* P, int64_t stride_elems, int32_t t, int64_t M,
+                             int64_t N, int64_t ldp, float* Y, int64_t ldy, hipStream_t stream);
+
+/* Bytes of workspace tp_col_linear / tp_row_linear need for this shard at
+ * this M (0 when the chosen kernels need none). */
+TP_API size_t tp_workspace_bytes(const tp_shard_desc* desc, int64_t M);
+
+/* A static, human-readable name for a status code. */
+TP_API const char* tp_status_str(tp_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_SHARD_H */

@@ -100,6 +100,21 @@ def normal_bf16(seed: int, shape, sigma: float, rows=None, cols=None) -> np.ndar
     return _fill_rows(fn, r1 - r0, out)
 
 
+def normal_f32(seed: int, shape, sigma: float) -> np.ndarray:
+    """binary32 values sigma * N(0, 1) from the same stream (no bf16 rounding)."""
+    R, C = int(shape[0]), int(shape[1])
+    out = np.empty((R, C), dtype=np.float32)
+    origin = _origin(seed)
+
+    def fn(a, b):
+        x1, x2 = _stream_pair(origin, _block_counters(C, a, b, 0, C))
+        u1 = ((x1 >> np.uint64(11)).astype(np.float64) + 0.5) * (2.0 ** -53)
+        u2 = (x2 >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+        out[a:b] = (np.sqrt(-2.0 * np.log(u1)) * np.cos((2.0 * np.pi) * u2) * sigma).astype(np.float32)
+
+    return _fill_rows(fn, R, out)
+
+
 def int_bf16(seed: int, shape, lo: int, hi: int) -> np.ndarray:
     """bf16 bits of uniform integers in [lo, hi] (exact in bf16 for |v| <= 256)."""
     R, C = int(shape[0]), int(shape[1])

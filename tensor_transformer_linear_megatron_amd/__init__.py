@@ -1,0 +1,167 @@
+"""One tensor-parallel rank's linear share of a Megatron-style transformer
+layer, on one MI355X (gfx950) GPU.
+
+Thin Python binding over the C ABI of ``include/tp_shard.h``: the functions
+below have the same names and only marshal arguments (torch tensors ->
+device pointers, the current HIP stream). Every step runs in the library's
+HIP kernels; torch supplies device memory and streams. Output tensors are
+allocated with torch when the caller does not pass them.
+
+The method ("Tensor vs Pipeline Parallelism" (xingyuzhitong.com), "Tensor
+parallelism: split inside each layer"): the first matrix of a block is split
+by columns, the second by rows, and the rows' partial outputs are summed.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    KIND_NAMES, TP_COL, TP_GATEUP_COL, TP_O_ROW, TP_PATH_AUTO, TP_PATH_DECODE, TP_PATH_PREFILL,
+    TP_QKV_COL, TP_ROW, TpHeads, TpShardDesc,
+)
+
+__all__ = ["tp_shard_plan", "tp_shard_pack", "tp_col_linear", "tp_row_linear", "tp_ffn_shard",
+           "tp_reduce_partials", "tp_workspace_bytes", "tp_status_str", "TpError", "TpShardDesc"]
+
+
+class TpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {tp_status_str(status)} ({status})")
+        self.status = status
+
+
+def tp_status_str(status: int) -> str:
+    return _lib.load().tp_status_str(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != _lib.TP_OK:
+        raise TpError(status, where)
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _mat(x: torch.Tensor, dtype, name: str):
+    """(pointer, leading dim) of a 2-D row-major device tensor."""
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise TypeError(f"{name} must be a CUDA/HIP tensor")
+    if x.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {x.dtype}")
+    if x.dim() != 2 or (x.size(1) > 1 and x.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return ctypes.c_void_p(x.data_ptr()), max(x.stride(0), x.size(1))
+
+
+def tp_shard_plan(kind, K: int, N: int, t: int, rank: int, heads=None) -> TpShardDesc:
+    """Plan rank ``rank`` of ``t`` for weight kind ``kind`` (name or TP_* value)."""
+    k = KIND_NAMES[kind] if isinstance(kind, str) else int(kind)
+    d = TpShardDesc()
+    hp = None
+    if heads is not None:
+        hp = ctypes.pointer(TpHeads(*heads))
+    _check(_lib.load().tp_shard_plan(k, K, N, t, rank, hp, ctypes.byref(d)), "tp_shard_plan")
+    return d
+
+
+def tp_shard_pack(desc: TpShardDesc, W: torch.Tensor, out: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """Pack the rank's shard of the full weight ``W`` [K x N] (bf16, device)."""
+    wp, ldw = _mat(W, torch.bfloat16, "W")
+    if tuple(W.shape) != (desc.K, desc.N):
+        raise ValueError(f"W is {tuple(W.shape)}, plan expects {(desc.K, desc.N)}")
+    if out is None:
+        out = torch.empty(desc.packed_bytes, dtype=torch.uint8, device=W.device)
+    if out.numel() * out.element_size() < desc.packed_bytes or not out.is_contiguous():
+        raise ValueError("packed buffer too small or not contiguous")
+    _check(_lib.load().tp_shard_pack(ctypes.byref(desc), wp, ldw, ctypes.c_void_p(out.data_ptr()),
+                                     _stream(stream)), "tp_shard_pack")
+    return out
+
+
+def tp_workspace_bytes(desc: TpShardDesc, M: int) -> int:
+    return int(_lib.load().tp_workspace_bytes(ctypes.byref(desc), M))
+
+
+def _ws(desc, M, ws):
+    if ws is None:
+        return ctypes.c_void_p(0), 0
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+def tp_col_linear(desc: TpShardDesc, X: torch.Tensor, W_packed: torch.Tensor,
+                  Y: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """Column-parallel linear: Y [M x out_n] bf16 (SwiGLU output for gate/up)."""
+    xp, ldx = _mat(X, torch.bfloat16, "X")
+    M = X.size(0)
+    if X.size(1) != desc.shard_k:
+        raise ValueError(f"X has {X.size(1)} columns, shard expects {desc.shard_k}")
+    if Y is None:
+        Y = torch.empty((M, desc.out_n), dtype=torch.bfloat16, device=X.device)
+    yp, ldy = _mat(Y, torch.bfloat16, "Y")
+    wsp, wsb = _ws(desc, M, ws)
+    _check(_lib.load().tp_col_linear(ctypes.byref(desc), xp, M, ldx,
+                                     ctypes.c_void_p(W_packed.data_ptr()), yp, ldy, wsp, wsb,
+                                     _stream(stream)), "tp_col_linear")
+    return Y
+
+
+def tp_row_linear(desc: TpShardDesc, Z: torch.Tensor, W_packed: torch.Tensor,
+                  P: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """Row-parallel linear: the fp32 partial P [M x N] of this rank."""
+    zp, ldz = _mat(Z, torch.bfloat16, "Z")
+    M = Z.size(0)
+    if Z.size(1) != desc.shard_k:
+        raise ValueError(f"Z has {Z.size(1)} columns, shard expects {desc.shard_k}")
+    if P is None:
+        P = torch.empty((M, desc.N), dtype=torch.float32, device=Z.device)
+    pp, ldp = _mat(P, torch.float32, "P")
+    wsp, wsb = _ws(desc, M, ws)
+    _check(_lib.load().tp_row_linear(ctypes.byref(desc), zp, M, ldz,
+                                     ctypes.c_void_p(W_packed.data_ptr()), pp, ldp, wsp, wsb,
+                                     _stream(stream)), "tp_row_linear")
+    return P
+
+
+def tp_ffn_shard(gateup: TpShardDesc, down: TpShardDesc, X: torch.Tensor, Wgu_packed: torch.Tensor,
+                 Wd_packed: torch.Tensor, H: torch.Tensor | None = None,
+                 P: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+    """One rank's feed-forward share; returns (H [M x I/t] bf16, P [M x hidden] fp32)."""
+    xp, ldx = _mat(X, torch.bfloat16, "X")
+    M = X.size(0)
+    if H is None:
+        H = torch.empty((M, gateup.out_n), dtype=torch.bfloat16, device=X.device)
+    if not H.is_contiguous() or tuple(H.shape) != (M, gateup.out_n) or H.dtype != torch.bfloat16:
+        raise ValueError("H must be a contiguous bf16 [M x I/t] tensor")
+    if P is None:
+        P = torch.empty((M, down.N), dtype=torch.float32, device=X.device)
+    pp, ldp = _mat(P, torch.float32, "P")
+    wsp, wsb = _ws(gateup, M, ws)
+    _check(_lib.load().tp_ffn_shard(ctypes.byref(gateup), ctypes.byref(down), xp, M, ldx,
+                                    ctypes.c_void_p(Wgu_packed.data_ptr()),
+                                    ctypes.c_void_p(Wd_packed.data_ptr()),
+                                    ctypes.c_void_p(H.data_ptr()), pp, ldp, wsp, wsb,
+                                    _stream(stream)), "tp_ffn_shard")
+    return H, P
+
+
+def tp_reduce_partials(P: torch.Tensor, Y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = P[0] + P[1] + ... + P[t-1] (fp32, rank order). ``P`` is [t x M x N]
+    with unit column stride; ``Y`` may be ``P[0]``."""
+    if P.dim() != 3 or P.dtype != torch.float32 or not P.is_cuda or P.stride(2) != 1:
+        raise ValueError("P must be a [t x M x N] fp32 device tensor with unit column stride")
+    t, M, N = P.shape
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=P.device)
+    yp, ldy = _mat(Y, torch.float32, "Y")
+    _check(_lib.load().tp_reduce_partials(ctypes.c_void_p(P.data_ptr()), P.stride(0), t, M, N,
+                                          max(P.stride(1), N), yp, ldy, _stream(stream)),
+           "tp_reduce_partials")
+    return Y

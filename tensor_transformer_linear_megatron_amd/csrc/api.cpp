@@ -1,0 +1,177 @@
+// The C-ABI entry points: host-side validation and kernel dispatch. Nothing
+// here allocates device memory or keeps state between calls.
+#include <cstdint>
+
+#include "tp_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_col(int32_t k) { return k == TP_COL || k == TP_QKV_COL || k == TP_GATEUP_COL; }
+bool is_row(int32_t k) { return k == TP_ROW || k == TP_O_ROW; }
+
+// Self-consistency of a caller-held descriptor (it is plain data the caller
+// may have edited).
+tp_status check_desc(const tp_shard_desc* d) {
+  if (d == nullptr) return TP_ERR_NULL;
+  if (!is_col(d->kind) && !is_row(d->kind)) return TP_ERR_KIND;
+  const bool gateup = d->kind == TP_GATEUP_COL;
+  if (d->shard_k <= 0 || d->shard_n <= 0 || d->out_n <= 0 || d->packed_k < d->shard_k ||
+      d->packed_k % tpk::kTileK || d->packed_n % tpk::kTileN ||
+      d->packed_bytes != d->packed_k * d->packed_n * 2)
+    return TP_ERR_SHAPE;
+  if (gateup) {
+    // gate and up tiles alternate: an even tile count, each half covering out_n
+    if (d->shard_n != 2 * d->out_n || d->packed_n % (2 * tpk::kTileN) || d->packed_n / 2 < d->out_n)
+      return TP_ERR_SHAPE;
+  } else if (d->out_n != d->shard_n || d->packed_n < d->shard_n) {
+    return TP_ERR_SHAPE;
+  }
+  if (d->shard_k % 8 || d->out_n % 8) return TP_ERR_ALIGN;
+  if (d->path < TP_PATH_AUTO || d->path > TP_PATH_PREFILL) return TP_ERR_KIND;
+  return TP_OK;
+}
+
+tpk::LinearArgs make_args(const tp_shard_desc* d, const uint16_t* X, int64_t M, int64_t ldx,
+                          const void* Wp, void* out, int64_t ldo) {
+  tpk::LinearArgs a;
+  a.X = X;
+  a.ldx = ldx;
+  a.M = M;
+  a.K = d->shard_k;
+  a.W = static_cast<const uint4*>(Wp);
+  a.ksteps = d->packed_k / tpk::kTileK;
+  a.ntiles = d->packed_n / tpk::kTileN;
+  a.out = out;
+  a.ldo = ldo;
+  a.out_n = d->out_n;
+  return a;
+}
+
+tp_status run_linear(const tp_shard_desc* d, const tpk::LinearArgs& a, tpk::Epilogue epi,
+                     hipStream_t s) {
+  int32_t path = d->path;
+  if (path == TP_PATH_AUTO) path = a.M <= 64 ? TP_PATH_DECODE : TP_PATH_PREFILL;
+  if (path == TP_PATH_DECODE && a.M > 64) return TP_ERR_SHAPE;
+  const hipError_t e = path == TP_PATH_DECODE ? tpk::launch_gemv(a, epi, s)
+                                              : tpk::launch_gemm(a, epi, s);
+  return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+}
+
+tp_status check_linear_io(const tp_shard_desc* d, const uint16_t* X, int64_t M, int64_t ldx,
+                          const void* Wp, const void* out, int64_t ldo, int64_t out_elem_align) {
+  if (M < 0) return TP_ERR_SHAPE;
+  if (M == 0) return TP_OK;  // nothing is read or written; empty tensors may have NULL data
+  if (X == nullptr || Wp == nullptr || out == nullptr) return TP_ERR_NULL;
+  if (ldx < d->shard_k || ldo < d->out_n) return TP_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(Wp) || !aligned16(out) || ldx % 8 || ldo % out_elem_align)
+    return TP_ERR_ALIGN;
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" size_t tp_workspace_bytes(const tp_shard_desc* desc, int64_t M) {
+  (void)desc;
+  (void)M;
+  return 0;  // every kernel reduces split-K partials inside its workgroup
+}
+
+extern "C" tp_status tp_shard_pack(const tp_shard_desc* d, const uint16_t* W, int64_t ldw,
+                                   void* W_packed, hipStream_t stream) {
+  tp_status st = check_desc(d);
+  if (st != TP_OK) return st;
+  if (W == nullptr || W_packed == nullptr) return TP_ERR_NULL;
+  if (ldw < d->N) return TP_ERR_SHAPE;
+  if (!aligned16(W_packed)) return TP_ERR_ALIGN;
+  if (d->row_begin < 0 || d->row_end > d->K || d->row_end - d->row_begin != d->shard_k ||
+      d->n_col_ranges < 1 || d->n_col_ranges > 3)
+    return TP_ERR_SHAPE;
+  tpk::PackArgs a;
+  a.W = W;
+  a.ldw = ldw;
+  a.out = static_cast<uint4*>(W_packed);
+  a.row_begin = d->row_begin;
+  a.shard_k = d->shard_k;
+  a.shard_n = d->shard_n;
+  a.out_n = d->out_n;
+  a.ksteps = d->packed_k / tpk::kTileK;
+  a.ntiles = d->packed_n / tpk::kTileN;
+  a.n_ranges = d->n_col_ranges;
+  a.gateup = d->kind == TP_GATEUP_COL;
+  for (int r = 0; r < 3; ++r) {
+    const tp_col_range c = r < d->n_col_ranges ? d->col_ranges[r] : tp_col_range{0, 0, 0};
+    if (r < d->n_col_ranges && (c.src_col < 0 || c.len < 0 || c.src_col + c.len > d->N ||
+                                c.dst_col < 0 || c.dst_col + c.len > d->shard_n))
+      return TP_ERR_SHAPE;
+    a.src[r] = c.src_col;
+    a.len[r] = c.len;
+    a.dst[r] = c.dst_col;
+  }
+  return tpk::launch_pack(a, stream) == hipSuccess ? TP_OK : TP_ERR_HIP;
+}
+
+extern "C" tp_status tp_col_linear(const tp_shard_desc* d, const uint16_t* X, int64_t M,
+                                   int64_t ldx, const void* W_packed, uint16_t* Y, int64_t ldy,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  tp_status st = check_desc(d);
+  if (st != TP_OK) return st;
+  if (!is_col(d->kind)) return TP_ERR_KIND;
+  st = check_linear_io(d, X, M, ldx, W_packed, Y, ldy, 8);
+  if (st != TP_OK || M == 0) return st;
+  const tpk::LinearArgs a = make_args(d, X, M, ldx, W_packed, Y, ldy);
+  return run_linear(d, a, d->kind == TP_GATEUP_COL ? tpk::kEpiSwiglu : tpk::kEpiBf16, stream);
+}
+
+extern "C" tp_status tp_row_linear(const tp_shard_desc* d, const uint16_t* Z, int64_t M,
+                                   int64_t ldz, const void* W_packed, float* P, int64_t ldp,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  tp_status st = check_desc(d);
+  if (st != TP_OK) return st;
+  if (!is_row(d->kind)) return TP_ERR_KIND;
+  st = check_linear_io(d, Z, M, ldz, W_packed, P, ldp, 4);
+  if (st != TP_OK || M == 0) return st;
+  const tpk::LinearArgs a = make_args(d, Z, M, ldz, W_packed, P, ldp);
+  return run_linear(d, a, tpk::kEpiF32, stream);
+}
+
+extern "C" tp_status tp_ffn_shard(const tp_shard_desc* gu, const tp_shard_desc* dn,
+                                  const uint16_t* X, int64_t M, int64_t ldx,
+                                  const void* Wgu_packed, const void* Wd_packed, uint16_t* H_ws,
+                                  float* P, int64_t ldp, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  tp_status st = check_desc(gu);
+  if (st != TP_OK) return st;
+  st = check_desc(dn);
+  if (st != TP_OK) return st;
+  if (gu->kind != TP_GATEUP_COL || dn->kind != TP_ROW) return TP_ERR_KIND;
+  if (gu->t != dn->t || gu->rank != dn->rank || gu->out_n != dn->shard_k || gu->K != dn->N)
+    return TP_ERR_SHAPE;
+  // Validate both halves before queueing either.
+  st = check_linear_io(gu, X, M, ldx, Wgu_packed, H_ws, gu->out_n, 8);
+  if (st != TP_OK) return st;
+  st = check_linear_io(dn, H_ws, M, gu->out_n, Wd_packed, P, ldp, 4);
+  if (st != TP_OK || M == 0) return st;
+  st = tp_col_linear(gu, X, M, ldx, Wgu_packed, H_ws, gu->out_n, ws, ws_bytes, stream);
+  if (st != TP_OK) return st;
+  return tp_row_linear(dn, H_ws, M, gu->out_n, Wd_packed, P, ldp, ws, ws_bytes, stream);
+}
+
+extern "C" tp_status tp_reduce_partials(const float* P, int64_t stride_elems, int32_t t, int64_t M,
+                                        int64_t N, int64_t ldp, float* Y, int64_t ldy,
+                                        hipStream_t stream) {
+  if (t <= 0 || M < 0 || N <= 0 || ldp < N || ldy < N) return TP_ERR_SHAPE;
+  if (M == 0) return TP_OK;
+  if (P == nullptr || Y == nullptr) return TP_ERR_NULL;
+  if (t > 1 && stride_elems < M * ldp) return TP_ERR_SHAPE;
+  if (!aligned16(P) || !aligned16(Y) || N % 4 || ldp % 4 || ldy % 4 || stride_elems % 4)
+    return TP_ERR_ALIGN;
+  return tpk::launch_reduce(P, stride_elems, t, M, N, ldp, Y, ldy, stream) == hipSuccess
+             ? TP_OK
+             : TP_ERR_HIP;
+}

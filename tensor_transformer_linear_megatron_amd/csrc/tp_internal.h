@@ -1,0 +1,94 @@
+// Internal declarations of the HIP library: packed-layout constants, device
+// helpers and kernel launchers. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "tp_shard.h"
+
+namespace tpk {
+
+// Packed weight layout (written by tp_shard_pack, read by every linear):
+// the shard, zero-padded to [packed_k x packed_n], is cut into tiles of
+// kTileN output columns x kTileK k. Tile (nt, ks) sits at tile index
+// nt * (packed_k / kTileK) + ks, 1 KiB each, so one tile column (all k of
+// 16 outputs) is contiguous. Inside a tile, lane l = 16 g + i of a wavefront
+// owns 16 bytes at offset 16 l: the 8 values W[ks*32 + 8g + e][nt*16 + i],
+// e = 0..7 -- exactly the A operand of v_mfma_f32_16x16x32_bf16 with output
+// columns as MFMA rows. A wavefront therefore loads a whole tile with one
+// fully coalesced 1 KiB dwordx4 load. For TP_GATEUP_COL the gate and up tiles
+// of the same 16 outputs are interleaved: packed tile 2j is gate tile j and
+// 2j + 1 is up tile j, so SwiGLU pairs sit in the same lanes.
+constexpr int kTileN = 16;
+constexpr int kTileK = 32;
+constexpr int kTileU4 = 64;  // uint4 per tile
+
+enum Epilogue { kEpiBf16 = 0, kEpiSwiglu = 1, kEpiF32 = 2 };
+
+// One linear: out = epilogue(X W_shard).
+struct LinearArgs {
+  const uint16_t* X;  // [M x K] bf16, leading dim ldx
+  int64_t ldx;
+  int64_t M;
+  int64_t K;          // valid k (shard_k); packed tiles are zero past it
+  const uint4* W;     // packed tiles
+  int64_t ksteps;     // packed_k / kTileK
+  int64_t ntiles;     // packed_n / kTileN
+  void* out;          // bf16 or fp32 [M x out_n], leading dim ldo
+  int64_t ldo;
+  int64_t out_n;      // valid output columns
+};
+
+struct PackArgs {
+  const uint16_t* W;
+  int64_t ldw;
+  uint4* out;
+  int64_t row_begin, shard_k, shard_n, out_n;
+  int64_t ksteps, ntiles;
+  int64_t src[3], len[3], dst[3];
+  int32_t n_ranges;
+  int32_t gateup;
+};
+
+hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+hipError_t launch_gemv(const LinearArgs& a, Epilogue epi, hipStream_t s);
+hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, hipStream_t s);
+hipError_t launch_reduce(const float* P, int64_t stride, int32_t t, int64_t M, int64_t N,
+                         int64_t ldp, float* Y, int64_t ldy, hipStream_t s);
+
+}  // namespace tpk
+
+#ifdef __HIPCC__
+namespace tpk {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// D = A B + C on one 16x16x32 bf16 MFMA. A: 16 output columns x 32 k (a
+// packed weight tile), B: 32 k x 16 tokens. Lane l = 16 g + i supplies
+// A[i][8g..8g+7] and B[8g..8g+7][i] and receives D[4g + r][i], r = 0..3.
+__device__ __forceinline__ f32x4_t mfma_16x16x32(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// SiLU(g) * u with SiLU(g) = g / (1 + e^-g). For g -> -inf, e^-g = inf and
+// the quotient is -0; for g -> +inf it is g.
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, float c, float d) {
+  uint2 v;
+  v.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  v.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+  *reinterpret_cast<uint2*>(p) = v;
+}
+
+}  // namespace tpk
+#endif

@@ -1,0 +1,203 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares,
+plans shards exactly as the oracle's independent planner does, and rejects
+bad arguments with the documented codes before any GPU work."""
+from __future__ import annotations
+
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import tensor_transformer_linear_megatron_amd as tp
+from tensor_transformer_linear_megatron_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CODES = {"indivisible": _lib.TP_ERR_INDIVISIBLE, "rank": _lib.TP_ERR_RANK,
+         "shape": _lib.TP_ERR_SHAPE, "kind": _lib.TP_ERR_KIND}
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "tp_shard.h")).read()
+    return sorted(set(re.findall(r"TP_API\s+[\w\s\*]+?\b(tp_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    lib = _lib.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    exported = set(re.findall(r" T (tp_\w+)", nm))
+    assert exported == set(names), exported ^ set(names)
+
+
+def test_status_strings():
+    for code in range(-8, 1):
+        assert tp.tp_status_str(code) not in ("", "unknown status")
+    assert tp.tp_status_str(-99) == "unknown status"
+
+
+def _expand(d):
+    rows = np.arange(d.row_begin, d.row_end)
+    cols = np.concatenate([np.arange(d.col_ranges[i].src_col, d.col_ranges[i].src_col + d.col_ranges[i].len)
+                           for i in range(d.n_col_ranges)])
+    dst = [d.col_ranges[i].dst_col for i in range(d.n_col_ranges)]
+    lens = [d.col_ranges[i].len for i in range(d.n_col_ranges)]
+    assert dst == list(np.cumsum([0] + lens[:-1]))  # ranges tile the shard in order
+    return rows, cols
+
+
+def _cases():
+    for kind in ("col", "row", "gateup_col"):
+        for K, N in ((64, 96), (4096, 4096), (8192, 57344), (128, 256)):
+            for t in (1, 2, 3, 4, 8):
+                for r in sorted({0, t // 2, t - 1}):
+                    yield kind, K, N, t, r, None
+    for (nq, nkv, d) in ((64, 8, 128), (32, 8, 64), (16, 4, 8), (8, 8, 16)):
+        for t in (1, 2, 3, 4, 6, 8, 16, 32):
+            for r in sorted({0, t // 2, t - 1}):
+                yield "qkv_col", 512, (nq + 2 * nkv) * d, t, r, (nq, nkv, d)
+                yield "o_row", nq * d, 256, t, r, (nq, nkv, d)
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,heads", list(_cases()))
+def test_plan_matches_oracle_planner(kind, K, N, t, r, heads):
+    try:
+        want = oracle.plan(kind, K, N, t, r, heads=heads)
+    except oracle.PlanError as e:
+        with pytest.raises(tp.TpError) as got:
+            tp.tp_shard_plan(kind, K, N, t, r, heads=heads)
+        assert got.value.status == CODES[e.code]
+        return
+    try:
+        d = tp.tp_shard_plan(kind, K, N, t, r, heads=heads)
+    except tp.TpError as e:  # the library may only add the 8-element alignment rule
+        assert e.status == _lib.TP_ERR_ALIGN
+        out_n = want["shard_n"] // 2 if kind == "gateup_col" else want["shard_n"]
+        assert want["shard_k"] % 8 or out_n % 8 or (heads and heads[2] % 8)
+        return
+    rows, cols = _expand(d)
+    np.testing.assert_array_equal(rows, want["rows"])
+    np.testing.assert_array_equal(cols, want["cols"])
+    assert (d.shard_k, d.shard_n, d.t, d.rank, d.K, d.N) == (want["shard_k"], want["shard_n"], t, r, K, N)
+    if heads is not None:
+        assert (d.q_head_begin, d.q_head_end) == want["q_heads"]
+        assert (d.kv_head_begin, d.kv_head_end) == want["kv_heads"]
+        assert bool(d.kv_replicated) == want["kv_replicated"]
+    assert d.out_n == (d.shard_n // 2 if kind == "gateup_col" else d.shard_n)
+    assert d.packed_k % 32 == 0 and d.packed_n % 16 == 0 and d.packed_k >= d.shard_k
+    assert d.packed_bytes == d.packed_k * d.packed_n * 2
+    assert d.path == tp.TP_PATH_AUTO
+
+
+def test_plan_error_codes():
+    lib = _lib.load()
+    d = tp.TpShardDesc()
+    assert lib.tp_shard_plan(0, 64, 64, 2, 0, None, None) == _lib.TP_ERR_NULL
+    assert lib.tp_shard_plan(9, 64, 64, 2, 0, None, ctypes.byref(d)) == _lib.TP_ERR_KIND
+    assert lib.tp_shard_plan(tp.TP_QKV_COL, 64, 64, 2, 0, None, ctypes.byref(d)) == _lib.TP_ERR_NULL
+    assert lib.tp_shard_plan(0, 64, 64, 0, 0, None, ctypes.byref(d)) == _lib.TP_ERR_SHAPE
+    assert lib.tp_shard_plan(0, 64, -8, 1, 0, None, ctypes.byref(d)) == _lib.TP_ERR_SHAPE
+    assert lib.tp_shard_plan(0, 64, 64, 2, 2, None, ctypes.byref(d)) == _lib.TP_ERR_RANK
+    assert lib.tp_shard_plan(0, 64, 96, 64, 0, None, ctypes.byref(d)) == _lib.TP_ERR_INDIVISIBLE
+    assert lib.tp_shard_plan(0, 64, 48, 8, 0, None, ctypes.byref(d)) == _lib.TP_ERR_ALIGN  # 6 columns
+    assert lib.tp_shard_plan(0, 60, 64, 1, 0, None, ctypes.byref(d)) == _lib.TP_ERR_ALIGN  # K % 8
+    h = _lib.TpHeads(64, 8, 128)
+    for t in (3, 5, 6, 7):
+        assert lib.tp_shard_plan(tp.TP_QKV_COL, 8192, 10240, t, 0, ctypes.byref(h), ctypes.byref(d)) \
+            == _lib.TP_ERR_INDIVISIBLE
+    assert lib.tp_shard_plan(tp.TP_QKV_COL, 8192, 10000, 8, 0, ctypes.byref(h), ctypes.byref(d)) \
+        == _lib.TP_ERR_SHAPE
+
+
+def test_worked_tp2_split_through_the_abi(golden):
+    g = golden("tp2_worked_split.json")
+    for r in range(2):
+        d = tp.tp_shard_plan("col", 4096, 4096, 2, r)
+        assert [d.shard_k, d.shard_n] == g["column_shards"][r]
+        assert d.packed_bytes == 4096 * 2048 * 2
+        e = tp.tp_shard_plan("row", 4096, 4096, 2, r)
+        assert [e.shard_k, e.shard_n] == g["row_shards"][r]
+
+
+# Fake, 16-byte aligned host addresses: every call below is rejected on the
+# host before anything is queued, so they are never dereferenced.
+A = ctypes.c_void_p(0x100000)
+B = ctypes.c_void_p(0x200000)
+C = ctypes.c_void_p(0x300000)
+MIS = ctypes.c_void_p(0x100008)
+NUL = ctypes.c_void_p(0)
+
+
+def test_linear_argument_errors():
+    lib = _lib.load()
+    col = tp.tp_shard_plan("col", 64, 64, 2, 0)
+    row = tp.tp_shard_plan("row", 64, 64, 2, 0)
+    gu = tp.tp_shard_plan("gateup_col", 64, 128, 2, 0)
+    dn = tp.tp_shard_plan("row", 64, 64, 2, 0)
+    cb, rb = ctypes.byref(col), ctypes.byref(row)
+    S = ctypes.c_void_p(0)
+    assert lib.tp_col_linear(None, A, 4, 64, B, C, 32, NUL, 0, S) == _lib.TP_ERR_NULL
+    assert lib.tp_col_linear(cb, NUL, 4, 64, B, C, 32, NUL, 0, S) == _lib.TP_ERR_NULL
+    assert lib.tp_col_linear(cb, A, 4, 64, NUL, C, 32, NUL, 0, S) == _lib.TP_ERR_NULL
+    assert lib.tp_col_linear(cb, A, -1, 64, B, C, 32, NUL, 0, S) == _lib.TP_ERR_SHAPE
+    assert lib.tp_col_linear(cb, A, 4, 56, B, C, 32, NUL, 0, S) == _lib.TP_ERR_SHAPE   # ldx < K
+    assert lib.tp_col_linear(cb, A, 4, 64, B, C, 24, NUL, 0, S) == _lib.TP_ERR_SHAPE   # ldy < out_n
+    assert lib.tp_col_linear(cb, MIS, 4, 64, B, C, 32, NUL, 0, S) == _lib.TP_ERR_ALIGN
+    assert lib.tp_col_linear(cb, A, 4, 68, B, C, 32, NUL, 0, S) == _lib.TP_ERR_ALIGN   # ldx % 8
+    assert lib.tp_col_linear(rb, A, 4, 64, B, C, 32, NUL, 0, S) == _lib.TP_ERR_KIND
+    assert lib.tp_col_linear(cb, A, 0, 64, B, C, 32, NUL, 0, S) == _lib.TP_OK          # M == 0: no-op
+    assert lib.tp_col_linear(cb, NUL, 0, 64, NUL, NUL, 32, NUL, 0, S) == _lib.TP_OK
+    assert lib.tp_row_linear(cb, A, 4, 32, B, C, 64, NUL, 0, S) == _lib.TP_ERR_KIND
+    assert lib.tp_row_linear(rb, A, 4, 32, B, C, 62, NUL, 0, S) == _lib.TP_ERR_SHAPE  # ldp < N
+    assert lib.tp_row_linear(rb, A, 4, 32, B, C, 66, NUL, 0, S) == _lib.TP_ERR_ALIGN  # ldp % 4
+    assert lib.tp_row_linear(rb, A, 0, 32, B, C, 64, NUL, 0, S) == _lib.TP_OK
+    forced = col.copy()
+    forced.path = tp.TP_PATH_DECODE
+    assert lib.tp_col_linear(ctypes.byref(forced), A, 65, 64, B, C, 32, NUL, 0, S) == _lib.TP_ERR_SHAPE
+    forced.path = 7
+    assert lib.tp_col_linear(ctypes.byref(forced), A, 4, 64, B, C, 32, NUL, 0, S) == _lib.TP_ERR_KIND
+    broken = col.copy()
+    broken.packed_bytes += 2
+    assert lib.tp_col_linear(ctypes.byref(broken), A, 4, 64, B, C, 32, NUL, 0, S) == _lib.TP_ERR_SHAPE
+    # the feed-forward pairing: same t and rank, I/t of gate/up == k of down
+    g, d = ctypes.byref(gu), ctypes.byref(dn)
+    assert lib.tp_ffn_shard(g, d, A, 0, 64, B, B, C, A, 64, NUL, 0, S) == _lib.TP_OK
+    assert lib.tp_ffn_shard(d, g, A, 4, 64, B, B, C, A, 64, NUL, 0, S) == _lib.TP_ERR_KIND
+    other = tp.tp_shard_plan("row", 64, 64, 2, 1)
+    assert lib.tp_ffn_shard(g, ctypes.byref(other), A, 4, 64, B, B, C, A, 64, NUL, 0, S) == _lib.TP_ERR_SHAPE
+    wide = tp.tp_shard_plan("row", 128, 64, 2, 0)
+    assert lib.tp_ffn_shard(g, ctypes.byref(wide), A, 4, 64, B, B, C, A, 64, NUL, 0, S) == _lib.TP_ERR_SHAPE
+    assert lib.tp_ffn_shard(g, d, A, 4, 64, B, B, NUL, A, 64, NUL, 0, S) == _lib.TP_ERR_NULL
+    assert lib.tp_ffn_shard(g, d, A, 4, 64, B, B, C, MIS, 64, NUL, 0, S) == _lib.TP_ERR_ALIGN
+
+
+def test_reduce_and_pack_argument_errors():
+    lib = _lib.load()
+    S = ctypes.c_void_p(0)
+    assert lib.tp_reduce_partials(NUL, 256, 2, 4, 64, 64, A, 64, S) == _lib.TP_ERR_NULL
+    assert lib.tp_reduce_partials(A, 256, 0, 4, 64, 64, B, 64, S) == _lib.TP_ERR_SHAPE
+    assert lib.tp_reduce_partials(A, 255, 2, 4, 64, 64, B, 64, S) == _lib.TP_ERR_SHAPE  # stride < M ld
+    assert lib.tp_reduce_partials(A, 256, 2, 4, 62, 64, B, 64, S) == _lib.TP_ERR_ALIGN  # N % 4
+    assert lib.tp_reduce_partials(MIS, 256, 2, 4, 64, 64, B, 64, S) == _lib.TP_ERR_ALIGN
+    assert lib.tp_reduce_partials(A, 256, 2, 0, 64, 64, B, 64, S) == _lib.TP_OK
+    assert lib.tp_reduce_partials(NUL, 256, 2, 0, 64, 64, NUL, 64, S) == _lib.TP_OK
+    col = tp.tp_shard_plan("col", 64, 64, 2, 0)
+    assert lib.tp_shard_pack(ctypes.byref(col), NUL, 64, B, S) == _lib.TP_ERR_NULL
+    assert lib.tp_shard_pack(ctypes.byref(col), A, 32, B, S) == _lib.TP_ERR_SHAPE
+    assert lib.tp_shard_pack(ctypes.byref(col), A, 64, MIS, S) == _lib.TP_ERR_ALIGN
+    bad = col.copy()
+    bad.col_ranges[0].src_col = 60
+    assert lib.tp_shard_pack(ctypes.byref(bad), A, 64, B, S) == _lib.TP_ERR_SHAPE
+
+
+def test_workspace_is_zero():
+    for kind, K, N in (("col", 4096, 4096), ("gateup_col", 8192, 57344), ("row", 28672, 8192)):
+        d = tp.tp_shard_plan(kind, K, N, 8, 0)
+        for M in (1, 64, 8192):
+            assert tp.tp_workspace_bytes(d, M) == 0

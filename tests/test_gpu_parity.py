@@ -1,0 +1,448 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs, at small ragged sizes and at the full model-shaped sizes.
+
+Bar: bit-exact for the shard bookkeeping and packing, for integer-valued and
+identity inputs; relative Frobenius error <= 1e-3 and max element error
+<= 1e-2 * max |oracle| otherwise.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+import tensor_transformer_linear_megatron_amd as tp
+from seeded_inputs import workloads as wl
+from tputil import assert_parity, dev, full_device, host_bits, host_f64, say, unpack
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def plan_both(kind, K, N, t, r, heads=None):
+    return tp.tp_shard_plan(kind, K, N, t, r, heads=heads), oracle.plan(kind, K, N, t, r, heads=heads)
+
+
+def with_path(d, path):
+    e = d.copy()
+    e.path = path
+    return e
+
+
+# ---------------------------------------------------------------------------
+# Packing and bookkeeping: bit-exact.
+# ---------------------------------------------------------------------------
+
+PACK_CASES = [("col", 96, 64, 2, 1, None), ("col", 264, 40, 1, 0, None), ("row", 96, 72, 3, 2, None),
+              ("gateup_col", 72, 2 * 24, 1, 0, None), ("gateup_col", 40, 2 * 96, 4, 3, None),
+              ("qkv_col", 64, (8 + 2 * 2) * 16, 4, 1, (8, 2, 16)),
+              ("qkv_col", 64, (8 + 2 * 2) * 16, 8, 5, (8, 2, 16)),
+              ("o_row", 8 * 16, 48, 4, 3, (8, 2, 16)), ("col", 4096, 4096, 2, 1, None)]
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,heads", PACK_CASES)
+def test_pack_is_the_planned_shard(kind, K, N, t, r, heads):
+    say("pack", kind, K, N, t, r, heads)
+    W = si.normal_bf16(21, (K, N), 1.0)
+    d, p = plan_both(kind, K, N, t, r, heads)
+    packed = tp.tp_shard_pack(d, dev(W))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(unpack(d, packed), W[np.ix_(p["rows"], p["cols"])])
+    # the zero padding is really zero
+    total = host_bits(packed.view(torch.bfloat16).view(1, -1))
+    assert np.count_nonzero(total) <= d.shard_k * d.shard_n
+
+
+# ---------------------------------------------------------------------------
+# Small, ragged shapes spanning several tiles, both paths.
+# ---------------------------------------------------------------------------
+
+def _col_case(kind, K, N, t, r, M, path, heads=None, seed=30):
+    X = si.normal_bf16(seed, (M, K), 1.0)
+    W = si.normal_bf16(seed + 1, (K, N), 0.05)
+    d, p = plan_both(kind, K, N, t, r, heads)
+    d = with_path(d, path)
+    Wp = tp.tp_shard_pack(d, dev(W))
+    Y = tp.tp_col_linear(d, dev(X), Wp)
+    if kind == "gateup_col":
+        ref = oracle.bf16_to_f64(oracle.gateup_swiglu(X, W, p))
+    else:
+        ref = oracle.bf16_to_f64(oracle.col_linear_bf16(X, W, p))
+    return host_f64(Y), ref
+
+
+def _row_case(kind, K, N, t, r, M, path, heads=None, seed=40):
+    Z = si.normal_bf16(seed, (M, K), 1.0)
+    W = si.normal_bf16(seed + 1, (K, N), 0.05)
+    d, p = plan_both(kind, K, N, t, r, heads)
+    d = with_path(d, path)
+    Zr = Z[:, p["rows"]]
+    P = tp.tp_row_linear(d, dev(Zr), tp.tp_shard_pack(d, dev(W)))
+    return host_f64(P), oracle.row_linear(Zr, W, p)
+
+
+SMALL_M = [1, 3, 16, 17, 33, 64, 65, 130, 257]
+SMALL_SHAPES = [(8, 32), (40, 24), (264, 136), (1000, 200)]
+PATHS = [tp.TP_PATH_AUTO, tp.TP_PATH_PREFILL]
+
+
+@pytest.mark.parametrize("M", SMALL_M)
+@pytest.mark.parametrize("K,N", SMALL_SHAPES)
+@pytest.mark.parametrize("path", PATHS)
+def test_col_small(M, K, N, path):
+    say("col small", M, K, N, path)
+    got, ref = _col_case("col", K, N, 1, 0, M, path)
+    assert_parity(got, ref, f"col M={M} K={K} N={N} path={path}")
+
+
+@pytest.mark.parametrize("M", SMALL_M)
+@pytest.mark.parametrize("path", PATHS)
+def test_gateup_small(M, path):
+    say("gateup small", M, path)
+    for K, inter, t, r in ((40, 24, 1, 0), (264, 96, 4, 2), (1000, 48, 2, 1)):
+        got, ref = _col_case("gateup_col", K, 2 * inter, t, r, M, path)
+        assert_parity(got, ref, f"gateup M={M} K={K} I={inter} t={t} r={r}")
+
+
+@pytest.mark.parametrize("M", SMALL_M)
+@pytest.mark.parametrize("path", PATHS)
+def test_row_small(M, path):
+    say("row small", M, path)
+    for K, N, t, r in ((64, 24, 2, 1), (528, 136, 2, 0), (2000, 40, 5, 4)):
+        got, ref = _row_case("row", K, N, t, r, M, path)
+        assert_parity(got, ref, f"row M={M} K={K} N={N} t={t} r={r}")
+
+
+@pytest.mark.parametrize("M", [1, 64, 200])
+def test_attention_kinds_small(M):
+    say("qkv/o small", M)
+    heads = (8, 2, 16)
+    for t in (1, 2, 4, 8):
+        for r in range(t):
+            got, ref = _col_case("qkv_col", 64, (8 + 4) * 16, t, r, M, tp.TP_PATH_AUTO, heads)
+            assert_parity(got, ref, f"qkv t={t} r={r}")
+            got, ref = _row_case("o_row", 8 * 16, 40, t, r, M, tp.TP_PATH_AUTO, heads)
+            assert_parity(got, ref, f"o t={t} r={r}")
+
+
+def test_m_zero_is_a_noop():
+    d = tp.tp_shard_plan("col", 64, 64, 1, 0)
+    Wp = tp.tp_shard_pack(d, dev(si.normal_bf16(1, (64, 64), 1.0)))
+    Y = torch.full((0, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    tp.tp_col_linear(d, torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), Wp, Y)
+    r = tp.tp_shard_plan("row", 64, 64, 1, 0)
+    tp.tp_row_linear(r, torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), Wp)
+
+
+# ---------------------------------------------------------------------------
+# Exact inputs: bit-exact on the GPU.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 8, 64, 130])
+@pytest.mark.parametrize("path", PATHS)
+def test_exact_integers_bit_exact(M, path):
+    """X, W in {-3..3}: every fp32 partial sum is an integer below 2^24, so the
+    GPU's sums are exact in any order and must match the oracle bit for bit
+    (the bf16 rounding of an exact integer is the same on both sides)."""
+    say("exact ints", M, path)
+    K, N, t = 4096, 512, 4
+    X = si.int_bf16(50, (M, K), -3, 3)
+    W = si.int_bf16(51, (K, N), -3, 3)
+    W2 = si.int_bf16(52, (N, K), -3, 3)
+    Ps, Ps_ref = [], []
+    for r in range(t):
+        dc, pc = plan_both("col", K, N, t, r)
+        dc = with_path(dc, path)
+        Y = tp.tp_col_linear(dc, dev(X), tp.tp_shard_pack(dc, dev(W)))
+        want_y = oracle.col_linear_bf16(X, W, pc)
+        np.testing.assert_array_equal(host_bits(Y), want_y)
+        dr, pr = plan_both("row", N, K, t, r)
+        dr = with_path(dr, path)
+        P = tp.tp_row_linear(dr, Y, tp.tp_shard_pack(dr, dev(W2)))
+        Ps_ref.append(oracle.row_linear(want_y, W2, pr))
+        np.testing.assert_array_equal(host_f64(P), Ps_ref[-1])
+        Ps.append(P)
+    Yr = tp.tp_reduce_partials(torch.stack(Ps))
+    np.testing.assert_array_equal(host_f64(Yr), oracle.sum_partials(np.stack(Ps_ref)))
+
+
+@pytest.mark.parametrize("M", [5, 64, 100])
+def test_identity_weight_bit_exact(M):
+    say("identity", M)
+    n = 256
+    X = si.normal_bf16(60, (M, n), 1.0)
+    I = si.identity_bf16(n)
+    parts = []
+    for t in (1, 4):
+        for r in range(t):
+            dc, pc = plan_both("col", n, n, t, r)
+            Y = tp.tp_col_linear(dc, dev(X), tp.tp_shard_pack(dc, dev(I)))
+            np.testing.assert_array_equal(host_bits(Y), X[:, pc["cols"]])
+            dr, pr = plan_both("row", n, n, t, r)
+            parts.append(tp.tp_row_linear(dr, dev(X[:, pr["rows"]]), tp.tp_shard_pack(dr, dev(I))))
+        Y = tp.tp_reduce_partials(torch.stack(parts[-t:]))
+        np.testing.assert_array_equal(host_f64(Y), si.bf16_bits_to_f32(X).astype(np.float64))
+
+
+def test_permutation_weight_bit_exact():
+    X = si.normal_bf16(61, (70, 128), 1.0)
+    W, perm = si.permutation_bf16(62, 128)
+    d = tp.tp_shard_plan("col", 128, 128, 1, 0)
+    for path in PATHS:
+        Y = tp.tp_col_linear(with_path(d, path), dev(X), tp.tp_shard_pack(d, dev(W)))
+        np.testing.assert_array_equal(host_bits(Y), X[:, perm])
+
+
+# ---------------------------------------------------------------------------
+# Reduction.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("t", [1, 2, 3, 8])
+@pytest.mark.parametrize("M,N", [(1, 8), (7, 4100), (64, 8192)])
+def test_reduce_partials(t, M, N):
+    say("reduce", t, M, N)
+    P = si.normal_f32(t * 1000 + M, (t * M, N), 1.0).reshape(t, M, N)
+    want = oracle.sum_partials(P.astype(np.float64))
+    Pd = torch.from_numpy(P).cuda()
+    got = host_f64(tp.tp_reduce_partials(Pd))
+    assert_parity(got, want, "reduce")
+    # fp32 rank-order sum is exactly what a sequential fp32 loop gives
+    seq = P[0].copy()
+    for r in range(1, t):
+        seq = seq + P[r]
+    np.testing.assert_array_equal(got, seq.astype(np.float64))
+    tp.tp_reduce_partials(Pd, Y=Pd[0])  # in place into slot 0
+    np.testing.assert_array_equal(host_f64(Pd[0]), got)
+
+
+# ---------------------------------------------------------------------------
+# The two paths where both are legal, determinism, composition.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [16, 64])
+def test_decode_and_prefill_agree_at_boundary(M):
+    say("boundary", M)
+    K, N = 4096, 1024
+    X = si.normal_bf16(70, (M, K), 1.0)
+    W = si.normal_bf16(71, (K, 2 * N), 0.02)
+    d, p = plan_both("gateup_col", K, 2 * N, 2, 1)
+    Wp = tp.tp_shard_pack(d, dev(W))
+    ref = oracle.bf16_to_f64(oracle.gateup_swiglu(X, W, p))
+    a = tp.tp_col_linear(with_path(d, tp.TP_PATH_DECODE), dev(X), Wp)
+    b = tp.tp_col_linear(with_path(d, tp.TP_PATH_PREFILL), dev(X), Wp)
+    assert_parity(host_f64(a), ref, "decode")
+    assert_parity(host_f64(b), ref, "prefill")
+    assert_parity(host_f64(a), host_f64(b), "decode vs prefill")
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    return t.cpu().view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
+def test_repeat_runs_are_bit_identical():
+    K, N = 4096, 2048
+    X = dev(si.normal_bf16(80, (48, K), 1.0))
+    W = dev(si.normal_bf16(81, (K, N), 0.02))
+    for kind, path in (("col", tp.TP_PATH_DECODE), ("col", tp.TP_PATH_PREFILL),
+                       ("row", tp.TP_PATH_DECODE), ("row", tp.TP_PATH_PREFILL)):
+        d = with_path(tp.tp_shard_plan(kind, K, N, 2, 1), path)
+        Wp = tp.tp_shard_pack(d, W)
+        f = tp.tp_col_linear if kind == "col" else tp.tp_row_linear
+        x = X if kind == "col" else X[:, :d.shard_k].contiguous()
+        assert torch.equal(_bits(f(d, x, Wp)), _bits(f(d, x, Wp))), (kind, path)
+
+
+def test_ffn_shard_is_col_then_row_and_ldy_slices():
+    K, inter, t = 512, 384, 3
+    X = si.normal_bf16(90, (9, K), 1.0)
+    Wgu = si.normal_bf16(91, (K, 2 * inter), 0.05)
+    Wd = si.normal_bf16(92, (inter, K), 0.05)
+    for r in range(t):
+        gu = tp.tp_shard_plan("gateup_col", K, 2 * inter, t, r)
+        dn = tp.tp_shard_plan("row", inter, K, t, r)
+        gp, dp = tp.tp_shard_pack(gu, dev(Wgu)), tp.tp_shard_pack(dn, dev(Wd))
+        H, P = tp.tp_ffn_shard(gu, dn, dev(X), gp, dp)
+        H2 = tp.tp_col_linear(gu, dev(X), gp)
+        P2 = tp.tp_row_linear(dn, H2, dp)
+        assert torch.equal(H.view(torch.int16), H2.view(torch.int16))
+        assert torch.equal(P.view(torch.int32), P2.view(torch.int32))
+    # column outputs written through ldy into a wider buffer: concatenation
+    W = si.normal_bf16(93, (K, 256), 0.05)
+    full = torch.full((9, 256 + 8), 5.0, dtype=torch.bfloat16, device="cuda")
+    for r in range(2):
+        d = tp.tp_shard_plan("col", K, 256, 2, r)
+        tp.tp_col_linear(d, dev(X), tp.tp_shard_pack(d, dev(W)), Y=full[:, r * 128:(r + 1) * 128])
+    p1 = oracle.plan("col", K, 256, 1, 0)
+    assert_parity(host_f64(full[:, :256]), oracle.bf16_to_f64(oracle.col_linear_bf16(X, W, p1)), "concat")
+    assert torch.all(full[:, 256:] == 5.0)
+
+
+# ---------------------------------------------------------------------------
+# The model-shaped workloads at full size.
+# ---------------------------------------------------------------------------
+
+def test_worked_tp2_split_full():
+    """X [8 x 4096]; W 4096 x 4096 cut into two 4096 x 2048 column shards; W2
+    4096 x 4096 cut into two 2048 x 4096 row shards; both ranks in turn on one
+    GPU; partials summed; against the unsharded bf16(X W) W2."""
+    say("worked TP=2 full")
+    X, W, W2 = wl.worked_tp2()
+    Xd, Wd_, W2d = dev(X), dev(W), dev(W2)
+    P = torch.empty((2, 8, 4096), dtype=torch.float32, device="cuda")
+    Ys = []
+    for r in range(2):
+        dc, pc = plan_both("col", 4096, 4096, 2, r)
+        dr, pr = plan_both("row", 4096, 4096, 2, r)
+        assert (dc.shard_k, dc.shard_n, dr.shard_k, dr.shard_n) == (4096, 2048, 2048, 4096)
+        Y = tp.tp_col_linear(dc, Xd, tp.tp_shard_pack(dc, Wd_))
+        tp.tp_row_linear(dr, Y, tp.tp_shard_pack(dr, W2d), P=P[r])
+        assert_parity(host_f64(Y), oracle.bf16_to_f64(oracle.col_linear_bf16(X, W, pc)), f"Y_{r}")
+        Ys.append(host_f64(Y))
+    out = host_f64(tp.tp_reduce_partials(P))
+    Yref = oracle.col_linear_bf16(X, W, oracle.plan("col", 4096, 4096, 1, 0))
+    ref = oracle.row_linear(Yref, W2, oracle.plan("row", 4096, 4096, 1, 0))
+    assert_parity(np.concatenate(Ys, axis=1), oracle.bf16_to_f64(Yref), "concat Y")
+    assert_parity(out, ref, "sum of partials vs unsharded")
+
+
+@pytest.fixture(scope="module")
+def llama8b():
+    c = wl.LLAMA8B
+    H, I = c["hidden"], c["inter"]
+    X = wl.activations(64, H)
+    Wgu = wl.gateup(H, I, c["sigma"])
+    Wd = wl.down(I, H, c["sigma"])
+    gu, pgu = plan_both("gateup_col", H, 2 * I, 1, 0)
+    dn, pdn = plan_both("row", I, H, 1, 0)
+    gp = tp.tp_shard_pack(gu, dev(Wgu))
+    dp = tp.tp_shard_pack(dn, dev(Wd))
+    torch.cuda.synchronize()
+    yield dict(X=X, Wgu=Wgu, Wd=Wd, gu=gu, dn=dn, pgu=pgu, pdn=pdn, gp=gp, dp=dp)
+    del gp, dp
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M", [1, 8, 32, 64])
+def test_llama8b_ffn_tp1_decode(llama8b, M):
+    say("llama8b ffn", M)
+    w = llama8b
+    X = w["X"][:M]
+    H, P = tp.tp_ffn_shard(w["gu"], w["dn"], dev(X), w["gp"], w["dp"])
+    Y = tp.tp_reduce_partials(P.unsqueeze(0))
+    Href, Pref = oracle.ffn_shard(X, w["Wgu"], w["Wd"], w["pgu"], w["pdn"])
+    assert_parity(host_f64(H), oracle.bf16_to_f64(Href), "H")
+    assert_parity(host_f64(P), Pref, "P")
+    np.testing.assert_array_equal(host_f64(Y), host_f64(P))  # t = 1: the sum is the partial
+
+
+@pytest.fixture(scope="module")
+def llama70b_ffn():
+    c = wl.LLAMA70B
+    H, I, t = c["hidden"], c["inter"], 8
+    X = wl.activations(32, H)
+    Wgu = wl.gateup(H, I, c["sigma"])
+    Wd = wl.down(I, H, c["sigma"])
+    Wgu_d, Wd_d = dev(Wgu), dev(Wd)
+    ranks = []
+    for r in range(t):
+        gu, pgu = plan_both("gateup_col", H, 2 * I, t, r)
+        dn, pdn = plan_both("row", I, H, t, r)
+        assert (gu.shard_k, gu.shard_n, dn.shard_k, dn.shard_n) == (8192, 7168, 3584, 8192)
+        ranks.append(dict(gu=gu, dn=dn, pgu=pgu, pdn=pdn, gp=tp.tp_shard_pack(gu, Wgu_d),
+                          dp=tp.tp_shard_pack(dn, Wd_d)))
+    del Wgu_d, Wd_d
+    torch.cuda.synchronize()
+    yield dict(X=X, Wgu=Wgu, Wd=Wd, ranks=ranks, t=t)
+    ranks.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_llama70b_ffn_tp8_all_ranks(llama70b_ffn, M):
+    say("llama70b ffn tp8", M)
+    w = llama70b_ffn
+    X = w["X"][:M]
+    Xd = dev(X)
+    P = torch.empty((w["t"], M, 8192), dtype=torch.float32, device="cuda")
+    for r, rk in enumerate(w["ranks"]):
+        tp.tp_ffn_shard(rk["gu"], rk["dn"], Xd, rk["gp"], rk["dp"], P=P[r])
+    Y = host_f64(tp.tp_reduce_partials(P))
+    rk = w["ranks"][0]
+    H0, P0 = oracle.ffn_shard(X, w["Wgu"], w["Wd"], rk["pgu"], rk["pdn"])
+    assert_parity(host_f64(P[0]), P0, "rank 0 partial")
+    rows = list(range(M)) if M <= 8 else [0, 5, 17, 31]
+    ref = oracle.ffn_unsharded(X[rows], w["Wgu"], w["Wd"])
+    assert_parity(Y[rows], ref, "sum over 8 ranks vs unsharded FFN")
+
+
+SAMPLE_ROWS_4096 = [0, 1, 15, 16, 127, 128, 129, 1000, 2047, 2048, 3071, 4094, 4095]
+
+
+def test_llama70b_attention_tp8_prefill():
+    """Rank 0's QKV column slice (8 Q + 1 K + 1 V head: 8192 x 1280) and O row
+    slice (1024 x 8192) at 4096 tokens; the O partials of all 8 ranks summed
+    against the unsharded projection, on sampled rows."""
+    say("llama70b attention tp8 prefill")
+    c = wl.LLAMA70B
+    heads = (c["n_q"], c["n_kv"], c["head_dim"])
+    Hd, t, M = c["hidden"], 8, 4096
+    X = wl.activations(M, Hd)
+    A = wl.attention_output(M, c["n_q"] * c["head_dim"])
+    Wqkv = wl.qkv_weight(Hd, *heads, c["sigma"])
+    Wo = wl.o_weight(c["n_q"], c["head_dim"], Hd, c["sigma"])
+    Xd, Ad, Wqkv_d, Wo_d = dev(X), dev(A), dev(Wqkv), dev(Wo)
+    rows = SAMPLE_ROWS_4096
+    P = torch.empty((t, M, Hd), dtype=torch.float32, device="cuda")
+    for r in range(t):
+        dq, pq = plan_both("qkv_col", Hd, Wqkv.shape[1], t, r, heads)
+        do, po = plan_both("o_row", c["n_q"] * c["head_dim"], Hd, t, r, heads)
+        assert (dq.shard_n, do.shard_k) == (1280, 1024)
+        QKV = tp.tp_col_linear(dq, Xd, tp.tp_shard_pack(dq, Wqkv_d))
+        Ar = Ad[:, do.row_begin:do.row_end].contiguous()
+        tp.tp_row_linear(do, Ar, tp.tp_shard_pack(do, Wo_d), P=P[r])
+        if r in (0, 7):
+            got = host_f64(QKV)[rows]
+            assert_parity(got, oracle.bf16_to_f64(oracle.col_linear_bf16(X[rows], Wqkv, pq)), f"QKV_{r}")
+            assert_parity(host_f64(P[r])[rows], oracle.row_linear(A[rows][:, po["rows"]], Wo, po), f"O_{r}")
+    Y = host_f64(tp.tp_reduce_partials(P))[rows]
+    ref = oracle.row_linear(A[rows], Wo, oracle.plan("o_row", 8192, 8192, 1, 0, heads=heads))
+    assert_parity(Y, ref, "O partials summed over 8 ranks vs unsharded")
+
+
+def test_llama405b_ffn_tp8_rank0_prefill():
+    """Rank 0's feed-forward share at 8192 tokens: gate/up 16384 x 13312 with
+    SwiGLU, down 6656 x 16384, fp32 partial; checked on sampled rows."""
+    say("llama405b ffn tp8 rank0 prefill")
+    c = wl.LLAMA405B
+    Hd, I, t, M, r = c["hidden"], c["inter"], 8, 8192, 0
+    w = I // t
+    X = wl.activations(M, Hd)
+    gu, pgu = plan_both("gateup_col", Hd, 2 * I, t, r)
+    dn, pdn = plan_both("row", I, Hd, t, r)
+    assert (gu.shard_k, gu.shard_n, dn.shard_k, dn.shard_n) == (16384, 13312, 6656, 16384)
+    cols = range(r * w, (r + 1) * w)
+    Wgu_r = wl.gateup(Hd, I, c["sigma"], cols=cols)     # [Wg[:, cols] | Wu[:, cols]]
+    Wd_r = wl.down(I, Hd, c["sigma"], rows=cols)
+    Wgu_full = full_device((Hd, 2 * I), [(range(0, Hd), cols, Wgu_r[:, :w]),
+                                         (range(0, Hd), range(I + cols.start, I + cols.stop), Wgu_r[:, w:])])
+    gp = tp.tp_shard_pack(gu, Wgu_full)
+    del Wgu_full
+    Wd_full = full_device((I, Hd), [(cols, range(0, Hd), Wd_r)])
+    dp = tp.tp_shard_pack(dn, Wd_full)
+    del Wd_full
+    H, P = tp.tp_ffn_shard(gu, dn, dev(X), gp, dp)
+    rows = [0, 1, 127, 128, 4095, 4096, 8190, 8191]
+    local = oracle.plan("gateup_col", Hd, 2 * w, 1, 0)  # the rank's block, columns in shard order
+    Href = oracle.gateup_swiglu(X[rows], Wgu_r, local)
+    Pref = oracle.row_linear(Href, Wd_r, oracle.plan("row", w, Hd, 1, 0))
+    assert_parity(host_f64(H)[rows], oracle.bf16_to_f64(Href), "H_0")
+    assert_parity(host_f64(P)[rows], Pref, "P_0")
