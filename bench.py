@@ -1,0 +1,303 @@
+"""Benchmark of one tensor-parallel rank's linear share on one MI355X.
+
+Headline (the decode half of the metric): the Llama-3.1-8B-shaped feed-forward
+share at TP = 1 -- gate/up column GEMV with fused SwiGLU (4096 x 28672), down
+row GEMV to an fp32 partial (14336 x 4096), and the partial sum -- for the
+decode batches M = 1, 8, 32 and 64. One step runs the four batches, each on
+its own copy of the layer's packed weights, so every call streams its weights
+from HBM (the copies total 1.4 GB, far beyond the 256 MB last-level cache).
+``value`` is algorithmic bytes / time (HBM GB/s) over the timed steps.
+
+Secondary (the prefill half): rank 0 of TP = 8 of the Llama-3.1-405B-shaped
+feed-forward layer at 8192 tokens (gate/up 16384 x 13312 + SwiGLU, down
+6656 x 16384 to an fp32 partial), in bf16 TFLOP/s.
+
+Kernel durations come from HIP events recorded on the stream the kernels run
+on, around every launch inside the timed region. The oracle's CPU baseline is
+timed on this host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "TP-shard linear: decode HBM GB/s, prefill bf16 TFLOP/s (% of roofline)"
+DECODE_MS = (1, 8, 32, 64)
+COPIES = 4
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(M, H, I, t=1):
+    """Algorithmic HBM bytes of one rank's feed-forward share at batch M:
+    weights once, X once, H written and read once (bf16), the fp32 partial
+    written once, and the partial sum reading t partials and writing Y."""
+    gateup = H * 2 * (I // t) * 2 + M * H * 2 + M * (I // t) * 2
+    down = (I // t) * H * 2 + M * (I // t) * 2 + M * H * 4
+    reduce = (t + 1) * M * H * 4
+    return gateup, down, reduce
+
+
+def ffn_flops(M, H, I, t=1):
+    return 2 * M * H * 2 * (I // t) + 2 * M * (I // t) * H
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "tensor_transformer_linear_megatron_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def to_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def run_decode(args):
+    import torch
+    import tensor_transformer_linear_megatron_amd as tp
+    from seeded_inputs import workloads as wl
+
+    c = wl.LLAMA8B
+    H, I = c["hidden"], c["inter"]
+    log(f"[bench] generating the 8B feed-forward layer (hidden {H}, intermediate {I})")
+    X = wl.activations(max(DECODE_MS), H)
+    Wgu = wl.gateup(H, I, c["sigma"])
+    Wd = wl.down(I, H, c["sigma"])
+    gu = tp.tp_shard_plan("gateup_col", H, 2 * I, 1, 0)
+    dn = tp.tp_shard_plan("row", I, H, 1, 0)
+    gp0 = tp.tp_shard_pack(gu, to_dev(Wgu))
+    dp0 = tp.tp_shard_pack(dn, to_dev(Wd))
+    copies = [(gp0, dp0)] + [(gp0.clone(), dp0.clone()) for _ in range(COPIES - 1)]
+    Xd = to_dev(X)
+    bufs = {M: dict(X=Xd[:M], H=torch.empty((M, I), dtype=torch.bfloat16, device="cuda"),
+                    P=torch.empty((1, M, H), dtype=torch.float32, device="cuda"),
+                    Y=torch.empty((M, H), dtype=torch.float32, device="cuda")) for M in DECODE_MS}
+    torch.cuda.synchronize()
+
+    # Pre-marshalled calls of the same C entry points, so the host's launch
+    # cost stays below the GPU's time per call and the stream never drains.
+    import ctypes
+    from tensor_transformer_linear_megatron_amd import _lib
+    lib = _lib.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    VP, null = ctypes.c_void_p, ctypes.c_void_p(0)
+    gub, dnb = ctypes.byref(gu), ctypes.byref(dn)
+    calls = []
+    for s_ in range(COPIES):
+        row = []
+        for j, M in enumerate(DECODE_MS):
+            gp, dp = copies[(s_ * len(DECODE_MS) + j) % COPIES]
+            b = bufs[M]
+            row.append((
+                (gub, VP(b["X"].data_ptr()), M, H, VP(gp.data_ptr()), VP(b["H"].data_ptr()), I, null, 0, stream),
+                (dnb, VP(b["H"].data_ptr()), M, I, VP(dp.data_ptr()), VP(b["P"].data_ptr()), H, null, 0, stream),
+                (VP(b["P"].data_ptr()), M * H, 1, M, H, H, VP(b["Y"].data_ptr()), H, stream)))
+        calls.append(row)
+
+    def step(s, events=None):
+        for j, M in enumerate(DECODE_MS):
+            c_col, c_row, c_red = calls[s % COPIES][j]
+            if events is not None:
+                events[M][0].record()
+            st = lib.tp_col_linear(*c_col)
+            if events is not None:
+                events[M][1].record()
+            st |= lib.tp_row_linear(*c_row)
+            if events is not None:
+                events[M][2].record()
+            st |= lib.tp_reduce_partials(*c_red)
+            if events is not None:
+                events[M][3].record()
+            if st:
+                raise RuntimeError(f"launch failed at M={M}: {st}")
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ev = [{M: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for M in DECODE_MS}
+          for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(args.warmup + s, ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {}
+    for M in DECODE_MS:
+        d = np.array([[e[M][0].elapsed_time(e[M][1]), e[M][1].elapsed_time(e[M][2]),
+                       e[M][2].elapsed_time(e[M][3])] for e in ev]) * 1e3  # us
+        gbytes, dbytes, rbytes = decode_bytes(M, H, I)
+        mean = d.mean(axis=0)
+        per[M] = dict(M=M, gateup_us=float(mean[0]), down_us=float(mean[1]), reduce_us=float(mean[2]),
+                      gateup_GBs=gbytes / mean[0] / 1e3, down_GBs=dbytes / mean[1] / 1e3,
+                      ffn_GBs=(gbytes + dbytes + rbytes) / mean.sum() / 1e3,
+                      bytes=gbytes + dbytes + rbytes)
+    step_bytes = sum(p["bytes"] for p in per.values())
+    value = step_bytes * args.steps / wall / 1e9
+
+    # The dominant kernel: the gate/up GEMV instantiation with the largest share of the step.
+    dom = max(DECODE_MS, key=lambda M: per[M]["gateup_us"])
+    gbytes = decode_bytes(dom, H, I)[0]
+    roof = dict(bound="hbm", kernel=f"gemv_kernel gate/up + SwiGLU, M={dom} (gemv_kernel<{(dom + 15) // 16},2,1,*>)",
+                achieved=round(gbytes / per[dom]["gateup_us"] / 1e3, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbytes / per[dom]["gateup_us"] / 1e3 / HBM_PEAK_GBS, 4),
+                traffic=None, bytes_per_launch=gbytes, avg_launch_us=round(per[dom]["gateup_us"], 2))
+    roof["traffic"] = load_traffic(f"gateup_M{dom}", source_hash("gemv.hip"))
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline_decode(X, Wgu, Wd, H, I)
+    return dict(value=value, wall=wall, per=per, roofline=roof, cpu=cpu, H=H, I=I)
+
+
+def load_traffic(key, src_hash):
+    """Measured HBM bytes per launch from the committed rocprofv3 counter
+    summary, or None if it is missing or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get("kernels", {}).get(key)
+    if not e or e.get("source_hash") != src_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline_decode(X, Wgu, Wd, H, I):
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    log(f"[bench] cpu baseline: the oracle on this host ({threads} threads)")
+    sample_ms = (1, 8)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for M in sample_ms:
+            oracle.ffn_unsharded(X[:M], Wgu, Wd)
+        reps += 1
+        if time.perf_counter() - t0 > 8.0 or reps >= 5:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    nbytes = sum(sum(decode_bytes(M, H, I)) for M in sample_ms)
+    return dict(value=round(nbytes / dt / 1e9, 3), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"the full 8B feed-forward share (t = 1) at M = 1 and M = 8, fp64 oracle, "
+                       f"{reps} repetition(s), {dt:.2f} s each; bytes counted as for the GPU")
+
+
+def run_prefill(args):
+    import torch
+    import tensor_transformer_linear_megatron_amd as tp
+    from seeded_inputs import workloads as wl
+
+    c = wl.LLAMA405B
+    Hd, I, t, M, r = c["hidden"], c["inter"], 8, 8192, 0
+    w = I // t
+    log(f"[bench] prefill: 405B feed-forward rank 0 of {t}, {M} tokens")
+    cols = range(r * w, (r + 1) * w)
+    X = to_dev(wl.activations(M, Hd))
+    Wgu_r = wl.gateup(Hd, I, c["sigma"], cols=cols)
+    Wd_r = wl.down(I, Hd, c["sigma"], rows=cols)
+    gu = tp.tp_shard_plan("gateup_col", Hd, 2 * I, t, r)
+    dn = tp.tp_shard_plan("row", I, Hd, t, r)
+    full = torch.empty((Hd, 2 * I), dtype=torch.bfloat16, device="cuda")
+    full[:, cols.start:cols.stop].copy_(to_dev(Wgu_r[:, :w]))
+    full[:, I + cols.start:I + cols.stop].copy_(to_dev(Wgu_r[:, w:]))
+    gp = tp.tp_shard_pack(gu, full)
+    del full
+    fulld = torch.empty((I, Hd), dtype=torch.bfloat16, device="cuda")
+    fulld[cols.start:cols.stop].copy_(to_dev(Wd_r))
+    dp = tp.tp_shard_pack(dn, fulld)
+    del fulld
+    Hb = torch.empty((M, w), dtype=torch.bfloat16, device="cuda")
+    P = torch.empty((M, Hd), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        tp.tp_col_linear(gu, X, gp, Y=Hb)
+        tp.tp_row_linear(dn, Hb, dp, P=P)
+    steps = max(3, args.steps // 4)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record()
+        tp.tp_col_linear(gu, X, gp, Y=Hb)
+        e[1].record()
+        tp.tp_row_linear(dn, Hb, dp, P=P)
+        e[2].record()
+    torch.cuda.synchronize()
+    d = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in ev]).mean(axis=0)  # ms
+    fg = 2 * M * Hd * 2 * w
+    fd = 2 * M * w * Hd
+    tf = (fg + fd) / d.sum() / 1e9
+    return dict(workload="llama3.1-405b FFN, TP=8 rank 0, prefill 8192 tokens", unit="TFLOP/s",
+                value=round(tf, 1), frac=round(tf / MFMA_BF16_PEAK_TFS, 4), peak=MFMA_BF16_PEAK_TFS,
+                gateup_ms=round(float(d[0]), 3), gateup_TFs=round(fg / d[0] / 1e9, 1),
+                down_ms=round(float(d[1]), 3), down_TFs=round(fd / d[1] / 1e9, 1), steps=steps)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs every tensor-parallel rank in turn on a "
+              "single MI355X and has no multi-GPU path; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dec = run_decode(args)
+    pre = None if args.no_prefill else run_prefill(args)
+    per = [dict(M=p["M"], gateup_us=round(p["gateup_us"], 2), down_us=round(p["down_us"], 2),
+                reduce_us=round(p["reduce_us"], 2), gateup_GBs=round(p["gateup_GBs"], 1),
+                down_GBs=round(p["down_GBs"], 1), ffn_GBs=round(p["ffn_GBs"], 1))
+           for p in dec["per"].values()]
+    line = {
+        "metric": METRIC,
+        "value": round(dec["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["wall"] / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) bf16 weights, random init)",
+        "config": {"workload": "llama3.1-8b FFN share, TP=1, decode batches M=1,8,32,64 per step",
+                   "hidden": dec["H"], "intermediate": dec["I"], "t": 1,
+                   "decode_batches": list(DECODE_MS), "weight_copies": COPIES,
+                   "frac_of_hbm_peak": round(dec["value"] / HBM_PEAK_GBS, 4)},
+        "roofline": dec["roofline"],
+        "cpu_baseline": dec["cpu"],
+        "per_batch": per,
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
