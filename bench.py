@@ -88,7 +88,9 @@ def run_decode(args):
     Xd = to_dev(X)
     bufs = {M: dict(X=Xd[:M], H=torch.empty((M, I), dtype=torch.bfloat16, device="cuda"),
                     P=torch.empty((1, M, H), dtype=torch.float32, device="cuda"),
-                    Y=torch.empty((M, H), dtype=torch.float32, device="cuda")) for M in DECODE_MS}
+                    Y=torch.empty((M, H), dtype=torch.float32, device="cuda"),
+                    ws=torch.empty(max(16, tp.tp_workspace_bytes(gu, M), tp.tp_workspace_bytes(dn, M)),
+                                   dtype=torch.uint8, device="cuda")) for M in DECODE_MS}
     torch.cuda.synchronize()
 
     # Pre-marshalled calls of the same C entry points, so the host's launch
@@ -105,9 +107,10 @@ def run_decode(args):
         for j, M in enumerate(DECODE_MS):
             gp, dp = copies[(s_ * len(DECODE_MS) + j) % COPIES]
             b = bufs[M]
+            ws, wsb = VP(b["ws"].data_ptr()), b["ws"].numel()
             row.append((
-                (gub, VP(b["X"].data_ptr()), M, H, VP(gp.data_ptr()), VP(b["H"].data_ptr()), I, null, 0, stream),
-                (dnb, VP(b["H"].data_ptr()), M, I, VP(dp.data_ptr()), VP(b["P"].data_ptr()), H, null, 0, stream),
+                (gub, VP(b["X"].data_ptr()), M, H, VP(gp.data_ptr()), VP(b["H"].data_ptr()), I, ws, wsb, stream),
+                (dnb, VP(b["H"].data_ptr()), M, I, VP(dp.data_ptr()), VP(b["P"].data_ptr()), H, ws, wsb, stream),
                 (VP(b["P"].data_ptr()), M * H, 1, M, H, H, VP(b["Y"].data_ptr()), H, stream)))
         calls.append(row)
 

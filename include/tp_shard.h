@@ -163,7 +163,10 @@ TP_API tp_status tp_shard_pack(const tp_shard_desc* desc, const uint16_t* W, int
  * Accumulation is fp32 from bf16 products; the result is rounded once to bf16.
  * ldy lets Y be a column slice of a wider buffer. M == 0 queues nothing and
  * returns TP_OK without looking at X, W_packed or Y (they may be NULL).
- * ws may be NULL when tp_workspace_bytes(desc, M) == 0.
+ * ws: device scratch of at least tp_workspace_bytes(desc, M) bytes, 16-byte
+ * aligned, owned by the caller (may be NULL when that is 0); its contents on
+ * entry do not matter and on return are undefined. Calls queued on different
+ * streams must not share one ws.
  */
 TP_API tp_status tp_col_linear(const tp_shard_desc* desc, const uint16_t* X, int64_t M, int64_t ldx,
                         const void* W_packed, uint16_t* Y, int64_t ldy, void* ws,
@@ -192,6 +195,7 @@ TP_API tp_status tp_row_linear(const tp_shard_desc* desc, const uint16_t* Z, int
  *   Wd [I x H] with the same t and rank, and gateup->out_n == down->shard_k
  *   (TP_ERR_SHAPE otherwise).
  *   H_ws device [M x I/t] bf16 (contiguous), P [M x H] fp32 with leading dim ldp.
+ *   ws: at least max(tp_workspace_bytes(gateup, M), tp_workspace_bytes(down, M)).
  */
 TP_API tp_status tp_ffn_shard(const tp_shard_desc* gateup, const tp_shard_desc* down,
                        const uint16_t* X, int64_t M, int64_t ldx, const void* Wgu_packed,
@@ -210,8 +214,10 @@ TP_API tp_status tp_ffn_shard(const tp_shard_desc* gateup, const tp_shard_desc* 
 TP_API tp_status tp_reduce_partials(const float* P, int64_t stride_elems, int32_t t, int64_t M,
                              int64_t N, int64_t ldp, float* Y, int64_t ldy, hipStream_t stream);
 
-/* Bytes of workspace tp_col_linear / tp_row_linear need for this shard at
- * this M (0 when the chosen kernels need none). */
+/* Bytes of device workspace tp_col_linear / tp_row_linear need for this
+ * shard at this M (fp32 partial sums of decode split-K; 0 when the chosen
+ * kernels need none or the descriptor is invalid). tp_ffn_shard needs the
+ * larger of its two descriptors' values. */
 TP_API size_t tp_workspace_bytes(const tp_shard_desc* desc, int64_t M);
 
 /* A static, human-readable name for a status code. */

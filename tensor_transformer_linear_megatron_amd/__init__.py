@@ -88,10 +88,15 @@ def tp_workspace_bytes(desc: TpShardDesc, M: int) -> int:
     return int(_lib.load().tp_workspace_bytes(ctypes.byref(desc), M))
 
 
-def _ws(desc, M, ws):
+def _ws(descs, M, ws, device):
+    """Workspace pointer and size; allocated here (torch, on the device) when
+    the caller passes none and the kernels need some."""
     if ws is None:
-        return ctypes.c_void_p(0), 0
-    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+        need = max(tp_workspace_bytes(d, M) for d in descs)
+        if need == 0:
+            return ctypes.c_void_p(0), 0, None
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), ws
 
 
 def tp_col_linear(desc: TpShardDesc, X: torch.Tensor, W_packed: torch.Tensor,
@@ -105,7 +110,7 @@ def tp_col_linear(desc: TpShardDesc, X: torch.Tensor, W_packed: torch.Tensor,
     if Y is None:
         Y = torch.empty((M, desc.out_n), dtype=torch.bfloat16, device=X.device)
     yp, ldy = _mat(Y, torch.bfloat16, "Y")
-    wsp, wsb = _ws(desc, M, ws)
+    wsp, wsb, _keep = _ws((desc,), M, ws, X.device)
     _check(_lib.load().tp_col_linear(ctypes.byref(desc), xp, M, ldx,
                                      ctypes.c_void_p(W_packed.data_ptr()), yp, ldy, wsp, wsb,
                                      _stream(stream)), "tp_col_linear")
@@ -123,7 +128,7 @@ def tp_row_linear(desc: TpShardDesc, Z: torch.Tensor, W_packed: torch.Tensor,
     if P is None:
         P = torch.empty((M, desc.N), dtype=torch.float32, device=Z.device)
     pp, ldp = _mat(P, torch.float32, "P")
-    wsp, wsb = _ws(desc, M, ws)
+    wsp, wsb, _keep = _ws((desc,), M, ws, Z.device)
     _check(_lib.load().tp_row_linear(ctypes.byref(desc), zp, M, ldz,
                                      ctypes.c_void_p(W_packed.data_ptr()), pp, ldp, wsp, wsb,
                                      _stream(stream)), "tp_row_linear")
@@ -143,7 +148,7 @@ def tp_ffn_shard(gateup: TpShardDesc, down: TpShardDesc, X: torch.Tensor, Wgu_pa
     if P is None:
         P = torch.empty((M, down.N), dtype=torch.float32, device=X.device)
     pp, ldp = _mat(P, torch.float32, "P")
-    wsp, wsb = _ws(gateup, M, ws)
+    wsp, wsb, _keep = _ws((gateup, down), M, ws, X.device)
     _check(_lib.load().tp_ffn_shard(ctypes.byref(gateup), ctypes.byref(down), xp, M, ldx,
                                     ctypes.c_void_p(Wgu_packed.data_ptr()),
                                     ctypes.c_void_p(Wd_packed.data_ptr()),

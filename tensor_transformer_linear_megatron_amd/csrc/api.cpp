@@ -49,13 +49,32 @@ tpk::LinearArgs make_args(const tp_shard_desc* d, const uint16_t* X, int64_t M, 
   return a;
 }
 
-tp_status run_linear(const tp_shard_desc* d, const tpk::LinearArgs& a, tpk::Epilogue epi,
+tpk::Epilogue epilogue_of(const tp_shard_desc* d) {
+  if (d->kind == TP_GATEUP_COL) return tpk::kEpiSwiglu;
+  return is_col(d->kind) ? tpk::kEpiBf16 : tpk::kEpiF32;
+}
+
+int32_t path_of(const tp_shard_desc* d, int64_t M) {
+  if (d->path != TP_PATH_AUTO) return d->path;
+  return M <= 64 ? TP_PATH_DECODE : TP_PATH_PREFILL;
+}
+
+size_t workspace_bytes(const tp_shard_desc* d, int64_t M) {
+  if (M <= 0 || path_of(d, M) != TP_PATH_DECODE) return 0;
+  return tpk::gemv_workspace_bytes(M, d->packed_k / tpk::kTileK, d->packed_n / tpk::kTileN,
+                                   epilogue_of(d));
+}
+
+tp_status run_linear(const tp_shard_desc* d, const tpk::LinearArgs& a, void* ws, size_t ws_bytes,
                      hipStream_t s) {
-  int32_t path = d->path;
-  if (path == TP_PATH_AUTO) path = a.M <= 64 ? TP_PATH_DECODE : TP_PATH_PREFILL;
+  const int32_t path = path_of(d, a.M);
   if (path == TP_PATH_DECODE && a.M > 64) return TP_ERR_SHAPE;
-  const hipError_t e = path == TP_PATH_DECODE ? tpk::launch_gemv(a, epi, s)
-                                              : tpk::launch_gemm(a, epi, s);
+  const size_t need = workspace_bytes(d, a.M);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return TP_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return TP_ERR_ALIGN;
+  const hipError_t e = path == TP_PATH_DECODE
+                           ? tpk::launch_gemv(a, epilogue_of(d), static_cast<float*>(ws), s)
+                           : tpk::launch_gemm(a, epilogue_of(d), s);
   return e == hipSuccess ? TP_OK : TP_ERR_HIP;
 }
 
@@ -73,9 +92,8 @@ tp_status check_linear_io(const tp_shard_desc* d, const uint16_t* X, int64_t M, 
 }  // namespace
 
 extern "C" size_t tp_workspace_bytes(const tp_shard_desc* desc, int64_t M) {
-  (void)desc;
-  (void)M;
-  return 0;  // every kernel reduces split-K partials inside its workgroup
+  if (check_desc(desc) != TP_OK) return 0;
+  return workspace_bytes(desc, M);
 }
 
 extern "C" tp_status tp_shard_pack(const tp_shard_desc* d, const uint16_t* W, int64_t ldw,
@@ -115,29 +133,25 @@ extern "C" tp_status tp_shard_pack(const tp_shard_desc* d, const uint16_t* W, in
 extern "C" tp_status tp_col_linear(const tp_shard_desc* d, const uint16_t* X, int64_t M,
                                    int64_t ldx, const void* W_packed, uint16_t* Y, int64_t ldy,
                                    void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   tp_status st = check_desc(d);
   if (st != TP_OK) return st;
   if (!is_col(d->kind)) return TP_ERR_KIND;
   st = check_linear_io(d, X, M, ldx, W_packed, Y, ldy, 8);
   if (st != TP_OK || M == 0) return st;
   const tpk::LinearArgs a = make_args(d, X, M, ldx, W_packed, Y, ldy);
-  return run_linear(d, a, d->kind == TP_GATEUP_COL ? tpk::kEpiSwiglu : tpk::kEpiBf16, stream);
+  return run_linear(d, a, ws, ws_bytes, stream);
 }
 
 extern "C" tp_status tp_row_linear(const tp_shard_desc* d, const uint16_t* Z, int64_t M,
                                    int64_t ldz, const void* W_packed, float* P, int64_t ldp,
                                    void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   tp_status st = check_desc(d);
   if (st != TP_OK) return st;
   if (!is_row(d->kind)) return TP_ERR_KIND;
   st = check_linear_io(d, Z, M, ldz, W_packed, P, ldp, 4);
   if (st != TP_OK || M == 0) return st;
   const tpk::LinearArgs a = make_args(d, Z, M, ldz, W_packed, P, ldp);
-  return run_linear(d, a, tpk::kEpiF32, stream);
+  return run_linear(d, a, ws, ws_bytes, stream);
 }
 
 extern "C" tp_status tp_ffn_shard(const tp_shard_desc* gu, const tp_shard_desc* dn,
@@ -157,6 +171,9 @@ extern "C" tp_status tp_ffn_shard(const tp_shard_desc* gu, const tp_shard_desc* 
   if (st != TP_OK) return st;
   st = check_linear_io(dn, H_ws, M, gu->out_n, Wd_packed, P, ldp, 4);
   if (st != TP_OK || M == 0) return st;
+  const size_t need_gu = workspace_bytes(gu, M), need_dn = workspace_bytes(dn, M);
+  const size_t need = need_gu > need_dn ? need_gu : need_dn;
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return TP_ERR_WORKSPACE;
   st = tp_col_linear(gu, X, M, ldx, Wgu_packed, H_ws, gu->out_n, ws, ws_bytes, stream);
   if (st != TP_OK) return st;
   return tp_row_linear(dn, H_ws, M, gu->out_n, Wd_packed, P, ldp, ws, ws_bytes, stream);

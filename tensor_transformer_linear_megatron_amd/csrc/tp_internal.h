@@ -53,7 +53,10 @@ struct PackArgs {
 };
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
-hipError_t launch_gemv(const LinearArgs& a, Epilogue epi, hipStream_t s);
+// Decode path. `ws` must hold gemv_workspace_bytes() bytes (fp32 split
+// partials) when that is non-zero.
+hipError_t launch_gemv(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s);
+size_t gemv_workspace_bytes(int64_t M, int64_t ksteps, int64_t ntiles, Epilogue epi);
 hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, hipStream_t s);
 hipError_t launch_reduce(const float* P, int64_t stride, int32_t t, int64_t M, int64_t N,
                          int64_t ldp, float* Y, int64_t ldy, hipStream_t s);

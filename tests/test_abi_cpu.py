@@ -196,8 +196,26 @@ def test_reduce_and_pack_argument_errors():
     assert lib.tp_shard_pack(ctypes.byref(bad), A, 64, B, S) == _lib.TP_ERR_SHAPE
 
 
-def test_workspace_is_zero():
-    for kind, K, N in (("col", 4096, 4096), ("gateup_col", 8192, 57344), ("row", 28672, 8192)):
-        d = tp.tp_shard_plan(kind, K, N, 8, 0)
-        for M in (1, 64, 8192):
+def test_workspace_bytes():
+    """Decode batches of 17..64 tokens may split K over workgroups; the fp32
+    partials need G * M * packed_n * 4 bytes. M <= 16, prefill and invalid
+    descriptors need none."""
+    lib = _lib.load()
+    for kind, K, N, t in (("col", 4096, 4096, 2), ("gateup_col", 8192, 57344, 8), ("row", 28672, 8192, 8),
+                          ("row", 14336, 4096, 1), ("gateup_col", 4096, 28672, 1)):
+        d = tp.tp_shard_plan(kind, K, N, t, 0)
+        for M in (1, 16, 65, 8192):
             assert tp.tp_workspace_bytes(d, M) == 0
+        for M in (17, 32, 64):
+            ws = tp.tp_workspace_bytes(d, M)
+            assert ws % (M * d.packed_n * 4) == 0 and ws // (M * d.packed_n * 4) <= 64
+        pre = d.copy()
+        pre.path = tp.TP_PATH_PREFILL
+        assert tp.tp_workspace_bytes(pre, 32) == 0
+    assert lib.tp_workspace_bytes(None, 32) == 0
+    d = tp.tp_shard_plan("row", 14336, 4096, 1, 0)
+    if tp.tp_workspace_bytes(d, 64):  # a too-small workspace is refused before any launch
+        assert lib.tp_row_linear(ctypes.byref(d), A, 64, 14336, B, C, 4096, NUL, 0, ctypes.c_void_p(0)) \
+            == _lib.TP_ERR_WORKSPACE
+        assert lib.tp_row_linear(ctypes.byref(d), A, 64, 14336, B, C, 4096, A, 16, ctypes.c_void_p(0)) \
+            == _lib.TP_ERR_WORKSPACE

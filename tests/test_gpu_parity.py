@@ -122,6 +122,22 @@ def test_row_small(M, path):
         assert_parity(got, ref, f"row M={M} K={K} N={N} t={t} r={r}")
 
 
+@pytest.mark.parametrize("M", [17, 33, 50, 64])
+def test_decode_split_k_ragged(M):
+    """Long ragged K with few output tiles: the decode path splits K over
+    workgroups (fp32 partials in the workspace, summed in split order)."""
+    say("decode split-K", M)
+    for kind, K, N, t, r in (("col", 8184, 80, 1, 0), ("gateup_col", 8184, 2 * 48, 1, 0),
+                             ("row", 2 * 8184, 72, 2, 1), ("col", 4096, 32, 1, 0)):
+        d = tp.tp_shard_plan(kind, K, N, t, r)
+        assert tp.tp_workspace_bytes(d, M) > 0, (kind, K, N)
+        if kind == "row":
+            got, ref = _row_case(kind, K, N, t, r, M, tp.TP_PATH_AUTO)
+        else:
+            got, ref = _col_case(kind, K, N, t, r, M, tp.TP_PATH_AUTO)
+        assert_parity(got, ref, f"{kind} K={K} N={N} M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 64, 200])
 def test_attention_kinds_small(M):
     say("qkv/o small", M)
