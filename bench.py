@@ -69,6 +69,41 @@ def to_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+class Timer:
+    """HIP events on the stream the kernels run on, recorded with a
+    device-scope release so they bracket the kernels tightly (a system-scope
+    release writes back and invalidates caches at every record)."""
+
+    FLAGS = 0x40000000  # hipEventReleaseToDevice
+
+    def __init__(self, stream_handle):
+        import ctypes
+        self.ct = ctypes
+        self.stream = ctypes.c_void_p(stream_handle)
+        # the HIP runtime torch already loaded (the library binds to the same one)
+        self.hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.c_void_p, ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+
+    def event(self):
+        e = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags({self.FLAGS:#x}) failed with {rc}")
+        return e
+
+    def record(self, e):
+        if self.hip.hipEventRecord(e, self.stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+
 def run_decode(args):
     import torch
     import tensor_transformer_linear_megatron_amd as tp
@@ -114,20 +149,22 @@ def run_decode(args):
                 (VP(b["P"].data_ptr()), M * H, 1, M, H, H, VP(b["Y"].data_ptr()), H, stream)))
         calls.append(row)
 
+    timer = Timer(torch.cuda.current_stream().cuda_stream)
+
     def step(s, events=None):
         for j, M in enumerate(DECODE_MS):
             c_col, c_row, c_red = calls[s % COPIES][j]
             if events is not None:
-                events[M][0].record()
+                timer.record(events[M][0])
             st = lib.tp_col_linear(*c_col)
             if events is not None:
-                events[M][1].record()
+                timer.record(events[M][1])
             st |= lib.tp_row_linear(*c_row)
             if events is not None:
-                events[M][2].record()
+                timer.record(events[M][2])
             st |= lib.tp_reduce_partials(*c_red)
             if events is not None:
-                events[M][3].record()
+                timer.record(events[M][3])
             if st:
                 raise RuntimeError(f"launch failed at M={M}: {st}")
 
@@ -135,8 +172,7 @@ def run_decode(args):
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    ev = [{M: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for M in DECODE_MS}
-          for _ in range(args.steps)]
+    ev = [{M: [timer.event() for _ in range(4)] for M in DECODE_MS} for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -147,8 +183,8 @@ def run_decode(args):
 
     per = {}
     for M in DECODE_MS:
-        d = np.array([[e[M][0].elapsed_time(e[M][1]), e[M][1].elapsed_time(e[M][2]),
-                       e[M][2].elapsed_time(e[M][3])] for e in ev]) * 1e3  # us
+        d = np.array([[timer.ms(e[M][0], e[M][1]), timer.ms(e[M][1], e[M][2]),
+                       timer.ms(e[M][2], e[M][3])] for e in ev]) * 1e3  # us
         gbytes, dbytes, rbytes = decode_bytes(M, H, I)
         mean = d.mean(axis=0)
         per[M] = dict(M=M, gateup_us=float(mean[0]), down_us=float(mean[1]), reduce_us=float(mean[2]),
@@ -158,14 +194,29 @@ def run_decode(args):
     step_bytes = sum(p["bytes"] for p in per.values())
     value = step_bytes * args.steps / wall / 1e9
 
-    # The dominant kernel: the gate/up GEMV instantiation with the largest share of the step.
-    dom = max(DECODE_MS, key=lambda M: per[M]["gateup_us"])
-    gbytes = decode_bytes(dom, H, I)[0]
-    roof = dict(bound="hbm", kernel=f"gemv_kernel gate/up + SwiGLU, M={dom} (gemv_kernel<{(dom + 15) // 16},2,1,*>)",
-                achieved=round(gbytes / per[dom]["gateup_us"] / 1e3, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(gbytes / per[dom]["gateup_us"] / 1e3 / HBM_PEAK_GBS, 4),
-                traffic=None, bytes_per_launch=gbytes, avg_launch_us=round(per[dom]["gateup_us"], 2))
-    roof["traffic"] = load_traffic(f"gateup_M{dom}", source_hash("gemv.hip"))
+    # The dominant kernel: the kernel symbol with the largest share of the
+    # step. Batches of up to 16 tokens share one decode kernel instantiation.
+    def symbol(M, part):
+        fam = "gemv_stream<1," if M <= 16 else f"gemv_shared<{(M + 15) // 16},"
+        return fam + ("2,..,SwiGLU>" if part == "gateup" else "1,..,fp32>")
+    groups = {}
+    for M in DECODE_MS:
+        gb, db, _ = decode_bytes(M, H, I)
+        for part, nbytes, us in (("gateup", gb, per[M]["gateup_us"]), ("down", db, per[M]["down_us"])):
+            g = groups.setdefault(symbol(M, part), dict(bytes=0, us=0.0, launches=0, batches=[]))
+            g["bytes"] += nbytes
+            g["us"] += us
+            g["launches"] += 1
+            g["batches"].append(M)
+    dom_name, dom = max(groups.items(), key=lambda kv: kv[1]["us"])
+    bpl = dom["bytes"] / dom["launches"]
+    avg_us = dom["us"] / dom["launches"]
+    roof = dict(bound="hbm", kernel=f"{dom_name} (decode batches M={dom['batches']})",
+                achieved=round(bpl / avg_us / 1e3, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(bpl / avg_us / 1e3 / HBM_PEAK_GBS, 4), traffic=None,
+                bytes_per_launch=int(bpl), avg_launch_us=round(avg_us, 2),
+                launches_per_step=dom["launches"])
+    roof["traffic"] = load_traffic(dom_name, source_hash("gemv.hip"))
 
     cpu = None if args.no_cpu_baseline else cpu_baseline_decode(X, Wgu, Wd, H, I)
     return dict(value=value, wall=wall, per=per, roofline=roof, cpu=cpu, H=H, I=I)
@@ -235,16 +286,17 @@ def run_prefill(args):
         tp.tp_col_linear(gu, X, gp, Y=Hb)
         tp.tp_row_linear(dn, Hb, dp, P=P)
     steps = max(3, args.steps // 4)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    timer = Timer(torch.cuda.current_stream().cuda_stream)
+    ev = [[timer.event() for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     for e in ev:
-        e[0].record()
+        timer.record(e[0])
         tp.tp_col_linear(gu, X, gp, Y=Hb)
-        e[1].record()
+        timer.record(e[1])
         tp.tp_row_linear(dn, Hb, dp, P=P)
-        e[2].record()
+        timer.record(e[2])
     torch.cuda.synchronize()
-    d = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in ev]).mean(axis=0)  # ms
+    d = np.array([[timer.ms(e[0], e[1]), timer.ms(e[1], e[2])] for e in ev]).mean(axis=0)  # ms
     fg = 2 * M * Hd * 2 * w
     fd = 2 * M * w * Hd
     tf = (fg + fd) / d.sum() / 1e9

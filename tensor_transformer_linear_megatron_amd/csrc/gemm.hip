@@ -2,7 +2,12 @@
 // matrix cores ("Tensor vs Pipeline Parallelism", "A worked communication
 // estimate": prompt compute is about 2 x parameters x tokens operations).
 //
-// Design for gfx950:
+// Two kernels. gemm_big (256 x 256 tiles, 32x32x16 MFMA) runs whenever the
+// grid fills the GPU; gemm_kernel (128 x 128 tiles, 16x16x32 MFMA) covers
+// grids too small for that. On gfx950 the 32x32x16 bf16 MFMA sustains about
+// 1.5x the rate of the 16x16x32 one when fed from LDS.
+//
+// gemm_kernel, for gfx950:
 //  * Workgroup tile: BN = 128 output columns (8 packed tiles) x BM = 128
 //    tokens, k in stages of BK = 64 (two MFMA k-steps). Four wavefronts in a
 //    2 x 2 grid, each owning 64 columns x 64 tokens = 4 x 4 MFMA 16x16x32
@@ -139,10 +144,185 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// gemm_big: 256 output columns x 256 tokens per workgroup, 4 wavefronts of
+// 128 x 128 (4 x 4 accumulators of v_mfma_f32_32x32x16_bf16, 256 AGPRs).
+//
+//  * Each k-step (32) stage is 16 packed weight tiles + 16 token chunks of
+//    16 rows x 32 k, 1 KiB each, kept in LDS in the 16x16x32 fragment order
+//    (lane l at byte 16 l). A 32x32x16 fragment of block b, k-half kh is then
+//    lane (h, j) -> chunk 2b + j/16, slot (2 kh + h) * 16 + j % 16: every
+//    quarter-wave reads 256 contiguous bytes, no bank conflicts.
+//  * Loads are buffer loads into registers two stages ahead; rows and tiles
+//    past the end fall outside the buffer's range and read as zero, and a
+//    ragged last k-step is masked the same way (an out-of-range offset).
+//  * Two LDS buffers, one barrier per stage.
+//  * Workgroup ids are spread so that the 32 workgroups an XCD runs together
+//    cover 8 token tiles x 4 column tiles (shared through that XCD's L2).
+//  * Epilogue in registers: lane (h, j) owns token j of each 32-token block
+//    and, for q = 0..3, output columns 8q + 4h .. +3 of each 32-column block
+//    (accumulator elements 4q .. 4q+3). For SwiGLU a 32-column block is one
+//    gate tile (q = 0, 1) and its up tile (q = 2, 3).
+// ---------------------------------------------------------------------------
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+constexpr int BIG_T = 16;        // packed tiles per workgroup
+constexpr int BIG_MT = 16;       // 16-token tiles per workgroup
+constexpr int BIG_CH = BIG_T + BIG_MT;  // 1 KiB chunks per stage
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_big(LinearArgs a, int ntn, int ntm) {
+  __shared__ uint4 L0[BIG_CH * 64], L1[BIG_CH * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
+
+  // Tile of this workgroup: ids that share an XCD (id mod 8) get consecutive
+  // tiles, grouped 8 token tiles deep.
+  int bid = blockIdx.x;
+  const int nb = ntn * ntm, per = nb / 8;
+  if (bid < per * 8) bid = (bid % 8) * per + bid / 8;
+  constexpr int GM = 8;
+  const int first_m = bid / (GM * ntn) * GM;
+  const int gsize = ntm - first_m < GM ? ntm - first_m : GM;
+  const int tm = first_m + (bid % (GM * ntn)) % gsize;
+  const int tn = (bid % (GM * ntn)) / gsize;
+  const int64_t nt0 = (int64_t)tn * BIG_T, m0 = (int64_t)tm * (BIG_MT * 16);
+  const int64_t ksteps = a.ksteps;
+
+  const int64_t wt = a.ntiles - nt0 < BIG_T ? a.ntiles - nt0 : BIG_T;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.W + nt0 * ksteps * kTileU4), (short)0, (int)(wt * ksteps * 1024), 0x00020000);
+  const int64_t rows = a.M - m0 < BIG_MT * 16 ? a.M - m0 : BIG_MT * 16;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.X + m0 * a.ldx), (short)0, (int)(rows * a.ldx * 2), 0x00020000);
+  const int g = lane >> 4, i = lane & 15;
+
+  // Wave w loads chunks 8w .. 8w+7 of every stage: waves 0, 1 weight tiles,
+  // waves 2, 3 token chunks (16 rows x 32 k each).
+  const bool load_w = wave < 2;
+  const __amdgpu_buffer_rsrc_t rsrc = load_w ? rw : rx;
+  unsigned off0[8], stp;
+  // This lane's k octet of stage ks is inside K while 32 ks < kvalid.
+  const unsigned kvalid = a.K > g * 8 ? (unsigned)(a.K - g * 8) : 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = wave * 8 + j;
+    off0[j] = load_w ? (unsigned)((int64_t)c * ksteps * 1024 + lane * 16)
+                     : (unsigned)((((int64_t)(c - BIG_T) * 16 + i) * a.ldx + g * 8) * 2);
+  }
+  stp = load_w ? 1024u : 64u;
+
+  i32x4_t RA[8], RB[8];
+#define TP_LOAD(R, KS)                                                                       \
+  {                                                                                          \
+    const bool ok_ = load_w || (unsigned)(KS) * 32u < kvalid;                                \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) R[j] = __builtin_amdgcn_raw_buffer_load_b128( \
+        rsrc, ok_ ? off0[j] + (unsigned)(KS) * stp : 0x80000000u, 0, 0);                     \
+  }
+#define TP_STORE(LB, R) \
+  _Pragma("unroll") for (int j = 0; j < 8; ++j) LB[(wave * 8 + j) * 64 + lane] = __builtin_bit_cast(uint4, R[j]);
+  const int fh = lane >> 5, fj = lane & 31;
+  const int fslot = (fj >> 4) * 64 + fh * 16 + (fj & 15);
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x16_t{};
+#define TP_COMPUTE(LB)                                                                       \
+  _Pragma("unroll") for (int kh = 0; kh < 2; ++kh) {                                         \
+    uint4 A[4], B[4];                                                                        \
+    _Pragma("unroll") for (int x = 0; x < 4; ++x) A[x] = LB[(wn * 8 + 2 * x) * 64 + kh * 32 + fslot]; \
+    _Pragma("unroll") for (int y = 0; y < 4; ++y)                                            \
+        B[y] = LB[(BIG_T + wm * 8 + 2 * y) * 64 + kh * 32 + fslot];                          \
+    _Pragma("unroll") for (int x = 0; x < 4; ++x)                                            \
+        _Pragma("unroll") for (int y = 0; y < 4; ++y) acc[x][y] = mfma_32x32x16(A[x], B[y], acc[x][y]); \
+  }
+
+  TP_LOAD(RA, 0)
+  TP_STORE(L0, RA)
+  if (ksteps > 1) TP_LOAD(RA, 1)
+  __syncthreads();
+  // Stage ks is in L0 (even) or L1 (odd); RA holds stage ks + 1; RB gets ks + 2.
+  int64_t ks = 0;
+  for (; ks + 1 < ksteps; ks += 2) {
+    if (ks + 2 < ksteps) TP_LOAD(RB, ks + 2)
+    TP_COMPUTE(L0)
+    TP_STORE(L1, RA)
+    __syncthreads();
+    if (ks + 3 < ksteps) TP_LOAD(RA, ks + 3)
+    TP_COMPUTE(L1)
+    if (ks + 2 < ksteps) TP_STORE(L0, RB)
+    __syncthreads();
+  }
+  if (ks < ksteps) TP_COMPUTE(L0)  // odd k-step count: the last stage sits in L0
+#undef TP_LOAD
+#undef TP_STORE
+#undef TP_COMPUTE
+
+#pragma unroll
+  for (int y = 0; y < 4; ++y) {
+    const int64_t m = m0 + (wm * 4 + y) * 32 + fj;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int64_t ntb = nt0 + wn * 8 + 2 * x;  // first packed tile of this 32-column block
+      if constexpr (EPI == kEpiSwiglu) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int64_t n = (ntb >> 1) * kTileN + 8 * q + 4 * fh;
+          if (ntb >= a.ntiles || n >= a.out_n) continue;
+          const f32x16_t& v = acc[x][y];
+          store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + n, swiglu(v[4 * q], v[4 * q + 8]),
+                       swiglu(v[4 * q + 1], v[4 * q + 9]), swiglu(v[4 * q + 2], v[4 * q + 10]),
+                       swiglu(v[4 * q + 3], v[4 * q + 11]));
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = ntb * kTileN + 8 * q + 4 * fh;
+          if (n >= a.out_n) continue;
+          const f32x16_t& v = acc[x][y];
+          if constexpr (EPI == kEpiBf16) {
+            store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + n, v[4 * q], v[4 * q + 1],
+                         v[4 * q + 2], v[4 * q + 3]);
+          } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + m * a.ldo + n) =
+                make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+          }
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, hipStream_t s) {
   if (a.M <= 0 || a.ntiles == 0) return hipSuccess;
+  const int64_t ntn = (a.ntiles + BIG_T - 1) / BIG_T, ntm = (a.M + BIG_MT * 16 - 1) / (BIG_MT * 16);
+  // The big tile needs buffer offsets below 2^31 and enough workgroups to fill the GPU.
+  const bool big = ntn * ntm >= 256 &&
+                   (int64_t)BIG_MT * 16 * a.ldx * 2 < (1LL << 31) &&
+                   BIG_T * a.ksteps * 1024 < (1LL << 31);
+  if (big) {
+    const dim3 grid((unsigned)(ntn * ntm));
+    switch (epi) {
+      case kEpiSwiglu: hipLaunchKernelGGL(gemm_big<kEpiSwiglu>, grid, dim3(256), 0, s, a, (int)ntn, (int)ntm); break;
+      case kEpiBf16: hipLaunchKernelGGL(gemm_big<kEpiBf16>, grid, dim3(256), 0, s, a, (int)ntn, (int)ntm); break;
+      case kEpiF32: hipLaunchKernelGGL(gemm_big<kEpiF32>, grid, dim3(256), 0, s, a, (int)ntn, (int)ntm); break;
+    }
+    return hipGetLastError();
+  }
+
   const dim3 grid((unsigned)((a.ntiles + BN_T - 1) / BN_T), (unsigned)((a.M + BM - 1) / BM));
   switch (epi) {
     case kEpiSwiglu: hipLaunchKernelGGL(gemm_kernel<kEpiSwiglu>, grid, dim3(256), 0, s, a); break;

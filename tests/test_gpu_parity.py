@@ -122,6 +122,23 @@ def test_row_small(M, path):
         assert_parity(got, ref, f"row M={M} K={K} N={N} t={t} r={r}")
 
 
+# Grids of at least 256 workgroups of 256 x 256 run the big-tile prefill
+# kernel: ragged token count, ragged last k-step, odd and partial column tiles.
+BIG_CASES = [("col", 8, 3904, 1, 0, 4000), ("col", 200, 4040, 1, 0, 3965), ("col", 360, 3880, 1, 0, 4097),
+             ("gateup_col", 200, 2 * 1944, 1, 0, 3965), ("gateup_col", 136, 2 * 7808, 4, 3, 4000),
+             ("row", 528, 3880, 2, 1, 4001), ("row", 64, 4096, 1, 0, 4096)]
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,M", BIG_CASES)
+def test_prefill_big_tile_ragged(kind, K, N, t, r, M):
+    say("prefill big tile", kind, K, N, t, r, M)
+    if kind == "row":
+        got, ref = _row_case(kind, K, N, t, r, M, tp.TP_PATH_PREFILL)
+    else:
+        got, ref = _col_case(kind, K, N, t, r, M, tp.TP_PATH_PREFILL)
+    assert_parity(got, ref, f"{kind} K={K} N={N} t={t} r={r} M={M}")
+
+
 @pytest.mark.parametrize("M", [17, 33, 50, 64])
 def test_decode_split_k_ragged(M):
     """Long ragged K with few output tiles: the decode path splits K over
