@@ -13,8 +13,10 @@ feed-forward layer at 8192 tokens (gate/up 16384 x 13312 + SwiGLU, down
 6656 x 16384 to an fp32 partial), in bf16 TFLOP/s.
 
 Kernel durations come from HIP events recorded on the stream the kernels run
-on, around every launch inside the timed region. The oracle's CPU baseline is
-timed on this host on a bounded sample of the same workload.
+on: around every launch in an untimed breakdown pass, and around the dominant
+kernel's launches inside the timed region. The interval of an event pair with
+nothing between it, measured in the same passes, is subtracted. The oracle's
+CPU baseline is timed on this host on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -150,41 +152,50 @@ def run_decode(args):
         calls.append(row)
 
     timer = Timer(torch.cuda.current_stream().cuda_stream)
+    PARTS = ("gateup", "down", "reduce")
 
-    def step(s, events=None):
+    def step(s, marks=None):
+        """One step: every decode batch's feed-forward share. ``marks`` maps
+        (M, part) to an (start, end) event pair recorded around that launch."""
         for j, M in enumerate(DECODE_MS):
-            c_col, c_row, c_red = calls[s % COPIES][j]
-            if events is not None:
-                timer.record(events[M][0])
-            st = lib.tp_col_linear(*c_col)
-            if events is not None:
-                timer.record(events[M][1])
-            st |= lib.tp_row_linear(*c_row)
-            if events is not None:
-                timer.record(events[M][2])
-            st |= lib.tp_reduce_partials(*c_red)
-            if events is not None:
-                timer.record(events[M][3])
-            if st:
-                raise RuntimeError(f"launch failed at M={M}: {st}")
+            launches = zip(PARTS, (lib.tp_col_linear, lib.tp_row_linear, lib.tp_reduce_partials),
+                           calls[s % COPIES][j])
+            for part, fn, a in launches:
+                ev = marks.get((M, part)) if marks else None
+                if ev:
+                    timer.record(ev[0])
+                st = fn(*a)
+                if ev:
+                    timer.record(ev[1])
+                if st:
+                    raise RuntimeError(f"{part} launch failed at M={M}: {st}")
+
+    def empty_pair(marks):
+        # Two events with nothing between them: what an event pair adds to an
+        # interval by itself, subtracted from the kernel intervals below.
+        timer.record(marks["empty"][0])
+        timer.record(marks["empty"][1])
+
+    def new_marks(keys):
+        return {k: (timer.event(), timer.event()) for k in list(keys) + ["empty"]}
 
     log(f"[bench] warmup {args.warmup} steps")
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    ev = [{M: [timer.event() for _ in range(4)] for M in DECODE_MS} for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(args.warmup + s, ev[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
+    # Breakdown pass (untimed): every launch bracketed, to report each part
+    # and to pick the dominant kernel.
+    nb = min(args.steps, 20)
+    bmarks = [new_marks([(M, p) for M in DECODE_MS for p in PARTS]) for _ in range(nb)]
+    for s in range(nb):
+        empty_pair(bmarks[s])
+        step(args.warmup + s, bmarks[s])
+    torch.cuda.synchronize()
+    ovh_b = float(np.mean([timer.ms(*m["empty"]) for m in bmarks])) * 1e3
     per = {}
     for M in DECODE_MS:
-        d = np.array([[timer.ms(e[M][0], e[M][1]), timer.ms(e[M][1], e[M][2]),
-                       timer.ms(e[M][2], e[M][3])] for e in ev]) * 1e3  # us
+        d = np.array([[timer.ms(*m[(M, p)]) for p in PARTS] for m in bmarks]) * 1e3 - ovh_b  # us
         gbytes, dbytes, rbytes = decode_bytes(M, H, I)
         mean = d.mean(axis=0)
         per[M] = dict(M=M, gateup_us=float(mean[0]), down_us=float(mean[1]), reduce_us=float(mean[2]),
@@ -192,7 +203,6 @@ def run_decode(args):
                       ffn_GBs=(gbytes + dbytes + rbytes) / mean.sum() / 1e3,
                       bytes=gbytes + dbytes + rbytes)
     step_bytes = sum(p["bytes"] for p in per.values())
-    value = step_bytes * args.steps / wall / 1e9
 
     # The dominant kernel: the kernel symbol with the largest share of the
     # step. Batches of up to 16 tokens share one decode kernel instantiation.
@@ -202,20 +212,37 @@ def run_decode(args):
     groups = {}
     for M in DECODE_MS:
         gb, db, _ = decode_bytes(M, H, I)
-        for part, nbytes, us in (("gateup", gb, per[M]["gateup_us"]), ("down", db, per[M]["down_us"])):
-            g = groups.setdefault(symbol(M, part), dict(bytes=0, us=0.0, launches=0, batches=[]))
+        for part, nbytes in (("gateup", gb), ("down", db)):
+            g = groups.setdefault(symbol(M, part), dict(bytes=0, us=0.0, launches=[]))
             g["bytes"] += nbytes
-            g["us"] += us
-            g["launches"] += 1
-            g["batches"].append(M)
+            g["us"] += per[M][part + "_us"]
+            g["launches"].append((M, part))
     dom_name, dom = max(groups.items(), key=lambda kv: kv[1]["us"])
-    bpl = dom["bytes"] / dom["launches"]
-    avg_us = dom["us"] / dom["launches"]
-    roof = dict(bound="hbm", kernel=f"{dom_name} (decode batches M={dom['batches']})",
+
+    # Timed region: only the dominant kernel's launches (and one empty pair)
+    # carry events, so the step is disturbed as little as possible.
+    tmarks = [new_marks(dom["launches"]) for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        empty_pair(tmarks[s])
+        step(args.warmup + nb + s, tmarks[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    value = step_bytes * args.steps / wall / 1e9
+
+    ovh = float(np.mean([timer.ms(*m["empty"]) for m in tmarks])) * 1e3
+    raw = float(np.mean([timer.ms(*m[k]) for m in tmarks for k in dom["launches"]])) * 1e3
+    avg_us = raw - ovh
+    nl = len(dom["launches"])
+    bpl = dom["bytes"] / nl
+    roof = dict(bound="hbm", kernel=f"{dom_name} (decode batches M={[M for M, _ in dom['launches']]})",
                 achieved=round(bpl / avg_us / 1e3, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(bpl / avg_us / 1e3 / HBM_PEAK_GBS, 4), traffic=None,
                 bytes_per_launch=int(bpl), avg_launch_us=round(avg_us, 2),
-                launches_per_step=dom["launches"])
+                event_interval_us=round(raw, 2), empty_event_pair_us=round(ovh, 2),
+                launches_per_step=nl)
     roof["traffic"] = load_traffic(dom_name, source_hash("gemv.hip"))
 
     cpu = None if args.no_cpu_baseline else cpu_baseline_decode(X, Wgu, Wd, H, I)
@@ -247,7 +274,7 @@ def cpu_baseline_decode(X, Wgu, Wd, H, I):
         for M in sample_ms:
             oracle.ffn_unsharded(X[:M], Wgu, Wd)
         reps += 1
-        if time.perf_counter() - t0 > 8.0 or reps >= 5:
+        if time.perf_counter() - t0 > 12.0:
             break
     dt = (time.perf_counter() - t0) / reps
     nbytes = sum(sum(decode_bytes(M, H, I)) for M in sample_ms)
@@ -306,6 +333,23 @@ def run_prefill(args):
                 down_ms=round(float(d[1]), 3), down_TFs=round(fd / d[1] / 1e9, 1), steps=steps)
 
 
+COPY_BYTES = 1 << 30
+
+
+def calibrate_copy():
+    """Three device-to-device copies of 1 GiB: a kernel whose HBM traffic is
+    known exactly (1 GiB read, 1 GiB written per launch), run under the same
+    counters as the decode kernels to scale their byte counts."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +357,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (the yardstick for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs every tensor-parallel rank in turn on a "
@@ -323,6 +369,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     dec = run_decode(args)
     pre = None if args.no_prefill else run_prefill(args)
     per = [dict(M=p["M"], gateup_us=round(p["gateup_us"], 2), down_us=round(p["down_us"], 2),
