@@ -2,10 +2,11 @@
 // matrix cores ("Tensor vs Pipeline Parallelism", "A worked communication
 // estimate": prompt compute is about 2 x parameters x tokens operations).
 //
-// Two kernels. gemm_big (256 x 256 tiles, 32x32x16 MFMA) runs whenever the
-// grid fills the GPU; gemm_kernel (128 x 128 tiles, 16x16x32 MFMA) covers
-// grids too small for that. On gfx950 the 32x32x16 bf16 MFMA sustains about
-// 1.5x the rate of the 16x16x32 one when fed from LDS.
+// Two kernels. gemm_big (256 x 256 tiles, 32x32x16 MFMA, stages landed in
+// LDS by DMA) runs whenever the grid fills the GPU; gemm_kernel (128 x 128
+// tiles, 16x16x32 MFMA, register-staged) covers grids too small for that. On
+// gfx950 the 32x32x16 bf16 MFMA sustains about 1.5x the rate of the 16x16x32
+// one when fed from LDS.
 //
 // gemm_kernel, for gfx950:
 //  * Workgroup tile: BN = 128 output columns (8 packed tiles) x BM = 128
@@ -149,15 +150,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
 // gemm_big: 256 output columns x 256 tokens per workgroup, 4 wavefronts of
 // 128 x 128 (4 x 4 accumulators of v_mfma_f32_32x32x16_bf16, 256 AGPRs).
 //
-//  * Each k-step (32) stage is 16 packed weight tiles + 16 token chunks of
-//    16 rows x 32 k, 1 KiB each, kept in LDS in the 16x16x32 fragment order
-//    (lane l at byte 16 l). A 32x32x16 fragment of block b, k-half kh is then
-//    lane (h, j) -> chunk 2b + j/16, slot (2 kh + h) * 16 + j % 16: every
-//    quarter-wave reads 256 contiguous bytes, no bank conflicts.
-//  * Loads are buffer loads into registers two stages ahead; rows and tiles
-//    past the end fall outside the buffer's range and read as zero, and a
-//    ragged last k-step is masked the same way (an out-of-range offset).
-//  * Two LDS buffers, one barrier per stage.
+//  * A stage is 64 k (two packed k-steps): 32 weight chunks of 1 KiB (tile t,
+//    k-step h at chunk 2t + h, copied verbatim from the packed layout) and
+//    256 token rows of 128 bytes. Stages land in LDS by buffer-load-to-LDS
+//    DMA: no staging registers and no LDS store instructions. Each token row
+//    is read as a whole 128-byte line; its octet o is stored at position
+//    o ^ ((row >> 1) & 7), which keeps both the DMA writes and the fragment
+//    reads free of bank conflicts.
+//  * Two 64 KiB LDS buffers and one barrier per stage. The barrier both
+//    publishes stage s + 1 (every wave has waited for its own DMA) and frees
+//    the buffer of stage s (every wave has read it), after which the DMA of
+//    stage s + 2 goes into that buffer.
+//  * A wave keeps the whole stage's fragments in registers (4 k-halves x
+//    (4 weight + 4 token) x 16 bytes). While it multiplies stage s it reads
+//    stage s + 1: each k-half's registers are refilled right after their
+//    MFMAs have been issued.
+//  * Rows and tiles past the end fall outside the buffer resource's range
+//    and land as zeros; so does a ragged last k-step (an out-of-range offset),
+//    and so does the padding stage when the stage count is odd.
 //  * Workgroup ids are spread so that the 32 workgroups an XCD runs together
 //    cover 8 token tiles x 4 column tiles (shared through that XCD's L2).
 //  * Epilogue in registers: lane (h, j) owns token j of each 32-token block
@@ -167,20 +177,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
 // ---------------------------------------------------------------------------
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ f32x16_t mfma_32x32x16(uint4 a, uint4 b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-constexpr int BIG_T = 16;        // packed tiles per workgroup
-constexpr int BIG_MT = 16;       // 16-token tiles per workgroup
-constexpr int BIG_CH = BIG_T + BIG_MT;  // 1 KiB chunks per stage
+constexpr int BIG_T = 16;                        // packed tiles per workgroup
+constexpr int BIG_MT = 16;                       // 16-token tiles per workgroup
+constexpr int BIG_WCH = 2 * BIG_T;               // weight chunks per stage
+constexpr int BIG_STAGE_U4 = BIG_WCH * 64 + 256 * 8;  // 64 KiB per stage
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_big(LinearArgs a, int ntn, int ntm) {
-  __shared__ uint4 L0[BIG_CH * 64], L1[BIG_CH * 64];
+  __shared__ uint4 L0[BIG_STAGE_U4], L1[BIG_STAGE_U4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
@@ -196,7 +211,7 @@ __global__ __launch_bounds__(256) void gemm_big(LinearArgs a, int ntn, int ntm) 
   const int tm = first_m + (bid % (GM * ntn)) % gsize;
   const int tn = (bid % (GM * ntn)) / gsize;
   const int64_t nt0 = (int64_t)tn * BIG_T, m0 = (int64_t)tm * (BIG_MT * 16);
-  const int64_t ksteps = a.ksteps;
+  const int64_t ksteps = a.ksteps, nst = (ksteps + 1) / 2;
 
   const int64_t wt = a.ntiles - nt0 < BIG_T ? a.ntiles - nt0 : BIG_T;
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -204,69 +219,87 @@ __global__ __launch_bounds__(256) void gemm_big(LinearArgs a, int ntn, int ntm) 
   const int64_t rows = a.M - m0 < BIG_MT * 16 ? a.M - m0 : BIG_MT * 16;
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.X + m0 * a.ldx), (short)0, (int)(rows * a.ldx * 2), 0x00020000);
-  const int g = lane >> 4, i = lane & 15;
 
-  // Wave w loads chunks 8w .. 8w+7 of every stage: waves 0, 1 weight tiles,
-  // waves 2, 3 token chunks (16 rows x 32 k each).
-  const bool load_w = wave < 2;
-  const __amdgpu_buffer_rsrc_t rsrc = load_w ? rw : rx;
-  unsigned off0[8], stp;
-  // This lane's k octet of stage ks is inside K while 32 ks < kvalid.
-  const unsigned kvalid = a.K > g * 8 ? (unsigned)(a.K - g * 8) : 0u;
+  // DMA sources of this wave: weight chunks c = 8 wave + j and token row
+  // blocks 8 wave + j (8 rows x 128 bytes each, one per instruction).
+  unsigned woff[8], xoff[8], kx[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int c = wave * 8 + j;
-    off0[j] = load_w ? (unsigned)((int64_t)c * ksteps * 1024 + lane * 16)
-                     : (unsigned)((((int64_t)(c - BIG_T) * 16 + i) * a.ldx + g * 8) * 2);
+    woff[j] = (unsigned)(((int64_t)(c >> 1) * ksteps + (c & 1)) * 1024 + lane * 16);
+    const int r = wave * 64 + j * 8 + (lane >> 3);
+    const int o = (lane & 7) ^ ((r >> 1) & 7);  // logical octet landing in this lane's slot
+    xoff[j] = (unsigned)(((int64_t)r * a.ldx + 8 * o) * 2);
+    kx[j] = a.K > 8 * o ? (unsigned)(a.K - 8 * o) : 0u;  // octet inside K while 64 s < kx
   }
-  stp = load_w ? 1024u : 64u;
-
-  i32x4_t RA[8], RB[8];
-#define TP_LOAD(R, KS)                                                                       \
-  {                                                                                          \
-    const bool ok_ = load_w || (unsigned)(KS) * 32u < kvalid;                                \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) R[j] = __builtin_amdgcn_raw_buffer_load_b128( \
-        rsrc, ok_ ? off0[j] + (unsigned)(KS) * stp : 0x80000000u, 0, 0);                     \
+#define TP_ISSUE(LB, S)                                                                          \
+  {                                                                                              \
+    const unsigned s_ = (unsigned)(S);                                                           \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
+        rw, (lds_void_t*)&LB[(wave * 8 + j) * 64], 16,                                           \
+        2 * s_ + (j & 1) < (unsigned)ksteps ? woff[j] + s_ * 2048u : 0x80000000u, 0, 0, 0);      \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
+        rx, (lds_void_t*)&LB[BIG_WCH * 64 + (wave * 8 + j) * 64], 16,                            \
+        64u * s_ < kx[j] ? xoff[j] + s_ * 128u : 0x80000000u, 0, 0, 0);                          \
   }
-#define TP_STORE(LB, R) \
-  _Pragma("unroll") for (int j = 0; j < 8; ++j) LB[(wave * 8 + j) * 64 + lane] = __builtin_bit_cast(uint4, R[j]);
+  // Fragment addresses. 32x32x16 A operand (weights) of block x, k-half kh:
+  // lane (h, j) takes tile 2 (4 wn + x) + j / 16, k-step kh / 2, octet
+  // 2 (kh % 2) + h, column j % 16. B operand (tokens): row 128 wm + 32 y + j,
+  // octet 2 kh + h, stored at octet position (2 kh + h) ^ ((j >> 1) & 7).
   const int fh = lane >> 5, fj = lane & 31;
-  const int fslot = (fj >> 4) * 64 + fh * 16 + (fj & 15);
+  const int fa = (fj >> 4) * 128 + fh * 16 + (fj & 15);
+  const int swz = fh ^ ((fj >> 1) & 7);
+  const int fb = BIG_WCH * 64 + (wm * 128 + fj) * 8;
+  uint4 FA[4][4], FB[4][4];
+#define TP_READ(LB, KH)                                                                          \
+  _Pragma("unroll") for (int x = 0; x < 4; ++x)                                                  \
+      FA[KH][x] = LB[(wn * 4 + x) * 256 + ((KH) >> 1) * 64 + ((KH) & 1) * 32 + fa];              \
+  _Pragma("unroll") for (int y = 0; y < 4; ++y) FB[KH][y] = LB[fb + y * 256 + ((2 * (KH)) ^ swz)];
+#define TP_MMA(KH)                                                                               \
+  _Pragma("unroll") for (int x = 0; x < 4; ++x) _Pragma("unroll") for (int y = 0; y < 4; ++y)   \
+      acc[x][y] = mfma_32x32x16(FA[KH][x], FB[KH][y], acc[x][y]);
+#define TP_SB __builtin_amdgcn_sched_barrier(0);
+  // Multiply the registers' stage while reading the next one from LB.
+#define TP_STAGE(LB)                                                                             \
+  TP_MMA(0) TP_SB TP_READ(LB, 0) TP_SB TP_MMA(1) TP_SB TP_READ(LB, 1) TP_SB                      \
+  TP_MMA(2) TP_SB TP_READ(LB, 2) TP_SB TP_MMA(3) TP_SB TP_READ(LB, 3)
+  // Every wave has finished its LDS reads and its DMA has landed; then the barrier.
+#define TP_SYNC()                                    \
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);            \
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);              \
+  __builtin_amdgcn_s_barrier();
+
   f32x16_t acc[4][4];
 #pragma unroll
   for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x16_t{};
-#define TP_COMPUTE(LB)                                                                       \
-  _Pragma("unroll") for (int kh = 0; kh < 2; ++kh) {                                         \
-    uint4 A[4], B[4];                                                                        \
-    _Pragma("unroll") for (int x = 0; x < 4; ++x) A[x] = LB[(wn * 8 + 2 * x) * 64 + kh * 32 + fslot]; \
-    _Pragma("unroll") for (int y = 0; y < 4; ++y)                                            \
-        B[y] = LB[(BIG_T + wm * 8 + 2 * y) * 64 + kh * 32 + fslot];                          \
-    _Pragma("unroll") for (int x = 0; x < 4; ++x)                                            \
-        _Pragma("unroll") for (int y = 0; y < 4; ++y) acc[x][y] = mfma_32x32x16(A[x], B[y], acc[x][y]); \
-  }
 
-  TP_LOAD(RA, 0)
-  TP_STORE(L0, RA)
-  if (ksteps > 1) TP_LOAD(RA, 1)
-  __syncthreads();
-  // Stage ks is in L0 (even) or L1 (odd); RA holds stage ks + 1; RB gets ks + 2.
-  int64_t ks = 0;
-  for (; ks + 1 < ksteps; ks += 2) {
-    if (ks + 2 < ksteps) TP_LOAD(RB, ks + 2)
-    TP_COMPUTE(L0)
-    TP_STORE(L1, RA)
-    __syncthreads();
-    if (ks + 3 < ksteps) TP_LOAD(RA, ks + 3)
-    TP_COMPUTE(L1)
-    if (ks + 2 < ksteps) TP_STORE(L0, RB)
-    __syncthreads();
+  TP_ISSUE(L0, 0)
+  TP_ISSUE(L1, 1)
+  __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): stage 0 has landed
+  __builtin_amdgcn_s_barrier();
+  TP_READ(L0, 0) TP_READ(L0, 1) TP_READ(L0, 2) TP_READ(L0, 3)
+  // The loop runs a whole number of stage pairs; with an odd stage count the
+  // last one is the all-zero padding stage.
+  for (int64_t s = 0; s < nst; s += 2) {
+    // registers: stage s; in flight: s + 1 (L1)
+    TP_SYNC()
+    TP_ISSUE(L0, s + 2)
+    TP_STAGE(L1)
+    // registers: stage s + 1; in flight: s + 2 (L0)
+    TP_SYNC()
+    TP_ISSUE(L1, s + 3)
+    TP_STAGE(L0)
   }
-  if (ks < ksteps) TP_COMPUTE(L0)  // odd k-step count: the last stage sits in L0
-#undef TP_LOAD
-#undef TP_STORE
-#undef TP_COMPUTE
+  // No DMA may still be landing in LDS when the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#undef TP_ISSUE
+#undef TP_READ
+#undef TP_MMA
+#undef TP_SB
+#undef TP_STAGE
+#undef TP_SYNC
 
 #pragma unroll
   for (int y = 0; y < 4; ++y) {
