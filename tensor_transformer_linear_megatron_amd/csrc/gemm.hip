@@ -2,8 +2,8 @@
 // matrix cores ("Tensor vs Pipeline Parallelism", "A worked communication
 // estimate": prompt compute is about 2 x parameters x tokens operations).
 //
-// Two kernels. gemm_big (256 x 256 tiles, 32x32x16 MFMA, stages landed in
-// LDS by DMA) runs whenever the grid fills the GPU; gemm_kernel (128 x 128
+// Two kernels. gemm_big (256 x 256 tiles, 8 wavefronts, 32x32x16 MFMA,
+// stages landed in LDS by DMA) runs whenever the grid fills the GPU; gemm_kernel (128 x 128
 // tiles, 16x16x32 MFMA, register-staged) covers grids too small for that. On
 // gfx950 the 32x32x16 bf16 MFMA sustains about 1.5x the rate of the 16x16x32
 // one when fed from LDS.
@@ -147,8 +147,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// gemm_big: 256 output columns x 256 tokens per workgroup, 4 wavefronts of
-// 128 x 128 (4 x 4 accumulators of v_mfma_f32_32x32x16_bf16, 256 AGPRs).
+// gemm_big: 256 output columns x 256 tokens per workgroup of 8 wavefronts
+// (2 per SIMD, so one wavefront's MFMAs cover the other's waits). Wavefront
+// (wn, wm) owns 128 columns x 64 tokens: 4 x 2 accumulators of
+// v_mfma_f32_32x32x16_bf16.
 //
 //  * A stage is 64 k (two packed k-steps): 32 weight chunks of 1 KiB (tile t,
 //    k-step h at chunk 2t + h, copied verbatim from the packed layout) and
@@ -160,9 +162,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
 //  * Two 64 KiB LDS buffers and one barrier per stage. The barrier both
 //    publishes stage s + 1 (every wave has waited for its own DMA) and frees
 //    the buffer of stage s (every wave has read it), after which the DMA of
-//    stage s + 2 goes into that buffer.
+//    stage s + 2 goes into that buffer, its instructions interleaved with the
+//    first MFMAs.
 //  * A wave keeps the whole stage's fragments in registers (4 k-halves x
-//    (4 weight + 4 token) x 16 bytes). While it multiplies stage s it reads
+//    (4 weight + 2 token) x 16 bytes). While it multiplies stage s it reads
 //    stage s + 1: each k-half's registers are refilled right after their
 //    MFMAs have been issued.
 //  * Rows and tiles past the end fall outside the buffer resource's range
@@ -188,17 +191,19 @@ constexpr int BIG_T = 16;                        // packed tiles per workgroup
 constexpr int BIG_MT = 16;                       // 16-token tiles per workgroup
 constexpr int BIG_WCH = 2 * BIG_T;               // weight chunks per stage
 constexpr int BIG_STAGE_U4 = BIG_WCH * 64 + 256 * 8;  // 64 KiB per stage
+constexpr int BIG_THREADS = 512;
 
 // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
+constexpr int kWaitVm8 = 0x0F78;    // vmcnt(8)
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
 template <int EPI>
-__global__ __launch_bounds__(256) void gemm_big(LinearArgs a, int ntn, int ntm) {
+__global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, int ntm) {
   __shared__ uint4 L0[BIG_STAGE_U4], L1[BIG_STAGE_U4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave & 1, wm = wave >> 1;  // column half, token quarter
 
   // Tile of this workgroup: ids that share an XCD (id mod 8) get consecutive
   // tiles, grouped 8 token tiles deep.
@@ -220,14 +225,14 @@ __global__ __launch_bounds__(256) void gemm_big(LinearArgs a, int ntn, int ntm) 
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.X + m0 * a.ldx), (short)0, (int)(rows * a.ldx * 2), 0x00020000);
 
-  // DMA sources of this wave: weight chunks c = 8 wave + j and token row
-  // blocks 8 wave + j (8 rows x 128 bytes each, one per instruction).
-  unsigned woff[8], xoff[8], kx[8];
+  // DMA sources of this wave: weight chunks c = 4 wave + j and token row
+  // blocks 4 wave + j (8 rows x 128 bytes each, one per instruction).
+  unsigned woff[4], xoff[4], kx[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int c = wave * 8 + j;
+  for (int j = 0; j < 4; ++j) {
+    const int c = wave * 4 + j;
     woff[j] = (unsigned)(((int64_t)(c >> 1) * ksteps + (c & 1)) * 1024 + lane * 16);
-    const int r = wave * 64 + j * 8 + (lane >> 3);
+    const int r = wave * 32 + j * 8 + (lane >> 3);
     const int o = (lane & 7) ^ ((r >> 1) & 7);  // logical octet landing in this lane's slot
     xoff[j] = (unsigned)(((int64_t)r * a.ldx + 8 * o) * 2);
     kx[j] = a.K > 8 * o ? (unsigned)(a.K - 8 * o) : 0u;  // octet inside K while 64 s < kx
@@ -235,33 +240,39 @@ __global__ __launch_bounds__(256) void gemm_big(LinearArgs a, int ntn, int ntm) 
 #define TP_ISSUE(LB, S)                                                                          \
   {                                                                                              \
     const unsigned s_ = (unsigned)(S);                                                           \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
-        rw, (lds_void_t*)&LB[(wave * 8 + j) * 64], 16,                                           \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
+        rw, (lds_void_t*)&LB[(wave * 4 + j) * 64], 16,                                           \
         2 * s_ + (j & 1) < (unsigned)ksteps ? woff[j] + s_ * 2048u : 0x80000000u, 0, 0, 0);      \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
-        rx, (lds_void_t*)&LB[BIG_WCH * 64 + (wave * 8 + j) * 64], 16,                            \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
+        rx, (lds_void_t*)&LB[BIG_WCH * 64 + (wave * 4 + j) * 64], 16,                            \
         64u * s_ < kx[j] ? xoff[j] + s_ * 128u : 0x80000000u, 0, 0, 0);                          \
   }
   // Fragment addresses. 32x32x16 A operand (weights) of block x, k-half kh:
   // lane (h, j) takes tile 2 (4 wn + x) + j / 16, k-step kh / 2, octet
-  // 2 (kh % 2) + h, column j % 16. B operand (tokens): row 128 wm + 32 y + j,
+  // 2 (kh % 2) + h, column j % 16. B operand (tokens): row 64 wm + 32 y + j,
   // octet 2 kh + h, stored at octet position (2 kh + h) ^ ((j >> 1) & 7).
   const int fh = lane >> 5, fj = lane & 31;
   const int fa = (fj >> 4) * 128 + fh * 16 + (fj & 15);
   const int swz = fh ^ ((fj >> 1) & 7);
-  const int fb = BIG_WCH * 64 + (wm * 128 + fj) * 8;
-  uint4 FA[4][4], FB[4][4];
+  const int fb = BIG_WCH * 64 + (wm * 64 + fj) * 8;
+  uint4 FA[4][4], FB[4][2];
 #define TP_READ(LB, KH)                                                                          \
   _Pragma("unroll") for (int x = 0; x < 4; ++x)                                                  \
       FA[KH][x] = LB[(wn * 4 + x) * 256 + ((KH) >> 1) * 64 + ((KH) & 1) * 32 + fa];              \
-  _Pragma("unroll") for (int y = 0; y < 4; ++y) FB[KH][y] = LB[fb + y * 256 + ((2 * (KH)) ^ swz)];
+  _Pragma("unroll") for (int y = 0; y < 2; ++y) FB[KH][y] = LB[fb + y * 256 + ((2 * (KH)) ^ swz)];
 #define TP_MMA(KH)                                                                               \
-  _Pragma("unroll") for (int x = 0; x < 4; ++x) _Pragma("unroll") for (int y = 0; y < 4; ++y)   \
+  _Pragma("unroll") for (int x = 0; x < 4; ++x) _Pragma("unroll") for (int y = 0; y < 2; ++y)   \
       acc[x][y] = mfma_32x32x16(FA[KH][x], FB[KH][y], acc[x][y]);
 #define TP_SB __builtin_amdgcn_sched_barrier(0);
+  // The DMA instructions alternate with the first k-half's MFMAs.
+#define TP_INTERLEAVE                                             \
+  _Pragma("unroll") for (int q = 0; q < 8; ++q) {                 \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* MFMA */ \
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* VMEM */ \
+  }
   // Multiply the registers' stage while reading the next one from LB.
 #define TP_STAGE(LB)                                                                             \
-  TP_MMA(0) TP_SB TP_READ(LB, 0) TP_SB TP_MMA(1) TP_SB TP_READ(LB, 1) TP_SB                      \
+  TP_MMA(0) TP_INTERLEAVE TP_SB TP_READ(LB, 0) TP_SB TP_MMA(1) TP_SB TP_READ(LB, 1) TP_SB        \
   TP_MMA(2) TP_SB TP_READ(LB, 2) TP_SB TP_MMA(3) TP_SB TP_READ(LB, 3)
   // Every wave has finished its LDS reads and its DMA has landed; then the barrier.
 #define TP_SYNC()                                    \
@@ -269,15 +280,15 @@ __global__ __launch_bounds__(256) void gemm_big(LinearArgs a, int ntn, int ntm) 
   __builtin_amdgcn_s_waitcnt(kWaitVm0);              \
   __builtin_amdgcn_s_barrier();
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = f32x16_t{};
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16_t{};
 
   TP_ISSUE(L0, 0)
   TP_ISSUE(L1, 1)
-  __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): stage 0 has landed
+  __builtin_amdgcn_s_waitcnt(kWaitVm8);  // stage 0 has landed
   __builtin_amdgcn_s_barrier();
   TP_READ(L0, 0) TP_READ(L0, 1) TP_READ(L0, 2) TP_READ(L0, 3)
   // The loop runs a whole number of stage pairs; with an odd stage count the
@@ -298,12 +309,13 @@ __global__ __launch_bounds__(256) void gemm_big(LinearArgs a, int ntn, int ntm) 
 #undef TP_READ
 #undef TP_MMA
 #undef TP_SB
+#undef TP_INTERLEAVE
 #undef TP_STAGE
 #undef TP_SYNC
 
 #pragma unroll
-  for (int y = 0; y < 4; ++y) {
-    const int64_t m = m0 + (wm * 4 + y) * 32 + fj;
+  for (int y = 0; y < 2; ++y) {
+    const int64_t m = m0 + (wm * 2 + y) * 32 + fj;
     if (m >= a.M) continue;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -349,9 +361,9 @@ hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, hipStream_t s) {
   if (big) {
     const dim3 grid((unsigned)(ntn * ntm));
     switch (epi) {
-      case kEpiSwiglu: hipLaunchKernelGGL(gemm_big<kEpiSwiglu>, grid, dim3(256), 0, s, a, (int)ntn, (int)ntm); break;
-      case kEpiBf16: hipLaunchKernelGGL(gemm_big<kEpiBf16>, grid, dim3(256), 0, s, a, (int)ntn, (int)ntm); break;
-      case kEpiF32: hipLaunchKernelGGL(gemm_big<kEpiF32>, grid, dim3(256), 0, s, a, (int)ntn, (int)ntm); break;
+      case kEpiSwiglu: hipLaunchKernelGGL(gemm_big<kEpiSwiglu>, grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm); break;
+      case kEpiBf16: hipLaunchKernelGGL(gemm_big<kEpiBf16>, grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm); break;
+      case kEpiF32: hipLaunchKernelGGL(gemm_big<kEpiF32>, grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm); break;
     }
     return hipGetLastError();
   }
