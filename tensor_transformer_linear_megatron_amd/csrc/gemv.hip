@@ -19,12 +19,14 @@
 //    and the epilogue (bf16 rounding, SwiGLU or fp32) runs in registers.
 //  * gemv_shared (16 < M <= 64): at larger M every wavefront would re-read
 //    all the token fragments from L2 for its own tiles, which caps the rate.
-//    Here SN wavefronts of a workgroup own different tiles over the same
-//    k-range and share each chunk of C token k-steps through LDS (double
-//    buffered, one barrier per chunk; the weight ring stays in flight across
-//    it). When the column count is too small to fill the GPU, the k-range is
-//    also split over G workgroups; each writes an fp32 partial and
-//    gemv_fixup adds them in split order and applies the epilogue.
+//    Here SN wavefronts of a workgroup own different 32-column blocks over
+//    the same k-range and share each chunk of C token k-steps through LDS
+//    (double buffered, one barrier per chunk; the weight ring stays in flight
+//    across it). They multiply on v_mfma_f32_32x32x16_bf16, so a token
+//    fragment serves 32 columns and the LDS traffic per weight byte halves.
+//    When the column count is too small to fill the GPU, the k-range is also
+//    split over G workgroups; each writes an fp32 partial and gemv_fixup
+//    adds them in split order and applies the epilogue.
 #include "tp_internal.h"
 
 namespace tpk {
@@ -199,131 +201,158 @@ __global__ __launch_bounds__(LB) void gemv_stream(LinearArgs a, int64_t chunk) {
 // gemv_shared
 // ---------------------------------------------------------------------------
 
-// Partial sums of split y go to part + y * M * pld (pld = ntiles * 16 columns).
-template <int MB, int T, int U, int C, int SN, int EPI>
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 16 < M <= 64 on v_mfma_f32_32x32x16_bf16: a 32-column block (two adjacent
+// packed tiles; for SwiGLU one gate tile and its up tile) times 32 tokens, so
+// each token fragment read from LDS serves 32 output columns.
+//  * Wave w of workgroup x owns block SN x + w for the workgroup's k-range
+//    (split y of G). Its weights stream through a ring of U k-steps of buffer
+//    loads; the A operand of k-half kh is lane (h, j) -> tile 2b + j / 16,
+//    octet 2 kh + h, column j % 16: two contiguous 512-byte runs per load.
+//    Loads past the split or the shard fall outside the buffer range and
+//    read as zero, so the loop has no branches around loads.
+//  * Token fragments (16 tokens x 32 k, the B layout of the 16x16x32 MFMA)
+//    are staged per chunk of C k-steps in LDS, double buffered, loaded two
+//    chunks ahead from clamped addresses and masked when stored (rows past M,
+//    octets past K). The 32x32x16 B operand of 32-token block t, k-half kh is
+//    lane (h, j) -> fragment 2t + j / 16, slot (2 kh + h) * 16 + j % 16.
+//  * Accumulator element r = 4q + e of lane (h, j) is output column
+//    8q + 4h + e of the block for token j: gate column 8q + 4h + e pairs with
+//    up element r + 8.
+//  * With G > 1 each split writes an fp32 partial part[y][m][n] and
+//    gemv_fixup adds them in split order.
+template <int MB32, int U, int C, int SN, int EPI>
 __global__ __launch_bounds__(64 * SN) void gemv_shared(LinearArgs a, int64_t per, float* part) {
   static_assert(C % U == 0, "the ring must divide the chunk");
-  constexpr int F = C * MB;               // token fragments per chunk
-  constexpr int FPW = (F + SN - 1) / SN;  // staged by each wave
+  constexpr int MB16 = 2 * MB32;  // 16-token fragments per k-step
+  constexpr int F = C * MB16;     // token fragments per chunk
+  static_assert(F % SN == 0, "staged fragments divide over the waves");
+  constexpr int FPW = F / SN;
   __shared__ uint4 xs[2 * F * 64];
   const int lane = threadIdx.x & 63, nw = wave_id();
-  const int g = lane >> 4, i = lane & 15;
-  const int64_t tile0 = (int64_t)blockIdx.x * (SN * T) + nw * T;
+  const int g = lane >> 4, i = lane & 15, fh = lane >> 5, fj = lane & 31;
   const int64_t ksteps = a.ksteps;
+  const int64_t blk = (int64_t)blockIdx.x * SN + nw;  // this wave's 32-column block
   const int64_t kbeg = (int64_t)blockIdx.y * per;
   const int64_t kend = kbeg + per < ksteps ? kbeg + per : ksteps;
   const int64_t n = kend > kbeg ? kend - kbeg : 0;  // uniform over the workgroup
   const int64_t nch = (n + C - 1) / C;
-  const uint4* wp = a.W + (tile0 * ksteps + (n > 0 ? kbeg : 0)) * kTileU4 + lane;
 
-  // Staging sources: fragment f = c * MB + mb of a chunk is loaded by wave f % SN.
+  // Weights of this workgroup's 2 SN tiles.
+  const int64_t t0 = (int64_t)blockIdx.x * SN * 2;
+  const int64_t wt = a.ntiles - t0 < 2 * SN ? a.ntiles - t0 : 2 * SN;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.W + t0 * ksteps * kTileU4), (short)0, (int)(wt * ksteps * 1024), 0x00020000);
+  const unsigned wl =
+      (unsigned)(((2 * nw + (fj >> 4)) * ksteps + kbeg) * 1024 + (fh * 16 + (fj & 15)) * 16);
+  uint4 wb[U][2];
+#define TP_WLOAD(SLOT, KS)                                                                     \
+  _Pragma("unroll") for (int kh = 0; kh < 2; ++kh) wb[SLOT][kh] = __builtin_bit_cast(         \
+      uint4, __builtin_amdgcn_raw_buffer_load_b128(                                            \
+                 rw, (KS) < n ? wl + (unsigned)(KS) * 1024u + kh * 512u : 0x80000000u, 0, 0));
+
+  // Staging: fragment f = c MB16 + mb of a chunk is loaded by wave f % SN.
   TokenRow sr[FPW];
-  int sc[FPW];
 #pragma unroll
-  for (int j = 0; j < FPW; ++j) {
-    const int f = nw + j * SN;
-    const int fc = f < F ? f : 0;
-    sr[j] = token_row(a, (fc % MB) * 16 + i, g);
-    sc[j] = fc / MB;
-  }
+  for (int j = 0; j < FPW; ++j) sr[j] = token_row(a, ((nw + j * SN) % MB16) * 16 + i, g);
   const int64_t xk0 = kbeg * kTileK;
+  uint4 st[FPW];
+#define TP_KOFF(CH, J) (xk0 + ((int64_t)(CH) * C + (nw + (J) * SN) / MB16) * kTileK)
+#define TP_SLOAD(CH) _Pragma("unroll") for (int j = 0; j < FPW; ++j) st[j] = sr[j].load(TP_KOFF(CH, j));
+#define TP_SSTORE(BUF, CH)                             \
+  _Pragma("unroll") for (int j = 0; j < FPW; ++j)      \
+      xs[((BUF) * F + nw + j * SN) * 64 + lane] = sr[j].use(st[j], TP_KOFF(CH, j));
 
-  f32x4_t acc[T][MB];
+  f32x16_t acc[MB32];
 #pragma unroll
-  for (int t = 0; t < T; ++t)
+  for (int t = 0; t < MB32; ++t) acc[t] = f32x16_t{};
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[t][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint4 wb[U][T], st[FPW];
-
-#define TP_STAGE_LOAD(CH)                                  \
-  _Pragma("unroll") for (int j = 0; j < FPW; ++j)          \
-      st[j] = sr[j].get(xk0 + ((int64_t)(CH) * C + sc[j]) * kTileK);
-#define TP_STAGE_STORE(BUF)                                \
-  _Pragma("unroll") for (int j = 0; j < FPW; ++j) {        \
-    const int f = nw + j * SN;                             \
-    if (f < F) xs[((BUF) * F + f) * 64 + lane] = st[j];    \
-  }
-
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (u < n)
-#pragma unroll
-      for (int t = 0; t < T; ++t) wb[u][t] = load_w(wp + ((int64_t)t * ksteps + u) * kTileU4);
-  if (nch > 0) {
-    TP_STAGE_LOAD(0)
-    TP_STAGE_STORE(0)
-  }
-  if (nch > 1) {
-    TP_STAGE_LOAD(1)
-  }
+  for (int u = 0; u < U; ++u) { TP_WLOAD(u, u) }
+  TP_SLOAD(0)
+  TP_SSTORE(0, 0)
+  if (nch > 1) { TP_SLOAD(1) }
   __syncthreads();
 
+  const int xsl = (fj >> 4) * 64 + fh * 16 + (fj & 15);
   for (int64_t ch = 0; ch < nch; ++ch) {
     const int buf = (int)(ch & 1);
     const int64_t c0 = ch * C;
-    if (c0 + C + U <= n) {
-      // Every step of this chunk and every refill target exist: no branches.
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        uint4 xf[MB];
+    for (int c = 0; c < C; ++c) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) xf[mb] = xs[((buf * C + c) * MB + mb) * 64 + lane];
+      for (int kh = 0; kh < 2; ++kh) {
+        uint4 xf[MB32];
 #pragma unroll
-        for (int t = 0; t < T; ++t)
+        for (int t = 0; t < MB32; ++t) xf[t] = xs[((buf * C + c) * MB16 + 2 * t) * 64 + kh * 32 + xsl];
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[t][mb] = mfma_16x16x32(wb[c % U][t], xf[mb], acc[t][mb]);
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-          wb[c % U][t] = load_w(wp + ((int64_t)t * ksteps + c0 + c + U) * kTileU4);
+        for (int t = 0; t < MB32; ++t) acc[t] = mfma_32x32x16(wb[c % U][kh], xf[t], acc[t]);
       }
-    } else {
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        if (c0 + c < n) {
-          uint4 xf[MB];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) xf[mb] = xs[((buf * C + c) * MB + mb) * 64 + lane];
-#pragma unroll
-          for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[t][mb] = mfma_16x16x32(wb[c % U][t], xf[mb], acc[t][mb]);
-          if (c0 + c + U < n)
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-              wb[c % U][t] = load_w(wp + ((int64_t)t * ksteps + c0 + c + U) * kTileU4);
-        }
-      }
+      TP_WLOAD(c % U, c0 + c + U)
     }
     if (ch + 1 < nch) {
-      TP_STAGE_STORE(buf ^ 1)
-      if (ch + 2 < nch) {
-        TP_STAGE_LOAD(ch + 2)
-      }
+      TP_SSTORE(buf ^ 1, ch + 1)
+      if (ch + 2 < nch) { TP_SLOAD(ch + 2) }
     }
     __syncthreads();
   }
-#undef TP_STAGE_LOAD
-#undef TP_STAGE_STORE
+#undef TP_WLOAD
+#undef TP_KOFF
+#undef TP_SLOAD
+#undef TP_SSTORE
 
+  const int64_t nblk = (a.ntiles + 1) / 2;
+  if (blk >= nblk) return;
   if (part == nullptr) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      f32x4_t v[T];
+    for (int t = 0; t < MB32; ++t) {
+      const int64_t m = t * 32 + fj;
+      if (m >= a.M) continue;
+      const f32x16_t& v = acc[t];
+      if constexpr (EPI == kEpiSwiglu) {
 #pragma unroll
-      for (int t = 0; t < T; ++t) v[t] = acc[t][mb];
-      epilogue<EPI, T>(a, v, mb * 16 + i, tile0, g);
+        for (int q = 0; q < 2; ++q) {
+          const int64_t col = blk * kTileN + 8 * q + 4 * fh;
+          if (col < a.out_n)
+            store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + col, swiglu(v[4 * q], v[4 * q + 8]),
+                         swiglu(v[4 * q + 1], v[4 * q + 9]), swiglu(v[4 * q + 2], v[4 * q + 10]),
+                         swiglu(v[4 * q + 3], v[4 * q + 11]));
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = blk * 2 * kTileN + 8 * q + 4 * fh;
+          if (col >= a.out_n) continue;
+          if constexpr (EPI == kEpiBf16) {
+            store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + col, v[4 * q], v[4 * q + 1],
+                         v[4 * q + 2], v[4 * q + 3]);
+          } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + m * a.ldo + col) =
+                make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+          }
+        }
+      }
     }
   } else {
     const int64_t pld = a.ntiles * kTileN;
     float* p = part + (int64_t)blockIdx.y * a.M * pld;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int64_t m = mb * 16 + i;
+    for (int t = 0; t < MB32; ++t) {
+      const int64_t m = t * 32 + fj;
       if (m >= a.M) continue;
 #pragma unroll
-      for (int t = 0; t < T; ++t)
-        *reinterpret_cast<float4*>(p + m * pld + (tile0 + t) * kTileN + g * 4) =
-            make_float4(acc[t][mb][0], acc[t][mb][1], acc[t][mb][2], acc[t][mb][3]);
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = blk * 2 * kTileN + 8 * q + 4 * fh;
+        if (col < pld)
+          *reinterpret_cast<float4*>(p + m * pld + col) =
+              make_float4(acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]);
+      }
     }
   }
 }
@@ -408,43 +437,39 @@ hipError_t launch_stream(const LinearArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// How gemv_shared splits the work: SN waves per workgroup, G splits of the
-// k-range of `per` k-steps each (a multiple of the chunk).
+// How gemv_shared splits the work: SN waves (one 32-column block each) per
+// workgroup, G splits of the k-range of `per` k-steps each (a multiple of the
+// chunk), G the smallest power of two that gives ~200 workgroups while each
+// split keeps at least 2 chunks.
 struct SharedPlan {
-  int SN, G;
-  int64_t per;
+  int G;
+  int64_t per, groups;
 };
 
-constexpr int shared_chunk(int MB) { return MB >= 4 ? 4 : 8; }
+constexpr int kSharedSN = 4;
+constexpr int shared_chunk(int MB32) { return MB32 >= 2 ? 4 : 8; }
 
-SharedPlan plan_shared(int64_t ntiles, int64_t ksteps, int MB, int T) {
+SharedPlan plan_shared(int64_t ntiles, int64_t ksteps, int MB32) {
   SharedPlan p;
-  p.SN = 8;
-  while (p.SN > 1 && (ntiles / T) % p.SN) p.SN >>= 1;
-  const int64_t groups = ntiles / (T * p.SN);
-  const int C = shared_chunk(MB);
-  // Aim for ~224+ workgroups while keeping >= 4 chunks of k per split.
+  const int64_t nblk = (ntiles + 1) / 2;
+  p.groups = (nblk + kSharedSN - 1) / kSharedSN;
+  const int C = shared_chunk(MB32);
   int G = 1;
-  while (groups * G < 224 && ksteps / (2 * G) >= 4 * C) G <<= 1;
+  while (p.groups * G < 200 && ksteps / (2 * G) >= 2 * C) G <<= 1;
   p.per = ((ksteps + G - 1) / G + C - 1) / C * C;
   p.G = (int)((ksteps + p.per - 1) / p.per);
   return p;
 }
 
-template <int MB, int T, int EPI>
+template <int MB32, int EPI>
 hipError_t launch_shared(const LinearArgs& a, float* ws, hipStream_t s) {
-  const SharedPlan p = plan_shared(a.ntiles, a.ksteps, MB, T);
-  constexpr int C = shared_chunk(MB);
-  constexpr int U = MB >= 4 ? 4 : 8;
+  const SharedPlan p = plan_shared(a.ntiles, a.ksteps, MB32);
+  constexpr int C = shared_chunk(MB32);
+  constexpr int U = C;
   if (p.G > 1 && ws == nullptr) return hipErrorInvalidValue;
   float* part = p.G > 1 ? ws : nullptr;
-  const dim3 grid((unsigned)(a.ntiles / (T * p.SN)), (unsigned)p.G);
-  switch (p.SN) {
-    case 8: hipLaunchKernelGGL((gemv_shared<MB, T, U, C, 8, EPI>), grid, dim3(512), 0, s, a, p.per, part); break;
-    case 4: hipLaunchKernelGGL((gemv_shared<MB, T, U, C, 4, EPI>), grid, dim3(256), 0, s, a, p.per, part); break;
-    case 2: hipLaunchKernelGGL((gemv_shared<MB, T, U, C, 2, EPI>), grid, dim3(128), 0, s, a, p.per, part); break;
-    default: hipLaunchKernelGGL((gemv_shared<MB, T, U, C, 1, EPI>), grid, dim3(64), 0, s, a, p.per, part); break;
-  }
+  hipLaunchKernelGGL((gemv_shared<MB32, U, C, kSharedSN, EPI>), dim3((unsigned)p.groups, (unsigned)p.G),
+                     dim3(64 * kSharedSN), 0, s, a, p.per, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.G == 1) return e;
   const int64_t pld = a.ntiles * kTileN;
@@ -458,9 +483,9 @@ template <int T, int EPI>
 hipError_t launch_t(const LinearArgs& a, float* ws, hipStream_t s) {
   switch ((a.M + 15) / 16) {
     case 1: return launch_stream<1, T, EPI>(a, s);
-    case 2: return launch_shared<2, T, EPI>(a, ws, s);
-    case 3: return launch_shared<3, T, EPI>(a, ws, s);
-    case 4: return launch_shared<4, T, EPI>(a, ws, s);
+    case 2: return launch_shared<1, EPI>(a, ws, s);
+    case 3:
+    case 4: return launch_shared<2, EPI>(a, ws, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -469,8 +494,8 @@ hipError_t launch_t(const LinearArgs& a, float* ws, hipStream_t s) {
 
 size_t gemv_workspace_bytes(int64_t M, int64_t ksteps, int64_t ntiles, Epilogue epi) {
   if (M <= 16 || M > 64) return 0;
-  const int MB = (int)((M + 15) / 16);
-  const SharedPlan p = plan_shared(ntiles, ksteps, MB, epi == kEpiSwiglu ? 2 : 1);
+  (void)epi;
+  const SharedPlan p = plan_shared(ntiles, ksteps, (int)((M + 31) / 32));
   return p.G > 1 ? (size_t)p.G * M * ntiles * kTileN * sizeof(float) : 0;
 }
 
