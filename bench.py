@@ -207,8 +207,9 @@ def run_decode(args):
     # The dominant kernel: the kernel symbol with the largest share of the
     # step. Batches of up to 16 tokens share one decode kernel instantiation.
     def symbol(M, part):
-        fam = "gemv_stream<1," if M <= 16 else f"gemv_shared<{(M + 15) // 16},"
-        return fam + ("2,..,SwiGLU>" if part == "gateup" else "1,..,fp32>")
+        if M <= 16:
+            return "gemv_stream<1," + ("2,..,SwiGLU>" if part == "gateup" else "1,..,fp32>")
+        return f"gemv_shared<{(M + 15) // 16},.." + (",SwiGLU>" if part == "gateup" else ",fp32>")
     groups = {}
     for M in DECODE_MS:
         gb, db, _ = decode_bytes(M, H, I)
