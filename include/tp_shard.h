@@ -144,7 +144,8 @@ TP_API tp_status tp_shard_plan(tp_kind kind, int64_t K, int64_t N, int32_t t, in
  *   W        device, full logical [K x N] bf16, row-major, leading dim ldw >= N
  *   W_packed device, desc->packed_bytes bytes, 16-byte aligned; its layout is
  *            private to the library (tiles of 16 output columns x 32 k,
- *            zero-padded to packed_n x packed_k, gate/up tiles interleaved).
+ *            zero-padded to packed_n x packed_k, pairs of tiles interleaved
+ *            by k-step, gate/up tiles paired).
  */
 TP_API tp_status tp_shard_pack(const tp_shard_desc* desc, const uint16_t* W, int64_t ldw,
                         void* W_packed, hipStream_t stream);

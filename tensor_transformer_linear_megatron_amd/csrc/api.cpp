@@ -18,7 +18,7 @@ tp_status check_desc(const tp_shard_desc* d) {
   if (!is_col(d->kind) && !is_row(d->kind)) return TP_ERR_KIND;
   const bool gateup = d->kind == TP_GATEUP_COL;
   if (d->shard_k <= 0 || d->shard_n <= 0 || d->out_n <= 0 || d->packed_k < d->shard_k ||
-      d->packed_k % tpk::kTileK || d->packed_n % tpk::kTileN ||
+      d->packed_k % tpk::kTileK || d->packed_n % (2 * tpk::kTileN) ||
       d->packed_bytes != d->packed_k * d->packed_n * 2)
     return TP_ERR_SHAPE;
   if (gateup) {

@@ -45,7 +45,7 @@ __device__ __forceinline__ void load_stage(uint4 (&rw)[4], uint4 (&rx)[4], const
     const int tl = c >> 6, l = c & 63;  // local tile index (nt_l * KS + ks_l), lane
     const int64_t nt = nt0 + (tl >> 1), ks = st * KS + (tl & 1);
     uint4 v = zero;
-    if (nt < ntiles && ks < ksteps) v = W[(nt * ksteps + ks) * kTileU4 + l];
+    if (nt < ntiles && ks < ksteps) v = W[tile_index(nt, ks, ksteps) * kTileU4 + l];
     rw[j] = v;
   }
 #pragma unroll
@@ -153,7 +153,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
 // v_mfma_f32_32x32x16_bf16.
 //
 //  * A stage is 64 k (two packed k-steps): 32 weight chunks of 1 KiB (tile t,
-//    k-step h at chunk 2t + h, copied verbatim from the packed layout) and
+//    k-step h at chunk 2t + h, copied verbatim from the packed layout, where
+//    a tile pair's two stage k-steps are 4 contiguous KiB) and
 //    256 token rows of 128 bytes. Stages land in LDS by buffer-load-to-LDS
 //    DMA: no staging registers and no LDS store instructions. Each token row
 //    is read as a whole 128-byte line; its octet o is stored at position
@@ -231,7 +232,8 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int c = wave * 4 + j;
-    woff[j] = (unsigned)(((int64_t)(c >> 1) * ksteps + (c & 1)) * 1024 + lane * 16);
+    // tile tt = c >> 1 of the workgroup (nt0 is even), k-step h = c & 1 of the stage
+    woff[j] = (unsigned)(tile_index(c >> 1, c & 1, ksteps) * 1024 + lane * 16);
     const int r = wave * 32 + j * 8 + (lane >> 3);
     const int o = (lane & 7) ^ ((r >> 1) & 7);  // logical octet landing in this lane's slot
     xoff[j] = (unsigned)(((int64_t)r * a.ldx + 8 * o) * 2);
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
     const unsigned s_ = (unsigned)(S);                                                           \
     _Pragma("unroll") for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
         rw, (lds_void_t*)&LB[(wave * 4 + j) * 64], 16,                                           \
-        2 * s_ + (j & 1) < (unsigned)ksteps ? woff[j] + s_ * 2048u : 0x80000000u, 0, 0, 0);      \
+        2 * s_ + (j & 1) < (unsigned)ksteps ? woff[j] + s_ * 4096u : 0x80000000u, 0, 0, 0);      \
     _Pragma("unroll") for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
         rx, (lds_void_t*)&LB[BIG_WCH * 64 + (wave * 4 + j) * 64], 16,                            \
         64u * s_ < kx[j] ? xoff[j] + s_ * 128u : 0x80000000u, 0, 0, 0);                          \

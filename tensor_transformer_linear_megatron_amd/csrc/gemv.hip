@@ -108,6 +108,7 @@ __device__ __forceinline__ void epilogue(const LinearArgs& a, const f32x4_t (&v)
 
 template <int MB, int T, int U, int EPI, int LB>
 __global__ __launch_bounds__(LB) void gemv_stream(LinearArgs a, int64_t chunk) {
+  static_assert(T == 1 || T == 2, "one tile or one tile pair per workgroup");
   extern __shared__ f32x4_t red[];  // [S][T][MB][64]
   const int lane = threadIdx.x & 63, wave = wave_id(), S = blockDim.x >> 6;
   const int g = lane >> 4, i = lane & 15;
@@ -116,7 +117,9 @@ __global__ __launch_bounds__(LB) void gemv_stream(LinearArgs a, int64_t chunk) {
   const int64_t k0 = (int64_t)wave * chunk;
   const int64_t k1 = k0 + chunk < ksteps ? k0 + chunk : ksteps;
   const int64_t n = k1 > k0 ? k1 - k0 : 0;
-  const uint4* wp = a.W + (tile0 * ksteps + (n > 0 ? k0 : 0)) * kTileU4 + lane;
+  // A pair's k-steps alternate between its two tiles: with T = 2 the wave
+  // reads one contiguous stream, with T = 1 every other KiB of it.
+  const uint4* wp = a.W + tile_index(tile0, n > 0 ? k0 : 0, ksteps) * kTileU4 + lane;
   TokenRow xr[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) xr[mb] = token_row(a, mb * 16 + i, g);
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(LB) void gemv_stream(LinearArgs a, int64_t chunk) {
 #define TP_FILL(SLOT, STEP)                                                                \
   {                                                                                        \
     _Pragma("unroll") for (int t = 0; t < T; ++t)                                          \
-        wb[SLOT][t] = load_w(wp + ((int64_t)t * ksteps + (STEP)) * kTileU4);               \
+        wb[SLOT][t] = load_w(wp + ((int64_t)(STEP) * 2 + t) * kTileU4);                    \
     _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                      \
         xb[SLOT][mb] = xr[mb].load(xk0 + (STEP) * kTileK);                                 \
   }
@@ -250,13 +253,15 @@ __global__ __launch_bounds__(64 * SN) void gemv_shared(LinearArgs a, int64_t per
   const int64_t wt = a.ntiles - t0 < 2 * SN ? a.ntiles - t0 : 2 * SN;
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.W + t0 * ksteps * kTileU4), (short)0, (int)(wt * ksteps * 1024), 0x00020000);
+  // Pair nw of the workgroup, tile (fj >> 4) of the pair: k-step s at 1 KiB
+  // index (nw ksteps + s) 2 + (fj >> 4).
   const unsigned wl =
-      (unsigned)(((2 * nw + (fj >> 4)) * ksteps + kbeg) * 1024 + (fh * 16 + (fj & 15)) * 16);
+      (unsigned)((((int64_t)nw * ksteps + kbeg) * 2 + (fj >> 4)) * 1024 + (fh * 16 + (fj & 15)) * 16);
   uint4 wb[U][2];
 #define TP_WLOAD(SLOT, KS)                                                                     \
   _Pragma("unroll") for (int kh = 0; kh < 2; ++kh) wb[SLOT][kh] = __builtin_bit_cast(         \
       uint4, __builtin_amdgcn_raw_buffer_load_b128(                                            \
-                 rw, (KS) < n ? wl + (unsigned)(KS) * 1024u + kh * 512u : 0x80000000u, 0, 0));
+                 rw, (KS) < n ? wl + (unsigned)(KS) * 2048u + kh * 512u : 0x80000000u, 0, 0));
 
   // Staging: fragment f = c MB16 + mb of a chunk is loaded by wave f % SN.
   TokenRow sr[FPW];
@@ -418,10 +423,12 @@ int pow2_at_least(int64_t v) {
 
 template <int MB, int T, int EPI>
 hipError_t launch_stream(const LinearArgs& a, hipStream_t s) {
-  const int64_t groups = a.ntiles / T;
-  // Enough wavefronts for ~1500 rings in flight, at most 16 per workgroup,
-  // and at least 8 k-steps each.
-  int S = pow2_at_least((1536 + groups - 1) / groups);
+  const int64_t groups = (a.ntiles + T - 1) / T;
+  // Wavefronts per workgroup (each takes a contiguous k-range). Measured on
+  // MI355X: a wave that streams a whole tile pair is fastest once the pairs
+  // alone give ~900 waves; otherwise ~1500 (pairs) or ~2000 (single tiles)
+  // waves in flight; at least 8 k-steps per wave.
+  int S = (T == 2 && groups >= 768) ? 1 : pow2_at_least(((T == 2 ? 1536 : 2048) + groups - 1) / groups);
   if (S > 16) S = 16;
   while (S > 1 && a.ksteps / S < 8) S >>= 1;
   const int64_t chunk = (a.ksteps + S - 1) / S;
@@ -429,7 +436,7 @@ hipError_t launch_stream(const LinearArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)groups), block(64 * S);
   if (S <= 4) {
     hipLaunchKernelGGL((gemv_stream<MB, T, 8, EPI, 256>), grid, block, lds, s, a, chunk);
-  } else if (S <= 8) {
+  } else if (S <= 8 && T == 2) {
     hipLaunchKernelGGL((gemv_stream<MB, T, 8, EPI, 512>), grid, block, lds, s, a, chunk);
   } else {
     hipLaunchKernelGGL((gemv_stream<MB, T, 4, EPI, 1024>), grid, block, lds, s, a, chunk);
@@ -503,8 +510,11 @@ hipError_t launch_gemv(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t
   if (a.M <= 0 || a.ntiles == 0) return hipSuccess;
   switch (epi) {
     case kEpiSwiglu: return launch_t<2, kEpiSwiglu>(a, ws, s);
-    case kEpiBf16: return launch_t<1, kEpiBf16>(a, ws, s);
-    case kEpiF32: return launch_t<1, kEpiF32>(a, ws, s);
+    // Other kinds stream tile pairs only when the pairs still fill the GPU.
+    case kEpiBf16:
+      return a.ntiles >= 512 ? launch_t<2, kEpiBf16>(a, ws, s) : launch_t<1, kEpiBf16>(a, ws, s);
+    case kEpiF32:
+      return a.ntiles >= 512 ? launch_t<2, kEpiF32>(a, ws, s) : launch_t<1, kEpiF32>(a, ws, s);
   }
   return hipErrorInvalidValue;
 }

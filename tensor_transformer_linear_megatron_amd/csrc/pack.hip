@@ -10,8 +10,10 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int64_t total_u4)
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= total_u4) return;
   const int lane = (int)(c & 63);
-  const int64_t tile = c >> 6;
-  const int64_t nt = tile / a.ksteps, ks = tile - nt * a.ksteps;
+  // 1 KiB index -> (tile pair, k-step, tile of the pair); see tile_index().
+  const int64_t idx = c >> 6;
+  const int64_t pair = idx / (2 * a.ksteps), rem = idx - pair * 2 * a.ksteps;
+  const int64_t ks = rem >> 1, nt = 2 * pair + (rem & 1);
   const int g = lane >> 4, i = lane & 15;
 
   // Shard column of this lane and whether it exists.

@@ -129,8 +129,9 @@ extern "C" tp_status tp_shard_plan(tp_kind kind, int64_t K, int64_t N, int32_t t
   if (d.shard_k % 8 || d.out_n % 8 || d.shard_n % 8) return TP_ERR_ALIGN;
 
   d.packed_k = round_up(d.shard_k, tpk::kTileK);
+  // Whole tile pairs (32 columns); gate/up pairs are a gate and an up tile.
   d.packed_n = kind == TP_GATEUP_COL ? 2 * round_up(d.out_n, tpk::kTileN)
-                                     : round_up(d.shard_n, tpk::kTileN);
+                                     : round_up(d.shard_n, 2 * tpk::kTileN);
   d.packed_bytes = d.packed_k * d.packed_n * 2;
   *out = d;
   return TP_OK;

@@ -11,10 +11,12 @@
 namespace tpk {
 
 // Packed weight layout (written by tp_shard_pack, read by every linear):
-// the shard, zero-padded to [packed_k x packed_n], is cut into tiles of
-// kTileN output columns x kTileK k. Tile (nt, ks) sits at tile index
-// nt * (packed_k / kTileK) + ks, 1 KiB each, so one tile column (all k of
-// 16 outputs) is contiguous. Inside a tile, lane l = 16 g + i of a wavefront
+// the shard, zero-padded to [packed_k x packed_n] (packed_n a multiple of
+// 32), is cut into tiles of kTileN output columns x kTileK k, 1 KiB each.
+// Tiles come in pairs (2p, 2p + 1) whose k-steps alternate: tile (nt, ks)
+// sits at 1 KiB index tile_index(nt, ks) = ((nt >> 1) * ksteps + ks) * 2 +
+// (nt & 1). A pair's whole k range (32 output columns) is one contiguous
+// run, read front to back as a single stream. Inside a tile, lane l = 16 g + i of a wavefront
 // owns 16 bytes at offset 16 l: the 8 values W[ks*32 + 8g + e][nt*16 + i],
 // e = 0..7 -- exactly the A operand of v_mfma_f32_16x16x32_bf16 with output
 // columns as MFMA rows. A wavefront therefore loads a whole tile with one
@@ -24,6 +26,11 @@ namespace tpk {
 constexpr int kTileN = 16;
 constexpr int kTileK = 32;
 constexpr int kTileU4 = 64;  // uint4 per tile
+
+// 1 KiB index of tile (nt, ks) in the packed layout.
+__host__ __device__ __forceinline__ int64_t tile_index(int64_t nt, int64_t ks, int64_t ksteps) {
+  return ((nt >> 1) * ksteps + ks) * 2 + (nt & 1);
+}
 
 enum Epilogue { kEpiBf16 = 0, kEpiSwiglu = 1, kEpiF32 = 2 };
 

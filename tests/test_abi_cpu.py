@@ -90,7 +90,7 @@ def test_plan_matches_oracle_planner(kind, K, N, t, r, heads):
         assert (d.kv_head_begin, d.kv_head_end) == want["kv_heads"]
         assert bool(d.kv_replicated) == want["kv_replicated"]
     assert d.out_n == (d.shard_n // 2 if kind == "gateup_col" else d.shard_n)
-    assert d.packed_k % 32 == 0 and d.packed_n % 16 == 0 and d.packed_k >= d.shard_k
+    assert d.packed_k % 32 == 0 and d.packed_n % 32 == 0 and d.packed_k >= d.shard_k
     assert d.packed_bytes == d.packed_k * d.packed_n * 2
     assert d.path == tp.TP_PATH_AUTO
 

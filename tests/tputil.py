@@ -53,12 +53,15 @@ def full_device(shape, blocks, dtype=torch.bfloat16) -> torch.Tensor:
 
 def unpack(desc, packed: torch.Tensor) -> np.ndarray:
     """Read the packed tiles back into the logical shard [shard_k x shard_n]:
-    tile (nt, ks) is 1 KiB at tile index nt * ksteps + ks; lane l = 16 g + i
-    holds W[32 ks + 8 g + e][16 nt + i], e = 0..7; for gate/up, packed tile
-    2j is gate tile j and 2j + 1 is up tile j."""
+    tiles come in pairs (2p, 2p + 1) whose k-steps alternate, so tile
+    (nt, ks) is 1 KiB at index ((nt // 2) * ksteps + ks) * 2 + nt % 2; lane
+    l = 16 g + i holds W[32 ks + 8 g + e][16 nt + i], e = 0..7; for gate/up,
+    packed tile 2j is gate tile j and 2j + 1 is up tile j."""
     ks_n = desc.packed_k // 32
     nt_n = desc.packed_n // 16
-    p = packed.view(torch.int16).cpu().numpy().view(np.uint16).reshape(nt_n, ks_n, 4, 16, 8)
+    assert nt_n % 2 == 0
+    q = packed.view(torch.int16).cpu().numpy().view(np.uint16).reshape(nt_n // 2, ks_n, 2, 4, 16, 8)
+    p = q.transpose(0, 2, 1, 3, 4, 5).reshape(nt_n, ks_n, 4, 16, 8)
     # -> [nt, i, ks, g, e] -> columns (nt, i), rows (ks, g, e)
     t = p.transpose(0, 3, 1, 2, 4).reshape(nt_n * 16, ks_n * 32)
     if desc.kind == 2:  # gate/up interleaved by tile
