@@ -189,52 +189,63 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(uint4 a, uint4 b, f32x16_t c) 
 }
 
 constexpr int BIG_T = 16;                        // packed tiles per workgroup
-constexpr int BIG_MT = 16;                       // 16-token tiles per workgroup
+constexpr int BIG_MT = 16;                       // 16-token tiles per full-height workgroup
 constexpr int BIG_WCH = 2 * BIG_T;               // weight chunks per stage
-constexpr int BIG_STAGE_U4 = BIG_WCH * 64 + 256 * 8;  // 64 KiB per stage
 constexpr int BIG_THREADS = 512;
 
 // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
-constexpr int kWaitVm8 = 0x0F78;    // vmcnt(8)
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
-template <int EPI>
-__global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, int ntm) {
-  __shared__ uint4 L0[BIG_STAGE_U4], L1[BIG_STAGE_U4];
+// TB = 2: 256 x 256 tiles, workgroup x takes tile x of the launch. TB = 1:
+// 128-token half tiles, workgroup x takes half x & 1 of tile tile_base +
+// x / 2 (the last, partial round of a grid, split so that it fills the GPU).
+template <int EPI, int TB>
+__global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, int ntm, int tile_base) {
+  constexpr int ROWS = 128 * TB;                       // tokens per workgroup
+  constexpr int XI = 2 * TB;                           // token DMA instructions per wave and stage
+  constexpr int STAGE_U4 = BIG_WCH * 64 + ROWS * 8;    // 64 or 48 KiB per stage
+  __shared__ uint4 L0[STAGE_U4], L1[STAGE_U4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;  // column half, token quarter
 
   // Tile of this workgroup: ids that share an XCD (id mod 8) get consecutive
   // tiles, grouped 8 token tiles deep.
-  int bid = blockIdx.x;
-  const int nb = ntn * ntm, per = nb / 8;
-  if (bid < per * 8) bid = (bid % 8) * per + bid / 8;
+  int bid = TB == 2 ? (int)blockIdx.x : tile_base + (int)(blockIdx.x >> 1);
+  if (TB == 2) {
+    const int per = (int)gridDim.x / 8;
+    if (bid < per * 8) bid = (bid % 8) * per + bid / 8;
+  }
   constexpr int GM = 8;
   const int first_m = bid / (GM * ntn) * GM;
   const int gsize = ntm - first_m < GM ? ntm - first_m : GM;
   const int tm = first_m + (bid % (GM * ntn)) % gsize;
   const int tn = (bid % (GM * ntn)) / gsize;
-  const int64_t nt0 = (int64_t)tn * BIG_T, m0 = (int64_t)tm * (BIG_MT * 16);
+  const int64_t nt0 = (int64_t)tn * BIG_T;
+  const int64_t m0 = (int64_t)tm * (BIG_MT * 16) + (TB == 1 ? (int64_t)(blockIdx.x & 1) * ROWS : 0);
   const int64_t ksteps = a.ksteps, nst = (ksteps + 1) / 2;
 
   const int64_t wt = a.ntiles - nt0 < BIG_T ? a.ntiles - nt0 : BIG_T;
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.W + nt0 * ksteps * kTileU4), (short)0, (int)(wt * ksteps * 1024), 0x00020000);
-  const int64_t rows = a.M - m0 < BIG_MT * 16 ? a.M - m0 : BIG_MT * 16;
+  // A second half tile can lie wholly past M: then no row is in range.
+  const int64_t rows = a.M - m0 < ROWS ? (a.M > m0 ? a.M - m0 : 0) : ROWS;
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.X + m0 * a.ldx), (short)0, (int)(rows * a.ldx * 2), 0x00020000);
 
   // DMA sources of this wave: weight chunks c = 4 wave + j and token row
-  // blocks 4 wave + j (8 rows x 128 bytes each, one per instruction).
-  unsigned woff[4], xoff[4], kx[4];
+  // blocks XI wave + j (8 rows x 128 bytes each, one per instruction).
+  unsigned woff[4], xoff[4], kx[4];  // the token arrays use their first XI entries
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int c = wave * 4 + j;
     // tile tt = c >> 1 of the workgroup (nt0 is even), k-step h = c & 1 of the stage
     woff[j] = (unsigned)(tile_index(c >> 1, c & 1, ksteps) * 1024 + lane * 16);
-    const int r = wave * 32 + j * 8 + (lane >> 3);
+  }
+#pragma unroll
+  for (int j = 0; j < XI; ++j) {
+    const int r = (wave * XI + j) * 8 + (lane >> 3);
     const int o = (lane & 7) ^ ((r >> 1) & 7);  // logical octet landing in this lane's slot
     xoff[j] = (unsigned)(((int64_t)r * a.ldx + 8 * o) * 2);
     kx[j] = a.K > 8 * o ? (unsigned)(a.K - 8 * o) : 0u;  // octet inside K while 64 s < kx
@@ -245,25 +256,25 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
     _Pragma("unroll") for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
         rw, (lds_void_t*)&LB[(wave * 4 + j) * 64], 16,                                           \
         2 * s_ + (j & 1) < (unsigned)ksteps ? woff[j] + s_ * 4096u : 0x80000000u, 0, 0, 0);      \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
-        rx, (lds_void_t*)&LB[BIG_WCH * 64 + (wave * 4 + j) * 64], 16,                            \
+    _Pragma("unroll") for (int j = 0; j < XI; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(     \
+        rx, (lds_void_t*)&LB[BIG_WCH * 64 + (wave * XI + j) * 64], 16,                           \
         64u * s_ < kx[j] ? xoff[j] + s_ * 128u : 0x80000000u, 0, 0, 0);                          \
   }
   // Fragment addresses. 32x32x16 A operand (weights) of block x, k-half kh:
   // lane (h, j) takes tile 2 (4 wn + x) + j / 16, k-step kh / 2, octet
-  // 2 (kh % 2) + h, column j % 16. B operand (tokens): row 64 wm + 32 y + j,
+  // 2 (kh % 2) + h, column j % 16. B operand (tokens): row 32 (TB wm + y) + j,
   // octet 2 kh + h, stored at octet position (2 kh + h) ^ ((j >> 1) & 7).
   const int fh = lane >> 5, fj = lane & 31;
   const int fa = (fj >> 4) * 128 + fh * 16 + (fj & 15);
   const int swz = fh ^ ((fj >> 1) & 7);
-  const int fb = BIG_WCH * 64 + (wm * 64 + fj) * 8;
-  uint4 FA[4][4], FB[4][2];
+  const int fb = BIG_WCH * 64 + (wm * 32 * TB + fj) * 8;
+  uint4 FA[4][4], FB[4][TB];
 #define TP_READ(LB, KH)                                                                          \
   _Pragma("unroll") for (int x = 0; x < 4; ++x)                                                  \
       FA[KH][x] = LB[(wn * 4 + x) * 256 + ((KH) >> 1) * 64 + ((KH) & 1) * 32 + fa];              \
-  _Pragma("unroll") for (int y = 0; y < 2; ++y) FB[KH][y] = LB[fb + y * 256 + ((2 * (KH)) ^ swz)];
+  _Pragma("unroll") for (int y = 0; y < TB; ++y) FB[KH][y] = LB[fb + y * 256 + ((2 * (KH)) ^ swz)];
 #define TP_MMA(KH)                                                                               \
-  _Pragma("unroll") for (int x = 0; x < 4; ++x) _Pragma("unroll") for (int y = 0; y < 2; ++y)   \
+  _Pragma("unroll") for (int x = 0; x < 4; ++x) _Pragma("unroll") for (int y = 0; y < TB; ++y)  \
       acc[x][y] = mfma_32x32x16(FA[KH][x], FB[KH][y], acc[x][y]);
 #define TP_SB __builtin_amdgcn_sched_barrier(0);
   // The DMA instructions alternate with the first k-half's MFMAs.
@@ -282,15 +293,16 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
   __builtin_amdgcn_s_waitcnt(kWaitVm0);              \
   __builtin_amdgcn_s_barrier();
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[4][TB];
 #pragma unroll
   for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16_t{};
+    for (int y = 0; y < TB; ++y) acc[x][y] = f32x16_t{};
 
   TP_ISSUE(L0, 0)
   TP_ISSUE(L1, 1)
-  __builtin_amdgcn_s_waitcnt(kWaitVm8);  // stage 0 has landed
+  constexpr int kWaitStage0 = 0x0F70 | ((4 + XI) & 15);  // vmcnt(4 + XI): stage 0 has landed
+  __builtin_amdgcn_s_waitcnt(kWaitStage0);
   __builtin_amdgcn_s_barrier();
   TP_READ(L0, 0) TP_READ(L0, 1) TP_READ(L0, 2) TP_READ(L0, 3)
   // The loop runs a whole number of stage pairs; with an odd stage count the
@@ -316,8 +328,8 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
 #undef TP_SYNC
 
 #pragma unroll
-  for (int y = 0; y < 2; ++y) {
-    const int64_t m = m0 + (wm * 2 + y) * 32 + fj;
+  for (int y = 0; y < TB; ++y) {
+    const int64_t m = m0 + (wm * TB + y) * 32 + fj;
     if (m >= a.M) continue;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -361,11 +373,24 @@ hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, hipStream_t s) {
                    (int64_t)BIG_MT * 16 * a.ldx * 2 < (1LL << 31) &&
                    BIG_T * a.ksteps * 1024 < (1LL << 31);
   if (big) {
-    const dim3 grid((unsigned)(ntn * ntm));
+    // One workgroup per CU at a time (128 KiB of LDS each). When the last
+    // round would run at most half full, its tiles are split into 128-token
+    // halves and run as a second launch that fills the GPU.
+    const int64_t nb = ntn * ntm, full = nb / 256 * 256, left = nb - full;
+    const bool split = left > 0 && left <= 128;
+    const unsigned n1 = (unsigned)(split ? full : nb);
     switch (epi) {
-      case kEpiSwiglu: hipLaunchKernelGGL(gemm_big<kEpiSwiglu>, grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm); break;
-      case kEpiBf16: hipLaunchKernelGGL(gemm_big<kEpiBf16>, grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm); break;
-      case kEpiF32: hipLaunchKernelGGL(gemm_big<kEpiF32>, grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm); break;
+      case kEpiSwiglu: hipLaunchKernelGGL((gemm_big<kEpiSwiglu, 2>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0); break;
+      case kEpiBf16: hipLaunchKernelGGL((gemm_big<kEpiBf16, 2>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0); break;
+      case kEpiF32: hipLaunchKernelGGL((gemm_big<kEpiF32, 2>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !split) return e;
+    const dim3 g2((unsigned)(2 * left));
+    switch (epi) {
+      case kEpiSwiglu: hipLaunchKernelGGL((gemm_big<kEpiSwiglu, 1>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full); break;
+      case kEpiBf16: hipLaunchKernelGGL((gemm_big<kEpiBf16, 1>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full); break;
+      case kEpiF32: hipLaunchKernelGGL((gemm_big<kEpiF32, 1>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full); break;
     }
     return hipGetLastError();
   }

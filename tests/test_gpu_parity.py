@@ -124,9 +124,12 @@ def test_row_small(M, path):
 
 # Grids of at least 256 workgroups of 256 x 256 run the big-tile prefill
 # kernel: ragged token count, ragged last k-step, odd and partial column tiles.
+# Grids of 256 + 16 tiles also run the half-height tail launch (including a
+# half tile wholly past M and a partial second half).
 BIG_CASES = [("col", 8, 3904, 1, 0, 4000), ("col", 200, 4040, 1, 0, 3965), ("col", 360, 3880, 1, 0, 4097),
              ("gateup_col", 200, 2 * 1944, 1, 0, 3965), ("gateup_col", 136, 2 * 7808, 4, 3, 4000),
-             ("row", 528, 3880, 2, 1, 4001), ("row", 64, 4096, 1, 0, 4096)]
+             ("gateup_col", 136, 2 * 2000, 1, 0, 4100),
+             ("row", 528, 3880, 2, 1, 4001), ("row", 64, 4096, 1, 0, 4096), ("row", 264, 3872, 1, 0, 4300)]
 
 
 @pytest.mark.parametrize("kind,K,N,t,r,M", BIG_CASES)
