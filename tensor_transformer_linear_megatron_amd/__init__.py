@@ -88,15 +88,29 @@ def tp_workspace_bytes(desc: TpShardDesc, M: int) -> int:
     return int(_lib.load().tp_workspace_bytes(ctypes.byref(desc), M))
 
 
-def _ws(descs, M, ws, device):
+def _ws(descs, M, ws, device, stream=None):
     """Workspace pointer and size; allocated here (torch, on the device) when
-    the caller passes none and the kernels need some."""
+    the caller passes none and the kernels need some. A workspace allocated
+    here is marked as used by ``stream`` so that torch's caching allocator
+    does not hand its memory out again before the queued kernels have run."""
     if ws is None:
         need = max(tp_workspace_bytes(d, M) for d in descs)
         if need == 0:
             return ctypes.c_void_p(0), 0, None
         ws = torch.empty(need, dtype=torch.uint8, device=device)
+        if stream is not None:
+            ws.record_stream(stream)
     return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), ws
+
+
+def _packed(W_packed: torch.Tensor, desc: TpShardDesc, name: str):
+    """Pointer of a packed shard, after checking it holds the plan's bytes."""
+    if not isinstance(W_packed, torch.Tensor) or not W_packed.is_cuda or not W_packed.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous CUDA/HIP tensor")
+    if W_packed.numel() * W_packed.element_size() < desc.packed_bytes:
+        raise ValueError(f"{name} holds {W_packed.numel() * W_packed.element_size()} bytes, "
+                         f"the plan packs {desc.packed_bytes}")
+    return ctypes.c_void_p(W_packed.data_ptr())
 
 
 def tp_col_linear(desc: TpShardDesc, X: torch.Tensor, W_packed: torch.Tensor,
@@ -110,9 +124,9 @@ def tp_col_linear(desc: TpShardDesc, X: torch.Tensor, W_packed: torch.Tensor,
     if Y is None:
         Y = torch.empty((M, desc.out_n), dtype=torch.bfloat16, device=X.device)
     yp, ldy = _mat(Y, torch.bfloat16, "Y")
-    wsp, wsb, _keep = _ws((desc,), M, ws, X.device)
+    wsp, wsb, _keep = _ws((desc,), M, ws, X.device, stream)
     _check(_lib.load().tp_col_linear(ctypes.byref(desc), xp, M, ldx,
-                                     ctypes.c_void_p(W_packed.data_ptr()), yp, ldy, wsp, wsb,
+                                     _packed(W_packed, desc, "W_packed"), yp, ldy, wsp, wsb,
                                      _stream(stream)), "tp_col_linear")
     return Y
 
@@ -128,9 +142,9 @@ def tp_row_linear(desc: TpShardDesc, Z: torch.Tensor, W_packed: torch.Tensor,
     if P is None:
         P = torch.empty((M, desc.N), dtype=torch.float32, device=Z.device)
     pp, ldp = _mat(P, torch.float32, "P")
-    wsp, wsb, _keep = _ws((desc,), M, ws, Z.device)
+    wsp, wsb, _keep = _ws((desc,), M, ws, Z.device, stream)
     _check(_lib.load().tp_row_linear(ctypes.byref(desc), zp, M, ldz,
-                                     ctypes.c_void_p(W_packed.data_ptr()), pp, ldp, wsp, wsb,
+                                     _packed(W_packed, desc, "W_packed"), pp, ldp, wsp, wsb,
                                      _stream(stream)), "tp_row_linear")
     return P
 
@@ -148,10 +162,10 @@ def tp_ffn_shard(gateup: TpShardDesc, down: TpShardDesc, X: torch.Tensor, Wgu_pa
     if P is None:
         P = torch.empty((M, down.N), dtype=torch.float32, device=X.device)
     pp, ldp = _mat(P, torch.float32, "P")
-    wsp, wsb, _keep = _ws((gateup, down), M, ws, X.device)
+    wsp, wsb, _keep = _ws((gateup, down), M, ws, X.device, stream)
     _check(_lib.load().tp_ffn_shard(ctypes.byref(gateup), ctypes.byref(down), xp, M, ldx,
-                                    ctypes.c_void_p(Wgu_packed.data_ptr()),
-                                    ctypes.c_void_p(Wd_packed.data_ptr()),
+                                    _packed(Wgu_packed, gateup, "Wgu_packed"),
+                                    _packed(Wd_packed, down, "Wd_packed"),
                                     ctypes.c_void_p(H.data_ptr()), pp, ldp, wsp, wsb,
                                     _stream(stream)), "tp_ffn_shard")
     return H, P

@@ -474,6 +474,8 @@ hipError_t launch_shared(const LinearArgs& a, float* ws, hipStream_t s) {
   constexpr int C = shared_chunk(MB32);
   constexpr int U = C;
   if (p.G > 1 && ws == nullptr) return hipErrorInvalidValue;
+  // A workgroup's weights are one buffer resource with 32-bit byte offsets.
+  if ((int64_t)2 * kSharedSN * a.ksteps * 1024 >= (1LL << 31)) return hipErrorInvalidValue;
   float* part = p.G > 1 ? ws : nullptr;
   hipLaunchKernelGGL((gemv_shared<MB32, U, C, kSharedSN, EPI>), dim3((unsigned)p.groups, (unsigned)p.G),
                      dim3(64 * kSharedSN), 0, s, a, p.per, part);

@@ -482,3 +482,33 @@ def test_llama405b_ffn_tp8_rank0_prefill():
     Pref = oracle.row_linear(Href, Wd_r, oracle.plan("row", w, Hd, 1, 0))
     assert_parity(host_f64(H)[rows], oracle.bf16_to_f64(Href), "H_0")
     assert_parity(host_f64(P)[rows], Pref, "P_0")
+
+
+def test_binding_rejects_short_packed_buffer():
+    """The binding checks the packed buffer against the plan before any kernel
+    reads it."""
+    d = tp.tp_shard_plan("col", 256, 256, 1, 0)
+    X = dev(si.normal_bf16(60, (4, 256), 1.0))
+    short = torch.empty(d.packed_bytes - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        tp.tp_col_linear(d, X, short)
+
+
+@pytest.mark.parametrize("M", [3, 40, 200])
+def test_side_stream_with_library_workspace(M):
+    """A call on a caller-given stream (not the current one), with the
+    workspace allocated by the binding, matches the oracle."""
+    say("side stream", M)
+    K, N = 1040, 4096
+    Z = si.normal_bf16(61, (M, K), 1.0)
+    W = si.normal_bf16(62, (K, N), 0.05)
+    d, p = plan_both("row", K, N, 1, 0)
+    Wp = tp.tp_shard_pack(d, dev(W))
+    Zd = dev(Z)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        P = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    tp.tp_row_linear(d, Zd, Wp, P=P, stream=side)
+    side.synchronize()
+    assert_parity(host_f64(P), oracle.row_linear(Z, W, p), f"side stream M={M}")
