@@ -351,6 +351,149 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
+def time_steps(timer, step, n, warm=3):
+    """Mean µs per step over n back-to-back steps between two events (the
+    events' own cost is spread over the n steps)."""
+    import torch
+    for i in range(warm):
+        step(i)
+    e0, e1 = timer.event(), timer.event()
+    torch.cuda.synchronize()
+    timer.record(e0)
+    for i in range(n):
+        step(warm + i)
+    timer.record(e1)
+    torch.cuda.synchronize()
+    return timer.ms(e0, e1) * 1e3 / n
+
+
+def _abi():
+    """The C library (already loaded by the binding) and pointer helpers, for
+    pre-marshalled calls whose host cost stays below the GPU time per call."""
+    import ctypes
+    import torch
+    from tensor_transformer_linear_megatron_amd import _lib
+    lib = _lib.load()
+    VP = ctypes.c_void_p
+    stream = VP(torch.cuda.current_stream().cuda_stream)
+    return lib, VP, ctypes.byref, stream
+
+
+def _run(calls):
+    for fn, a in calls:
+        st = fn(*a)
+        if st:
+            raise RuntimeError(f"{fn.__name__} failed: {st}")
+
+
+def config_worked_tp2(timer):
+    """The pages' worked TP = 2 split at 8 tokens: both ranks' column and row
+    shards in turn and the sum of their partials."""
+    import torch
+    import tensor_transformer_linear_megatron_amd as tp
+    from seeded_inputs import workloads as wl
+    lib, VP, ref, stream = _abi()
+    X, W, W2 = wl.worked_tp2()
+    M, H, t = X.shape[0], X.shape[1], 2
+    Xd, Wd, W2d = to_dev(X), to_dev(W), to_dev(W2)
+    cols = [tp.tp_shard_plan("col", H, H, t, r) for r in range(t)]
+    rows = [tp.tp_shard_plan("row", H, H, t, r) for r in range(t)]
+    copies = 8  # 8 x 64 MiB of packed shards, past the 256 MB last-level cache
+    packs = [[(tp.tp_shard_pack(cols[r], Wd), tp.tp_shard_pack(rows[r], W2d)) for r in range(t)]
+             for _ in range(copies)]
+    Y = [torch.empty((M, H // t), dtype=torch.bfloat16, device="cuda") for _ in range(t)]
+    P = torch.empty((t, M, H), dtype=torch.float32, device="cuda")
+    out = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    wsn = max(16, max(tp.tp_workspace_bytes(d, M) for d in cols + rows))
+    ws = torch.empty(wsn, dtype=torch.uint8, device="cuda")
+    steps = []
+    for c in range(copies):
+        calls = []
+        for r in range(t):
+            cp, rp = packs[c][r]
+            calls.append((lib.tp_col_linear, (ref(cols[r]), VP(Xd.data_ptr()), M, H, VP(cp.data_ptr()),
+                                              VP(Y[r].data_ptr()), H // t, VP(ws.data_ptr()), wsn, stream)))
+            calls.append((lib.tp_row_linear, (ref(rows[r]), VP(Y[r].data_ptr()), M, H // t, VP(rp.data_ptr()),
+                                              VP(P[r].data_ptr()), H, VP(ws.data_ptr()), wsn, stream)))
+        calls.append((lib.tp_reduce_partials, (VP(P.data_ptr()), M * H, t, M, H, H, VP(out.data_ptr()), H, stream)))
+        steps.append(calls)
+    us = time_steps(timer, lambda i: _run(steps[i % copies]), 40)
+    w = H * (H // t) * 2
+    nbytes = t * (w + M * H * 2 + M * (H // t) * 2) + t * (w + M * (H // t) * 2 + M * H * 4) + (t + 1) * M * H * 4
+    gbs = nbytes / us / 1e3
+    return dict(config="worked TP=2 split: X [8 x 4096], W and W2 4096 x 4096, both ranks + sum",
+                unit="GB/s", value=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4), peak=HBM_PEAK_GBS,
+                us_per_step=round(us, 2), bytes_per_step=nbytes)
+
+
+def config_70b_ffn_decode(timer):
+    """Llama-3.1-70B feed-forward layer at TP = 8 decode: all 8 rank shares in
+    turn (each gate/up + SwiGLU + down) and the sum of the 8 partials."""
+    import torch
+    import tensor_transformer_linear_megatron_amd as tp
+    from seeded_inputs import workloads as wl
+    lib, VP, ref, stream = _abi()
+    c = wl.LLAMA70B
+    H, I, t = c["hidden"], c["inter"], 8
+    w = I // t
+    log(f"[bench] 70B feed-forward at TP=8: generating [Wg | Wu] {H} x {2 * I} and Wd {I} x {H}")
+    gu = [tp.tp_shard_plan("gateup_col", H, 2 * I, t, r) for r in range(t)]
+    dn = [tp.tp_shard_plan("row", I, H, t, r) for r in range(t)]
+    Wg = to_dev(wl.gateup(H, I, c["sigma"]))
+    gp = [tp.tp_shard_pack(d, Wg) for d in gu]
+    del Wg
+    Wdn = to_dev(wl.down(I, H, c["sigma"]))
+    dp = [tp.tp_shard_pack(d, Wdn) for d in dn]
+    del Wdn
+    X = to_dev(wl.activations(32, H))
+    res = []
+    for M in (1, 8, 32):
+        Hs = torch.empty((M, w), dtype=torch.bfloat16, device="cuda")
+        P = torch.empty((t, M, H), dtype=torch.float32, device="cuda")
+        out = torch.empty((M, H), dtype=torch.float32, device="cuda")
+        wsn = max(16, max(tp.tp_workspace_bytes(d, M) for d in gu + dn))
+        ws = torch.empty(wsn, dtype=torch.uint8, device="cuda")
+        calls = [(lib.tp_ffn_shard, (ref(gu[r]), ref(dn[r]), VP(X.data_ptr()), M, H, VP(gp[r].data_ptr()),
+                                     VP(dp[r].data_ptr()), VP(Hs.data_ptr()), VP(P[r].data_ptr()), H,
+                                     VP(ws.data_ptr()), wsn, stream)) for r in range(t)]
+        calls.append((lib.tp_reduce_partials, (VP(P.data_ptr()), M * H, t, M, H, H, VP(out.data_ptr()), H, stream)))
+        us = time_steps(timer, lambda i: _run(calls), 20)
+        g, d_, _ = decode_bytes(M, H, I, t)
+        nbytes = t * (g + d_) + (t + 1) * M * H * 4
+        gbs = nbytes / us / 1e3
+        res.append(dict(M=M, us_per_step=round(us, 2), rank_share_us=round(us / t, 2), value=round(gbs, 1),
+                        frac=round(gbs / HBM_PEAK_GBS, 4)))
+    return dict(config="llama3.1-70b FFN, TP=8 decode: 8 rank shares in turn + sum of 8 partials",
+                unit="GB/s", peak=HBM_PEAK_GBS, batches=res)
+
+
+def config_70b_attention_prefill(timer):
+    """Llama-3.1-70B attention projections, rank 0 of TP = 8 at 4096 tokens:
+    the QKV column slice (8 Q + 1 K + 1 V head) and the O row slice."""
+    import torch
+    import tensor_transformer_linear_megatron_amd as tp
+    from seeded_inputs import workloads as wl
+    c = wl.LLAMA70B
+    H, t, M = c["hidden"], 8, 4096
+    heads = (c["n_q"], c["n_kv"], c["head_dim"])
+    dq = tp.tp_shard_plan("qkv_col", H, (c["n_q"] + 2 * c["n_kv"]) * c["head_dim"], t, 0, heads=heads)
+    do = tp.tp_shard_plan("o_row", c["n_q"] * c["head_dim"], H, t, 0, heads=heads)
+    qp = tp.tp_shard_pack(dq, to_dev(wl.qkv_weight(H, *heads, c["sigma"])))
+    op = tp.tp_shard_pack(do, to_dev(wl.o_weight(c["n_q"], c["head_dim"], H, c["sigma"])))
+    X = to_dev(wl.activations(M, H))
+    A = to_dev(wl.attention_output(M, c["n_q"] * c["head_dim"], cols=range(do.row_begin, do.row_end)))
+    QKV = torch.empty((M, dq.out_n), dtype=torch.bfloat16, device="cuda")
+    P = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    tq = time_steps(timer, lambda i: tp.tp_col_linear(dq, X, qp, Y=QKV), 10)
+    to_ = time_steps(timer, lambda i: tp.tp_row_linear(do, A, op, P=P), 10)
+    fq, fo = 2 * M * H * dq.shard_n, 2 * M * do.shard_k * H
+    tf = (fq + fo) / (tq + to_) / 1e6
+    return dict(config="llama3.1-70b attention, TP=8 rank 0, prefill 4096 tokens: QKV 8192 x 1280 + O 1024 x 8192",
+                unit="TFLOP/s", value=round(tf, 1), frac=round(tf / MFMA_BF16_PEAK_TFS, 4),
+                peak=MFMA_BF16_PEAK_TFS, qkv_us=round(tq, 1), qkv_TFs=round(fq / tq / 1e6, 1),
+                o_us=round(to_, 1), o_TFs=round(fo / to_ / 1e6, 1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,6 +501,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (worked TP=2 split, 70B decode and attention prefill)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (the yardstick for HBM byte counters)")
     args = ap.parse_args()
@@ -375,6 +520,10 @@ def main():
         return
     dec = run_decode(args)
     pre = None if args.no_prefill else run_prefill(args)
+    others = None
+    if not args.no_configs:
+        timer = Timer(torch.cuda.current_stream().cuda_stream)
+        others = [config_worked_tp2(timer), config_70b_ffn_decode(timer), config_70b_attention_prefill(timer)]
     per = [dict(M=p["M"], gateup_us=round(p["gateup_us"], 2), down_us=round(p["down_us"], 2),
                 reduce_us=round(p["reduce_us"], 2), gateup_GBs=round(p["gateup_GBs"], 1),
                 down_GBs=round(p["down_GBs"], 1), ffn_GBs=round(p["ffn_GBs"], 1))
@@ -400,6 +549,7 @@ def main():
         "cpu_baseline": dec["cpu"],
         "per_batch": per,
         "prefill": pre,
+        "other_configs": others,
     }
     print(json.dumps(line), flush=True)
 
