@@ -13,10 +13,15 @@ feed-forward layer at 8192 tokens (gate/up 16384 x 13312 + SwiGLU, down
 6656 x 16384 to an fp32 partial), in bf16 TFLOP/s.
 
 Kernel durations come from HIP events recorded on the stream the kernels run
-on: around every launch in an untimed breakdown pass, and around the dominant
-kernel's launches inside the timed region. The interval of an event pair with
-nothing between it, measured in the same passes, is subtracted. The oracle's
-CPU baseline is timed on this host on a bounded sample of the same workload.
+on: around every launch in an untimed breakdown pass, and inside the timed
+region around one launch of the dominant kernel per step (its launches in
+turn; each recorded event costs the step a few microseconds, so no more are
+recorded there). The interval of an event pair with nothing between it,
+measured in the same passes, is subtracted. The other workloads (the worked
+TP = 2 split, the 70B feed-forward layer at TP = 8 decode, the 70B attention
+projections at prefill) are timed as whole back-to-back steps between two
+events. The oracle's CPU baseline is timed on this host on a bounded sample
+of the same workload.
 """
 from __future__ import annotations
 
@@ -220,23 +225,30 @@ def run_decode(args):
             g["launches"].append((M, part))
     dom_name, dom = max(groups.items(), key=lambda kv: kv[1]["us"])
 
-    # Timed region: only the dominant kernel's launches (and one empty pair)
-    # carry events, so the step is disturbed as little as possible.
-    tmarks = [new_marks(dom["launches"]) for _ in range(args.steps)]
+    # Timed region: each step brackets one launch of the dominant kernel
+    # (its launches in turn) with an event pair, and every eighth step adds an
+    # empty pair; every event recorded costs the step a few microseconds.
+    nl = len(dom["launches"])
+    tmarks = []
+    for s in range(args.steps):
+        m = {dom["launches"][s % nl]: (timer.event(), timer.event())}
+        if s % 8 == 0:
+            m["empty"] = (timer.event(), timer.event())
+        tmarks.append(m)
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        empty_pair(tmarks[s])
+        if "empty" in tmarks[s]:
+            empty_pair(tmarks[s])
         step(args.warmup + nb + s, tmarks[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     value = step_bytes * args.steps / wall / 1e9
 
-    ovh = float(np.mean([timer.ms(*m["empty"]) for m in tmarks])) * 1e3
-    raw = float(np.mean([timer.ms(*m[k]) for m in tmarks for k in dom["launches"]])) * 1e3
+    ovh = float(np.mean([timer.ms(*m["empty"]) for m in tmarks if "empty" in m])) * 1e3
+    raw = float(np.mean([timer.ms(*v) for m in tmarks for k, v in m.items() if k != "empty"])) * 1e3
     avg_us = raw - ovh
-    nl = len(dom["launches"])
     bpl = dom["bytes"] / nl
     roof = dict(bound="hbm", kernel=f"{dom_name} (decode batches M={[M for M, _ in dom['launches']]})",
                 achieved=round(bpl / avg_us / 1e3, 1), peak=HBM_PEAK_GBS, unit="GB/s",
