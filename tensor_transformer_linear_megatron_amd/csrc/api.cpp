@@ -59,22 +59,28 @@ int32_t path_of(const tp_shard_desc* d, int64_t M) {
   return M <= 64 ? TP_PATH_DECODE : TP_PATH_PREFILL;
 }
 
+// Workspace of the kernels chosen for this shard at this M. The prefill plan
+// is taken at the smallest leading dimension (shard_k); a wider X can only
+// turn the split off, never need more.
 size_t workspace_bytes(const tp_shard_desc* d, int64_t M) {
-  if (M <= 0 || path_of(d, M) != TP_PATH_DECODE) return 0;
-  return tpk::gemv_workspace_bytes(M, d->packed_k / tpk::kTileK, d->packed_n / tpk::kTileN,
-                                   epilogue_of(d));
+  if (M <= 0) return 0;
+  const int64_t ksteps = d->packed_k / tpk::kTileK, ntiles = d->packed_n / tpk::kTileN;
+  if (path_of(d, M) == TP_PATH_DECODE) return tpk::gemv_workspace_bytes(M, ksteps, ntiles, epilogue_of(d));
+  return tpk::gemm_workspace_bytes(M, d->shard_k, ksteps, ntiles);
 }
 
 tp_status run_linear(const tp_shard_desc* d, const tpk::LinearArgs& a, void* ws, size_t ws_bytes,
                      hipStream_t s) {
   const int32_t path = path_of(d, a.M);
   if (path == TP_PATH_DECODE && a.M > 64) return TP_ERR_SHAPE;
-  const size_t need = workspace_bytes(d, a.M);
+  const size_t need = path == TP_PATH_DECODE
+                          ? workspace_bytes(d, a.M)
+                          : tpk::gemm_workspace_bytes(a.M, a.ldx, a.ksteps, a.ntiles);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return TP_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return TP_ERR_ALIGN;
-  const hipError_t e = path == TP_PATH_DECODE
-                           ? tpk::launch_gemv(a, epilogue_of(d), static_cast<float*>(ws), s)
-                           : tpk::launch_gemm(a, epilogue_of(d), s);
+  float* w = need > 0 ? static_cast<float*>(ws) : nullptr;
+  const hipError_t e = path == TP_PATH_DECODE ? tpk::launch_gemv(a, epilogue_of(d), w, s)
+                                              : tpk::launch_gemm(a, epilogue_of(d), w, s);
   return e == hipSuccess ? TP_OK : TP_ERR_HIP;
 }
 

@@ -200,8 +200,9 @@ constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 // TB = 2: 256 x 256 tiles, workgroup x takes tile x of the launch. TB = 1:
 // 128-token half tiles, workgroup x takes half x & 1 of tile tile_base +
 // x / 2 (the last, partial round of a grid, split so that it fills the GPU).
-template <int EPI, int TB>
-__global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, int ntm, int tile_base) {
+template <int EPI, int TB, bool SPLIT>
+__global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, int ntm, int tile_base,
+                                                        int64_t kper, float* part) {
   constexpr int ROWS = 128 * TB;                       // tokens per workgroup
   constexpr int XI = 2 * TB;                           // token DMA instructions per wave and stage
   constexpr int STAGE_U4 = BIG_WCH * 64 + ROWS * 8;    // 64 or 48 KiB per stage
@@ -224,7 +225,22 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
   const int tn = (bid % (GM * ntn)) / gsize;
   const int64_t nt0 = (int64_t)tn * BIG_T;
   const int64_t m0 = (int64_t)tm * (BIG_MT * 16) + (TB == 1 ? (int64_t)(blockIdx.x & 1) * ROWS : 0);
-  const int64_t ksteps = a.ksteps, nst = (ksteps + 1) / 2;
+  // ksteps is the packed layout's pair stride; kcnt the k-steps this
+  // workgroup multiplies. A split takes k-steps [y kper, y kper + kcnt) and
+  // writes its fp32 sum to part[y] ([M x ntiles 16], split order y).
+  const int64_t ksteps = a.ksteps;
+  int64_t kcnt = ksteps;
+  if constexpr (SPLIT) {
+    const int64_t k0 = (int64_t)blockIdx.y * kper;
+    kcnt = ksteps - k0 < kper ? ksteps - k0 : kper;
+    a.W += k0 * 2 * kTileU4;  // pair p, k-step ks sits at 1 KiB index (p ksteps + ks) 2 + t
+    a.X += k0 * kTileK;
+    a.K = a.K - k0 * kTileK < kcnt * kTileK ? a.K - k0 * kTileK : kcnt * kTileK;
+    a.out = part + (int64_t)blockIdx.y * a.M * (a.ntiles * kTileN);
+    a.ldo = a.ntiles * kTileN;
+    a.out_n = a.ldo;
+  }
+  const int64_t nst = (kcnt + 1) / 2;
 
   const int64_t wt = a.ntiles - nt0 < BIG_T ? a.ntiles - nt0 : BIG_T;
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -255,7 +271,7 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
     const unsigned s_ = (unsigned)(S);                                                           \
     _Pragma("unroll") for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
         rw, (lds_void_t*)&LB[(wave * 4 + j) * 64], 16,                                           \
-        2 * s_ + (j & 1) < (unsigned)ksteps ? woff[j] + s_ * 4096u : 0x80000000u, 0, 0, 0);      \
+        2 * s_ + (j & 1) < (unsigned)kcnt ? woff[j] + s_ * 4096u : 0x80000000u, 0, 0, 0);        \
     _Pragma("unroll") for (int j = 0; j < XI; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(     \
         rx, (lds_void_t*)&LB[BIG_WCH * 64 + (wave * XI + j) * 64], 16,                           \
         64u * s_ < kx[j] ? xoff[j] + s_ * 128u : 0x80000000u, 0, 0, 0);                          \
@@ -363,16 +379,56 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
   }
 }
 
+// How a prefill linear is launched. The big tile needs buffer offsets below
+// 2^31. When its tiles alone cannot fill the 256 CUs (one workgroup per CU),
+// K is split G ways, G = the whole number of tile sets that fit in one round
+// (each split keeping at least 16 k-steps); the splits write fp32 partials and
+// the split fix-up adds them in split order and applies the epilogue.
+struct GemmPlan {
+  bool big;
+  int G;         // K splits of the big tile (1: none)
+  int64_t kper;  // k-steps per split (even: whole stages)
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t ldx, int64_t ksteps, int64_t ntiles) {
+  GemmPlan p{false, 1, ksteps};
+  const int64_t ntn = (ntiles + BIG_T - 1) / BIG_T, ntm = (M + BIG_MT * 16 - 1) / (BIG_MT * 16);
+  p.big = (int64_t)BIG_MT * 16 * ldx * 2 < (1LL << 31) && BIG_T * ksteps * 1024 < (1LL << 31);
+  if (!p.big) return p;
+  const int64_t tiles = ntn * ntm;
+  if (tiles >= 256) return p;
+  int64_t G = 256 / tiles;
+  if (G > ksteps / 16) G = ksteps / 16;
+  if (G < 2) {
+    p.big = false;  // neither whole tiles nor splits fill the GPU: 128 x 128 tiles
+    return p;
+  }
+  p.kper = ((ksteps + G - 1) / G + 1) / 2 * 2;
+  p.G = (int)((ksteps + p.kper - 1) / p.kper);
+  return p;
+}
+
 }  // namespace
 
-hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, hipStream_t s) {
+size_t gemm_workspace_bytes(int64_t M, int64_t ldx, int64_t ksteps, int64_t ntiles) {
+  if (M <= 0) return 0;
+  const GemmPlan p = plan_gemm(M, ldx, ksteps, ntiles);
+  return p.big && p.G > 1 ? (size_t)p.G * M * ntiles * kTileN * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s) {
   if (a.M <= 0 || a.ntiles == 0) return hipSuccess;
   const int64_t ntn = (a.ntiles + BIG_T - 1) / BIG_T, ntm = (a.M + BIG_MT * 16 - 1) / (BIG_MT * 16);
-  // The big tile needs buffer offsets below 2^31 and enough workgroups to fill the GPU.
-  const bool big = ntn * ntm >= 256 &&
-                   (int64_t)BIG_MT * 16 * a.ldx * 2 < (1LL << 31) &&
-                   BIG_T * a.ksteps * 1024 < (1LL << 31);
-  if (big) {
+  const GemmPlan p = plan_gemm(a.M, a.ldx, a.ksteps, a.ntiles);
+  if (p.big && p.G > 1) {
+    if (ws == nullptr) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_big<kEpiF32, 2, true>), dim3((unsigned)(ntn * ntm), (unsigned)p.G),
+                       dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0, p.kper, ws);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_split_fixup(a, epi, ws, p.G, s);
+  }
+  if (p.big) {
     // One workgroup per CU at a time (128 KiB of LDS each). When the last
     // round would run at most half full, its tiles are split into 128-token
     // halves and run as a second launch that fills the GPU.
@@ -380,17 +436,17 @@ hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, hipStream_t s) {
     const bool split = left > 0 && left <= 128;
     const unsigned n1 = (unsigned)(split ? full : nb);
     switch (epi) {
-      case kEpiSwiglu: hipLaunchKernelGGL((gemm_big<kEpiSwiglu, 2>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0); break;
-      case kEpiBf16: hipLaunchKernelGGL((gemm_big<kEpiBf16, 2>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0); break;
-      case kEpiF32: hipLaunchKernelGGL((gemm_big<kEpiF32, 2>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0); break;
+      case kEpiSwiglu: hipLaunchKernelGGL((gemm_big<kEpiSwiglu, 2, false>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0, 0, nullptr); break;
+      case kEpiBf16: hipLaunchKernelGGL((gemm_big<kEpiBf16, 2, false>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0, 0, nullptr); break;
+      case kEpiF32: hipLaunchKernelGGL((gemm_big<kEpiF32, 2, false>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0, 0, nullptr); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !split) return e;
     const dim3 g2((unsigned)(2 * left));
     switch (epi) {
-      case kEpiSwiglu: hipLaunchKernelGGL((gemm_big<kEpiSwiglu, 1>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full); break;
-      case kEpiBf16: hipLaunchKernelGGL((gemm_big<kEpiBf16, 1>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full); break;
-      case kEpiF32: hipLaunchKernelGGL((gemm_big<kEpiF32, 1>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full); break;
+      case kEpiSwiglu: hipLaunchKernelGGL((gemm_big<kEpiSwiglu, 1, false>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full, 0, nullptr); break;
+      case kEpiBf16: hipLaunchKernelGGL((gemm_big<kEpiBf16, 1, false>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full, 0, nullptr); break;
+      case kEpiF32: hipLaunchKernelGGL((gemm_big<kEpiF32, 1, false>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full, 0, nullptr); break;
     }
     return hipGetLastError();
   }

@@ -503,6 +503,18 @@ hipError_t launch_t(const LinearArgs& a, float* ws, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_split_fixup(const LinearArgs& a, Epilogue epi, const float* part, int G, hipStream_t s) {
+  const int64_t pld = a.ntiles * kTileN;
+  const int64_t threads = a.M * (epi == kEpiSwiglu ? pld / 2 : pld) / 4;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  switch (epi) {
+    case kEpiSwiglu: hipLaunchKernelGGL(gemv_fixup<kEpiSwiglu>, grid, dim3(256), 0, s, a, part, G); break;
+    case kEpiBf16: hipLaunchKernelGGL(gemv_fixup<kEpiBf16>, grid, dim3(256), 0, s, a, part, G); break;
+    case kEpiF32: hipLaunchKernelGGL(gemv_fixup<kEpiF32>, grid, dim3(256), 0, s, a, part, G); break;
+  }
+  return hipGetLastError();
+}
+
 size_t gemv_workspace_bytes(int64_t M, int64_t ksteps, int64_t ntiles, Epilogue epi) {
   if (M <= 16 || M > 64) return 0;
   (void)epi;

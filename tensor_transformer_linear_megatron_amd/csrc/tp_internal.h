@@ -64,7 +64,14 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 // partials) when that is non-zero.
 hipError_t launch_gemv(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s);
 size_t gemv_workspace_bytes(int64_t M, int64_t ksteps, int64_t ntiles, Epilogue epi);
-hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, hipStream_t s);
+// Prefill path. `ws` must hold gemm_workspace_bytes() bytes (fp32 split-K
+// partials, when the output tiles alone do not fill the GPU) when that is
+// non-zero.
+hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s);
+size_t gemm_workspace_bytes(int64_t M, int64_t ldx, int64_t ksteps, int64_t ntiles);
+// Adds G fp32 split partials part[y] ([M x ntiles kTileN], split order) and
+// applies the epilogue into a.out.
+hipError_t launch_split_fixup(const LinearArgs& a, Epilogue epi, const float* part, int G, hipStream_t s);
 hipError_t launch_reduce(const float* P, int64_t stride, int32_t t, int64_t M, int64_t N,
                          int64_t ldp, float* Y, int64_t ldy, hipStream_t s);
 

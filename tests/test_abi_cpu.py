@@ -196,22 +196,39 @@ def test_reduce_and_pack_argument_errors():
     assert lib.tp_shard_pack(ctypes.byref(bad), A, 64, B, S) == _lib.TP_ERR_SHAPE
 
 
+def _big_tiles(d, M):
+    """256 x 256 output tiles of a prefill linear (16 packed tiles x 256 tokens)."""
+    return -(-d.packed_n // 256) * -(-M // 256)
+
+
 def test_workspace_bytes():
     """Decode batches of 17..64 tokens may split K over workgroups; the fp32
-    partials need G * M * packed_n * 4 bytes. M <= 16, prefill and invalid
-    descriptors need none."""
+    partials need G * M * packed_n * 4 bytes. Prefill splits K only when its
+    256 x 256 tiles cannot fill the 256 CUs: then G >= 2 splits of at least 16
+    k-steps with G * tiles <= 256. M <= 16 and invalid descriptors need none."""
     lib = _lib.load()
     for kind, K, N, t in (("col", 4096, 4096, 2), ("gateup_col", 8192, 57344, 8), ("row", 28672, 8192, 8),
-                          ("row", 14336, 4096, 1), ("gateup_col", 4096, 28672, 1)):
+                          ("row", 14336, 4096, 1), ("gateup_col", 4096, 28672, 1), ("row", 1024, 8192, 1)):
         d = tp.tp_shard_plan(kind, K, N, t, 0)
-        for M in (1, 16, 65, 8192):
+        for M in (1, 16):
             assert tp.tp_workspace_bytes(d, M) == 0
         for M in (17, 32, 64):
             ws = tp.tp_workspace_bytes(d, M)
             assert ws % (M * d.packed_n * 4) == 0 and ws // (M * d.packed_n * 4) <= 64
         pre = d.copy()
         pre.path = tp.TP_PATH_PREFILL
-        assert tp.tp_workspace_bytes(pre, 32) == 0
+        for M in (32, 65, 300, 4096, 8192):
+            dd = pre if M <= 64 else d
+            ws = tp.tp_workspace_bytes(dd, M)
+            assert ws % (M * d.packed_n * 4) == 0
+            G, tiles, ksteps = ws // (M * d.packed_n * 4), _big_tiles(d, M), d.packed_k // 32
+            if tiles >= 256 or min(256 // tiles, ksteps // 16) < 2:
+                assert G == 0, (kind, K, N, M)
+            else:
+                assert G >= 2 and G * tiles <= 256 and -(-ksteps // G) >= 16, (kind, K, N, M, G)
+    # The 70B attention QKV slice of one TP = 8 rank at 4096 tokens: 80 tiles, K split 3 ways.
+    dq = tp.tp_shard_plan("qkv_col", 8192, 10240, 8, 0, heads=(64, 8, 128))
+    assert tp.tp_workspace_bytes(dq, 4096) == 3 * 4096 * dq.packed_n * 4
     assert lib.tp_workspace_bytes(None, 32) == 0
     d = tp.tp_shard_plan("row", 14336, 4096, 1, 0)
     if tp.tp_workspace_bytes(d, 64):  # a too-small workspace is refused before any launch

@@ -142,6 +142,27 @@ def test_prefill_big_tile_ragged(kind, K, N, t, r, M):
     assert_parity(got, ref, f"{kind} K={K} N={N} t={t} r={r} M={M}")
 
 
+# Few 256 x 256 output tiles and a long ragged K: the prefill path splits K
+# over workgroups (fp32 partials in the workspace, summed in split order by
+# the fix-up, which applies the epilogue). The last split has an odd number of
+# k-steps and ends inside a k-step; the last token tile is partial.
+SPLIT_CASES = [("col", 4104, 520, 1, 0, 300, None), ("gateup_col", 2056, 2 * 600, 1, 0, 520, None),
+               ("row", 3088, 1000, 2, 1, 257, None), ("qkv_col", 2048, 1536, 4, 1, 700, (16, 4, 64)),
+               ("o_row", 4096, 1000, 2, 0, 300, (32, 8, 128))]
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,M,heads", SPLIT_CASES)
+def test_prefill_split_k_ragged(kind, K, N, t, r, M, heads):
+    say("prefill split-K", kind, K, N, t, r, M, heads)
+    d = with_path(tp.tp_shard_plan(kind, K, N, t, r, heads=heads), tp.TP_PATH_PREFILL)
+    assert tp.tp_workspace_bytes(d, M) >= 2 * M * d.packed_n * 4, "the split path is not taken"
+    if kind in ("row", "o_row"):
+        got, ref = _row_case(kind, K, N, t, r, M, tp.TP_PATH_PREFILL, heads=heads)
+    else:
+        got, ref = _col_case(kind, K, N, t, r, M, tp.TP_PATH_PREFILL, heads=heads)
+    assert_parity(got, ref, f"{kind} K={K} N={N} t={t} r={r} M={M}")
+
+
 @pytest.mark.parametrize("M", [17, 33, 50, 64])
 def test_decode_split_k_ragged(M):
     """Long ragged K with few output tiles: the decode path splits K over
