@@ -216,8 +216,11 @@ TP_API tp_status tp_reduce_partials(const float* P, int64_t stride_elems, int32_
                              int64_t N, int64_t ldp, float* Y, int64_t ldy, hipStream_t stream);
 
 /* Bytes of device workspace tp_col_linear / tp_row_linear need for this
- * shard at this M (fp32 partial sums of decode split-K; 0 when the chosen
- * kernels need none or the descriptor is invalid). tp_ffn_shard needs the
+ * shard at this M: fp32 partial sums when K is split over workgroups (decode
+ * batches of 17..64 tokens with few output tiles; prefill shapes whose output
+ * tiles alone cannot fill the GPU); 0 when the chosen kernels need none or
+ * the descriptor is invalid. The value assumes X at its smallest leading
+ * dimension (shard_k); a wider one never needs more. tp_ffn_shard needs the
  * larger of its two descriptors' values. */
 TP_API size_t tp_workspace_bytes(const tp_shard_desc* desc, int64_t M);
 
