@@ -276,6 +276,18 @@ def load_traffic(key, src_hash):
     return e.get("bytes_per_launch")
 
 
+def host_cpu():
+    """The host's CPU model, as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_decode(X, Wgu, Wd, H, I):
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
@@ -293,7 +305,32 @@ def cpu_baseline_decode(X, Wgu, Wd, H, I):
     nbytes = sum(sum(decode_bytes(M, H, I)) for M in sample_ms)
     return dict(value=round(nbytes / dt / 1e9, 3), unit="GB/s", cores=threads, kind="oracle",
                 sample=f"the full 8B feed-forward share (t = 1) at M = 1 and M = 8, fp64 oracle, "
-                       f"{reps} repetition(s), {dt:.2f} s each; bytes counted as for the GPU")
+                       f"{reps} repetition(s), {dt:.2f} s each; bytes counted as for the GPU",
+                cpu_model=host_cpu(), nproc=os.cpu_count())
+
+
+def cpu_baseline_prefill(Wgu_r, Wd_r, Hd, w, M):
+    """The oracle on the same rank share (gate/up + SwiGLU, then down) for the
+    first rows of the same X, in blocks of 16 rows until about 8 s have
+    passed; rows are independent, so the rate carries over to all M rows."""
+    import oracle
+    from seeded_inputs import workloads as wl
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    log(f"[bench] cpu baseline (prefill): the oracle on this host ({threads} threads)")
+    p_gu = oracle.plan("gateup_col", Hd, 2 * w, 1, 0)  # the rank's own [Wg_r | Wu_r]
+    p_d = oracle.plan("row", w, Hd, 1, 0)
+    rows, t0 = 0, time.perf_counter()
+    while rows < M:
+        Xb = wl.activations(M, Hd, rows=range(rows, rows + 16))
+        oracle.row_linear(oracle.gateup_swiglu(Xb, Wgu_r, p_gu), Wd_r, p_d)
+        rows += 16
+        if time.perf_counter() - t0 > 8.0:
+            break
+    dt = time.perf_counter() - t0
+    flops = rows * (2 * Hd * 2 * w + 2 * w * Hd)
+    return dict(value=round(flops / dt / 1e12, 5), unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"rows 0..{rows - 1} of the 8192-token 405B rank-0 feed-forward share, fp64 oracle, "
+                       f"{dt:.1f} s", cpu_model=host_cpu(), nproc=os.cpu_count())
 
 
 def run_prefill(args):
@@ -340,10 +377,12 @@ def run_prefill(args):
     fg = 2 * M * Hd * 2 * w
     fd = 2 * M * w * Hd
     tf = (fg + fd) / d.sum() / 1e9
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(Wgu_r, Wd_r, Hd, w, M)
     return dict(workload="llama3.1-405b FFN, TP=8 rank 0, prefill 8192 tokens", unit="TFLOP/s",
                 value=round(tf, 1), frac=round(tf / MFMA_BF16_PEAK_TFS, 4), peak=MFMA_BF16_PEAK_TFS,
                 gateup_ms=round(float(d[0]), 3), gateup_TFs=round(fg / d[0] / 1e9, 1),
-                down_ms=round(float(d[1]), 3), down_TFs=round(fd / d[1] / 1e9, 1), steps=steps)
+                down_ms=round(float(d[1]), 3), down_TFs=round(fd / d[1] / 1e9, 1), steps=steps,
+                cpu_baseline=cpu)
 
 
 COPY_BYTES = 1 << 30
