@@ -39,6 +39,11 @@ Readings where the pages are silent (the same list is in the design notes):
 * Rounding points: a column output consumed in bf16 (Y_r, H_r, QKV_r) is
   rounded to bf16 (nearest, ties to even) from the fp64 value; row partials
   and their sum stay unrounded.
+* Sequence parallelism (the pages name only what it splits): after the
+  row-parallel product rank r keeps rows [r M/t, (r+1) M/t) of the summed
+  partials (a reduce-scatter along the tokens), and the full activations for
+  the next column-parallel product are the ranks' row blocks stacked in rank
+  order (an all-gather); M must divide by t.
 
 Every function below is parity-pinned by ``tests/test_oracle_pins.py``.
 """
@@ -234,6 +239,34 @@ def sum_partials(P: np.ndarray) -> np.ndarray:
     stride = int(np.prod(P.shape[1:]))
     _load().orc_sum_partials(_ptr(P), stride, t, stride, _ptr(Y))
     return Y
+
+
+def reduce_scatter(P: np.ndarray, rank: int) -> np.ndarray:
+    """Sequence-parallel partial sum of rank ``rank``: its own 1/t of the token
+    rows of P[0] + ... + P[t-1], added in rank order, fp64 [M/t x N].
+
+    "AI Infrastructure series, Part 5", "What about MoE models and very long
+    prompts?": sequence parallelism splits the parts of a layer that tensor
+    parallelism leaves whole along the sequence, inside the tensor-parallel
+    group. After the row-parallel product each rank then keeps only its token
+    rows of the summed output; rank r's rows are [r M/t, (r+1) M/t). M must
+    divide by t."""
+    P = np.asarray(P)
+    t, M = P.shape[0], P.shape[1]
+    if not 0 <= rank < t:
+        raise PlanError("rank", f"rank {rank} of {t}")
+    if M % t != 0:
+        raise PlanError("indivisible", f"{M} token rows over {t} ranks")
+    Mt = M // t
+    return sum_partials(P[:, rank * Mt:(rank + 1) * Mt])
+
+
+def gather_rows(blocks) -> np.ndarray:
+    """The matching gather of the activations before the next column-parallel
+    product: the t ranks' row blocks [M/t x N], stacked in rank order."""
+    blocks = [np.asarray(b) for b in blocks]
+    assert blocks and all(b.shape == blocks[0].shape for b in blocks)
+    return np.concatenate(blocks, axis=0)
 
 
 # --------------------------------------------------------------------------

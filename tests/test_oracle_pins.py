@@ -211,6 +211,72 @@ def test_sum_partials_in_rank_order():
 
 
 # ---------------------------------------------------------------------------
+# Sequence-parallel partial sum and row gather ("AI Infrastructure series,
+# Part 5", "What about MoE models and very long prompts?").
+# ---------------------------------------------------------------------------
+
+def test_reduce_scatter_brute_force():
+    rng = np.random.default_rng(5)
+    t, M, N = 4, 12, 5
+    P = rng.standard_normal((t, M, N))
+    for r in range(t):
+        got = oracle.reduce_scatter(P, r)
+        assert got.shape == (M // t, N)
+        for i in range(M // t):
+            for n in range(N):
+                acc = 0.0
+                for s_ in range(t):  # plain Python floats, rank order
+                    acc += float(P[s_, r * (M // t) + i, n])
+                assert got[i, n] == acc
+
+
+def test_reduce_scatter_then_gather_is_the_full_sum():
+    # all-reduce = reduce-scatter along the rows followed by the row gather,
+    # bit for bit: each element is the same rank-order sum
+    rng = np.random.default_rng(6)
+    for t, M, N in ((1, 3, 4), (2, 8, 3), (8, 64, 16), (3, 9, 2)):
+        P = rng.standard_normal((t, M, N)) * 10.0 ** rng.integers(-3, 4, size=(t, M, N))
+        parts = [oracle.reduce_scatter(P, r) for r in range(t)]
+        assert np.array_equal(oracle.gather_rows(parts), oracle.sum_partials(P))
+
+
+def test_reduce_scatter_exact_integers():
+    rng = np.random.default_rng(7)
+    P = rng.integers(-1000, 1000, size=(8, 32, 24))
+    for r in range(8):
+        want = P[:, r * 4:(r + 1) * 4].sum(axis=0)  # int64, exact
+        assert np.array_equal(oracle.reduce_scatter(P.astype(np.float64), r), want.astype(np.float64))
+
+
+def test_reduce_scatter_keeps_rank_order():
+    # row 1 of rank 1's block holds the 1e16 cancellation; only order 0, 1, 2 gives 0
+    P = np.zeros((3, 6, 1))
+    P[:, 3, 0] = [1e16, 1.0, -1e16]
+    assert oracle.reduce_scatter(P, 1)[1, 0] == 0.0
+    assert oracle.reduce_scatter(P[[0, 2, 1]], 1)[1, 0] == 1.0
+
+
+def test_reduce_scatter_errors():
+    P = np.zeros((4, 10, 2))
+    with pytest.raises(oracle.PlanError) as e:
+        oracle.reduce_scatter(P, 0)  # 10 rows over 4 ranks
+    assert e.value.code == "indivisible"
+    with pytest.raises(oracle.PlanError) as e:
+        oracle.reduce_scatter(np.zeros((4, 8, 2)), 4)
+    assert e.value.code == "rank"
+
+
+def test_gather_rows_restores_the_activations():
+    X = si.normal_bf16(21, (24, 40), 1.0)
+    for t in (1, 2, 3, 4, 8):
+        blocks = [X[r * (24 // t):(r + 1) * (24 // t)] for r in range(t)]
+        assert np.array_equal(oracle.gather_rows(blocks), X)
+    # a gather in the wrong rank order is caught
+    blocks = [X[r * 6:(r + 1) * 6] for r in range(4)]
+    assert not np.array_equal(np.concatenate(blocks[::-1], axis=0), X)
+
+
+# ---------------------------------------------------------------------------
 # SwiGLU.
 # ---------------------------------------------------------------------------
 
