@@ -545,6 +545,41 @@ def config_70b_attention_prefill(timer):
                 o_us=round(to_, 1), o_TFs=round(fo / to_ / 1e6, 1))
 
 
+def config_sequence_parallel(timer):
+    """Sequence-parallel partial sum on the 70B attention O partials of TP = 8
+    at 4096 tokens ([8 x 4096 x 8192] fp32): the full rank-order sum (the
+    all-reduce's arithmetic), each rank's reduce-scatter in turn, and the row
+    gather of the ranks' bf16 blocks."""
+    import torch
+    lib, VP, ref, stream = _abi()
+    t, M, N = 8, 4096, 8192
+    Mt = M // t
+    g = torch.Generator(device="cuda").manual_seed(0)
+    P = torch.randn((t, M, N), generator=g, dtype=torch.float32, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    Yr = torch.empty((t, Mt, N), dtype=torch.float32, device="cuda")
+    Xs = torch.randn((t, Mt, N), generator=g, dtype=torch.float32, device="cuda").to(torch.bfloat16)
+    X = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    full = [(lib.tp_reduce_partials, (VP(P.data_ptr()), M * N, t, M, N, N, VP(Y.data_ptr()), N, stream))]
+    scatter = [(lib.tp_reduce_scatter_partials, (VP(P.data_ptr()), M * N, t, M, N, N, r,
+                                                 VP(Yr[r].data_ptr()), N, stream)) for r in range(t)]
+    gather = [(lib.tp_gather_rows, (VP(Xs.data_ptr()), Mt * N, t, Mt, N, N, VP(X.data_ptr()), N, stream))]
+    us_full = time_steps(timer, lambda i: _run(full), 20)
+    us_rs = time_steps(timer, lambda i: _run(scatter), 20)
+    us_g = time_steps(timer, lambda i: _run(gather), 20)
+    b_red = (t + 1) * M * N * 4  # the full sum; the t reduce-scatters move the same bytes in total
+    b_g = 2 * M * N * 2
+    return dict(config="sequence-parallel partial sum, 70B attention O partials at TP=8, 4096 tokens",
+                unit="GB/s", peak=HBM_PEAK_GBS,
+                full_sum=dict(us=round(us_full, 1), value=round(b_red / us_full / 1e3, 1),
+                              frac=round(b_red / us_full / 1e3 / HBM_PEAK_GBS, 4)),
+                reduce_scatter_all_ranks=dict(us=round(us_rs, 1), rank_us=round(us_rs / t, 2),
+                                              value=round(b_red / us_rs / 1e3, 1),
+                                              frac=round(b_red / us_rs / 1e3 / HBM_PEAK_GBS, 4)),
+                gather=dict(us=round(us_g, 1), value=round(b_g / us_g / 1e3, 1),
+                            frac=round(b_g / us_g / 1e3 / HBM_PEAK_GBS, 4)))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -553,7 +588,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
-                    help="skip the other workloads (worked TP=2 split, 70B decode and attention prefill)")
+                    help="skip the other workloads (worked TP=2 split, 70B decode and attention prefill, "
+                         "sequence-parallel partial sum)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (the yardstick for HBM byte counters)")
     args = ap.parse_args()
@@ -574,7 +610,8 @@ def main():
     others = None
     if not args.no_configs:
         timer = Timer(torch.cuda.current_stream().cuda_stream)
-        others = [config_worked_tp2(timer), config_70b_ffn_decode(timer), config_70b_attention_prefill(timer)]
+        others = [config_worked_tp2(timer), config_70b_ffn_decode(timer), config_70b_attention_prefill(timer),
+                  config_sequence_parallel(timer)]
     per = [dict(M=p["M"], gateup_us=round(p["gateup_us"], 2), down_us=round(p["down_us"], 2),
                 reduce_us=round(p["reduce_us"], 2), gateup_GBs=round(p["gateup_GBs"], 1),
                 down_GBs=round(p["down_GBs"], 1), ffn_GBs=round(p["ffn_GBs"], 1))

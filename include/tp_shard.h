@@ -215,6 +215,36 @@ TP_API tp_status tp_ffn_shard(const tp_shard_desc* gateup, const tp_shard_desc* 
 TP_API tp_status tp_reduce_partials(const float* P, int64_t stride_elems, int32_t t, int64_t M,
                              int64_t N, int64_t ldp, float* Y, int64_t ldy, hipStream_t stream);
 
+/*
+ * Sequence-parallel form of the partial sum ("AI Infrastructure series,
+ * Part 5", "What about MoE models and very long prompts?": sequence
+ * parallelism splits the parts of a layer that tensor parallelism leaves
+ * whole along the sequence, inside the tensor-parallel group). Rank `rank`
+ * keeps only its token rows of the summed partials:
+ *   Y[i][n] = P_0[rank Mt + i][n] + ... + P_{t-1}[rank Mt + i][n], Mt = M / t,
+ * added in fp32 in rank order, so Y is bit for bit rows [rank Mt, (rank+1) Mt)
+ * of tp_reduce_partials' result. P_r = P + r * stride_elems is [M x N] fp32
+ * with leading dim ldp; Y [Mt x N] fp32 with leading dim ldy must not overlap
+ * any P_r. M not divisible by t -> TP_ERR_INDIVISIBLE; rank outside [0, t)
+ * -> TP_ERR_RANK. Pointers, N, ldp, ldy and stride_elems: 16-byte aligned /
+ * multiples of 4 (TP_ERR_ALIGN). M == 0 queues nothing.
+ */
+TP_API tp_status tp_reduce_scatter_partials(const float* P, int64_t stride_elems, int32_t t, int64_t M,
+                                     int64_t N, int64_t ldp, int32_t rank, float* Y, int64_t ldy,
+                                     hipStream_t stream);
+
+/*
+ * The gather that goes with it (same passage): before the next
+ * column-parallel product every rank needs the whole sequence again, the t
+ * ranks' row blocks stacked in rank order:
+ *   X[r Mt + i][n] = X_r[i][n],  X_r = Xs + r * stride_elems ([Mt x N] bf16,
+ *   leading dim ldb);  X [t Mt x N] bf16 with leading dim ldx.
+ * X must not overlap the blocks. Pointers, N, ldb, ldx and stride_elems:
+ * 16-byte aligned / multiples of 8 (TP_ERR_ALIGN). Mt == 0 queues nothing.
+ */
+TP_API tp_status tp_gather_rows(const uint16_t* Xs, int64_t stride_elems, int32_t t, int64_t Mt,
+                         int64_t N, int64_t ldb, uint16_t* X, int64_t ldx, hipStream_t stream);
+
 /* Bytes of device workspace tp_col_linear / tp_row_linear need for this
  * shard at this M: fp32 partial sums when K is split over workgroups (decode
  * batches of 17..64 tokens with few output tiles; prefill shapes whose output

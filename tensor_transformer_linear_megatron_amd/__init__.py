@@ -24,7 +24,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["tp_shard_plan", "tp_shard_pack", "tp_col_linear", "tp_row_linear", "tp_ffn_shard",
-           "tp_reduce_partials", "tp_workspace_bytes", "tp_status_str", "TpError", "TpShardDesc"]
+           "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows", "tp_workspace_bytes",
+           "tp_status_str", "TpError", "TpShardDesc"]
 
 
 class TpError(RuntimeError):
@@ -184,3 +185,34 @@ def tp_reduce_partials(P: torch.Tensor, Y: torch.Tensor | None = None, stream=No
                                           max(P.stride(1), N), yp, ldy, _stream(stream)),
            "tp_reduce_partials")
     return Y
+
+
+def tp_reduce_scatter_partials(P: torch.Tensor, rank: int, Y: torch.Tensor | None = None,
+                               stream=None) -> torch.Tensor:
+    """Rank ``rank``'s token rows of P[0] + ... + P[t-1] (fp32, rank order):
+    [M/t x N]. ``P`` is [t x M x N] with unit column stride."""
+    if P.dim() != 3 or P.dtype != torch.float32 or not P.is_cuda or P.stride(2) != 1:
+        raise ValueError("P must be a [t x M x N] fp32 device tensor with unit column stride")
+    t, M, N = P.shape
+    if Y is None:
+        Y = torch.empty((M // t if t else 0, N), dtype=torch.float32, device=P.device)
+    yp, ldy = _mat(Y, torch.float32, "Y")
+    _check(_lib.load().tp_reduce_scatter_partials(ctypes.c_void_p(P.data_ptr()), P.stride(0), t, M, N,
+                                                  max(P.stride(1), N), rank, yp, ldy, _stream(stream)),
+           "tp_reduce_scatter_partials")
+    return Y
+
+
+def tp_gather_rows(Xs: torch.Tensor, X: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The t ranks' bf16 row blocks ``Xs`` [t x Mt x N] stacked in rank order:
+    [t Mt x N]."""
+    if Xs.dim() != 3 or Xs.dtype != torch.bfloat16 or not Xs.is_cuda or Xs.stride(2) != 1:
+        raise ValueError("Xs must be a [t x Mt x N] bf16 device tensor with unit column stride")
+    t, Mt, N = Xs.shape
+    if X is None:
+        X = torch.empty((t * Mt, N), dtype=torch.bfloat16, device=Xs.device)
+    xp, ldx = _mat(X, torch.bfloat16, "X")
+    _check(_lib.load().tp_gather_rows(ctypes.c_void_p(Xs.data_ptr()), Xs.stride(0), t, Mt, N,
+                                      max(Xs.stride(1), N), xp, ldx, _stream(stream)),
+           "tp_gather_rows")
+    return X

@@ -30,7 +30,8 @@ KIND_NAMES = {"col": TP_COL, "row": TP_ROW, "gateup_col": TP_GATEUP_COL,
               "qkv_col": TP_QKV_COL, "o_row": TP_O_ROW}
 
 EXPORTS = ("tp_shard_plan", "tp_shard_pack", "tp_col_linear", "tp_row_linear", "tp_ffn_shard",
-           "tp_reduce_partials", "tp_workspace_bytes", "tp_status_str")
+           "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows", "tp_workspace_bytes",
+           "tp_status_str")
 
 
 class TpHeads(ctypes.Structure):
@@ -90,12 +91,14 @@ def load() -> ctypes.CDLL:
     lib.tp_row_linear.argtypes = [D, P, I64, I64, P, P, I64, P, SZ, P]
     lib.tp_ffn_shard.argtypes = [D, D, P, I64, I64, P, P, P, P, I64, P, SZ, P]
     lib.tp_reduce_partials.argtypes = [P, I64, I32, I64, I64, I64, P, I64, P]
+    lib.tp_reduce_scatter_partials.argtypes = [P, I64, I32, I64, I64, I64, I32, P, I64, P]
+    lib.tp_gather_rows.argtypes = [P, I64, I32, I64, I64, I64, P, I64, P]
     lib.tp_workspace_bytes.argtypes = [D, I64]
     lib.tp_workspace_bytes.restype = SZ
     lib.tp_status_str.argtypes = [I32]
     lib.tp_status_str.restype = ctypes.c_char_p
     for name in ("tp_shard_plan", "tp_shard_pack", "tp_col_linear", "tp_row_linear",
-                 "tp_ffn_shard", "tp_reduce_partials"):
+                 "tp_ffn_shard", "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib

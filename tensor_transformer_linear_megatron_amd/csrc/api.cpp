@@ -198,3 +198,35 @@ extern "C" tp_status tp_reduce_partials(const float* P, int64_t stride_elems, in
              ? TP_OK
              : TP_ERR_HIP;
 }
+
+extern "C" tp_status tp_reduce_scatter_partials(const float* P, int64_t stride_elems, int32_t t,
+                                                int64_t M, int64_t N, int64_t ldp, int32_t rank,
+                                                float* Y, int64_t ldy, hipStream_t stream) {
+  if (t <= 0 || M < 0 || N <= 0 || ldp < N || ldy < N) return TP_ERR_SHAPE;
+  if (rank < 0 || rank >= t) return TP_ERR_RANK;
+  if (M % t) return TP_ERR_INDIVISIBLE;
+  if (M == 0) return TP_OK;
+  if (P == nullptr || Y == nullptr) return TP_ERR_NULL;
+  if (t > 1 && stride_elems < M * ldp) return TP_ERR_SHAPE;
+  if (!aligned16(P) || !aligned16(Y) || N % 4 || ldp % 4 || ldy % 4 || stride_elems % 4)
+    return TP_ERR_ALIGN;
+  const int64_t Mt = M / t;
+  return tpk::launch_reduce(P + (int64_t)rank * Mt * ldp, stride_elems, t, Mt, N, ldp, Y, ldy,
+                            stream) == hipSuccess
+             ? TP_OK
+             : TP_ERR_HIP;
+}
+
+extern "C" tp_status tp_gather_rows(const uint16_t* Xs, int64_t stride_elems, int32_t t, int64_t Mt,
+                                    int64_t N, int64_t ldb, uint16_t* X, int64_t ldx,
+                                    hipStream_t stream) {
+  if (t <= 0 || Mt < 0 || N <= 0 || ldb < N || ldx < N) return TP_ERR_SHAPE;
+  if (Mt == 0) return TP_OK;
+  if (Xs == nullptr || X == nullptr) return TP_ERR_NULL;
+  if (t > 1 && stride_elems < Mt * ldb) return TP_ERR_SHAPE;
+  if (!aligned16(Xs) || !aligned16(X) || N % 8 || ldb % 8 || ldx % 8 || stride_elems % 8)
+    return TP_ERR_ALIGN;
+  return tpk::launch_gather(Xs, stride_elems, t, Mt, N, ldb, X, ldx, stream) == hipSuccess
+             ? TP_OK
+             : TP_ERR_HIP;
+}

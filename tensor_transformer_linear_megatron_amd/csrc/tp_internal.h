@@ -74,6 +74,8 @@ size_t gemm_workspace_bytes(int64_t M, int64_t ldx, int64_t ksteps, int64_t ntil
 hipError_t launch_split_fixup(const LinearArgs& a, Epilogue epi, const float* part, int G, hipStream_t s);
 hipError_t launch_reduce(const float* P, int64_t stride, int32_t t, int64_t M, int64_t N,
                          int64_t ldp, float* Y, int64_t ldy, hipStream_t s);
+hipError_t launch_gather(const uint16_t* Xs, int64_t stride, int32_t t, int64_t Mt, int64_t N,
+                         int64_t ldb, uint16_t* X, int64_t ldx, hipStream_t s);
 
 }  // namespace tpk
 

@@ -177,6 +177,29 @@ def test_linear_argument_errors():
     assert lib.tp_ffn_shard(g, d, A, 4, 64, B, B, C, MIS, 64, NUL, 0, S) == _lib.TP_ERR_ALIGN
 
 
+def test_sequence_parallel_argument_errors():
+    """Every refusal happens on the host, before any launch."""
+    lib = _lib.load()
+    S = ctypes.c_void_p(0)
+    rs, g = lib.tp_reduce_scatter_partials, lib.tp_gather_rows
+    assert rs(A, 256, 3, 4, 64, 64, 0, B, 64, S) == _lib.TP_ERR_INDIVISIBLE  # 4 rows over 3 ranks
+    assert rs(A, 256, 2, 4, 64, 64, 2, B, 64, S) == _lib.TP_ERR_RANK
+    assert rs(A, 256, 2, 4, 64, 64, -1, B, 64, S) == _lib.TP_ERR_RANK
+    assert rs(NUL, 256, 2, 4, 64, 64, 0, B, 64, S) == _lib.TP_ERR_NULL
+    assert rs(A, 256, 0, 4, 64, 64, 0, B, 64, S) == _lib.TP_ERR_SHAPE
+    assert rs(A, 255, 2, 4, 64, 64, 0, B, 64, S) == _lib.TP_ERR_SHAPE  # stride < M ld
+    assert rs(A, 256, 2, 4, 62, 64, 0, B, 64, S) == _lib.TP_ERR_ALIGN  # N % 4
+    assert rs(MIS, 256, 2, 4, 64, 64, 0, B, 64, S) == _lib.TP_ERR_ALIGN
+    assert rs(NUL, 256, 2, 0, 64, 64, 1, NUL, 64, S) == _lib.TP_OK  # M == 0
+    assert g(NUL, 256, 2, 4, 64, 64, B, 64, S) == _lib.TP_ERR_NULL
+    assert g(A, 256, 0, 4, 64, 64, B, 64, S) == _lib.TP_ERR_SHAPE
+    assert g(A, 255, 2, 4, 64, 64, B, 64, S) == _lib.TP_ERR_SHAPE  # stride < Mt ldb
+    assert g(A, 256, 2, 4, 60, 64, B, 64, S) == _lib.TP_ERR_ALIGN  # N % 8
+    assert g(A, 256, 2, 4, 64, 64, MIS, 64, S) == _lib.TP_ERR_ALIGN
+    assert g(A, 256, 2, 4, 64, 32, B, 64, S) == _lib.TP_ERR_SHAPE  # ldb < N
+    assert g(NUL, 256, 2, 0, 64, 64, NUL, 64, S) == _lib.TP_OK  # Mt == 0
+
+
 def test_reduce_and_pack_argument_errors():
     lib = _lib.load()
     S = ctypes.c_void_p(0)

@@ -281,6 +281,56 @@ def test_reduce_partials(t, M, N):
     np.testing.assert_array_equal(host_f64(Pd[0]), got)
 
 
+@pytest.mark.parametrize("t", [1, 2, 3, 8])
+@pytest.mark.parametrize("Mt,N", [(1, 8), (3, 4100), (8, 8192)])
+def test_reduce_scatter_partials(t, Mt, N):
+    """Sequence-parallel partial sum: each rank's token rows of the rank-order
+    sum, bit for bit the rows of the full sum, within tolerance of the oracle,
+    and exact against it on integer-valued partials."""
+    say("reduce-scatter", t, Mt, N)
+    M = t * Mt
+    P = si.normal_f32(t * 2000 + Mt, (t * M, N), 1.0).reshape(t, M, N)
+    Pd = torch.from_numpy(P).cuda()
+    full = tp.tp_reduce_partials(Pd)
+    Pi = si.int_bf16(t * 3000 + Mt, (t * M, N), -256, 256)
+    Pi = oracle.bf16_to_f64(Pi).reshape(t, M, N)
+    Pid = torch.from_numpy(Pi.astype(np.float32)).cuda()
+    for r in range(t):
+        Y = tp.tp_reduce_scatter_partials(Pd, r)
+        assert Y.shape == (Mt, N)
+        assert torch.equal(Y, full[r * Mt:(r + 1) * Mt]), r
+        assert_parity(host_f64(Y), oracle.reduce_scatter(P.astype(np.float64), r), f"rank {r}")
+        np.testing.assert_array_equal(host_f64(tp.tp_reduce_scatter_partials(Pid, r)),
+                                      oracle.reduce_scatter(Pi, r))
+    # into a column slice of a wider buffer
+    wide = torch.zeros((Mt, N + 8), dtype=torch.float32, device="cuda")
+    tp.tp_reduce_scatter_partials(Pd, t - 1, Y=wide[:, 4:4 + N])
+    assert torch.equal(wide[:, 4:4 + N], full[(t - 1) * Mt:])
+    assert not wide[:, :4].any() and not wide[:, 4 + N:].any()
+
+
+@pytest.mark.parametrize("t", [1, 2, 3, 8])
+@pytest.mark.parametrize("Mt,N", [(1, 8), (5, 4104), (64, 8192)])
+def test_gather_rows(t, Mt, N):
+    """The row gather: the ranks' bf16 row blocks stacked in rank order, bit-exact."""
+    say("gather", t, Mt, N)
+    Xs = si.normal_bf16(t * 4000 + Mt, (t * Mt, N), 1.0).reshape(t, Mt, N)
+    got = host_bits(tp.tp_gather_rows(dev(Xs)))
+    np.testing.assert_array_equal(got, oracle.gather_rows(list(Xs)))
+
+
+def test_sequence_parallel_round_trip():
+    """All-reduce = reduce-scatter then gather: the 70B TP = 8 O-projection
+    partials of 256 tokens, reduce-scattered per rank, rounded to bf16 and
+    gathered, equal the rounded full sum bit for bit."""
+    say("sequence-parallel round trip")
+    t, M, N = 8, 256, 8192
+    P = torch.from_numpy(si.normal_f32(77, (t * M, N), 1.0).reshape(t, M, N)).cuda()
+    blocks = torch.stack([tp.tp_reduce_scatter_partials(P, r) for r in range(t)]).to(torch.bfloat16)
+    X = tp.tp_gather_rows(blocks.contiguous())
+    assert torch.equal(X, tp.tp_reduce_partials(P).to(torch.bfloat16))
+
+
 # ---------------------------------------------------------------------------
 # The two paths where both are legal, determinism, composition.
 # ---------------------------------------------------------------------------
