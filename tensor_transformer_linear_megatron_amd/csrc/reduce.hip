@@ -19,6 +19,15 @@
 namespace tpk {
 namespace {
 
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
+// One partial's 4 columns, read once: non-temporal.
+__device__ __forceinline__ f32x4v_t load_part(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(p));
+}
+
+// The loads of up to 8 ranks are issued before their sum, so a thread keeps
+// that many 16-byte reads in flight; the additions still run in rank order.
 __global__ __launch_bounds__(256) void reduce_kernel(const float* P, int64_t stride, int32_t t,
                                                      int64_t M, int64_t n4, int64_t ldp, float* Y,
                                                      int64_t ldy) {
@@ -27,15 +36,18 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* P, int64_t str
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int64_t m = idx / n4, c = (idx - m * n4) * 4;
     const float* p = P + m * ldp + c;
-    float4 s = *reinterpret_cast<const float4*>(p);
-    for (int32_t r = 1; r < t; ++r) {
-      const float4 v = *reinterpret_cast<const float4*>(p + (int64_t)r * stride);
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
+    f32x4v_t s = load_part(p);
+    for (int32_t r0 = 1; r0 < t; r0 += 8) {
+      const int32_t n = t - r0 < 8 ? t - r0 : 8;
+      f32x4v_t v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < n) v[j] = load_part(p + (int64_t)(r0 + j) * stride);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < n) s += v[j];
     }
-    *reinterpret_cast<float4*>(Y + m * ldy + c) = s;
+    *reinterpret_cast<f32x4v_t*>(Y + m * ldy + c) = s;
   }
 }
 
