@@ -39,6 +39,10 @@ Readings where the pages are silent (the same list is in the design notes):
 * Rounding points: a column output consumed in bf16 (Y_r, H_r, QKV_r) is
   rounded to bf16 (nearest, ties to even) from the fp64 value; row partials
   and their sum stay unrounded.
+* 8-bit weights (the pages fix no format): OCP FP8 E4M3 codes, one
+  power-of-two scale per output column of the rank's shard, the smallest that
+  keeps every scaled weight within 448; codes round to nearest, ties to even;
+  activations stay bf16.
 * Sequence parallelism (the pages name only what it splits): after the
   row-parallel product rank r keeps rows [r M/t, (r+1) M/t) of the summed
   partials (a reduce-scatter along the tokens), and the full activations for
@@ -267,6 +271,103 @@ def gather_rows(blocks) -> np.ndarray:
     blocks = [np.asarray(b) for b in blocks]
     assert blocks and all(b.shape == blocks[0].shape for b in blocks)
     return np.concatenate(blocks, axis=0)
+
+
+# --------------------------------------------------------------------------
+# 8-bit weights for decode ("AI Infrastructure series, Part 5", "Reason 2":
+# in decode every token reads every weight, so a 70B model in 8-bit reads
+# 70.6 GB per token, half its 16-bit bytes). The pages fix no format. Reading
+# taken: OCP FP8 E4M3 codes with one power-of-two scale per output column of
+# the rank's shard; the activations stay bf16 (weight-only quantisation).
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0  # largest finite E4M3 value, 1.75 * 2^8
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """fp64 values of OCP E4M3 codes: sign bit, 4 exponent bits (bias 7), 3
+    mantissa bits; exponent field 0 holds the subnormals m 2^-9; the two codes
+    S.1111.111 are NaN; there are no infinities."""
+    c = np.asarray(codes).astype(np.int64)
+    s, e, m = c >> 7, (c >> 3) & 15, c & 7
+    v = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return np.where(s == 1, -v, v)
+
+
+def column_exponents(W: np.ndarray) -> np.ndarray:
+    """e_n = the smallest integer with max_k |W[k, n]| <= 448 * 2^e_n; 0 for an
+    all-zero column. With amax = f 2^x, f in [0.5, 1), and 448 = 0.875 2^9:
+    e = x - 9 when f <= 0.875, else x - 8 (exact, no rounding)."""
+    amax = np.abs(np.asarray(W, dtype=np.float64)).max(axis=0)
+    e = np.zeros(amax.shape, dtype=np.int64)
+    nz = amax > 0
+    f, x = np.frexp(amax[nz])
+    e[nz] = np.where(f <= 0.875, x - 9, x - 8)
+    return e
+
+
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """E4M3 codes nearest to v (|v| <= 448), ties to the even code (mantissa bit
+    0 clear); the sign is kept, so a negative value that rounds to zero gives
+    the code of -0."""
+    v = np.asarray(v, dtype=np.float64)
+    assert np.all(np.abs(v) <= E4M3_MAX), "scaled weights must lie within the E4M3 range"
+    table = e4m3_decode(np.arange(0x7F))  # non-negative finite codes 0 .. 0x7E, increasing
+    a = np.abs(v).ravel()
+    hi = np.minimum(np.searchsorted(table, a, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - table[lo], table[hi] - a  # exact: both sides are short dyadic numbers
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    mag = np.where(a == table[hi], hi, np.where(pick_hi, hi, lo))
+    sign = np.signbit(v.ravel()).astype(np.int64) << 7
+    return (mag | sign).astype(np.uint8).reshape(v.shape)
+
+
+def quantize_columns(W: np.ndarray):
+    """(codes uint8 [K x N], exponents int64 [N]) of a weight matrix in fp64:
+    codes = E4M3 round of W[k, n] 2^-e_n."""
+    W = np.asarray(W, dtype=np.float64)
+    e = column_exponents(W)
+    return e4m3_round(W * np.exp2(-e.astype(np.float64))), e
+
+
+def dequantize_columns(codes: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """The weights the 8-bit linear multiplies by: decode(q) 2^e_n, exact."""
+    return e4m3_decode(codes) * np.exp2(np.asarray(e, dtype=np.float64))
+
+
+def _shard_f64(W: np.ndarray, rows, cols) -> np.ndarray:
+    return bf16_to_f64(np.ascontiguousarray(W[np.asarray(rows)][:, np.asarray(cols)]))
+
+
+def shard_weight_fp8(W: np.ndarray, p: dict) -> np.ndarray:
+    """The rank's shard as its 8-bit form multiplies it: each of the shard's
+    output columns quantised on its own (for gate/up: gate and up columns
+    separately), then dequantised, fp64 [shard_k x shard_n]."""
+    q, e = quantize_columns(_shard_f64(W, p["rows"], p["cols"]))
+    return dequantize_columns(q, e)
+
+
+def col_linear_fp8(X: np.ndarray, W: np.ndarray, p: dict) -> np.ndarray:
+    """X W'_r in fp64, unrounded (W'_r: the dequantised 8-bit shard)."""
+    assert p["kind"] in ("col", "qkv_col")
+    return bf16_to_f64(X) @ shard_weight_fp8(W, p)
+
+
+def gateup_swiglu_fp8(X: np.ndarray, Wgu: np.ndarray, p: dict) -> np.ndarray:
+    """H_r = bf16(SiLU(X W'_g) * (X W'_u)) with 8-bit gate and up shards."""
+    assert p["kind"] == "gateup_col"
+    Wq = shard_weight_fp8(Wgu, p)
+    half = p["shard_n"] // 2
+    Xf = bf16_to_f64(X)
+    return swiglu(Xf @ Wq[:, :half], Xf @ Wq[:, half:])
+
+
+def row_linear_fp8(Z: np.ndarray, W: np.ndarray, p: dict) -> np.ndarray:
+    """P_r = Z_r W'[rows_r, :] in fp64 with the 8-bit row shard."""
+    assert p["kind"] in ("row", "o_row")
+    return bf16_to_f64(Z) @ shard_weight_fp8(W, p)
 
 
 # --------------------------------------------------------------------------

@@ -277,6 +277,135 @@ def test_gather_rows_restores_the_activations():
 
 
 # ---------------------------------------------------------------------------
+# 8-bit weights ("AI Infrastructure series, Part 5", "Reason 2": a 70B model
+# in 8-bit reads 70.6 GB per token). Format reading: OCP FP8 E4M3 with one
+# power-of-two scale per output column.
+# ---------------------------------------------------------------------------
+
+def _e4m3_exact(code: int) -> Fraction | None:
+    """Exact value of an E4M3 code from the format's definition."""
+    s, e, m = code >> 7, (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return None
+    v = Fraction(m, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    return -v if s else v
+
+
+def test_e4m3_decode_closed_forms():
+    d = oracle.e4m3_decode(np.arange(256))
+    for c in range(256):
+        want = _e4m3_exact(c)
+        if want is None:
+            assert math.isnan(d[c]), hex(c)
+        else:
+            assert Fraction(d[c]) == want, hex(c)
+    assert d[0x7E] == 448.0 and d[0x08] == 2.0 ** -6 and d[0x01] == 2.0 ** -9 and d[0x00] == 0.0
+    assert math.copysign(1.0, d[0x80]) < 0 and d[0x80] == 0.0
+    # a library routine: torch's float8_e4m3fn type
+    t = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(d), np.isnan(t)) and np.array_equal(d[~np.isnan(d)], t[~np.isnan(t)])
+
+
+def test_e4m3_round_against_torch_on_every_bf16_value():
+    # every bf16 value within +-448: one rounding from binary32 in torch's cast
+    bits = np.arange(65536, dtype=np.uint32)
+    f = ((bits << 16).astype(np.uint32)).view(np.float32)
+    f = f[np.isfinite(f) & (np.abs(f) <= 448.0)]
+    want = torch.from_numpy(f).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_round(f.astype(np.float64)), want)
+
+
+def test_e4m3_round_midpoints_tie_to_even():
+    d = oracle.e4m3_decode(np.arange(0x7F))
+    for c in range(0x7E):
+        mid = (d[c] + d[c + 1]) / 2  # exact in fp64
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_round(np.array([mid]))[0] == even, hex(c)
+        assert oracle.e4m3_round(np.array([-mid]))[0] == even | 0x80, hex(c)
+        # just off the midpoint, the nearest code wins, by exact rational comparison
+        for x in (np.nextafter(mid, 0), np.nextafter(mid, 1000)):
+            got = oracle.e4m3_round(np.array([x]))[0]
+            lo, hi = Fraction(d[c]), Fraction(d[c + 1])
+            want = c if abs(Fraction(x) - lo) < abs(Fraction(x) - hi) else c + 1
+            assert got == want, (hex(c), x)
+    # a negative value that rounds to zero keeps its sign
+    assert oracle.e4m3_round(np.array([-2.0 ** -11]))[0] == 0x80
+
+
+def test_column_exponent_rule():
+    W = np.array([[448.0, 448.0 * (1 + 2 ** -20), 224.0, 0.0, -3.0e-5, 1.0, 449.0, 2.0 ** -30]])
+    e = oracle.column_exponents(W)
+    assert list(e) == [0, 1, -1, 0, math.ceil(math.log2(3.0e-5 / 448)), math.ceil(math.log2(1 / 448)), 1, -38]
+    rng = np.random.default_rng(8)
+    A = rng.standard_normal((64, 500)) * 10.0 ** rng.integers(-8, 8, size=500)
+    e = oracle.column_exponents(A).astype(np.float64)
+    amax = np.abs(A).max(axis=0)
+    assert np.all(amax * np.exp2(-e) <= 448.0) and np.all(amax * np.exp2(-(e - 1)) > 448.0)
+
+
+def test_dequantised_weight_error_bound():
+    # 3 mantissa bits: within half a unit of the code spacing, i.e. 2^-4 relative
+    # for normal codes and 2^-10 2^e absolute in the subnormal range
+    W = si.normal_bf16(31, (256, 96), 0.02)
+    Wf = decode(W)
+    q, e = oracle.quantize_columns(Wf)
+    Wq = oracle.dequantize_columns(q, e)
+    scale = np.exp2(e.astype(np.float64))
+    err = np.abs(Wq - Wf)
+    assert np.all(err <= np.maximum(np.abs(Wf) * 2.0 ** -4, 2.0 ** -10 * scale))
+    assert np.abs(Wq).max(axis=0).max() <= (np.abs(Wf).max(axis=0) * (1 + 2 ** -4)).max()
+
+
+def test_small_integer_weights_quantise_exactly():
+    # integers up to 15 in magnitude have at most 4 significant bits: the 8-bit
+    # form is exact, so the 8-bit linear equals the exact integer product
+    W = si.int_bf16(32, (64, 48), -15, 15)
+    X = si.int_bf16(33, (5, 64), -3, 3)
+    p = oracle.plan("col", 64, 48, 1, 0)
+    assert np.array_equal(oracle.shard_weight_fp8(W, p), decode(W))
+    Xi, Wi = decode(X).astype(np.int64), decode(W).astype(np.int64)
+    assert np.array_equal(oracle.col_linear_fp8(X, W, p), (Xi @ Wi).astype(np.float64))
+
+
+def test_fp8_shards_follow_the_plan():
+    # columns are quantised one by one, so 8-bit column shards concatenate to the
+    # unsharded 8-bit product; row shards quantise their own rows, so their
+    # partials sum to the product with the ranks' dequantised rows stacked
+    X, W = normal(34, (6, 128)), normal(35, (128, 96), 0.05)
+    full = oracle.col_linear_fp8(X, W, oracle.plan("col", 128, 96, 1, 0))
+    Xf = decode(X)
+    for t in (2, 4):
+        parts = [oracle.col_linear_fp8(X, W, oracle.plan("col", 128, 96, t, r)) for r in range(t)]
+        np.testing.assert_allclose(np.concatenate(parts, axis=1), full, rtol=0, atol=1e-12)
+        ps = [oracle.plan("row", 128, 96, t, r) for r in range(t)]
+        P = sum(oracle.row_linear_fp8(X[:, p["rows"]], W, p) for p in ps)
+        Wst = np.concatenate([oracle.shard_weight_fp8(W, p) for p in ps], axis=0)
+        bound = reassoc_bound(Xf, np.abs(Wst), 128)
+        assert np.all(np.abs(P - Xf @ Wst) <= bound + 1e-300)
+
+
+def test_pages_8bit_decode_closed_forms():
+    # 70B in 8-bit: 70.6 GB per token; at 3.35 TB/s about 21 ms; a TP = 4 rank
+    # reads a quarter, about 5.3 ms ("Reason 2")
+    assert round(70.6e9 / 3.35e12 * 1e3) == 21
+    assert round(70.6e9 / 4 / 3.35e12 * 1e3, 1) == 5.3
+    # one code byte per weight: an 8-bit shard is half its bf16 bytes, plus 4
+    # bytes of scale per column (the 70B feed-forward rank share of TP = 8)
+    K, N = 8192, 7168
+    assert K * N + 4 * N < (K * N * 2) // 2 * 1.001
+
+
+def test_planted_round_toward_zero_is_caught():
+    # truncating the scaled weights instead of rounding them moves many codes
+    bits = np.arange(0, 65536, 7, dtype=np.uint32)
+    f32 = ((bits << 16).astype(np.uint32)).view(np.float32)
+    f = f32[np.isfinite(f32) & (np.abs(f32) <= 448.0)].astype(np.float64)
+    table = oracle.e4m3_decode(np.arange(0x7F))
+    trunc = np.searchsorted(table, np.abs(f), side="right") - 1
+    assert np.count_nonzero(trunc != (oracle.e4m3_round(f) & 0x7F)) > 100
+
+
+# ---------------------------------------------------------------------------
 # SwiGLU.
 # ---------------------------------------------------------------------------
 
