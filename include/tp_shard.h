@@ -91,6 +91,12 @@ typedef enum {
   TP_PATH_PREFILL = 2  /* LDS-tiled MFMA GEMM, compute-bound */
 } tp_path;
 
+/* How the packed shard stores its weights. */
+typedef enum {
+  TP_W_BF16 = 0,     /* bf16 values as given */
+  TP_W_FP8_E4M3 = 1  /* one byte per weight: OCP FP8 E4M3 codes, one power-of-two scale per output column */
+} tp_wformat;
+
 /* Attention shape: query heads, key-value heads, head dimension. */
 typedef struct {
   int32_t n_q, n_kv, head_dim;
@@ -116,6 +122,8 @@ typedef struct {
   int64_t out_n;                /* width of the column output: shard_n, or shard_n / 2 (= I/t) for TP_GATEUP_COL */
   int64_t packed_k, packed_n;   /* padded sizes of the packed layout */
   int64_t packed_bytes;         /* bytes tp_shard_pack writes */
+  int32_t wformat;              /* tp_wformat; tp_shard_plan sets TP_W_BF16 (see tp_shard_set_wformat) */
+  int32_t reserved;             /* 0 */
 } tp_shard_desc;
 
 /*
@@ -138,14 +146,36 @@ TP_API tp_status tp_shard_plan(tp_kind kind, int64_t K, int64_t N, int32_t t, in
                         const tp_heads* heads, tp_shard_desc* out);
 
 /*
+ * Switches a planned shard to another weight storage before it is packed
+ * ("AI Infrastructure series, Part 5", "Reason 2": in decode every token
+ * reads every weight, so a 70B model in 8-bit reads 70.6 GB per token, half
+ * its 16-bit bytes). Sets desc->wformat and recomputes packed_k and
+ * packed_bytes; everything else is unchanged.
+ *   TP_W_BF16: packed_k = shard_k rounded up to 32, 2 bytes per weight.
+ *   TP_W_FP8_E4M3: weight-only 8-bit storage; the activations stay bf16.
+ *     Output column n of the shard gets the exponent e_n, the smallest
+ *     integer with max_k |W[k][n]| <= 448 * 2^e_n (0 for an all-zero column),
+ *     and each weight the OCP FP8 E4M3 code (1 sign, 4 exponent bits with
+ *     bias 7, 3 mantissa bits, subnormals, largest finite 448) nearest to
+ *     W[k][n] * 2^-e_n, ties to even, sign kept. The linears multiply by the
+ *     dequantised weights decode(code) * 2^e_n, which are exact in bf16.
+ *     packed_k = shard_k rounded up to 64; packed_bytes = packed_k * packed_n
+ *     (codes) + 4 * packed_n (the scales 2^e_n as fp32).
+ * Unknown format -> TP_ERR_KIND; an invalid descriptor -> its check's error.
+ */
+TP_API tp_status tp_shard_set_wformat(tp_shard_desc* desc, int32_t wformat);
+
+/*
  * Copies the rank's shard out of the full weight into the kernels' packed
  * layout ("AI Infrastructure series, Part 5", "What does it look like in vLLM
  * ...": the engine splits the weights as it loads them). Load-time work.
  *   W        device, full logical [K x N] bf16, row-major, leading dim ldw >= N
  *   W_packed device, desc->packed_bytes bytes, 16-byte aligned; its layout is
- *            private to the library (tiles of 16 output columns x 32 k,
- *            zero-padded to packed_n x packed_k, pairs of tiles interleaved
- *            by k-step, gate/up tiles paired).
+ *            private to the library (tiles of 16 output columns x 32 k for
+ *            bf16, x 64 k for 8-bit codes, zero-padded to packed_n x
+ *            packed_k, pairs of tiles interleaved by k-step, gate/up tiles
+ *            paired; 8-bit shards end with their column scales).
+ * For TP_W_FP8_E4M3 the pack quantises as tp_shard_set_wformat states.
  */
 TP_API tp_status tp_shard_pack(const tp_shard_desc* desc, const uint16_t* W, int64_t ldw,
                         void* W_packed, hipStream_t stream);

@@ -20,10 +20,11 @@ import torch
 from . import _lib
 from ._lib import (  # noqa: F401
     KIND_NAMES, TP_COL, TP_GATEUP_COL, TP_O_ROW, TP_PATH_AUTO, TP_PATH_DECODE, TP_PATH_PREFILL,
+    TP_W_BF16, TP_W_FP8_E4M3,
     TP_QKV_COL, TP_ROW, TpHeads, TpShardDesc,
 )
 
-__all__ = ["tp_shard_plan", "tp_shard_pack", "tp_col_linear", "tp_row_linear", "tp_ffn_shard",
+__all__ = ["tp_shard_plan", "tp_shard_set_wformat", "tp_shard_pack", "tp_col_linear", "tp_row_linear", "tp_ffn_shard",
            "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows", "tp_workspace_bytes",
            "tp_status_str", "TpError", "TpShardDesc"]
 
@@ -67,6 +68,16 @@ def tp_shard_plan(kind, K: int, N: int, t: int, rank: int, heads=None) -> TpShar
     if heads is not None:
         hp = ctypes.pointer(TpHeads(*heads))
     _check(_lib.load().tp_shard_plan(k, K, N, t, rank, hp, ctypes.byref(d)), "tp_shard_plan")
+    return d
+
+
+def tp_shard_set_wformat(desc: TpShardDesc, wformat) -> TpShardDesc:
+    """A copy of ``desc`` switched to ``wformat`` ("bf16", "fp8_e4m3" or a
+    TP_W_* code): packed_k and packed_bytes follow the format."""
+    codes = {"bf16": _lib.TP_W_BF16, "fp8_e4m3": _lib.TP_W_FP8_E4M3}
+    f = codes[wformat] if isinstance(wformat, str) else int(wformat)
+    d = desc.copy()
+    _check(_lib.load().tp_shard_set_wformat(ctypes.byref(d), f), "tp_shard_set_wformat")
     return d
 
 

@@ -22,6 +22,7 @@ TP_ERR_ALIGN = -5
 TP_ERR_WORKSPACE = -6
 TP_ERR_HIP = -7
 TP_ERR_KIND = -8
+TP_W_BF16, TP_W_FP8_E4M3 = 0, 1
 
 TP_COL, TP_ROW, TP_GATEUP_COL, TP_QKV_COL, TP_O_ROW = range(5)
 TP_PATH_AUTO, TP_PATH_DECODE, TP_PATH_PREFILL = range(3)
@@ -29,7 +30,7 @@ TP_PATH_AUTO, TP_PATH_DECODE, TP_PATH_PREFILL = range(3)
 KIND_NAMES = {"col": TP_COL, "row": TP_ROW, "gateup_col": TP_GATEUP_COL,
               "qkv_col": TP_QKV_COL, "o_row": TP_O_ROW}
 
-EXPORTS = ("tp_shard_plan", "tp_shard_pack", "tp_col_linear", "tp_row_linear", "tp_ffn_shard",
+EXPORTS = ("tp_shard_plan", "tp_shard_set_wformat", "tp_shard_pack", "tp_col_linear", "tp_row_linear", "tp_ffn_shard",
            "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows", "tp_workspace_bytes",
            "tp_status_str")
 
@@ -56,6 +57,7 @@ class TpShardDesc(ctypes.Structure):
         ("out_n", ctypes.c_int64),
         ("packed_k", ctypes.c_int64), ("packed_n", ctypes.c_int64),
         ("packed_bytes", ctypes.c_int64),
+        ("wformat", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
     def copy(self) -> "TpShardDesc":
@@ -86,6 +88,7 @@ def load() -> ctypes.CDLL:
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     D = ctypes.POINTER(TpShardDesc)
     lib.tp_shard_plan.argtypes = [ctypes.c_int, I64, I64, I32, I32, ctypes.POINTER(TpHeads), D]
+    lib.tp_shard_set_wformat.argtypes = [D, I32]
     lib.tp_shard_pack.argtypes = [D, P, I64, P, P]
     lib.tp_col_linear.argtypes = [D, P, I64, I64, P, P, I64, P, SZ, P]
     lib.tp_row_linear.argtypes = [D, P, I64, I64, P, P, I64, P, SZ, P]
@@ -97,7 +100,7 @@ def load() -> ctypes.CDLL:
     lib.tp_workspace_bytes.restype = SZ
     lib.tp_status_str.argtypes = [I32]
     lib.tp_status_str.restype = ctypes.c_char_p
-    for name in ("tp_shard_plan", "tp_shard_pack", "tp_col_linear", "tp_row_linear",
+    for name in ("tp_shard_plan", "tp_shard_set_wformat", "tp_shard_pack", "tp_col_linear", "tp_row_linear",
                  "tp_ffn_shard", "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows"):
         getattr(lib, name).restype = I32
     _lib = lib

@@ -17,9 +17,12 @@ tp_status check_desc(const tp_shard_desc* d) {
   if (d == nullptr) return TP_ERR_NULL;
   if (!is_col(d->kind) && !is_row(d->kind)) return TP_ERR_KIND;
   const bool gateup = d->kind == TP_GATEUP_COL;
+  if (d->wformat != TP_W_BF16 && d->wformat != TP_W_FP8_E4M3) return TP_ERR_KIND;
+  const bool fp8 = d->wformat == TP_W_FP8_E4M3;
   if (d->shard_k <= 0 || d->shard_n <= 0 || d->out_n <= 0 || d->packed_k < d->shard_k ||
-      d->packed_k % tpk::kTileK || d->packed_n % (2 * tpk::kTileN) ||
-      d->packed_bytes != d->packed_k * d->packed_n * 2)
+      d->packed_k % (fp8 ? tpk::kTileK8 : tpk::kTileK) || d->packed_n % (2 * tpk::kTileN) ||
+      d->packed_bytes != (fp8 ? d->packed_k * d->packed_n + 4 * d->packed_n
+                              : d->packed_k * d->packed_n * 2))
     return TP_ERR_SHAPE;
   if (gateup) {
     // gate and up tiles alternate: an even tile count, each half covering out_n
@@ -33,6 +36,13 @@ tp_status check_desc(const tp_shard_desc* d) {
   return TP_OK;
 }
 
+bool is_fp8(const tp_shard_desc* d) { return d->wformat == TP_W_FP8_E4M3; }
+
+// k-steps of the packed layout: 32 k for bf16 tiles, 64 k for 8-bit tiles.
+int64_t ksteps_of(const tp_shard_desc* d) {
+  return d->packed_k / (is_fp8(d) ? tpk::kTileK8 : tpk::kTileK);
+}
+
 tpk::LinearArgs make_args(const tp_shard_desc* d, const uint16_t* X, int64_t M, int64_t ldx,
                           const void* Wp, void* out, int64_t ldo) {
   tpk::LinearArgs a;
@@ -41,12 +51,23 @@ tpk::LinearArgs make_args(const tp_shard_desc* d, const uint16_t* X, int64_t M, 
   a.M = M;
   a.K = d->shard_k;
   a.W = static_cast<const uint4*>(Wp);
-  a.ksteps = d->packed_k / tpk::kTileK;
+  a.ksteps = ksteps_of(d);
   a.ntiles = d->packed_n / tpk::kTileN;
   a.out = out;
   a.ldo = ldo;
   a.out_n = d->out_n;
+  // An 8-bit shard's column scales follow its codes.
+  a.wscale = is_fp8(d) ? reinterpret_cast<const float*>(static_cast<const uint8_t*>(Wp) +
+                                                        d->packed_k * d->packed_n)
+                       : nullptr;
   return a;
+}
+
+// An 8-bit shard at prefill is first dequantised into a bf16 packed copy
+// (2 k-steps of 32 per step of 64) at the start of the workspace; the GEMM's
+// own workspace follows it.
+size_t dequant_bytes(const tp_shard_desc* d) {
+  return ((size_t)d->packed_k * d->packed_n * 2 + 255) / 256 * 256;
 }
 
 tpk::Epilogue epilogue_of(const tp_shard_desc* d) {
@@ -62,25 +83,47 @@ int32_t path_of(const tp_shard_desc* d, int64_t M) {
 // Workspace of the kernels chosen for this shard at this M. The prefill plan
 // is taken at the smallest leading dimension (shard_k); a wider X can only
 // turn the split off, never need more.
-size_t workspace_bytes(const tp_shard_desc* d, int64_t M) {
+size_t workspace_bytes(const tp_shard_desc* d, int64_t M, int64_t ldx) {
   if (M <= 0) return 0;
-  const int64_t ksteps = d->packed_k / tpk::kTileK, ntiles = d->packed_n / tpk::kTileN;
-  if (path_of(d, M) == TP_PATH_DECODE) return tpk::gemv_workspace_bytes(M, ksteps, ntiles, epilogue_of(d));
-  return tpk::gemm_workspace_bytes(M, d->shard_k, ksteps, ntiles);
+  const int64_t ntiles = d->packed_n / tpk::kTileN;
+  if (is_fp8(d)) {
+    if (path_of(d, M) == TP_PATH_DECODE) return 0;
+    return dequant_bytes(d) + tpk::gemm_workspace_bytes(M, ldx, 2 * ksteps_of(d), ntiles);
+  }
+  if (path_of(d, M) == TP_PATH_DECODE)
+    return tpk::gemv_workspace_bytes(M, ksteps_of(d), ntiles, epilogue_of(d));
+  return tpk::gemm_workspace_bytes(M, ldx, ksteps_of(d), ntiles);
 }
+size_t workspace_bytes(const tp_shard_desc* d, int64_t M) { return workspace_bytes(d, M, d->shard_k); }
 
 tp_status run_linear(const tp_shard_desc* d, const tpk::LinearArgs& a, void* ws, size_t ws_bytes,
                      hipStream_t s) {
   const int32_t path = path_of(d, a.M);
   if (path == TP_PATH_DECODE && a.M > 64) return TP_ERR_SHAPE;
-  const size_t need = path == TP_PATH_DECODE
-                          ? workspace_bytes(d, a.M)
-                          : tpk::gemm_workspace_bytes(a.M, a.ldx, a.ksteps, a.ntiles);
+  const size_t need = workspace_bytes(d, a.M, a.ldx);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return TP_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return TP_ERR_ALIGN;
   float* w = need > 0 ? static_cast<float*>(ws) : nullptr;
-  const hipError_t e = path == TP_PATH_DECODE ? tpk::launch_gemv(a, epilogue_of(d), w, s)
-                                              : tpk::launch_gemm(a, epilogue_of(d), w, s);
+  hipError_t e;
+  if (is_fp8(d) && path == TP_PATH_DECODE) {
+    e = tpk::launch_gemv8(a, epilogue_of(d), s);
+  } else if (is_fp8(d)) {
+    // prefill: dequantise into the workspace, then the bf16 GEMM on that copy
+    uint4* w16 = static_cast<uint4*>(ws);
+    e = tpk::launch_dequant8(a.W, a.wscale, a.ksteps, a.ntiles, w16, s);
+    if (e == hipSuccess) {
+      tpk::LinearArgs b = a;
+      b.W = w16;
+      b.ksteps = 2 * a.ksteps;
+      b.wscale = nullptr;
+      const size_t db = dequant_bytes(d);
+      float* rest = need > db ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + db) : nullptr;
+      e = tpk::launch_gemm(b, epilogue_of(d), rest, s);
+    }
+  } else {
+    e = path == TP_PATH_DECODE ? tpk::launch_gemv(a, epilogue_of(d), w, s)
+                               : tpk::launch_gemm(a, epilogue_of(d), w, s);
+  }
   return e == hipSuccess ? TP_OK : TP_ERR_HIP;
 }
 
@@ -120,10 +163,13 @@ extern "C" tp_status tp_shard_pack(const tp_shard_desc* d, const uint16_t* W, in
   a.shard_k = d->shard_k;
   a.shard_n = d->shard_n;
   a.out_n = d->out_n;
-  a.ksteps = d->packed_k / tpk::kTileK;
+  a.ksteps = ksteps_of(d);
   a.ntiles = d->packed_n / tpk::kTileN;
   a.n_ranges = d->n_col_ranges;
   a.gateup = d->kind == TP_GATEUP_COL;
+  a.scales = is_fp8(d) ? reinterpret_cast<float*>(static_cast<uint8_t*>(W_packed) +
+                                                  d->packed_k * d->packed_n)
+                       : nullptr;
   for (int r = 0; r < 3; ++r) {
     const tp_col_range c = r < d->n_col_ranges ? d->col_ranges[r] : tp_col_range{0, 0, 0};
     if (r < d->n_col_ranges && (c.src_col < 0 || c.len < 0 || c.src_col + c.len > d->N ||
@@ -133,7 +179,8 @@ extern "C" tp_status tp_shard_pack(const tp_shard_desc* d, const uint16_t* W, in
     a.len[r] = c.len;
     a.dst[r] = c.dst_col;
   }
-  return tpk::launch_pack(a, stream) == hipSuccess ? TP_OK : TP_ERR_HIP;
+  const hipError_t e = is_fp8(d) ? tpk::launch_pack8(a, stream) : tpk::launch_pack(a, stream);
+  return e == hipSuccess ? TP_OK : TP_ERR_HIP;
 }
 
 extern "C" tp_status tp_col_linear(const tp_shard_desc* d, const uint16_t* X, int64_t M,

@@ -201,6 +201,131 @@ __global__ __launch_bounds__(LB) void gemv_stream(LinearArgs a, int64_t chunk) {
 }
 
 // ---------------------------------------------------------------------------
+// gemv8_stream: 8-bit shards (TP_W_FP8_E4M3), 1 <= M <= 64
+// ---------------------------------------------------------------------------
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two E4M3 codes (word `hi` of d) -> their bf16 values decode * 2^e, packed.
+// The hardware conversion scales exactly by the power of two; the results
+// have at most 4 significant bits, so their upper halves are the bf16 bits.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t d, float scale) {
+  const f32x2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d, scale, HI);
+  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+
+// A lane's 16 codes -> the A operands of the step's two bf16 k-steps.
+__device__ __forceinline__ void decode_fp8_tile(uint4 w, float sc, uint4& a0, uint4& a1) {
+  a0 = make_uint4(fp8x2_bf16x2<false>(w.x, sc), fp8x2_bf16x2<true>(w.x, sc),
+                  fp8x2_bf16x2<false>(w.y, sc), fp8x2_bf16x2<true>(w.y, sc));
+  a1 = make_uint4(fp8x2_bf16x2<false>(w.z, sc), fp8x2_bf16x2<true>(w.z, sc),
+                  fp8x2_bf16x2<false>(w.w, sc), fp8x2_bf16x2<true>(w.w, sc));
+}
+
+// As gemv_stream, over steps of 64 k: a workgroup owns T adjacent tiles for
+// the whole K, its S wavefronts take contiguous step ranges, and each keeps a
+// ring of U steps of code and token loads in flight. A step is one 16-byte
+// code load per lane and tile (half the bytes of the bf16 path for the same
+// k) and 2 MB token fragments (MB blocks of 16 tokens); the codes are decoded
+// in registers with the lane's column scale and multiplied on the bf16 MFMA.
+template <int MB, int T, int U, int EPI, int LB>
+__global__ __launch_bounds__(LB) void gemv8_stream(LinearArgs a, int64_t chunk) {
+  static_assert(T == 1 || T == 2, "one tile or one tile pair per workgroup");
+  extern __shared__ f32x4_t red[];  // [S][T][MB][64]
+  const int lane = threadIdx.x & 63, wave = wave_id(), S = blockDim.x >> 6;
+  const int g = lane >> 4, i = lane & 15;
+  const int64_t tile0 = (int64_t)blockIdx.x * T;
+  const int64_t ksteps = a.ksteps;  // steps of 64 k
+  const int64_t k0 = (int64_t)wave * chunk;
+  const int64_t k1 = k0 + chunk < ksteps ? k0 + chunk : ksteps;
+  const int64_t n = k1 > k0 ? k1 - k0 : 0;
+  const uint4* wp = a.W + tile_index(tile0, n > 0 ? k0 : 0, ksteps) * kTileU4 + lane;
+  float sc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) sc[t] = a.wscale[(tile0 + t) * kTileN + i];
+  TokenRow xr[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) xr[mb] = token_row(a, mb * 16 + i, g);
+  const int64_t xk0 = k0 * kTileK8;
+
+  f32x4_t acc[T][MB];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[t][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 wb[U][T], xb[U][MB][2];
+#define TP_FILL(SLOT, STEP)                                                                \
+  {                                                                                        \
+    _Pragma("unroll") for (int t = 0; t < T; ++t)                                          \
+        wb[SLOT][t] = load_w(wp + ((int64_t)(STEP) * 2 + t) * kTileU4);                    \
+    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) _Pragma("unroll") for (int h = 0; h < 2; ++h) \
+        xb[SLOT][mb][h] = xr[mb].load(xk0 + (STEP) * kTileK8 + h * kTileK);                \
+  }
+#define TP_MMA(SLOT, STEP)                                                                 \
+  {                                                                                        \
+    _Pragma("unroll") for (int t = 0; t < T; ++t) {                                        \
+      uint4 a0, a1;                                                                        \
+      decode_fp8_tile(wb[SLOT][t], sc[t], a0, a1);                                         \
+      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                  \
+        const int64_t ko = xk0 + (STEP) * kTileK8;                                         \
+        acc[t][mb] = mfma_16x16x32(a0, xr[mb].use(xb[SLOT][mb][0], ko), acc[t][mb]);      \
+        acc[t][mb] = mfma_16x16x32(a1, xr[mb].use(xb[SLOT][mb][1], ko + kTileK), acc[t][mb]); \
+      }                                                                                    \
+    }                                                                                      \
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (u < n) TP_FILL(u, u)
+  const int64_t full = n / U;
+  for (int64_t r = 0; r + 1 < full; ++r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      TP_MMA(u, r * U + u)
+      TP_FILL(u, (r + 1) * U + u)
+    }
+  }
+  if (full >= 1) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      TP_MMA(u, (full - 1) * U + u)
+      if (full * U + u < n) TP_FILL(u, full * U + u)
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (full * U + u < n) TP_MMA(u, full * U + u)
+#undef TP_FILL
+#undef TP_MMA
+
+  if (S > 1) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) red[((wave * T + t) * MB + mb) * 64 + lane] = acc[t][mb];
+    __syncthreads();
+    for (int mb = wave; mb < MB; mb += S) {
+      f32x4_t v[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        v[t] = red[(t * MB + mb) * 64 + lane];
+        for (int s2 = 1; s2 < S; ++s2) v[t] += red[((s2 * T + t) * MB + mb) * 64 + lane];
+      }
+      epilogue<EPI, T>(a, v, mb * 16 + i, tile0, g);
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      f32x4_t v[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) v[t] = acc[t][mb];
+      epilogue<EPI, T>(a, v, mb * 16 + i, tile0, g);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // gemv_shared
 // ---------------------------------------------------------------------------
 
@@ -501,7 +626,54 @@ hipError_t launch_t(const LinearArgs& a, float* ws, hipStream_t s) {
   }
 }
 
+// Launch plan of gemv8_stream: the same workgroup and wavefront counts as
+// gemv_stream (pairs, S from the group count, at least 4 steps of 64 k per
+// wavefront); the ring shrinks as the token blocks grow, keeping its
+// registers bounded.
+template <int MB, int T, int EPI>
+hipError_t launch_stream8(const LinearArgs& a, hipStream_t s) {
+  constexpr int U = MB == 1 ? 8 : (MB == 2 ? 4 : 2);
+  const int64_t groups = a.ntiles / T;
+  int S = (T == 2 && groups >= 768) ? 1 : pow2_at_least(((T == 2 ? 1536 : 2048) + groups - 1) / groups);
+  if (S > 16) S = 16;
+  while (S > 1 && a.ksteps / S < 4) S >>= 1;
+  const int64_t chunk = (a.ksteps + S - 1) / S;
+  const size_t lds = S > 1 ? (size_t)S * T * MB * 64 * sizeof(f32x4_t) : 0;
+  const dim3 grid((unsigned)groups), block(64 * S);
+  if (S <= 4) {
+    hipLaunchKernelGGL((gemv8_stream<MB, T, U, EPI, 256>), grid, block, lds, s, a, chunk);
+  } else {
+    constexpr int U16 = MB == 1 ? 4 : (MB == 2 ? 2 : 1);  // 16 waves per workgroup: 128 VGPRs each
+    hipLaunchKernelGGL((gemv8_stream<MB, T, U16, EPI, 1024>), grid, block, lds, s, a, chunk);
+  }
+  return hipGetLastError();
+}
+
+template <int T, int EPI>
+hipError_t launch_t8(const LinearArgs& a, hipStream_t s) {
+  switch ((a.M + 15) / 16) {
+    case 1: return launch_stream8<1, T, EPI>(a, s);
+    case 2: return launch_stream8<2, T, EPI>(a, s);
+    case 3: return launch_stream8<3, T, EPI>(a, s);
+    case 4: return launch_stream8<4, T, EPI>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gemv8(const LinearArgs& a, Epilogue epi, hipStream_t s) {
+  if (a.M <= 0 || a.ntiles == 0) return hipSuccess;
+  if (a.wscale == nullptr || a.ntiles % 2) return hipErrorInvalidValue;
+  switch (epi) {
+    case kEpiSwiglu: return launch_t8<2, kEpiSwiglu>(a, s);
+    case kEpiBf16:
+      return a.ntiles >= 512 ? launch_t8<2, kEpiBf16>(a, s) : launch_t8<1, kEpiBf16>(a, s);
+    case kEpiF32:
+      return a.ntiles >= 512 ? launch_t8<2, kEpiF32>(a, s) : launch_t8<1, kEpiF32>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_split_fixup(const LinearArgs& a, Epilogue epi, const float* part, int G, hipStream_t s) {
   const int64_t pld = a.ntiles * kTileN;

@@ -1,22 +1,17 @@
 // Load-time cut of one rank's shard out of the full weight into the packed
 // tile layout described in tp_internal.h ("AI Infrastructure series, Part 5",
 // "What does it look like in vLLM ...": the weights are split as they load).
+// 8-bit shards are quantised on the way ("AI Infrastructure series, Part 5",
+// "Reason 2": a 70B model in 8-bit reads half the bytes per token): OCP FP8
+// E4M3 codes with one power-of-two scale per output column.
 #include "tp_internal.h"
 
 namespace tpk {
 namespace {
 
-__global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int64_t total_u4) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= total_u4) return;
-  const int lane = (int)(c & 63);
-  // 1 KiB index -> (tile pair, k-step, tile of the pair); see tile_index().
-  const int64_t idx = c >> 6;
-  const int64_t pair = idx / (2 * a.ksteps), rem = idx - pair * 2 * a.ksteps;
-  const int64_t ks = rem >> 1, nt = 2 * pair + (rem & 1);
-  const int g = lane >> 4, i = lane & 15;
-
-  // Shard column of this lane and whether it exists.
+// Column i of packed tile nt: the column of the full weight it holds, or
+// false for padding.
+__device__ __forceinline__ bool source_col(const PackArgs& a, int64_t nt, int i, int64_t* wcol) {
   int64_t n;
   bool valid;
   if (a.gateup) {
@@ -27,17 +22,28 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int64_t total_u4)
     n = nt * kTileN + i;
     valid = n < a.shard_n;
   }
-  // Shard column -> column of the full weight.
-  int64_t wcol = 0;
-  if (valid) {
-    valid = false;
-    for (int r = 0; r < a.n_ranges; ++r) {
-      if (n >= a.dst[r] && n < a.dst[r] + a.len[r]) {
-        wcol = a.src[r] + (n - a.dst[r]);
-        valid = true;
-      }
+  *wcol = 0;
+  if (!valid) return false;
+  for (int r = 0; r < a.n_ranges; ++r) {
+    if (n >= a.dst[r] && n < a.dst[r] + a.len[r]) {
+      *wcol = a.src[r] + (n - a.dst[r]);
+      return true;
     }
   }
+  return false;
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int64_t total_u4) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= total_u4) return;
+  const int lane = (int)(c & 63);
+  // 1 KiB index -> (tile pair, k-step, tile of the pair); see tile_index().
+  const int64_t idx = c >> 6;
+  const int64_t pair = idx / (2 * a.ksteps), rem = idx - pair * 2 * a.ksteps;
+  const int64_t ks = rem >> 1, nt = 2 * pair + (rem & 1);
+  const int g = lane >> 4, i = lane & 15;
+  int64_t wcol;
+  const bool valid = source_col(a, nt, i, &wcol);
   uint16_t v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -52,7 +58,135 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int64_t total_u4)
   a.out[c] = o;
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit shards (TP_W_FP8_E4M3).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Pass 1: one thread per packed column. e = the smallest integer with
+// amax <= 448 2^e: with amax = f 2^x, f in [0.5, 1) and 448 = 0.875 2^9,
+// e = x - 9 if f <= 0.875, else x - 8. Padding and all-zero columns get 2^0.
+__global__ __launch_bounds__(256) void pack8_scale_kernel(PackArgs a) {
+  const int64_t pc = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (pc >= a.ntiles * kTileN) return;
+  int64_t wcol;
+  float amax = 0.0f;
+  if (source_col(a, pc / kTileN, (int)(pc % kTileN), &wcol)) {
+    for (int64_t k = 0; k < a.shard_k; ++k)
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(a.W[(a.row_begin + k) * a.ldw + wcol])));
+  }
+  int e = 0;
+  if (amax > 0.0f) {
+    int x;
+    const float f = frexpf(amax, &x);
+    e = f <= 0.875f ? x - 9 : x - 8;
+  }
+  a.scales[pc] = ldexpf(1.0f, e);
+}
+
+// E4M3 code of v, |v| <= 448, round to nearest, ties to even, sign kept.
+// v = sig 2^(x - 23) (sig with its hidden bit); the code spacing at this
+// magnitude is 2^q, q = max(x, -6) - 3, and n = v / 2^q is rounded to an
+// integer: n in [8, 16] is a normal code (16 carries into the exponent),
+// n in [0, 8] below 2^-6 is a subnormal code (8 is the smallest normal).
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t mag = u & 0x7FFFFFFFu;
+  if (mag == 0) return sign;
+  const int E = (int)(mag >> 23);
+  const uint32_t sig = (mag & 0x7FFFFFu) | (E ? 0x800000u : 0u);
+  const int x = E ? E - 127 : -126;
+  const int q = (x < -6 ? -6 : x) - 3;
+  const int sh = q - x + 23;  // >= 20
+  if (sh >= 26) return sign;  // below a quarter of the smallest spacing: rounds to 0
+  uint32_t n = sig >> sh;
+  const uint32_t r = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
+  if (r > half || (r == half && (n & 1u))) ++n;
+  if (x < -6) return sign | n;  // subnormal codes 0..7, or 8 = 2^-6
+  int ex = x + 7;
+  if (n == 16) {
+    n = 8;
+    ++ex;
+  }
+  return sign | ((uint32_t)ex << 3) | (n - 8);
+}
+
+// Pass 2: one thread per 16-byte lane slot of a 1 KiB tile of 16 columns x
+// 64 k: bytes 0..7 hold k = 64 s + 8 g + e, bytes 8..15 k = 64 s + 32 + 8 g + e.
+__global__ __launch_bounds__(256) void pack8_kernel(PackArgs a, int64_t total_u4) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= total_u4) return;
+  const int lane = (int)(c & 63);
+  const int64_t idx = c >> 6;
+  const int64_t pair = idx / (2 * a.ksteps), rem = idx - pair * 2 * a.ksteps;
+  const int64_t s = rem >> 1, nt = 2 * pair + (rem & 1);
+  const int g = lane >> 4, i = lane & 15;
+  int64_t wcol;
+  const bool valid = source_col(a, nt, i, &wcol);
+  const float inv = 1.0f / a.scales[nt * kTileN + i];  // 2^-e: exact
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int b = 0; b < 16; ++b) {
+    const int64_t k = s * kTileK8 + (b >> 3) * kTileK + g * 8 + (b & 7);
+    const float v = (valid && k < a.shard_k) ? bf16_bits_to_f32(a.W[(a.row_begin + k) * a.ldw + wcol]) : 0.0f;
+    w[b >> 2] |= e4m3_rne(v * inv) << (8 * (b & 3));
+  }
+  a.out[c] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two E4M3 codes (word `hi` of d) -> two bf16 values decode * scale, packed:
+// the scaled values are exact in fp32 with at most 4 significant bits, so
+// their upper halves are the bf16 bits.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t d, float scale) {
+  const f32x2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d, scale, HI);
+  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+
+// Dequantise into the bf16 layout: output 1 KiB tile (nt, ks) lane l is half
+// ks & 1 of the 8-bit tile (nt, ks >> 1), same lane.
+__global__ __launch_bounds__(256) void dequant8_kernel(const uint4* W8, const float* scales,
+                                                       int64_t ksteps8, uint4* W16, int64_t total_u4) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= total_u4) return;
+  const int lane = (int)(c & 63);
+  const int64_t ksteps16 = 2 * ksteps8;
+  const int64_t idx = c >> 6;
+  const int64_t pair = idx / (2 * ksteps16), rem = idx - pair * 2 * ksteps16;
+  const int64_t ks = rem >> 1, nt = 2 * pair + (rem & 1);
+  const uint4 q = W8[tile_index(nt, ks >> 1, ksteps8) * kTileU4 + lane];
+  const float sc = scales[nt * kTileN + (lane & 15)];
+  const uint32_t d0 = (ks & 1) ? q.z : q.x, d1 = (ks & 1) ? q.w : q.y;
+  W16[c] = make_uint4(fp8x2_to_bf16x2<false>(d0, sc), fp8x2_to_bf16x2<true>(d0, sc),
+                      fp8x2_to_bf16x2<false>(d1, sc), fp8x2_to_bf16x2<true>(d1, sc));
+}
+
 }  // namespace
+
+hipError_t launch_pack8(const PackArgs& a, hipStream_t s) {
+  const int64_t cols = a.ntiles * kTileN;
+  if (cols == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack8_scale_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total = a.ksteps * a.ntiles * kTileU4;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack8_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant8(const uint4* W8, const float* scales, int64_t ksteps8, int64_t ntiles,
+                           uint4* W16, hipStream_t s) {
+  const int64_t total = 2 * ksteps8 * ntiles * kTileU4;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant8_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, W8,
+                     scales, ksteps8, W16, total);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   const int64_t total = a.ksteps * a.ntiles * kTileU4;

@@ -133,7 +133,28 @@ extern "C" tp_status tp_shard_plan(tp_kind kind, int64_t K, int64_t N, int32_t t
   d.packed_n = kind == TP_GATEUP_COL ? 2 * round_up(d.out_n, tpk::kTileN)
                                      : round_up(d.shard_n, 2 * tpk::kTileN);
   d.packed_bytes = d.packed_k * d.packed_n * 2;
+  d.wformat = TP_W_BF16;
+  d.reserved = 0;
   *out = d;
+  return TP_OK;
+}
+
+extern "C" tp_status tp_shard_set_wformat(tp_shard_desc* d, int32_t wformat) {
+  if (d == nullptr) return TP_ERR_NULL;
+  if (d->shard_k <= 0 || d->packed_n <= 0) return TP_ERR_SHAPE;
+  switch (wformat) {
+    case TP_W_BF16:
+      d->packed_k = round_up(d->shard_k, tpk::kTileK);
+      d->packed_bytes = d->packed_k * d->packed_n * 2;
+      break;
+    case TP_W_FP8_E4M3:
+      d->packed_k = round_up(d->shard_k, tpk::kTileK8);
+      d->packed_bytes = d->packed_k * d->packed_n + 4 * d->packed_n;
+      break;
+    default:
+      return TP_ERR_KIND;
+  }
+  d->wformat = wformat;
   return TP_OK;
 }
 

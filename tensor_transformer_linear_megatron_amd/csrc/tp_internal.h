@@ -26,6 +26,13 @@ namespace tpk {
 constexpr int kTileN = 16;
 constexpr int kTileK = 32;
 constexpr int kTileU4 = 64;  // uint4 per tile
+// 8-bit shards (TP_W_FP8_E4M3): tiles of 16 columns x 64 k, also 1 KiB, in
+// the same pair-interleaved order (tile_index with k-steps of 64). Lane l =
+// 16 g + i owns 16 bytes: the codes of column i at k = 64 s + 8 g + e
+// (bytes 0..7) and k = 64 s + 32 + 8 g + e (bytes 8..15), e = 0..7, i.e. the
+// A operands of two consecutive bf16 k-steps. The packed_n fp32 column
+// scales 2^e_n follow the codes.
+constexpr int kTileK8 = 64;
 
 // 1 KiB index of tile (nt, ks) in the packed layout.
 __host__ __device__ __forceinline__ int64_t tile_index(int64_t nt, int64_t ks, int64_t ksteps) {
@@ -46,6 +53,7 @@ struct LinearArgs {
   void* out;          // bf16 or fp32 [M x out_n], leading dim ldo
   int64_t ldo;
   int64_t out_n;      // valid output columns
+  const float* wscale;  // 8-bit shards: the ntiles kTileN column scales 2^e_n; else null
 };
 
 struct PackArgs {
@@ -57,9 +65,18 @@ struct PackArgs {
   int64_t src[3], len[3], dst[3];
   int32_t n_ranges;
   int32_t gateup;
+  float* scales;      // 8-bit shards: where the column scales go (ksteps counts 64-k steps); else null
 };
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+// 8-bit shards: column scales, then the E4M3 codes (a.scales must be set).
+hipError_t launch_pack8(const PackArgs& a, hipStream_t s);
+// 8-bit shard -> the bf16 packed layout of the dequantised weights (ksteps16
+// = 2 ksteps8 k-steps of 32), for the prefill GEMM.
+hipError_t launch_dequant8(const uint4* W8, const float* scales, int64_t ksteps8, int64_t ntiles,
+                           uint4* W16, hipStream_t s);
+// Decode path for 8-bit shards, 1 <= M <= 64; no workspace.
+hipError_t launch_gemv8(const LinearArgs& a, Epilogue epi, hipStream_t s);
 // Decode path. `ws` must hold gemv_workspace_bytes() bytes (fp32 split
 // partials) when that is non-zero.
 hipError_t launch_gemv(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s);

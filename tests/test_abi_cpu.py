@@ -177,6 +177,34 @@ def test_linear_argument_errors():
     assert lib.tp_ffn_shard(g, d, A, 4, 64, B, B, C, MIS, 64, NUL, 0, S) == _lib.TP_ERR_ALIGN
 
 
+def test_set_wformat_sizes_and_errors():
+    """tp_shard_plan gives bf16 storage; switching to 8-bit re-plans packed_k to
+    a multiple of 64 and packed_bytes to codes + 4 bytes of scale per packed
+    column; switching back restores the bf16 plan; a descriptor whose sizes do
+    not match its format is refused before any launch."""
+    lib = _lib.load()
+    S = ctypes.c_void_p(0)
+    for kind, K, N, t, r in (("col", 4104, 1040, 2, 1), ("gateup_col", 8192, 57344, 8, 3), ("row", 1000, 64, 1, 0)):
+        d = tp.tp_shard_plan(kind, K, N, t, r)
+        assert d.wformat == tp.TP_W_BF16 and d.reserved == 0
+        e = tp.tp_shard_set_wformat(d, "fp8_e4m3")
+        assert e.wformat == tp.TP_W_FP8_E4M3 and e.packed_k % 64 == 0
+        assert e.packed_k == -(-d.shard_k // 64) * 64 and e.packed_n == d.packed_n
+        assert e.packed_bytes == e.packed_k * e.packed_n + 4 * e.packed_n
+        back = tp.tp_shard_set_wformat(e, "bf16")
+        assert (back.packed_k, back.packed_bytes, back.wformat) == (d.packed_k, d.packed_bytes, 0)
+        assert tp.tp_workspace_bytes(e, 1) == 0 and tp.tp_workspace_bytes(e, 64) == 0
+        assert tp.tp_workspace_bytes(e, 4096) >= e.packed_k * e.packed_n * 2
+    d = tp.tp_shard_plan("col", 64, 64, 1, 0)
+    assert lib.tp_shard_set_wformat(ctypes.byref(d), 7) == _lib.TP_ERR_KIND
+    assert lib.tp_shard_set_wformat(None, 1) == _lib.TP_ERR_NULL
+    bad = d.copy()
+    bad.wformat = tp.TP_W_FP8_E4M3  # sizes still those of the bf16 plan
+    assert lib.tp_col_linear(ctypes.byref(bad), A, 4, 64, B, C, 64, NUL, 0, S) == _lib.TP_ERR_SHAPE
+    bad.wformat = 9
+    assert lib.tp_col_linear(ctypes.byref(bad), A, 4, 64, B, C, 64, NUL, 0, S) == _lib.TP_ERR_KIND
+
+
 def test_sequence_parallel_argument_errors():
     """Every refusal happens on the host, before any launch."""
     lib = _lib.load()

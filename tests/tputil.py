@@ -70,3 +70,26 @@ def unpack(desc, packed: torch.Tensor) -> np.ndarray:
         up = cols[:, 1].reshape(-1, ks_n * 32)[:desc.out_n]
         t = np.concatenate([gate, up], axis=0)
     return np.ascontiguousarray(t[:desc.shard_n, :desc.shard_k].T)
+
+
+def unpack8(desc, packed: torch.Tensor):
+    """Read an 8-bit packed shard back: (codes uint8 [shard_k x shard_n],
+    column scales float32 [shard_n]). Tiles of 16 columns x 64 k, 1 KiB, in
+    the same pair-interleaved order as the bf16 layout (k-steps of 64); lane
+    l = 16 g + i holds the codes of column 16 nt + i at k = 64 s + 32 h + 8 g + e
+    in byte 8 h + e; the packed_n fp32 scales follow the codes."""
+    ks_n = desc.packed_k // 64
+    nt_n = desc.packed_n // 16
+    assert nt_n % 2 == 0 and desc.wformat == 1
+    buf = packed.view(torch.uint8).cpu().numpy()
+    nc = desc.packed_k * desc.packed_n
+    q = buf[:nc].reshape(nt_n // 2, ks_n, 2, 4, 16, 2, 8)          # pair, s, t, g, i, h, e
+    t = q.transpose(0, 2, 4, 1, 5, 3, 6).reshape(nt_n * 16, ks_n * 64)  # (nt, i) x (s, h, g, e)
+    sc = buf[nc:nc + 4 * desc.packed_n].view(np.float32)
+    if desc.kind == 2:  # gate/up interleaved by tile
+        cols = t.reshape(nt_n // 2, 2, 16, -1)
+        t = np.concatenate([cols[:, 0].reshape(-1, ks_n * 64)[:desc.out_n],
+                            cols[:, 1].reshape(-1, ks_n * 64)[:desc.out_n]], axis=0)
+        s2 = sc.reshape(nt_n // 2, 2, 16)
+        sc = np.concatenate([s2[:, 0].reshape(-1)[:desc.out_n], s2[:, 1].reshape(-1)[:desc.out_n]])
+    return np.ascontiguousarray(t[:desc.shard_n, :desc.shard_k].T), np.ascontiguousarray(sc[:desc.shard_n])
