@@ -477,9 +477,22 @@ def config_worked_tp2(timer):
                 us_per_step=round(us, 2), bytes_per_step=nbytes)
 
 
+def decode_bytes_fp8(M, H, I, t=1):
+    """Bytes one rank's feed-forward share moves with 8-bit weights: one code
+    byte per weight and a 4-byte scale per output column, activations as in
+    decode_bytes."""
+    w = I // t
+    gateup = H * 2 * w + 2 * w * 4 + M * H * 2 + M * w * 2
+    down = w * H + H * 4 + M * w * 2 + M * H * 4
+    return gateup, down
+
+
 def config_70b_ffn_decode(timer):
     """Llama-3.1-70B feed-forward layer at TP = 8 decode: all 8 rank shares in
-    turn (each gate/up + SwiGLU + down) and the sum of the 8 partials."""
+    turn (each gate/up + SwiGLU + down) and the sum of the 8 partials, with
+    bf16 weights and with the same weights in 8-bit (OCP FP8 E4M3, one
+    power-of-two scale per column; the pages' decode example is this model in
+    8-bit)."""
     import torch
     import tensor_transformer_linear_megatron_amd as tp
     from seeded_inputs import workloads as wl
@@ -488,34 +501,47 @@ def config_70b_ffn_decode(timer):
     H, I, t = c["hidden"], c["inter"], 8
     w = I // t
     log(f"[bench] 70B feed-forward at TP=8: generating [Wg | Wu] {H} x {2 * I} and Wd {I} x {H}")
-    gu = [tp.tp_shard_plan("gateup_col", H, 2 * I, t, r) for r in range(t)]
-    dn = [tp.tp_shard_plan("row", I, H, t, r) for r in range(t)]
+    plans = {}
+    for fmt in ("bf16", "fp8_e4m3"):
+        plans[fmt] = ([tp.tp_shard_set_wformat(tp.tp_shard_plan("gateup_col", H, 2 * I, t, r), fmt) for r in range(t)],
+                      [tp.tp_shard_set_wformat(tp.tp_shard_plan("row", I, H, t, r), fmt) for r in range(t)])
+    packs = {}
     Wg = to_dev(wl.gateup(H, I, c["sigma"]))
-    gp = [tp.tp_shard_pack(d, Wg) for d in gu]
+    for fmt, (gu, _) in plans.items():
+        packs[fmt] = [[tp.tp_shard_pack(d, Wg) for d in gu]]
     del Wg
     Wdn = to_dev(wl.down(I, H, c["sigma"]))
-    dp = [tp.tp_shard_pack(d, Wdn) for d in dn]
+    for fmt, (_, dn) in plans.items():
+        packs[fmt].append([tp.tp_shard_pack(d, Wdn) for d in dn])
     del Wdn
     X = to_dev(wl.activations(32, H))
-    res = []
-    for M in (1, 8, 32):
-        Hs = torch.empty((M, w), dtype=torch.bfloat16, device="cuda")
-        P = torch.empty((t, M, H), dtype=torch.float32, device="cuda")
-        out = torch.empty((M, H), dtype=torch.float32, device="cuda")
-        wsn = max(16, max(tp.tp_workspace_bytes(d, M) for d in gu + dn))
-        ws = torch.empty(wsn, dtype=torch.uint8, device="cuda")
-        calls = [(lib.tp_ffn_shard, (ref(gu[r]), ref(dn[r]), VP(X.data_ptr()), M, H, VP(gp[r].data_ptr()),
-                                     VP(dp[r].data_ptr()), VP(Hs.data_ptr()), VP(P[r].data_ptr()), H,
-                                     VP(ws.data_ptr()), wsn, stream)) for r in range(t)]
-        calls.append((lib.tp_reduce_partials, (VP(P.data_ptr()), M * H, t, M, H, H, VP(out.data_ptr()), H, stream)))
-        us = time_steps(timer, lambda i: _run(calls), 20)
-        g, d_, _ = decode_bytes(M, H, I, t)
-        nbytes = t * (g + d_) + (t + 1) * M * H * 4
-        gbs = nbytes / us / 1e3
-        res.append(dict(M=M, us_per_step=round(us, 2), rank_share_us=round(us / t, 2), value=round(gbs, 1),
-                        frac=round(gbs / HBM_PEAK_GBS, 4)))
+    out_all = {}
+    for fmt in ("bf16", "fp8_e4m3"):
+        gu, dn = plans[fmt]
+        gp, dp = packs[fmt]
+        res = []
+        for M in (1, 8, 32):
+            Hs = torch.empty((M, w), dtype=torch.bfloat16, device="cuda")
+            P = torch.empty((t, M, H), dtype=torch.float32, device="cuda")
+            out = torch.empty((M, H), dtype=torch.float32, device="cuda")
+            wsn = max(16, max(tp.tp_workspace_bytes(d, M) for d in gu + dn))
+            ws = torch.empty(wsn, dtype=torch.uint8, device="cuda")
+            calls = [(lib.tp_ffn_shard, (ref(gu[r]), ref(dn[r]), VP(X.data_ptr()), M, H, VP(gp[r].data_ptr()),
+                                         VP(dp[r].data_ptr()), VP(Hs.data_ptr()), VP(P[r].data_ptr()), H,
+                                         VP(ws.data_ptr()), wsn, stream)) for r in range(t)]
+            calls.append((lib.tp_reduce_partials, (VP(P.data_ptr()), M * H, t, M, H, H, VP(out.data_ptr()), H,
+                                                   stream)))
+            us = time_steps(timer, lambda i: _run(calls), 20)
+            g, d_ = decode_bytes(M, H, I, t)[:2] if fmt == "bf16" else decode_bytes_fp8(M, H, I, t)
+            nbytes = t * (g + d_) + (t + 1) * M * H * 4
+            gbs = nbytes / us / 1e3
+            res.append(dict(M=M, us_per_step=round(us, 2), rank_share_us=round(us / t, 2), value=round(gbs, 1),
+                            frac=round(gbs / HBM_PEAK_GBS, 4)))
+        out_all[fmt] = res
+    for a, b in zip(out_all["bf16"], out_all["fp8_e4m3"]):
+        b["speedup_vs_bf16"] = round(a["us_per_step"] / b["us_per_step"], 3)
     return dict(config="llama3.1-70b FFN, TP=8 decode: 8 rank shares in turn + sum of 8 partials",
-                unit="GB/s", peak=HBM_PEAK_GBS, batches=res)
+                unit="GB/s", peak=HBM_PEAK_GBS, batches=out_all["bf16"], batches_fp8_e4m3=out_all["fp8_e4m3"])
 
 
 def config_70b_attention_prefill(timer):

@@ -642,6 +642,10 @@ hipError_t launch_stream8(const LinearArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)groups), block(64 * S);
   if (S <= 4) {
     hipLaunchKernelGGL((gemv8_stream<MB, T, U, EPI, 256>), grid, block, lds, s, a, chunk);
+  } else if (S <= 8 && MB > 1) {
+    // measured on the 70B TP = 8 shares: with several token blocks the deeper
+    // ring of 8-wave workgroups wins; with one block, 16 waves of 4 steps
+    hipLaunchKernelGGL((gemv8_stream<MB, T, U, EPI, 512>), grid, block, lds, s, a, chunk);
   } else {
     constexpr int U16 = MB == 1 ? 4 : (MB == 2 ? 2 : 1);  // 16 waves per workgroup: 128 VGPRs each
     hipLaunchKernelGGL((gemv8_stream<MB, T, U16, EPI, 1024>), grid, block, lds, s, a, chunk);
