@@ -87,7 +87,8 @@ size_t workspace_bytes(const tp_shard_desc* d, int64_t M, int64_t ldx) {
   if (M <= 0) return 0;
   const int64_t ntiles = d->packed_n / tpk::kTileN;
   if (is_fp8(d)) {
-    if (path_of(d, M) == TP_PATH_DECODE) return 0;
+    if (path_of(d, M) == TP_PATH_DECODE)
+      return tpk::gemv_workspace_bytes(M, 2 * ksteps_of(d), ntiles, epilogue_of(d));
     return dequant_bytes(d) + tpk::gemm_workspace_bytes(M, ldx, 2 * ksteps_of(d), ntiles);
   }
   if (path_of(d, M) == TP_PATH_DECODE)
@@ -106,7 +107,7 @@ tp_status run_linear(const tp_shard_desc* d, const tpk::LinearArgs& a, void* ws,
   float* w = need > 0 ? static_cast<float*>(ws) : nullptr;
   hipError_t e;
   if (is_fp8(d) && path == TP_PATH_DECODE) {
-    e = tpk::launch_gemv8(a, epilogue_of(d), s);
+    e = tpk::launch_gemv8(a, epilogue_of(d), w, s);
   } else if (is_fp8(d)) {
     // prefill: dequantise into the workspace, then the bf16 GEMM on that copy
     uint4* w16 = static_cast<uint4*>(ws);

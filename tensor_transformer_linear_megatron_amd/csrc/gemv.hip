@@ -356,9 +356,17 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(uint4 a, uint4 b, f32x16_t c) 
 //    up element r + 8.
 //  * With G > 1 each split writes an fp32 partial part[y][m][n] and
 //    gemv_fixup adds them in split order.
-template <int MB32, int U, int C, int SN, int EPI>
+//  * F8: 8-bit shards. A weight step is 64 k (two bf16 k-steps of tokens).
+//    The same two 16-byte loads per lane and step bring, for lane (h, j),
+//    the codes of column j of the pair at k-octets h and 4 + h (first load,
+//    lane h 16 + j % 16 of the 8-bit tile) and 2 + h and 6 + h (second load):
+//    exactly its A operands of the step's four 16-k blocks, decoded in
+//    registers with the column scale. U and per count weight steps; C counts
+//    the bf16 k-steps of a token chunk.
+template <int MB32, int U, int C, int SN, int EPI, bool F8 = false>
 __global__ __launch_bounds__(64 * SN) void gemv_shared(LinearArgs a, int64_t per, float* part) {
-  static_assert(C % U == 0, "the ring must divide the chunk");
+  constexpr int KX = F8 ? 2 : 1;  // bf16 k-steps of tokens per weight step
+  static_assert(C % KX == 0 && (C / KX) % U == 0, "the ring must divide the chunk");
   constexpr int MB16 = 2 * MB32;  // 16-token fragments per k-step
   constexpr int F = C * MB16;     // token fragments per chunk
   static_assert(F % SN == 0, "staged fragments divide over the waves");
@@ -366,12 +374,15 @@ __global__ __launch_bounds__(64 * SN) void gemv_shared(LinearArgs a, int64_t per
   __shared__ uint4 xs[2 * F * 64];
   const int lane = threadIdx.x & 63, nw = wave_id();
   const int g = lane >> 4, i = lane & 15, fh = lane >> 5, fj = lane & 31;
-  const int64_t ksteps = a.ksteps;
+  const int64_t ksteps = a.ksteps;  // weight steps
   const int64_t blk = (int64_t)blockIdx.x * SN + nw;  // this wave's 32-column block
   const int64_t kbeg = (int64_t)blockIdx.y * per;
   const int64_t kend = kbeg + per < ksteps ? kbeg + per : ksteps;
-  const int64_t n = kend > kbeg ? kend - kbeg : 0;  // uniform over the workgroup
-  const int64_t nch = (n + C - 1) / C;
+  const int64_t n = kend > kbeg ? kend - kbeg : 0;  // weight steps, uniform over the workgroup
+  const int64_t nch = (n * KX + C - 1) / C;
+  const int64_t nblk = (a.ntiles + 1) / 2;
+  float sc = 1.0f;  // the lane's column scale (8-bit shards)
+  if (F8 && blk < nblk) sc = a.wscale[blk * 2 * kTileN + fj];
 
   // Weights of this workgroup's 2 SN tiles.
   const int64_t t0 = (int64_t)blockIdx.x * SN * 2;
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(64 * SN) void gemv_shared(LinearArgs a, int64_t per
   TokenRow sr[FPW];
 #pragma unroll
   for (int j = 0; j < FPW; ++j) sr[j] = token_row(a, ((nw + j * SN) % MB16) * 16 + i, g);
-  const int64_t xk0 = kbeg * kTileK;
+  const int64_t xk0 = kbeg * KX * kTileK;
   uint4 st[FPW];
 #define TP_KOFF(CH, J) (xk0 + ((int64_t)(CH) * C + (nw + (J) * SN) / MB16) * kTileK)
 #define TP_SLOAD(CH) _Pragma("unroll") for (int j = 0; j < FPW; ++j) st[j] = sr[j].load(TP_KOFF(CH, j));
@@ -415,18 +426,41 @@ __global__ __launch_bounds__(64 * SN) void gemv_shared(LinearArgs a, int64_t per
   const int xsl = (fj >> 4) * 64 + fh * 16 + (fj & 15);
   for (int64_t ch = 0; ch < nch; ++ch) {
     const int buf = (int)(ch & 1);
-    const int64_t c0 = ch * C;
+    const int64_t c0 = ch * (C / KX);  // first weight step of the chunk
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
+    for (int cw = 0; cw < C / KX; ++cw) {
+      if constexpr (F8) {
+        // 16-k block q of the step: bf16 k-step 2 cw + q / 2, k-half q % 2
+        const uint4 w0 = wb[cw % U][0], w1 = wb[cw % U][1];
+        const uint4 A[4] = {make_uint4(fp8x2_bf16x2<false>(w0.x, sc), fp8x2_bf16x2<true>(w0.x, sc),
+                                       fp8x2_bf16x2<false>(w0.y, sc), fp8x2_bf16x2<true>(w0.y, sc)),
+                            make_uint4(fp8x2_bf16x2<false>(w1.x, sc), fp8x2_bf16x2<true>(w1.x, sc),
+                                       fp8x2_bf16x2<false>(w1.y, sc), fp8x2_bf16x2<true>(w1.y, sc)),
+                            make_uint4(fp8x2_bf16x2<false>(w0.z, sc), fp8x2_bf16x2<true>(w0.z, sc),
+                                       fp8x2_bf16x2<false>(w0.w, sc), fp8x2_bf16x2<true>(w0.w, sc)),
+                            make_uint4(fp8x2_bf16x2<false>(w1.z, sc), fp8x2_bf16x2<true>(w1.z, sc),
+                                       fp8x2_bf16x2<false>(w1.w, sc), fp8x2_bf16x2<true>(w1.w, sc))};
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        uint4 xf[MB32];
+        for (int q = 0; q < 4; ++q) {
+          const int c = 2 * cw + (q >> 1), kh = q & 1;
+          uint4 xf[MB32];
 #pragma unroll
-        for (int t = 0; t < MB32; ++t) xf[t] = xs[((buf * C + c) * MB16 + 2 * t) * 64 + kh * 32 + xsl];
+          for (int t = 0; t < MB32; ++t) xf[t] = xs[((buf * C + c) * MB16 + 2 * t) * 64 + kh * 32 + xsl];
 #pragma unroll
-        for (int t = 0; t < MB32; ++t) acc[t] = mfma_32x32x16(wb[c % U][kh], xf[t], acc[t]);
+          for (int t = 0; t < MB32; ++t) acc[t] = mfma_32x32x16(A[q], xf[t], acc[t]);
+        }
+      } else {
+        const int c = cw;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          uint4 xf[MB32];
+#pragma unroll
+          for (int t = 0; t < MB32; ++t) xf[t] = xs[((buf * C + c) * MB16 + 2 * t) * 64 + kh * 32 + xsl];
+#pragma unroll
+          for (int t = 0; t < MB32; ++t) acc[t] = mfma_32x32x16(wb[c % U][kh], xf[t], acc[t]);
+        }
       }
-      TP_WLOAD(c % U, c0 + c + U)
+      TP_WLOAD(cw % U, c0 + cw + U)
     }
     if (ch + 1 < nch) {
       TP_SSTORE(buf ^ 1, ch + 1)
@@ -439,7 +473,6 @@ __global__ __launch_bounds__(64 * SN) void gemv_shared(LinearArgs a, int64_t per
 #undef TP_SLOAD
 #undef TP_SSTORE
 
-  const int64_t nblk = (a.ntiles + 1) / 2;
   if (blk >= nblk) return;
   if (part == nullptr) {
 #pragma unroll
@@ -595,17 +628,21 @@ SharedPlan plan_shared(int64_t ntiles, int64_t ksteps, int MB32) {
   return p;
 }
 
-template <int MB32, int EPI>
+// F8: an 8-bit shard's weight steps are 64 k; the plan is made in bf16
+// k-steps (the token chunks) and halved for the weight side.
+template <int MB32, int EPI, bool F8 = false>
 hipError_t launch_shared(const LinearArgs& a, float* ws, hipStream_t s) {
-  const SharedPlan p = plan_shared(a.ntiles, a.ksteps, MB32);
+  constexpr int KX = F8 ? 2 : 1;
+  const SharedPlan p = plan_shared(a.ntiles, a.ksteps * KX, MB32);
   constexpr int C = shared_chunk(MB32);
-  constexpr int U = C;
+  constexpr int U = C / KX;
+  const int64_t per = p.per / KX;  // p.per is a multiple of C
   if (p.G > 1 && ws == nullptr) return hipErrorInvalidValue;
   // A workgroup's weights are one buffer resource with 32-bit byte offsets.
   if ((int64_t)2 * kSharedSN * a.ksteps * 1024 >= (1LL << 31)) return hipErrorInvalidValue;
   float* part = p.G > 1 ? ws : nullptr;
-  hipLaunchKernelGGL((gemv_shared<MB32, U, C, kSharedSN, EPI>), dim3((unsigned)p.groups, (unsigned)p.G),
-                     dim3(64 * kSharedSN), 0, s, a, p.per, part);
+  hipLaunchKernelGGL((gemv_shared<MB32, U, C, kSharedSN, EPI, F8>), dim3((unsigned)p.groups, (unsigned)p.G),
+                     dim3(64 * kSharedSN), 0, s, a, per, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.G == 1) return e;
   const int64_t pld = a.ntiles * kTileN;
@@ -626,7 +663,7 @@ hipError_t launch_t(const LinearArgs& a, float* ws, hipStream_t s) {
   }
 }
 
-// Launch plan of gemv8_stream: the same workgroup and wavefront counts as
+// Launch plan of gemv8_stream (M <= 16): the same workgroup and wavefront counts as
 // gemv_stream (pairs, S from the group count, at least 4 steps of 64 k per
 // wavefront); the ring shrinks as the token blocks grow, keeping its
 // registers bounded.
@@ -653,28 +690,30 @@ hipError_t launch_stream8(const LinearArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Up to 16 tokens stream (one token block per wavefront); beyond, the
+// shared-token kernel in its 8-bit form.
 template <int T, int EPI>
-hipError_t launch_t8(const LinearArgs& a, hipStream_t s) {
+hipError_t launch_t8(const LinearArgs& a, float* ws, hipStream_t s) {
   switch ((a.M + 15) / 16) {
     case 1: return launch_stream8<1, T, EPI>(a, s);
-    case 2: return launch_stream8<2, T, EPI>(a, s);
-    case 3: return launch_stream8<3, T, EPI>(a, s);
-    case 4: return launch_stream8<4, T, EPI>(a, s);
+    case 2: return launch_shared<1, EPI, true>(a, ws, s);
+    case 3:
+    case 4: return launch_shared<2, EPI, true>(a, ws, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemv8(const LinearArgs& a, Epilogue epi, hipStream_t s) {
+hipError_t launch_gemv8(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s) {
   if (a.M <= 0 || a.ntiles == 0) return hipSuccess;
   if (a.wscale == nullptr || a.ntiles % 2) return hipErrorInvalidValue;
   switch (epi) {
-    case kEpiSwiglu: return launch_t8<2, kEpiSwiglu>(a, s);
+    case kEpiSwiglu: return launch_t8<2, kEpiSwiglu>(a, ws, s);
     case kEpiBf16:
-      return a.ntiles >= 512 ? launch_t8<2, kEpiBf16>(a, s) : launch_t8<1, kEpiBf16>(a, s);
+      return a.ntiles >= 512 ? launch_t8<2, kEpiBf16>(a, ws, s) : launch_t8<1, kEpiBf16>(a, ws, s);
     case kEpiF32:
-      return a.ntiles >= 512 ? launch_t8<2, kEpiF32>(a, s) : launch_t8<1, kEpiF32>(a, s);
+      return a.ntiles >= 512 ? launch_t8<2, kEpiF32>(a, ws, s) : launch_t8<1, kEpiF32>(a, ws, s);
   }
   return hipErrorInvalidValue;
 }

@@ -75,8 +75,9 @@ hipError_t launch_pack8(const PackArgs& a, hipStream_t s);
 // = 2 ksteps8 k-steps of 32), for the prefill GEMM.
 hipError_t launch_dequant8(const uint4* W8, const float* scales, int64_t ksteps8, int64_t ntiles,
                            uint4* W16, hipStream_t s);
-// Decode path for 8-bit shards, 1 <= M <= 64; no workspace.
-hipError_t launch_gemv8(const LinearArgs& a, Epilogue epi, hipStream_t s);
+// Decode path for 8-bit shards, 1 <= M <= 64. `ws` as for launch_gemv, with
+// gemv_workspace_bytes(M, 2 ksteps, ntiles) (the plan counts bf16 k-steps).
+hipError_t launch_gemv8(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s);
 // Decode path. `ws` must hold gemv_workspace_bytes() bytes (fp32 split
 // partials) when that is non-zero.
 hipError_t launch_gemv(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s);

@@ -193,7 +193,9 @@ def test_set_wformat_sizes_and_errors():
         assert e.packed_bytes == e.packed_k * e.packed_n + 4 * e.packed_n
         back = tp.tp_shard_set_wformat(e, "bf16")
         assert (back.packed_k, back.packed_bytes, back.wformat) == (d.packed_k, d.packed_bytes, 0)
-        assert tp.tp_workspace_bytes(e, 1) == 0 and tp.tp_workspace_bytes(e, 64) == 0
+        assert tp.tp_workspace_bytes(e, 1) == 0  # up to 16 tokens stream, no split
+        ws64 = tp.tp_workspace_bytes(e, 64)  # shared-token kernel: split-K partials or none
+        assert ws64 % (64 * e.packed_n * 4) == 0 and ws64 // (64 * e.packed_n * 4) <= 64
         assert tp.tp_workspace_bytes(e, 4096) >= e.packed_k * e.packed_n * 2
     d = tp.tp_shard_plan("col", 64, 64, 1, 0)
     assert lib.tp_shard_set_wformat(ctypes.byref(d), 7) == _lib.TP_ERR_KIND

@@ -145,10 +145,13 @@ def test_fp8_decode_and_prefill_agree_with_oracle_at_boundary():
 
 
 def test_fp8_workspace():
-    """No workspace at decode; at prefill the dequantised bf16 copy (plus any
-    split-K partials); a short workspace is refused."""
+    """No workspace up to 16 tokens; split-K partials for the shared-token
+    kernel when its column blocks do not fill the GPU; at prefill the
+    dequantised bf16 copy (plus any split-K partials); a short workspace is
+    refused."""
     d, _ = plan8("col", 4096, 1024, 1, 0)
-    assert tp.tp_workspace_bytes(d, 1) == 0 and tp.tp_workspace_bytes(d, 64) == 0
+    assert tp.tp_workspace_bytes(d, 1) == 0 and tp.tp_workspace_bytes(d, 16) == 0
+    assert tp.tp_workspace_bytes(d, 64) % (64 * d.packed_n * 4) == 0
     ws = tp.tp_workspace_bytes(d, 300)
     assert ws >= d.packed_k * d.packed_n * 2
     X = dev(si.normal_bf16(90, (300, 4096), 1.0))
