@@ -198,6 +198,10 @@ TP_API tp_status tp_shard_pack(const tp_shard_desc* desc, const uint16_t* W, int
  * aligned, owned by the caller (may be NULL when that is 0); its contents on
  * entry do not matter and on return are undefined. Calls queued on different
  * streams must not share one ws.
+ * 8-bit shards (tp_shard_set_wformat): the product uses the dequantised
+ * weights decode(code) * 2^e_n with the activations in bf16. The decode path
+ * reads the codes and decodes them in registers; the prefill path first
+ * writes a bf16 copy of the dequantised shard into ws.
  */
 TP_API tp_status tp_col_linear(const tp_shard_desc* desc, const uint16_t* X, int64_t M, int64_t ldx,
                         const void* W_packed, uint16_t* Y, int64_t ldy, void* ws,
@@ -211,6 +215,7 @@ TP_API tp_status tp_col_linear(const tp_shard_desc* desc, const uint16_t* X, int
  *   Z [M x shard_k] bf16, leading dim ldz: the rank's own input slice (its
  *     column output, or its heads' attention output for TP_O_ROW)
  *   P [M x N] fp32, leading dim ldp
+ * Workspace and 8-bit shards as for tp_col_linear.
  */
 TP_API tp_status tp_row_linear(const tp_shard_desc* desc, const uint16_t* Z, int64_t M, int64_t ldz,
                         const void* W_packed, float* P, int64_t ldp, void* ws,

@@ -148,7 +148,9 @@ def test_prefill_big_tile_ragged(kind, K, N, t, r, M):
 # k-steps and ends inside a k-step; the last token tile is partial.
 SPLIT_CASES = [("col", 4104, 520, 1, 0, 300, None), ("gateup_col", 2056, 2 * 600, 1, 0, 520, None),
                ("row", 3088, 1000, 2, 1, 257, None), ("qkv_col", 2048, 1536, 4, 1, 700, (16, 4, 64)),
-               ("o_row", 4096, 1000, 2, 0, 300, (32, 8, 128))]
+               ("o_row", 4096, 1000, 2, 0, 300, (32, 8, 128)),
+               # fewer tokens than one big tile: the tile's rows past M read as zeros
+               ("col", 8192, 512, 1, 0, 100, None), ("gateup_col", 4096, 2 * 256, 1, 0, 65, None)]
 
 
 @pytest.mark.parametrize("kind,K,N,t,r,M,heads", SPLIT_CASES)
