@@ -43,6 +43,10 @@ Readings where the pages are silent (the same list is in the design notes):
   power-of-two scale per output column of the rank's shard, the smallest that
   keeps every scaled weight within 448; codes round to nearest, ties to even;
   activations stay bf16.
+* Backward: the input gradient of a rank's linear is dC_r W_r^T (for the
+  column kinds a partial, summed over the ranks like the forward partials),
+  its weight gradient A_r^T dC_r; the gate/up gradient [dG | dU] is rounded
+  to bf16 once, as the products that consume it read bf16.
 * Sequence parallelism (the pages name only what it splits): after the
   row-parallel product rank r keeps rows [r M/t, (r+1) M/t) of the summed
   partials (a reduce-scatter along the tokens), and the full activations for
@@ -368,6 +372,58 @@ def row_linear_fp8(Z: np.ndarray, W: np.ndarray, p: dict) -> np.ndarray:
     """P_r = Z_r W'[rows_r, :] in fp64 with the 8-bit row shard."""
     assert p["kind"] in ("row", "o_row")
     return bf16_to_f64(Z) @ shard_weight_fp8(W, p)
+
+
+# --------------------------------------------------------------------------
+# Backward of the rank share ("Tensor vs Pipeline Parallelism", "Tensor
+# parallelism: split inside each layer": training adds two all-reduces per
+# layer in the backward pass, one per block, which sum the ranks' input
+# gradients; "AI Infrastructure series, Part 5", "Why are 8 GPUs not 8 times
+# faster?": training costs 6 x parameters x tokens, the backward twice the
+# forward -- one input-gradient and one weight-gradient product per linear).
+# --------------------------------------------------------------------------
+
+def _shard_weight_f64(W: np.ndarray, p: dict) -> np.ndarray:
+    return bf16_to_f64(np.ascontiguousarray(W[np.asarray(p["rows"])][:, np.asarray(p["cols"])]))
+
+
+def grad_input(dC: np.ndarray, W: np.ndarray, p: dict) -> np.ndarray:
+    """dA_r = dC_r W_r^T, fp64 [M x shard_k]: the gradient of the rank's
+    linear with respect to its input. dC_r (bf16 bits) is the gradient of the
+    rank's output: [M x shard_n] in shard column order for the column kinds
+    ([dG | dU] for gate/up), the full [M x N] output gradient for the row kinds."""
+    return bf16_to_f64(dC) @ _shard_weight_f64(W, p).T
+
+
+def grad_weight(A: np.ndarray, dC: np.ndarray, p: dict) -> np.ndarray:
+    """dW_r = A_r^T dC_r, fp64 [shard_k x shard_n]: A_r (bf16 bits) is the
+    rank's input (X for the column kinds, its own Z_r for the row kinds)."""
+    return bf16_to_f64(A).T @ bf16_to_f64(dC)
+
+
+def gateup_preact(X: np.ndarray, Wgu: np.ndarray, p: dict):
+    """(G, U) in fp64: the gate/up products of rank p before SwiGLU."""
+    assert p["kind"] == "gateup_col"
+    half = p["shard_n"] // 2
+    return (shard_matmul(X, Wgu, p["rows"], p["cols"][:half]),
+            shard_matmul(X, Wgu, p["rows"], p["cols"][half:]))
+
+
+def swiglu_backward_f64(G: np.ndarray, U: np.ndarray, dH: np.ndarray):
+    """(dG, dU) of H = SiLU(G) U, SiLU(g) = g s, s = 1 / (1 + e^-g):
+    dSiLU/dg = s (1 + g (1 - s)), so dG = dH U s (1 + g (1 - s)) and
+    dU = dH g s, in fp64."""
+    G, U, dH = (np.asarray(a, dtype=np.float64) for a in (G, U, dH))
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-G))
+    return dH * U * s * (1.0 + G * (1.0 - s)), dH * G * s
+
+
+def swiglu_backward(G: np.ndarray, U: np.ndarray, dH: np.ndarray) -> np.ndarray:
+    """bf16 bits of [dG | dU] [M x 2w], each rounded once from fp64: the
+    gradient the gate/up weight and input gradients consume."""
+    dG, dU = swiglu_backward_f64(G, U, dH)
+    return round_bf16(np.concatenate([dG, dU], axis=1))
 
 
 # --------------------------------------------------------------------------

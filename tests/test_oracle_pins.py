@@ -406,6 +406,117 @@ def test_planted_round_toward_zero_is_caught():
 
 
 # ---------------------------------------------------------------------------
+# Backward of the rank share ("Tensor vs Pipeline Parallelism", "Tensor
+# parallelism: split inside each layer": two more all-reduces per layer in the
+# backward pass).
+# ---------------------------------------------------------------------------
+
+def _ffn_backward_oracle(X, Wgu, Wd, dY, t):
+    """Per rank: (dX_r, dWgu_r, dWd_r) from the oracle's backward pieces, in fp64
+    (the gate/up gradient kept unrounded)."""
+    H = Wd.shape[0]
+    out = []
+    for r in range(t):
+        pg = oracle.plan("gateup_col", Wgu.shape[0], Wgu.shape[1], t, r)
+        pd = oracle.plan("row", H, Wd.shape[1], t, r)
+        G, U = oracle.gateup_preact(X, Wgu, pg)
+        Hr = oracle.swiglu(G, U)
+        dH = oracle.grad_input(dY, Wd, pd)
+        dG, dU = oracle.swiglu_backward_f64(G, U, dH)
+        dGU = np.concatenate([dG, dU], axis=1)
+        Wgu_r = decode(np.ascontiguousarray(Wgu[:, pg["cols"]]))
+        out.append((dGU @ Wgu_r.T, decode(X).T @ dGU, oracle.grad_weight(Hr, dY, pd)))
+    return out
+
+
+def test_ffn_backward_against_torch_autograd():
+    """A library routine: torch autograd in fp64 on the same feed-forward share
+    (loss = sum(P * dY)); the rank's H is used as the oracle rounds it (bf16),
+    so the down projection's input matches exactly."""
+    X, Wgu, Wd = normal(40, (5, 48)), normal(41, (48, 2 * 32), 0.2), normal(42, (32, 48), 0.2)
+    dY = normal(43, (5, 48))
+    for t in (1, 2, 4):
+        for r, (dX_r, dWgu_r, dWd_r) in enumerate(_ffn_backward_oracle(X, Wgu, Wd, dY, t)):
+            pg = oracle.plan("gateup_col", 48, 64, t, r)
+            pd = oracle.plan("row", 32, 48, t, r)
+            Xt = torch.tensor(decode(X), requires_grad=True)
+            Wg = torch.tensor(decode(np.ascontiguousarray(Wgu[:, pg["cols"]])), requires_grad=True)
+            Wdt = torch.tensor(decode(np.ascontiguousarray(Wd[pd["rows"]])), requires_grad=True)
+            GU = Xt @ Wg
+            w = pg["shard_n"] // 2
+            Hh = torch.nn.functional.silu(GU[:, :w]) * GU[:, w:]
+            Hq = Hh + (torch.tensor(oracle.bf16_to_f64(oracle.swiglu(GU[:, :w].detach().numpy(),
+                                                                      GU[:, w:].detach().numpy()))) - Hh).detach()
+            (Hq @ Wdt * torch.tensor(decode(dY))).sum().backward()
+            np.testing.assert_allclose(dX_r, Xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(dWgu_r, Wg.grad.numpy(), rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(dWd_r, Wdt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_backward_exact_integers():
+    """Integer inputs: every product is exact in fp64, so the input and
+    weight gradients equal the int64 products exactly."""
+    X, W, dC = si.int_bf16(44, (6, 40), -3, 3), si.int_bf16(45, (40, 24), -3, 3), si.int_bf16(46, (6, 24), -3, 3)
+    Xi, Wi, dCi = (decode(a).astype(np.int64) for a in (X, W, dC))
+    p = oracle.plan("col", 40, 24, 1, 0)
+    assert np.array_equal(oracle.grad_input(dC, W, p), (dCi @ Wi.T).astype(np.float64))
+    assert np.array_equal(oracle.grad_weight(X, dC, p), (Xi.T @ dCi).astype(np.float64))
+
+
+def test_backward_shards_add_up():
+    """The sum of the ranks' input gradients is the unsharded one (the
+    backward all-reduce); the ranks' weight gradients tile the unsharded
+    weight gradient (columns for the column kinds, rows for the row kinds)."""
+    X, W, dY = normal(47, (7, 64), 1.0), normal(48, (64, 48), 0.1), normal(49, (7, 48), 1.0)
+    full_dX = oracle.grad_input(dY, W, oracle.plan("col", 64, 48, 1, 0))
+    full_dW = oracle.grad_weight(X, dY, oracle.plan("col", 64, 48, 1, 0))
+    Xf, Wf, dYf = decode(X), decode(W), decode(dY)
+    for t in (2, 4, 8):
+        ps = [oracle.plan("col", 64, 48, t, r) for r in range(t)]
+        dX = sum(oracle.grad_input(np.ascontiguousarray(dY[:, p["cols"]]), W, p) for p in ps)
+        bound = reassoc_bound(np.abs(dYf), np.abs(Wf.T), 48)
+        assert np.all(np.abs(dX - full_dX) <= bound + 1e-300)
+        dW = np.concatenate([oracle.grad_weight(X, np.ascontiguousarray(dY[:, p["cols"]]), p) for p in ps], axis=1)
+        np.testing.assert_allclose(dW, full_dW, rtol=0, atol=1e-12)
+        prs = [oracle.plan("row", 64, 48, t, r) for r in range(t)]
+        dWr = np.concatenate([oracle.grad_weight(np.ascontiguousarray(X[:, p["rows"]]), dY, p) for p in prs], axis=0)
+        np.testing.assert_allclose(dWr, full_dW, rtol=0, atol=1e-12)
+        dZ = np.concatenate([oracle.grad_input(dY, W, p) for p in prs], axis=1)
+        np.testing.assert_allclose(dZ, full_dX, rtol=0, atol=1e-12)
+
+
+def test_swiglu_backward_closed_forms_and_differences():
+    # dSiLU/dg at 0 is 1/2; with dH = 1, U = 1: dG(0) = 1/2, dU(0) = 0
+    dG, dU = oracle.swiglu_backward_f64(np.array([[0.0]]), np.array([[1.0]]), np.array([[1.0]]))
+    assert dG[0, 0] == 0.5 and dU[0, 0] == 0.0
+    # far from 0 the derivative tends to 1 (g > 0) and 0 (g < 0); no NaN at the extremes
+    dG, dU = oracle.swiglu_backward_f64(np.array([[60.0, -800.0]]), np.ones((1, 2)), np.ones((1, 2)))
+    assert abs(dG[0, 0] - 1.0) < 1e-20 and dG[0, 1] == 0.0 and np.isfinite(dU).all()
+    # central differences of H = SiLU(g) u against the closed forms
+    rng = np.random.default_rng(9)
+    g, u, dh = rng.standard_normal(50) * 3, rng.standard_normal(50), rng.standard_normal(50)
+    hfun = lambda gg, uu: gg / (1 + np.exp(-gg)) * uu
+    eps = 1e-6
+    dG, dU = oracle.swiglu_backward_f64(g[None], u[None], dh[None])
+    np.testing.assert_allclose(dG[0], dh * (hfun(g + eps, u) - hfun(g - eps, u)) / (2 * eps), rtol=1e-7, atol=1e-9)
+    np.testing.assert_allclose(dU[0], dh * (hfun(g, u + eps) - hfun(g, u - eps)) / (2 * eps), rtol=1e-7, atol=1e-9)
+
+
+def test_training_flops_closed_form():
+    # 6 x parameters x tokens ("AI Infrastructure series, Part 5"): the forward is
+    # 2 x parameters x tokens, so the backward (input and weight gradients) is 4
+    M, K, N = 4096, 8192, 1280
+    fwd = 2 * M * K * N
+    assert 2 * M * N * K + 2 * K * M * N == 2 * fwd
+
+
+def test_planted_swapped_swiglu_gradients_are_caught():
+    g, u, dh = np.array([[0.7, -1.3]]), np.array([[0.4, 2.0]]), np.array([[1.0, -0.5]])
+    dG, dU = oracle.swiglu_backward_f64(g, u, dh)
+    assert not np.allclose(dG, dU)  # a mix-up of the two halves would show
+
+
+# ---------------------------------------------------------------------------
 # SwiGLU.
 # ---------------------------------------------------------------------------
 
