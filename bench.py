@@ -606,6 +606,60 @@ def config_sequence_parallel(timer):
                             frac=round(b_g / us_g / 1e3 / HBM_PEAK_GBS, 4)))
 
 
+def config_405b_ffn_backward(timer):
+    """Backward of rank 0's Llama-3.1-405B feed-forward share at TP = 8 and
+    8192 tokens (the prefill workload above): dH through the down projection's
+    transposed shard, the SwiGLU gradient, dX_0 through the gate/up transposed
+    shard, and the two weight gradients; saved activations X, [G | U], H and
+    the output gradient dY are resident."""
+    import torch
+    import tensor_transformer_linear_megatron_amd as tp
+    from seeded_inputs import workloads as wl
+    c = wl.LLAMA405B
+    Hd, I, t, M, r = c["hidden"], c["inter"], 8, 8192, 0
+    w = I // t
+    gu = tp.tp_shard_plan("gateup_col", Hd, 2 * I, t, r)
+    dn = tp.tp_shard_plan("row", I, Hd, t, r)
+    dgu, ddn = tp.tp_shard_plan_dgrad(gu), tp.tp_shard_plan_dgrad(dn)
+    g = torch.Generator(device="cuda").manual_seed(405)
+
+    def randn(shape, sigma, dtype=torch.bfloat16):
+        return (torch.randn(shape, generator=g, dtype=torch.float32, device="cuda") * sigma).to(dtype)
+
+    full = torch.empty((Hd, 2 * I), dtype=torch.bfloat16, device="cuda")
+    full[:, r * w:(r + 1) * w] = randn((Hd, w), c["sigma"])
+    full[:, I + r * w:I + (r + 1) * w] = randn((Hd, w), c["sigma"])
+    gp = tp.tp_shard_pack(dgu, full)
+    del full
+    fulld = torch.empty((I, Hd), dtype=torch.bfloat16, device="cuda")
+    fulld[r * w:(r + 1) * w] = randn((w, Hd), c["sigma"])
+    dp = tp.tp_shard_pack(ddn, fulld)
+    del fulld
+    X, dY = randn((M, Hd), 1.0), randn((M, Hd), 1.0)
+    GU, H = randn((M, 2 * w), 1.0), randn((M, w), 0.5)
+    dH = torch.empty((M, w), dtype=torch.float32, device="cuda")
+    dGU = torch.empty((M, 2 * w), dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty((M, Hd), dtype=torch.float32, device="cuda")
+    dWgu = torch.empty((Hd, 2 * w), dtype=torch.float32, device="cuda")
+    dWd = torch.empty((w, Hd), dtype=torch.float32, device="cuda")
+    us = dict(dgrad_down=time_steps(timer, lambda i: tp.tp_row_linear(ddn, dY, dp, P=dH), 5),
+              swiglu_bwd=time_steps(timer, lambda i: tp.tp_swiglu_backward(GU, dH, dGU=dGU), 10),
+              dgrad_gateup=time_steps(timer, lambda i: tp.tp_row_linear(dgu, dGU, gp, P=dX), 5),
+              wgrad_gateup=time_steps(timer, lambda i: tp.tp_weight_grad(gu, X, dGU, dW=dWgu), 5),
+              wgrad_down=time_steps(timer, lambda i: tp.tp_weight_grad(dn, H, dY, dW=dWd), 5))
+    fl = dict(dgrad_down=2 * M * Hd * w, dgrad_gateup=2 * M * 2 * w * Hd, wgrad_gateup=2 * M * Hd * 2 * w,
+              wgrad_down=2 * M * w * Hd)
+    total = sum(fl.values()) / sum(us.values()) / 1e6
+    sw_bytes = M * w * (2 * 2 + 4 + 2 * 2)
+    per = {k: dict(us=round(v, 1), **({"TFLOP/s": round(fl[k] / v / 1e6, 1)} if k in fl else
+                                       {"GB/s": round(sw_bytes / v / 1e3, 1)}))
+           for k, v in us.items()}
+    return dict(config="llama3.1-405b FFN backward, TP=8 rank 0, 8192 tokens: dgrad + wgrad of gate/up "
+                       "16384 x 13312 and down 6656 x 16384, SwiGLU gradient",
+                unit="TFLOP/s", value=round(total, 1), frac=round(total / MFMA_BF16_PEAK_TFS, 4),
+                peak=MFMA_BF16_PEAK_TFS, per_op=per)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -615,7 +669,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (worked TP=2 split, 70B decode and attention prefill, "
-                         "sequence-parallel partial sum)")
+                         "sequence-parallel partial sum, 405B feed-forward backward)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (the yardstick for HBM byte counters)")
     args = ap.parse_args()
@@ -637,7 +691,7 @@ def main():
     if not args.no_configs:
         timer = Timer(torch.cuda.current_stream().cuda_stream)
         others = [config_worked_tp2(timer), config_70b_ffn_decode(timer), config_70b_attention_prefill(timer),
-                  config_sequence_parallel(timer)]
+                  config_sequence_parallel(timer), config_405b_ffn_backward(timer)]
     per = [dict(M=p["M"], gateup_us=round(p["gateup_us"], 2), down_us=round(p["down_us"], 2),
                 reduce_us=round(p["reduce_us"], 2), gateup_GBs=round(p["gateup_GBs"], 1),
                 down_GBs=round(p["down_GBs"], 1), ffn_GBs=round(p["ffn_GBs"], 1))

@@ -81,7 +81,8 @@ typedef enum {
   TP_ROW = 1,        /* rows    [r K/t, (r+1) K/t) of W [K x N] */
   TP_GATEUP_COL = 2, /* W = [Wg | Wu], N = 2 I: columns [r I/t, (r+1) I/t) of Wg and of Wu */
   TP_QKV_COL = 3,    /* W = [Wq | Wk | Wv], N = (n_q + 2 n_kv) d: the rank's Q, K and V heads */
-  TP_O_ROW = 4       /* W [n_q d x N]: the rows of the rank's Q heads */
+  TP_O_ROW = 4,      /* W [n_q d x N]: the rows of the rank's Q heads */
+  TP_DGRAD = 5       /* the transpose of a planned shard, for its input gradient (tp_shard_plan_dgrad) */
 } tp_kind;
 
 /* Which kernel family runs a linear. AUTO picks DECODE for M <= 64. */
@@ -279,6 +280,57 @@ TP_API tp_status tp_reduce_scatter_partials(const float* P, int64_t stride_elems
  */
 TP_API tp_status tp_gather_rows(const uint16_t* Xs, int64_t stride_elems, int32_t t, int64_t Mt,
                          int64_t N, int64_t ldb, uint16_t* X, int64_t ldx, hipStream_t stream);
+
+/*
+ * Backward of a rank's linear ("Tensor vs Pipeline Parallelism", "Tensor
+ * parallelism: split inside each layer": training adds two all-reduces per
+ * layer in the backward pass, one per block; "AI Infrastructure series,
+ * Part 5", "Why are 8 GPUs not 8 times faster?": training costs 6 x
+ * parameters x tokens, the backward twice the forward).
+ *
+ * Input gradient: dA_r = dC_r W_r^T. tp_shard_plan_dgrad turns the plan of a
+ * rank's linear (any kind but TP_DGRAD) into a TP_DGRAD plan of W_r^T:
+ * shard_k = fwd->shard_n (the contraction, in the forward shard's column
+ * order, [gate | up] for TP_GATEUP_COL), shard_n = out_n = fwd->shard_k;
+ * it keeps fwd's rows and column ranges so that tp_shard_pack cuts the
+ * transposed shard out of the same full W. tp_row_linear with that plan and
+ * its packed copy then computes dA_r [M x fwd->shard_k] in fp32 from dC_r
+ * [M x fwd->shard_n] bf16 (for a column layer a partial, summed over the
+ * ranks with tp_reduce_partials: the backward all-reduce). bf16 storage only:
+ * tp_shard_set_wformat refuses 8-bit for TP_DGRAD (TP_ERR_KIND).
+ */
+TP_API tp_status tp_shard_plan_dgrad(const tp_shard_desc* fwd, tp_shard_desc* out);
+
+/*
+ * Weight gradient of a rank's linear (same passages):
+ *   dW[k][n] = sum_m A[m][k] dC[m][n], fp32 [fwd->shard_k x fwd->shard_n],
+ *   leading dim lddw, in the forward shard's row and column order;
+ *   A [M x fwd->shard_k] bf16 (leading dim lda): the rank's input (X for the
+ *   column kinds, its own Z_r for the row kinds); dC [M x fwd->shard_n] bf16
+ *   (leading dim lddc): the gradient of the rank's output ([dG | dU] for
+ *   TP_GATEUP_COL, the full output gradient for the row kinds).
+ * Accumulation is fp32 over the tokens in order of 32-token blocks; dW is
+ * overwritten (M == 0 writes zeros). lda, lddc multiples of 8, lddw of 4,
+ * pointers 16-byte aligned (TP_ERR_ALIGN).
+ */
+TP_API tp_status tp_weight_grad(const tp_shard_desc* fwd, const uint16_t* A, int64_t lda,
+                         const uint16_t* dC, int64_t lddc, int64_t M, float* dW, int64_t lddw,
+                         hipStream_t stream);
+
+/*
+ * Gradient through the fused SwiGLU, H = SiLU(G) * U, SiLU(g) = g s,
+ * s = 1 / (1 + e^-g) (same passages; the nonlinearity as tp_col_linear's):
+ *   dG = dH * U * s * (1 + G (1 - s)),  dU = dH * G * s,
+ * evaluated in fp32 and rounded once to bf16 into dGU = [dG | dU]
+ * [M x 2w] (leading dim lddgu). GU [M x 2w] bf16 (leading dim ldgu) holds the
+ * pre-activations [G | U] (e.g. from two TP_COL plans over the gate and the
+ * up half of [Wg | Wu], written side by side with ldy); dH [M x w] fp32
+ * (leading dim lddh) is the gradient of H (tp_row_linear with the down
+ * projection's TP_DGRAD plan). w, ldgu, lddgu multiples of 8; lddh of 4.
+ */
+TP_API tp_status tp_swiglu_backward(const uint16_t* GU, int64_t ldgu, const float* dH, int64_t lddh,
+                             int64_t M, int64_t w, uint16_t* dGU, int64_t lddgu,
+                             hipStream_t stream);
 
 /* Bytes of device workspace tp_col_linear / tp_row_linear need for this
  * shard at this M: fp32 partial sums when K is split over workgroups (decode

@@ -19,14 +19,15 @@ import torch
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    KIND_NAMES, TP_COL, TP_GATEUP_COL, TP_O_ROW, TP_PATH_AUTO, TP_PATH_DECODE, TP_PATH_PREFILL,
+    KIND_NAMES, TP_COL, TP_DGRAD, TP_GATEUP_COL, TP_O_ROW, TP_PATH_AUTO, TP_PATH_DECODE, TP_PATH_PREFILL,
     TP_W_BF16, TP_W_FP8_E4M3,
     TP_QKV_COL, TP_ROW, TpHeads, TpShardDesc,
 )
 
 __all__ = ["tp_shard_plan", "tp_shard_set_wformat", "tp_shard_pack", "tp_col_linear", "tp_row_linear", "tp_ffn_shard",
-           "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows", "tp_workspace_bytes",
-           "tp_status_str", "TpError", "TpShardDesc"]
+           "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows", "tp_shard_plan_dgrad",
+           "tp_weight_grad", "tp_swiglu_backward", "tp_workspace_bytes", "tp_status_str", "TpError",
+           "TpShardDesc"]
 
 
 class TpError(RuntimeError):
@@ -55,7 +56,7 @@ def _mat(x: torch.Tensor, dtype, name: str):
         raise TypeError(f"{name} must be a CUDA/HIP tensor")
     if x.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {x.dtype}")
-    if x.dim() != 2 or (x.size(1) > 1 and x.stride(1) != 1):
+    if x.dim() != 2 or (x.numel() > 0 and x.size(1) > 1 and x.stride(1) != 1):
         raise ValueError(f"{name} must be 2-D with unit column stride")
     return ctypes.c_void_p(x.data_ptr()), max(x.stride(0), x.size(1))
 
@@ -146,13 +147,14 @@ def tp_col_linear(desc: TpShardDesc, X: torch.Tensor, W_packed: torch.Tensor,
 def tp_row_linear(desc: TpShardDesc, Z: torch.Tensor, W_packed: torch.Tensor,
                   P: torch.Tensor | None = None, ws: torch.Tensor | None = None,
                   stream=None) -> torch.Tensor:
-    """Row-parallel linear: the fp32 partial P [M x N] of this rank."""
+    """Row-parallel linear: the fp32 partial P [M x out_n] of this rank (out_n
+    = N for the row kinds, the forward shard's input width for TP_DGRAD)."""
     zp, ldz = _mat(Z, torch.bfloat16, "Z")
     M = Z.size(0)
     if Z.size(1) != desc.shard_k:
         raise ValueError(f"Z has {Z.size(1)} columns, shard expects {desc.shard_k}")
     if P is None:
-        P = torch.empty((M, desc.N), dtype=torch.float32, device=Z.device)
+        P = torch.empty((M, desc.out_n), dtype=torch.float32, device=Z.device)
     pp, ldp = _mat(P, torch.float32, "P")
     wsp, wsb, _keep = _ws((desc,), M, ws, Z.device, stream)
     _check(_lib.load().tp_row_linear(ctypes.byref(desc), zp, M, ldz,
@@ -227,3 +229,52 @@ def tp_gather_rows(Xs: torch.Tensor, X: torch.Tensor | None = None, stream=None)
                                       max(Xs.stride(1), N), xp, ldx, _stream(stream)),
            "tp_gather_rows")
     return X
+
+
+def tp_shard_plan_dgrad(fwd: TpShardDesc) -> TpShardDesc:
+    """The TP_DGRAD plan of ``fwd``'s transposed shard: packed with
+    tp_shard_pack from the same full W, it turns tp_row_linear into the input
+    gradient dA_r [M x fwd.shard_k] = dC_r W_r^T (fp32)."""
+    d = TpShardDesc()
+    _check(_lib.load().tp_shard_plan_dgrad(ctypes.byref(fwd), ctypes.byref(d)), "tp_shard_plan_dgrad")
+    return d
+
+
+def tp_weight_grad(fwd: TpShardDesc, A: torch.Tensor, dC: torch.Tensor, dW: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """dW [fwd.shard_k x fwd.shard_n] fp32 = A^T dC, A [M x fwd.shard_k] and
+    dC [M x fwd.shard_n] bf16."""
+    ap, lda = _mat(A, torch.bfloat16, "A")
+    cp, ldc = _mat(dC, torch.bfloat16, "dC")
+    if A.size(0) != dC.size(0):
+        raise ValueError(f"A has {A.size(0)} rows, dC {dC.size(0)}")
+    if A.size(1) != fwd.shard_k or dC.size(1) != fwd.shard_n:
+        raise ValueError(f"A, dC are {tuple(A.shape)}, {tuple(dC.shape)}; the shard is "
+                         f"{fwd.shard_k} x {fwd.shard_n}")
+    if dW is None:
+        dW = torch.empty((fwd.shard_k, fwd.shard_n), dtype=torch.float32, device=A.device)
+    wp, ldw = _mat(dW, torch.float32, "dW")
+    if tuple(dW.shape) != (fwd.shard_k, fwd.shard_n):
+        raise ValueError(f"dW is {tuple(dW.shape)}, expected {(fwd.shard_k, fwd.shard_n)}")
+    _check(_lib.load().tp_weight_grad(ctypes.byref(fwd), ap, lda, cp, ldc, A.size(0), wp, ldw,
+                                      _stream(stream)), "tp_weight_grad")
+    return dW
+
+
+def tp_swiglu_backward(GU: torch.Tensor, dH: torch.Tensor, dGU: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """[dG | dU] bf16 [M x 2w] from the pre-activations GU = [G | U] bf16
+    [M x 2w] and dH fp32 [M x w]."""
+    gp, ldg = _mat(GU, torch.bfloat16, "GU")
+    hp, ldh = _mat(dH, torch.float32, "dH")
+    M, w = dH.shape
+    if tuple(GU.shape) != (M, 2 * w):
+        raise ValueError(f"GU is {tuple(GU.shape)}, dH {tuple(dH.shape)}")
+    if dGU is None:
+        dGU = torch.empty((M, 2 * w), dtype=torch.bfloat16, device=GU.device)
+    op, ldo = _mat(dGU, torch.bfloat16, "dGU")
+    if tuple(dGU.shape) != (M, 2 * w):
+        raise ValueError(f"dGU is {tuple(dGU.shape)}, expected {(M, 2 * w)}")
+    _check(_lib.load().tp_swiglu_backward(gp, ldg, hp, ldh, M, w, op, ldo, _stream(stream)),
+           "tp_swiglu_backward")
+    return dGU

@@ -24,15 +24,15 @@ TP_ERR_HIP = -7
 TP_ERR_KIND = -8
 TP_W_BF16, TP_W_FP8_E4M3 = 0, 1
 
-TP_COL, TP_ROW, TP_GATEUP_COL, TP_QKV_COL, TP_O_ROW = range(5)
+TP_COL, TP_ROW, TP_GATEUP_COL, TP_QKV_COL, TP_O_ROW, TP_DGRAD = range(6)
 TP_PATH_AUTO, TP_PATH_DECODE, TP_PATH_PREFILL = range(3)
 
 KIND_NAMES = {"col": TP_COL, "row": TP_ROW, "gateup_col": TP_GATEUP_COL,
               "qkv_col": TP_QKV_COL, "o_row": TP_O_ROW}
 
 EXPORTS = ("tp_shard_plan", "tp_shard_set_wformat", "tp_shard_pack", "tp_col_linear", "tp_row_linear", "tp_ffn_shard",
-           "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows", "tp_workspace_bytes",
-           "tp_status_str")
+           "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows", "tp_shard_plan_dgrad",
+           "tp_weight_grad", "tp_swiglu_backward", "tp_workspace_bytes", "tp_status_str")
 
 
 class TpHeads(ctypes.Structure):
@@ -96,12 +96,16 @@ def load() -> ctypes.CDLL:
     lib.tp_reduce_partials.argtypes = [P, I64, I32, I64, I64, I64, P, I64, P]
     lib.tp_reduce_scatter_partials.argtypes = [P, I64, I32, I64, I64, I64, I32, P, I64, P]
     lib.tp_gather_rows.argtypes = [P, I64, I32, I64, I64, I64, P, I64, P]
+    lib.tp_shard_plan_dgrad.argtypes = [D, D]
+    lib.tp_weight_grad.argtypes = [D, P, I64, P, I64, I64, P, I64, P]
+    lib.tp_swiglu_backward.argtypes = [P, I64, P, I64, I64, I64, P, I64, P]
     lib.tp_workspace_bytes.argtypes = [D, I64]
     lib.tp_workspace_bytes.restype = SZ
     lib.tp_status_str.argtypes = [I32]
     lib.tp_status_str.restype = ctypes.c_char_p
     for name in ("tp_shard_plan", "tp_shard_set_wformat", "tp_shard_pack", "tp_col_linear", "tp_row_linear",
-                 "tp_ffn_shard", "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows"):
+                 "tp_ffn_shard", "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows",
+                 "tp_shard_plan_dgrad", "tp_weight_grad", "tp_swiglu_backward"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib

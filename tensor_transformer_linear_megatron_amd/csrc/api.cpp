@@ -9,7 +9,7 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool is_col(int32_t k) { return k == TP_COL || k == TP_QKV_COL || k == TP_GATEUP_COL; }
-bool is_row(int32_t k) { return k == TP_ROW || k == TP_O_ROW; }
+bool is_row(int32_t k) { return k == TP_ROW || k == TP_O_ROW || k == TP_DGRAD; }
 
 // Self-consistency of a caller-held descriptor (it is plain data the caller
 // may have edited).
@@ -19,6 +19,7 @@ tp_status check_desc(const tp_shard_desc* d) {
   const bool gateup = d->kind == TP_GATEUP_COL;
   if (d->wformat != TP_W_BF16 && d->wformat != TP_W_FP8_E4M3) return TP_ERR_KIND;
   const bool fp8 = d->wformat == TP_W_FP8_E4M3;
+  if (fp8 && d->kind == TP_DGRAD) return TP_ERR_KIND;
   if (d->shard_k <= 0 || d->shard_n <= 0 || d->out_n <= 0 || d->packed_k < d->shard_k ||
       d->packed_k % (fp8 ? tpk::kTileK8 : tpk::kTileK) || d->packed_n % (2 * tpk::kTileN) ||
       d->packed_bytes != (fp8 ? d->packed_k * d->packed_n + 4 * d->packed_n
@@ -153,7 +154,11 @@ extern "C" tp_status tp_shard_pack(const tp_shard_desc* d, const uint16_t* W, in
   if (W == nullptr || W_packed == nullptr) return TP_ERR_NULL;
   if (ldw < d->N) return TP_ERR_SHAPE;
   if (!aligned16(W_packed)) return TP_ERR_ALIGN;
-  if (d->row_begin < 0 || d->row_end > d->K || d->row_end - d->row_begin != d->shard_k ||
+  // A TP_DGRAD plan keeps the forward shard's rows and column ranges: its
+  // output columns are the forward rows, its contraction the forward columns.
+  const bool dgrad = d->kind == TP_DGRAD;
+  const int64_t nrows = dgrad ? d->shard_n : d->shard_k, ncols = dgrad ? d->shard_k : d->shard_n;
+  if (d->row_begin < 0 || d->row_end > d->K || d->row_end - d->row_begin != nrows ||
       d->n_col_ranges < 1 || d->n_col_ranges > 3)
     return TP_ERR_SHAPE;
   tpk::PackArgs a;
@@ -174,13 +179,14 @@ extern "C" tp_status tp_shard_pack(const tp_shard_desc* d, const uint16_t* W, in
   for (int r = 0; r < 3; ++r) {
     const tp_col_range c = r < d->n_col_ranges ? d->col_ranges[r] : tp_col_range{0, 0, 0};
     if (r < d->n_col_ranges && (c.src_col < 0 || c.len < 0 || c.src_col + c.len > d->N ||
-                                c.dst_col < 0 || c.dst_col + c.len > d->shard_n))
+                                c.dst_col < 0 || c.dst_col + c.len > ncols))
       return TP_ERR_SHAPE;
     a.src[r] = c.src_col;
     a.len[r] = c.len;
     a.dst[r] = c.dst_col;
   }
-  const hipError_t e = is_fp8(d) ? tpk::launch_pack8(a, stream) : tpk::launch_pack(a, stream);
+  const hipError_t e = dgrad ? tpk::launch_pack_dgrad(a, stream)
+                             : (is_fp8(d) ? tpk::launch_pack8(a, stream) : tpk::launch_pack(a, stream));
   return e == hipSuccess ? TP_OK : TP_ERR_HIP;
 }
 
@@ -275,6 +281,36 @@ extern "C" tp_status tp_gather_rows(const uint16_t* Xs, int64_t stride_elems, in
   if (!aligned16(Xs) || !aligned16(X) || N % 8 || ldb % 8 || ldx % 8 || stride_elems % 8)
     return TP_ERR_ALIGN;
   return tpk::launch_gather(Xs, stride_elems, t, Mt, N, ldb, X, ldx, stream) == hipSuccess
+             ? TP_OK
+             : TP_ERR_HIP;
+}
+
+extern "C" tp_status tp_weight_grad(const tp_shard_desc* fwd, const uint16_t* A, int64_t lda,
+                                    const uint16_t* dC, int64_t lddc, int64_t M, float* dW,
+                                    int64_t lddw, hipStream_t stream) {
+  tp_status st = check_desc(fwd);
+  if (st != TP_OK) return st;
+  if (fwd->kind == TP_DGRAD) return TP_ERR_KIND;
+  const int64_t K = fwd->shard_k, N = fwd->shard_n;
+  if (M < 0 || lda < K || lddc < N || lddw < N) return TP_ERR_SHAPE;
+  if (dW == nullptr || (M > 0 && (A == nullptr || dC == nullptr))) return TP_ERR_NULL;
+  if (!aligned16(dW) || (M > 0 && (!aligned16(A) || !aligned16(dC))) || lda % 8 || lddc % 8 ||
+      lddw % 4)
+    return TP_ERR_ALIGN;
+  return tpk::launch_wgrad(A, lda, dC, lddc, M, K, N, dW, lddw, stream) == hipSuccess ? TP_OK
+                                                                                      : TP_ERR_HIP;
+}
+
+extern "C" tp_status tp_swiglu_backward(const uint16_t* GU, int64_t ldgu, const float* dH,
+                                        int64_t lddh, int64_t M, int64_t w, uint16_t* dGU,
+                                        int64_t lddgu, hipStream_t stream) {
+  if (M < 0 || w <= 0 || ldgu < 2 * w || lddh < w || lddgu < 2 * w) return TP_ERR_SHAPE;
+  if (M == 0) return TP_OK;
+  if (GU == nullptr || dH == nullptr || dGU == nullptr) return TP_ERR_NULL;
+  if (!aligned16(GU) || !aligned16(dH) || !aligned16(dGU) || w % 8 || ldgu % 8 || lddgu % 8 ||
+      lddh % 4)
+    return TP_ERR_ALIGN;
+  return tpk::launch_swiglu_bwd(GU, ldgu, dH, lddh, M, w, dGU, lddgu, stream) == hipSuccess
              ? TP_OK
              : TP_ERR_HIP;
 }

@@ -165,7 +165,41 @@ __global__ __launch_bounds__(256) void dequant8_kernel(const uint4* W8, const fl
                       fp8x2_to_bf16x2<false>(d1, sc), fp8x2_to_bf16x2<true>(d1, sc));
 }
 
+// TP_DGRAD: the transposed shard T = W_r^T in the bf16 layout. Output column
+// n = 16 nt + i is forward row row_begin + n; contraction index k is forward
+// shard column k, the column of W the forward's ranges map it to.
+__global__ __launch_bounds__(256) void pack_dgrad_kernel(PackArgs a, int64_t total_u4) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= total_u4) return;
+  const int lane = (int)(c & 63);
+  const int64_t idx = c >> 6;
+  const int64_t pair = idx / (2 * a.ksteps), rem = idx - pair * 2 * a.ksteps;
+  const int64_t ks = rem >> 1, nt = 2 * pair + (rem & 1);
+  const int g = lane >> 4, i = lane & 15;
+  const int64_t n = nt * kTileN + i;
+  uint16_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t k = ks * kTileK + g * 8 + e;
+    int64_t wcol = -1;
+    if (n < a.shard_n && k < a.shard_k) {
+      for (int r = 0; r < a.n_ranges; ++r)
+        if (k >= a.dst[r] && k < a.dst[r] + a.len[r]) wcol = a.src[r] + (k - a.dst[r]);
+    }
+    v[e] = wcol >= 0 ? a.W[(a.row_begin + n) * a.ldw + wcol] : (uint16_t)0;
+  }
+  a.out[c] = make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
+                        v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
+}
+
 }  // namespace
+
+hipError_t launch_pack_dgrad(const PackArgs& a, hipStream_t s) {
+  const int64_t total = a.ksteps * a.ntiles * kTileU4;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_dgrad_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, total);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack8(const PackArgs& a, hipStream_t s) {
   const int64_t cols = a.ntiles * kTileN;

@@ -139,9 +139,30 @@ extern "C" tp_status tp_shard_plan(tp_kind kind, int64_t K, int64_t N, int32_t t
   return TP_OK;
 }
 
+extern "C" tp_status tp_shard_plan_dgrad(const tp_shard_desc* fwd, tp_shard_desc* out) {
+  if (fwd == nullptr || out == nullptr) return TP_ERR_NULL;
+  if (fwd->kind < TP_COL || fwd->kind > TP_O_ROW) return TP_ERR_KIND;
+  if (fwd->shard_k <= 0 || fwd->shard_n <= 0 || fwd->n_col_ranges < 1 || fwd->n_col_ranges > 3)
+    return TP_ERR_SHAPE;
+  if (fwd->shard_k % 8 || fwd->shard_n % 8) return TP_ERR_ALIGN;
+  tp_shard_desc d = *fwd;  // keeps t, rank, K, N, rows, column ranges, heads
+  d.kind = TP_DGRAD;
+  d.shard_k = fwd->shard_n;  // contraction: the forward output columns
+  d.shard_n = d.out_n = fwd->shard_k;
+  d.path = TP_PATH_AUTO;
+  d.packed_k = round_up(d.shard_k, tpk::kTileK);
+  d.packed_n = round_up(d.shard_n, 2 * tpk::kTileN);
+  d.packed_bytes = d.packed_k * d.packed_n * 2;
+  d.wformat = TP_W_BF16;
+  d.reserved = 0;
+  *out = d;
+  return TP_OK;
+}
+
 extern "C" tp_status tp_shard_set_wformat(tp_shard_desc* d, int32_t wformat) {
   if (d == nullptr) return TP_ERR_NULL;
   if (d->shard_k <= 0 || d->packed_n <= 0) return TP_ERR_SHAPE;
+  if (d->kind == TP_DGRAD && wformat != TP_W_BF16) return TP_ERR_KIND;
   switch (wformat) {
     case TP_W_BF16:
       d->packed_k = round_up(d->shard_k, tpk::kTileK);

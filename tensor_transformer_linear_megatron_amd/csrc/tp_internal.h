@@ -75,6 +75,16 @@ hipError_t launch_pack8(const PackArgs& a, hipStream_t s);
 // = 2 ksteps8 k-steps of 32), for the prefill GEMM.
 hipError_t launch_dequant8(const uint4* W8, const float* scales, int64_t ksteps8, int64_t ntiles,
                            uint4* W16, hipStream_t s);
+// TP_DGRAD: the transposed shard of a forward plan, in the bf16 layout
+// (a.shard_k = forward shard_n is the contraction, a.shard_n = forward
+// shard_k the output columns; rows and column ranges are the forward's).
+hipError_t launch_pack_dgrad(const PackArgs& a, hipStream_t s);
+// dW [K x N] fp32 = A^T dC over M tokens (A [M x K], dC [M x N] bf16).
+hipError_t launch_wgrad(const uint16_t* A, int64_t lda, const uint16_t* dC, int64_t lddc, int64_t M,
+                        int64_t K, int64_t N, float* dW, int64_t lddw, hipStream_t s);
+// [dG | dU] bf16 from [G | U] bf16 and dH fp32.
+hipError_t launch_swiglu_bwd(const uint16_t* GU, int64_t ldgu, const float* dH, int64_t lddh,
+                             int64_t M, int64_t w, uint16_t* dGU, int64_t lddgu, hipStream_t s);
 // Decode path for 8-bit shards, 1 <= M <= 64. `ws` as for launch_gemv, with
 // gemv_workspace_bytes(M, 2 ksteps, ntiles) (the plan counts bf16 k-steps).
 hipError_t launch_gemv8(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s);

@@ -289,3 +289,71 @@ def test_workspace_bytes():
             == _lib.TP_ERR_WORKSPACE
         assert lib.tp_row_linear(ctypes.byref(d), A, 64, 14336, B, C, 4096, A, 16, ctypes.c_void_p(0)) \
             == _lib.TP_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,heads", [("col", 4096, 1024, 4, 1, None), ("row", 1024, 4096, 4, 3, None),
+                                                 ("gateup_col", 8192, 2 * 28672, 8, 5, None),
+                                                 ("qkv_col", 512, (8 + 2 * 2) * 64, 2, 1, (8, 2, 64)),
+                                                 ("o_row", 8 * 64, 512, 2, 0, (8, 2, 64))])
+def test_plan_dgrad_is_the_transposed_shard(kind, K, N, t, r, heads):
+    """The TP_DGRAD plan swaps the shard's two sizes, keeps the rows, the column
+    ranges and the rank, and plans bf16 tiles over the swapped sizes."""
+    f = tp.tp_shard_plan(kind, K, N, t, r, heads=heads)
+    d = tp.tp_shard_plan_dgrad(f)
+    assert d.kind == tp.TP_DGRAD and d.wformat == tp.TP_W_BF16
+    assert (d.shard_k, d.shard_n, d.out_n) == (f.shard_n, f.shard_k, f.shard_k)
+    assert (d.K, d.N, d.t, d.rank, d.row_begin, d.row_end) == (f.K, f.N, f.t, f.rank, f.row_begin, f.row_end)
+    assert d.n_col_ranges == f.n_col_ranges
+    for a, b in zip(d.col_ranges[:d.n_col_ranges], f.col_ranges[:f.n_col_ranges]):
+        assert (a.src_col, a.len, a.dst_col) == (b.src_col, b.len, b.dst_col)
+    assert d.packed_k == -(-f.shard_n // 32) * 32 and d.packed_n == -(-f.shard_k // 32) * 32
+    assert d.packed_bytes == 2 * d.packed_k * d.packed_n
+    p = oracle.plan(kind, K, N, t, r, heads=heads)
+    assert (d.shard_k, d.shard_n) == (len(p["cols"]), len(p["rows"]))
+
+
+def test_backward_argument_errors():
+    """Every refusal happens on the host, before any launch."""
+    lib = _lib.load()
+    S = ctypes.c_void_p(0)
+    f = tp.tp_shard_plan("col", 64, 128, 2, 1)  # shard 64 x 64
+    d = tp.tp_shard_plan_dgrad(f)
+    fb, db = ctypes.byref(f), ctypes.byref(d)
+    out = tp.TpShardDesc()
+    assert lib.tp_shard_plan_dgrad(None, ctypes.byref(out)) == _lib.TP_ERR_NULL
+    assert lib.tp_shard_plan_dgrad(fb, None) == _lib.TP_ERR_NULL
+    assert lib.tp_shard_plan_dgrad(db, ctypes.byref(out)) == _lib.TP_ERR_KIND  # no transpose of a transpose
+    assert lib.tp_shard_set_wformat(ctypes.byref(d.copy()), tp.TP_W_FP8_E4M3) == _lib.TP_ERR_KIND
+    edited = d.copy()
+    edited.wformat = tp.TP_W_FP8_E4M3
+    edited.packed_k, edited.packed_bytes = 64, 64 * edited.packed_n + 4 * edited.packed_n
+    assert lib.tp_row_linear(ctypes.byref(edited), A, 4, 64, B, C, 64, NUL, 0, S) == _lib.TP_ERR_KIND
+    # the transposed plan runs on the row entry point only
+    assert lib.tp_col_linear(db, A, 4, 64, B, C, 64, NUL, 0, S) == _lib.TP_ERR_KIND
+    assert lib.tp_row_linear(db, A, 4, 64, B, C, 60, NUL, 0, S) == _lib.TP_ERR_SHAPE  # ldp < out_n
+    # pack: W is the forward's full [K x N]
+    assert lib.tp_shard_pack(db, A, 120, B, S) == _lib.TP_ERR_SHAPE
+    wg = lib.tp_weight_grad
+    assert wg(None, A, 64, B, 64, 4, C, 64, S) == _lib.TP_ERR_NULL
+    assert wg(db, A, 64, B, 64, 4, C, 64, S) == _lib.TP_ERR_KIND
+    assert wg(fb, NUL, 64, B, 64, 4, C, 64, S) == _lib.TP_ERR_NULL
+    assert wg(fb, A, 64, B, 64, 4, NUL, 64, S) == _lib.TP_ERR_NULL
+    assert wg(fb, A, 56, B, 64, 4, C, 64, S) == _lib.TP_ERR_SHAPE  # lda < shard_k
+    assert wg(fb, A, 64, B, 56, 4, C, 64, S) == _lib.TP_ERR_SHAPE  # lddc < shard_n
+    assert wg(fb, A, 64, B, 64, 4, C, 60, S) == _lib.TP_ERR_SHAPE  # lddw < shard_n
+    assert wg(fb, A, 64, B, 64, -1, C, 64, S) == _lib.TP_ERR_SHAPE
+    assert wg(fb, A, 68, B, 64, 4, C, 64, S) == _lib.TP_ERR_ALIGN  # lda % 8
+    assert wg(fb, A, 64, B, 64, 4, C, 66, S) == _lib.TP_ERR_ALIGN  # lddw % 4
+    assert wg(fb, MIS, 64, B, 64, 4, C, 64, S) == _lib.TP_ERR_ALIGN
+    sb = lib.tp_swiglu_backward
+    assert sb(A, 120, B, 64, 4, 64, C, 128, S) == _lib.TP_ERR_SHAPE  # ldgu < 2w
+    assert sb(A, 128, B, 60, 4, 64, C, 128, S) == _lib.TP_ERR_SHAPE  # lddh < w
+    assert sb(A, 128, B, 64, 4, 64, C, 120, S) == _lib.TP_ERR_SHAPE  # lddgu < 2w
+    assert sb(A, 128, B, 64, -1, 64, C, 128, S) == _lib.TP_ERR_SHAPE
+    assert sb(A, 128, B, 64, 4, 0, C, 128, S) == _lib.TP_ERR_SHAPE
+    assert sb(NUL, 128, B, 64, 4, 64, C, 128, S) == _lib.TP_ERR_NULL
+    assert sb(A, 128, B, 64, 4, 64, NUL, 128, S) == _lib.TP_ERR_NULL
+    assert sb(A, 120, B, 60, 4, 60, C, 120, S) == _lib.TP_ERR_ALIGN  # w % 8
+    assert sb(MIS, 128, B, 64, 4, 64, C, 128, S) == _lib.TP_ERR_ALIGN
+    assert sb(A, 128, B, 66, 4, 64, C, 128, S) == _lib.TP_ERR_ALIGN  # lddh % 4
+    assert sb(NUL, 128, NUL, 64, 0, 64, NUL, 128, S) == _lib.TP_OK  # M == 0

@@ -1,0 +1,309 @@
+"""GPU parity of the backward of a rank's share: the transposed-shard packing
+(bit-exact), the input gradient through tp_row_linear with a TP_DGRAD plan,
+the weight gradient, the SwiGLU gradient, and the whole feed-forward rank
+backward composed from them -- each against the fp64 oracle on the same
+seeded inputs.
+
+Bar: bit-exact for packing and integer-valued inputs; relative Frobenius
+error <= 1e-3 and max element error <= 1e-2 * max |oracle| otherwise; the
+SwiGLU gradient, rounded once to bf16 on both sides, within one bf16 unit in
+the last place of the oracle's rounding.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+import tensor_transformer_linear_megatron_amd as tp
+from seeded_inputs import workloads as wl
+from tputil import assert_parity, dev, full_device, host_bits, host_f64, say, unpack
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def f32_dev(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+# Forward shards with ragged tails: shard sizes multiples of 8, not of 32.
+SHARDS = [("col", 520, 2 * 392, 2, 1, None), ("gateup_col", 264, 2 * 2 * 200, 2, 0, None),
+          ("row", 2 * 336, 264, 2, 1, None), ("qkv_col", 256, (8 + 2 * 2) * 40, 2, 1, (8, 2, 40)),
+          ("o_row", 8 * 40, 200, 4, 2, (8, 2, 40)), ("gateup_col", 1000, 2 * 4 * 1096, 4, 3, None)]
+
+
+def _pack_dgrad(kind, K, N, t, r, heads, seed, sigma=0.05, W=None):
+    f = tp.tp_shard_plan(kind, K, N, t, r, heads=heads)
+    p = oracle.plan(kind, K, N, t, r, heads=heads)
+    d = tp.tp_shard_plan_dgrad(f)
+    if W is None:
+        W = si.normal_bf16(seed, (K, N), sigma)
+    return f, d, p, W, tp.tp_shard_pack(d, dev(W))
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,heads", SHARDS)
+def test_dgrad_pack_is_the_transposed_shard(kind, K, N, t, r, heads):
+    say("dgrad pack", kind, K, N, t, r, heads)
+    f, d, p, W, packed = _pack_dgrad(kind, K, N, t, r, heads, 300)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(unpack(d, packed), W[np.ix_(p["rows"], p["cols"])].T)
+    # the padding is zero
+    full = packed.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.count_nonzero(full) <= np.count_nonzero(W[np.ix_(p["rows"], p["cols"])])
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,heads", SHARDS)
+@pytest.mark.parametrize("M", [1, 17, 64, 65, 300])
+def test_input_grad_matches_oracle(kind, K, N, t, r, heads, M):
+    say("dgrad", kind, K, N, t, r, heads, M)
+    f, d, p, W, packed = _pack_dgrad(kind, K, N, t, r, heads, 301)
+    dC = si.normal_bf16(302 + M, (M, f.shard_n), 1.0)
+    dA = tp.tp_row_linear(d, dev(dC), packed)
+    assert tuple(dA.shape) == (M, f.shard_k)
+    assert_parity(host_f64(dA), oracle.grad_input(dC, W, p), f"dA {kind} M={M}")
+
+
+@pytest.mark.parametrize("path", [tp.TP_PATH_DECODE, tp.TP_PATH_PREFILL])
+@pytest.mark.parametrize("M", [5, 64])
+def test_input_grad_exact_integers_bit_exact(path, M):
+    """W, dC in {-3..3}: every fp32 partial sum is an integer below 2^24, so
+    both kernel families must reproduce the oracle's value exactly."""
+    say("dgrad exact", path, M)
+    K, N = 1000, 2 * 4 * 1096
+    W = si.int_bf16(310, (K, N), -3, 3)
+    f, d, p, _, packed = _pack_dgrad("gateup_col", K, N, 4, 3, None, 0, W=W)
+    d.path = path
+    dC = si.int_bf16(311, (M, f.shard_n), -3, 3)
+    got = host_f64(tp.tp_row_linear(d, dev(dC), packed))
+    np.testing.assert_array_equal(got, oracle.grad_input(dC, W, p))
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,heads", SHARDS)
+@pytest.mark.parametrize("M", [0, 1, 31, 33, 200, 1000])
+def test_weight_grad_matches_oracle(kind, K, N, t, r, heads, M):
+    say("wgrad", kind, K, N, t, r, heads, M)
+    f = tp.tp_shard_plan(kind, K, N, t, r, heads=heads)
+    p = oracle.plan(kind, K, N, t, r, heads=heads)
+    A = si.normal_bf16(320 + M, (M, f.shard_k), 1.0)
+    dC = si.normal_bf16(321 + M, (M, f.shard_n), 1.0)
+    dW = torch.full((f.shard_k, f.shard_n), float("nan"), dtype=torch.float32, device="cuda")
+    tp.tp_weight_grad(f, dev(A), dev(dC), dW=dW)
+    got = host_f64(dW)
+    if M == 0:
+        assert np.all(got == 0.0)
+        return
+    assert_parity(got, oracle.grad_weight(A, dC, p), f"dW {kind} M={M}")
+
+
+@pytest.mark.parametrize("M", [7, 100, 4097])
+def test_weight_grad_exact_integers_bit_exact(M):
+    say("wgrad exact", M)
+    f = tp.tp_shard_plan("row", 4 * 264, 520, 4, 1)
+    p = oracle.plan("row", 4 * 264, 520, 4, 1)
+    A = si.int_bf16(330, (M, f.shard_k), -3, 3)
+    dC = si.int_bf16(331, (M, f.shard_n), -3, 3)
+    got = host_f64(tp.tp_weight_grad(f, dev(A), dev(dC)))
+    np.testing.assert_array_equal(got, oracle.grad_weight(A, dC, p))
+
+
+def test_weight_grad_strided_operands():
+    """Leading dimensions wider than the shard: only the shard's columns are
+    read and only dW's shard block is written."""
+    say("wgrad strided")
+    f = tp.tp_shard_plan("col", 256, 2 * 136, 2, 0)
+    p = oracle.plan("col", 256, 2 * 136, 2, 0)
+    M = 77
+    Abig = si.normal_bf16(340, (M, 264), 1.0)
+    Cbig = si.normal_bf16(341, (M, 152), 1.0)
+    Wbig = torch.full((256, 140), -7.0, dtype=torch.float32, device="cuda")
+    tp.tp_weight_grad(f, dev(Abig)[:, :256], dev(Cbig)[:, :136], dW=Wbig[:, :136])
+    got = host_f64(Wbig)
+    assert np.all(got[:, 136:] == -7.0)
+    assert_parity(got[:, :136], oracle.grad_weight(Abig[:, :256], Cbig[:, :136], p), "dW strided")
+
+
+def _ulp_ok(got_bits: np.ndarray, ref_bits: np.ndarray):
+    """At most one bf16 unit in the last place apart (sign-magnitude order);
+    values below 1e-30 in magnitude on both sides (fp32 underflow of s) pass."""
+    def order(b):
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    gap = np.abs(order(got_bits) - order(ref_bits))
+    tiny = (np.abs(oracle.bf16_to_f64(got_bits)) < 1e-30) & (np.abs(oracle.bf16_to_f64(ref_bits)) < 1e-30)
+    bad = (gap > 1) & ~tiny
+    assert not bad.any(), f"{bad.sum()} elements more than 1 ulp apart, first at {np.argwhere(bad)[0]}"
+    return float(np.mean(gap > 0))
+
+
+@pytest.mark.parametrize("M,w", [(1, 8), (37, 200), (256, 3584)])
+def test_swiglu_backward_matches_oracle(M, w):
+    say("swiglu bwd", M, w)
+    G = si.normal_bf16(350 + w, (M, w), 3.0)
+    U = si.normal_bf16(351 + w, (M, w), 1.0)
+    dH = si.normal_f32(352 + w, (M, w), 1.0)
+    # special pre-activations in the first row: 0, saturating both ways, and
+    # the bf16 values around the zero of 1 + g (1 - s)
+    special = np.array([0.0, -0.0, 40.0, -40.0, 89.0, -89.0, 100.0, -100.0, -1.2734375, -1.28125],
+                       dtype=np.float32)
+    n = min(w, special.size)
+    G[0, :n] = si.f32_to_bf16_bits(special[:n])
+    GU = np.concatenate([G, U], axis=1)
+    dGU = tp.tp_swiglu_backward(dev(GU), f32_dev(dH))
+    got = host_bits(dGU)
+    ref = oracle.swiglu_backward(oracle.bf16_to_f64(G), oracle.bf16_to_f64(U), dH.astype(np.float64))
+    frac = _ulp_ok(got, ref)
+    # fp32 evaluation error moves a rounding across a bf16 boundary rarely; on
+    # a tiny case the planted special values dominate the count
+    assert frac < 0.01 or got.size < 1000, f"{frac:.4f} of the elements differ by one ulp"
+    assert_parity(oracle.bf16_to_f64(got), oracle.bf16_to_f64(ref), f"dGU M={M} w={w}")
+
+
+def test_swiglu_backward_strided():
+    say("swiglu bwd strided")
+    M, w = 19, 64
+    GU = si.normal_bf16(360, (M, 2 * w + 16), 2.0)
+    dH = si.normal_f32(361, (M, w + 4), 1.0)
+    out = torch.full((M, 2 * w + 8), 3.0, dtype=torch.bfloat16, device="cuda")
+    tp.tp_swiglu_backward(dev(GU)[:, :2 * w], f32_dev(dH)[:, :w], dGU=out[:, :2 * w])
+    got = host_bits(out)
+    assert np.all(oracle.bf16_to_f64(got[:, 2 * w:]) == 3.0)
+    ref = oracle.swiglu_backward(oracle.bf16_to_f64(GU[:, :w]), oracle.bf16_to_f64(GU[:, w:2 * w]),
+                                 dH[:, :w].astype(np.float64))
+    _ulp_ok(got[:, :2 * w], ref)
+
+
+@pytest.mark.parametrize("M", [24, 100])
+def test_ffn_rank_backward_composed(M):
+    """The feed-forward layer's backward at t = 2, each rank's share through
+    the library: pre-activations from two column plans over the gate and up
+    halves, dH through the down projection's transposed shard, the SwiGLU
+    gradient, dX_r through the gate/up transposed shard, summed over the ranks
+    (the backward all-reduce), and both weight gradients. The oracle takes the
+    same steps in fp64 with the same bf16 rounding points."""
+    say("ffn backward", M)
+    hidden, I, t = 200, 272, 2
+    w = I // t
+    X = si.normal_bf16(370, (M, hidden), 1.0)
+    Wgu = si.normal_bf16(371, (hidden, 2 * I), 0.08)
+    Wd = si.normal_bf16(372, (I, hidden), 0.08)
+    dY = si.normal_bf16(373, (M, hidden), 1.0)
+    Xd, Wgud, Wdd, dYd = dev(X), dev(Wgu), dev(Wd), dev(dY)
+    dX_parts = torch.empty((t, M, hidden), dtype=torch.float32, device="cuda")
+    dX_ref = np.zeros((M, hidden))
+    for r in range(t):
+        gu = tp.tp_shard_plan("gateup_col", hidden, 2 * I, t, r)
+        dn = tp.tp_shard_plan("row", I, hidden, t, r)
+        pgu = oracle.plan("gateup_col", hidden, 2 * I, t, r)
+        pdn = oracle.plan("row", I, hidden, t, r)
+        # forward: H (fused SwiGLU) and the pre-activations [G | U]
+        H = tp.tp_col_linear(gu, Xd, tp.tp_shard_pack(gu, Wgud))
+        half = tp.tp_shard_plan("col", hidden, I, t, r)
+        GU = torch.empty((M, 2 * w), dtype=torch.bfloat16, device="cuda")
+        tp.tp_col_linear(half, Xd, tp.tp_shard_pack(half, Wgud[:, :I]), Y=GU[:, :w])
+        tp.tp_col_linear(half, Xd, tp.tp_shard_pack(half, Wgud[:, I:]), Y=GU[:, w:])
+        # backward
+        dH = tp.tp_row_linear(tp.tp_shard_plan_dgrad(dn), dYd, tp.tp_shard_pack(tp.tp_shard_plan_dgrad(dn), Wdd))
+        dGU = tp.tp_swiglu_backward(GU, dH)
+        dgu = tp.tp_shard_plan_dgrad(gu)
+        tp.tp_row_linear(dgu, dGU, tp.tp_shard_pack(dgu, Wgud), P=dX_parts[r])
+        dWgu = tp.tp_weight_grad(gu, Xd, dGU)
+        dWd = tp.tp_weight_grad(dn, H, dYd)
+        # the oracle, step by step
+        Gr, Ur = oracle.gateup_preact(X, Wgu, pgu)
+        Gb, Ub = oracle.round_bf16(Gr), oracle.round_bf16(Ur)
+        Hb = oracle.gateup_swiglu(X, Wgu, pgu)
+        dH_ref = oracle.grad_input(dY, Wd, pdn)
+        dGU_ref = oracle.swiglu_backward(oracle.bf16_to_f64(Gb), oracle.bf16_to_f64(Ub), dH_ref)
+        dX_ref += oracle.grad_input(dGU_ref, Wgu, pgu)
+        assert_parity(host_f64(GU), oracle.bf16_to_f64(np.concatenate([Gb, Ub], axis=1)), f"GU_{r}")
+        assert_parity(host_f64(dH), dH_ref, f"dH_{r}")
+        assert_parity(host_f64(dGU), oracle.bf16_to_f64(dGU_ref), f"dGU_{r}")
+        assert_parity(host_f64(dWgu), oracle.grad_weight(X, dGU_ref, pgu), f"dWgu_{r}")
+        assert_parity(host_f64(dWd), oracle.grad_weight(Hb, dY, pdn), f"dWd_{r}")
+    dX = tp.tp_reduce_partials(dX_parts)
+    assert_parity(host_f64(dX), dX_ref, "dX summed over ranks")
+
+
+# ---------------------------------------------------------------------------
+# Full size: Llama-3.1-405B feed-forward, rank 0 of TP = 8, 8192 tokens, in
+# the launch configuration the benchmark times; sampled outputs.
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def b405():
+    c = wl.LLAMA405B
+    Hd, I, t, M, r = c["hidden"], c["inter"], 8, 8192, 0
+    w = I // t
+    cols = range(r * w, (r + 1) * w)
+    gu = tp.tp_shard_plan("gateup_col", Hd, 2 * I, t, r)
+    dn = tp.tp_shard_plan("row", I, Hd, t, r)
+    Wgu_r = wl.gateup(Hd, I, c["sigma"], cols=cols)
+    Wd_r = wl.down(I, Hd, c["sigma"], rows=cols)
+    dgu, ddn = tp.tp_shard_plan_dgrad(gu), tp.tp_shard_plan_dgrad(dn)
+    full = full_device((Hd, 2 * I), [(range(0, Hd), cols, Wgu_r[:, :w]),
+                                     (range(0, Hd), range(I + cols.start, I + cols.stop), Wgu_r[:, w:])])
+    gp = tp.tp_shard_pack(dgu, full)
+    del full
+    fulld = full_device((I, Hd), [(cols, range(0, Hd), Wd_r)])
+    dp = tp.tp_shard_pack(ddn, fulld)
+    del fulld
+    return dict(Hd=Hd, w=w, M=M, gu=gu, dn=dn, dgu=dgu, ddn=ddn, gp=gp, dp=dp, Wgu_r=Wgu_r, Wd_r=Wd_r)
+
+
+ROWS = [0, 1, 255, 256, 4095, 4096, 8190, 8191]
+
+
+def test_llama405b_input_grads(b405):
+    say("405b dgrad down and gate/up")
+    Hd, w, M = b405["Hd"], b405["w"], b405["M"]
+    dY = si.normal_bf16(380, (M, Hd), 1.0)
+    dH = tp.tp_row_linear(b405["ddn"], dev(dY), b405["dp"])
+    ref = oracle.grad_input(dY[ROWS], b405["Wd_r"], oracle.plan("row", w, Hd, 1, 0))
+    assert_parity(host_f64(dH)[ROWS], ref, "dH rows")
+    del dH
+    dGU = si.normal_bf16(381, (M, 2 * w), 1.0)
+    dX = tp.tp_row_linear(b405["dgu"], dev(dGU), b405["gp"])
+    ref = oracle.grad_input(dGU[ROWS], b405["Wgu_r"], oracle.plan("gateup_col", Hd, 2 * w, 1, 0))
+    assert_parity(host_f64(dX)[ROWS], ref, "dX_0 rows")
+
+
+def test_llama405b_weight_grads(b405):
+    say("405b wgrad gate/up and down")
+    Hd, w, M = b405["Hd"], b405["w"], b405["M"]
+    X = wl.activations(M, Hd)
+    dGU = si.normal_bf16(381, (M, 2 * w), 1.0)
+    dW = tp.tp_weight_grad(b405["gu"], dev(X), dev(dGU))
+    ks = [0, 1, 127, 128, 8191, 16383]
+    ns = [0, 15, 16, 3583, 3584, 6655, 6656, 13311]
+    one = {"kind": "gateup_col"}
+    assert_parity(host_f64(dW)[np.ix_(ks, ns)], oracle.grad_weight(X[:, ks], dGU[:, ns], one), "dWgu sample")
+    del dW
+    H = si.normal_bf16(382, (M, w), 0.5)
+    dY = si.normal_bf16(380, (M, Hd), 1.0)
+    dW = tp.tp_weight_grad(b405["dn"], dev(H), dev(dY))
+    ks = [0, 1, 127, 128, 3583, 6655]
+    ns = [0, 127, 128, 8191, 16383]
+    assert_parity(host_f64(dW)[np.ix_(ks, ns)], oracle.grad_weight(H[:, ks], dY[:, ns], one), "dWd sample")
+
+
+def test_llama405b_swiglu_backward_rows():
+    say("405b swiglu bwd")
+    M, w = 8192, 6656
+    G = si.normal_bf16(383, (M, w), 3.0)
+    U = si.normal_bf16(384, (M, w), 1.0)
+    dH = si.normal_f32(385, (M, w), 1.0)
+    dGU = tp.tp_swiglu_backward(dev(np.concatenate([G, U], axis=1)), f32_dev(dH))
+    got = host_bits(dGU)[ROWS]
+    ref = oracle.swiglu_backward(oracle.bf16_to_f64(G[ROWS]), oracle.bf16_to_f64(U[ROWS]),
+                                 dH[ROWS].astype(np.float64))
+    _ulp_ok(got, ref)
