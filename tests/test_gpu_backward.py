@@ -116,6 +116,36 @@ def test_weight_grad_exact_integers_bit_exact(M):
     np.testing.assert_array_equal(got, oracle.grad_weight(A, dC, p))
 
 
+@pytest.mark.parametrize("M", [0, 1, 64, 65, 200])
+def test_weight_grad_large_tiles(M):
+    """A shard with at least 256 tiles of 256 x 256 runs the large-tile kernel:
+    ragged last tiles in both dimensions (4104 = 16 x 256 + 8, 3848 = 15 x 256
+    + 8), token counts that end mid-stage and odd stage counts."""
+    say("wgrad large", M)
+    f = tp.tp_shard_plan("col", 4104, 2 * 3848, 2, 1)
+    p = oracle.plan("col", 4104, 2 * 3848, 2, 1)
+    A = si.normal_bf16(390 + M, (M, f.shard_k), 1.0)
+    dC = si.normal_bf16(391 + M, (M, f.shard_n), 1.0)
+    dW = torch.full((f.shard_k, f.shard_n), float("nan"), dtype=torch.float32, device="cuda")
+    tp.tp_weight_grad(f, dev(A), dev(dC), dW=dW)
+    got = host_f64(dW)
+    if M == 0:
+        assert np.all(got == 0.0)
+        return
+    assert_parity(got, oracle.grad_weight(A, dC, p), f"dW large M={M}")
+
+
+def test_weight_grad_large_tiles_exact_integers():
+    say("wgrad large exact")
+    M = 1000
+    f = tp.tp_shard_plan("row", 2 * 4104, 3848, 2, 1)
+    p = oracle.plan("row", 2 * 4104, 3848, 2, 1)
+    A = si.int_bf16(392, (M, f.shard_k), -3, 3)
+    dC = si.int_bf16(393, (M, f.shard_n), -3, 3)
+    got = host_f64(tp.tp_weight_grad(f, dev(A), dev(dC)))
+    np.testing.assert_array_equal(got, oracle.grad_weight(A, dC, p))
+
+
 def test_weight_grad_strided_operands():
     """Leading dimensions wider than the shard: only the shard's columns are
     read and only dW's shard block is written."""
