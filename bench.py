@@ -660,6 +660,11 @@ def config_405b_ffn_backward(timer):
                 peak=MFMA_BF16_PEAK_TFS, per_op=per)
 
 
+CONFIGS = {"worked_tp2": config_worked_tp2, "70b_ffn_decode": config_70b_ffn_decode,
+           "70b_attention_prefill": config_70b_attention_prefill, "sequence_parallel": config_sequence_parallel,
+           "405b_ffn_backward": config_405b_ffn_backward}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -670,6 +675,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (worked TP=2 split, 70B decode and attention prefill, "
                          "sequence-parallel partial sum, 405B feed-forward backward)")
+    ap.add_argument("--config", choices=sorted(CONFIGS),
+                    help="only run this one workload and print its line (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (the yardstick for HBM byte counters)")
     args = ap.parse_args()
@@ -685,13 +692,16 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.config:
+        timer = Timer(torch.cuda.current_stream().cuda_stream)
+        print(json.dumps(CONFIGS[args.config](timer)), flush=True)
+        return
     dec = run_decode(args)
     pre = None if args.no_prefill else run_prefill(args)
     others = None
     if not args.no_configs:
         timer = Timer(torch.cuda.current_stream().cuda_stream)
-        others = [config_worked_tp2(timer), config_70b_ffn_decode(timer), config_70b_attention_prefill(timer),
-                  config_sequence_parallel(timer), config_405b_ffn_backward(timer)]
+        others = [fn(timer) for fn in CONFIGS.values()]
     per = [dict(M=p["M"], gateup_us=round(p["gateup_us"], 2), down_us=round(p["down_us"], 2),
                 reduce_us=round(p["reduce_us"], 2), gateup_GBs=round(p["gateup_GBs"], 1),
                 down_GBs=round(p["down_GBs"], 1), ffn_GBs=round(p["ffn_GBs"], 1))
