@@ -309,8 +309,10 @@ TP_API tp_status tp_shard_plan_dgrad(const tp_shard_desc* fwd, tp_shard_desc* ou
  *   column kinds, its own Z_r for the row kinds); dC [M x fwd->shard_n] bf16
  *   (leading dim lddc): the gradient of the rank's output ([dG | dU] for
  *   TP_GATEUP_COL, the full output gradient for the row kinds).
- * Accumulation is fp32 over the tokens in order of 32-token blocks; dW is
- * overwritten (M == 0 writes zeros). lda, lddc multiples of 8, lddw of 4,
+ * Accumulation is fp32 over the tokens, one MFMA block of 16 or 32 tokens
+ * after another in token order (the block size depends on the shard's size
+ * only, so a given shape always sums in the same order); dW is overwritten
+ * (M == 0 writes zeros). lda, lddc multiples of 8, lddw of 4,
  * pointers 16-byte aligned (TP_ERR_ALIGN).
  */
 TP_API tp_status tp_weight_grad(const tp_shard_desc* fwd, const uint16_t* A, int64_t lda,
