@@ -47,6 +47,14 @@ Readings where the pages are silent (the same list is in the design notes):
   column kinds a partial, summed over the ranks like the forward partials),
   its weight gradient A_r^T dC_r; the gate/up gradient [dG | dU] is rounded
   to bf16 once, as the products that consume it read bf16.
+* Attention core on the rank's heads (the pages give no formula): scaled
+  dot-product attention softmax(q k^T / sqrt(d)) v per query head, causal (a
+  new token at cache position p sees positions 0..p of its sequence), no
+  position encoding, no bias; query head q uses key-value head
+  floor(q / (n_q / n_kv)), which for a rank is its own local copy. The rank
+  keeps K and V of its key-value heads for every token (its share of the KV
+  cache). Output rows are the rank's query heads side by side, rounded to
+  bf16 once (the O projection reads bf16).
 * Sequence parallelism (the pages name only what it splits): after the
   row-parallel product rank r keeps rows [r M/t, (r+1) M/t) of the summed
   partials (a reduce-scatter along the tokens), and the full activations for
@@ -170,7 +178,7 @@ def plan(kind: str, K: int, N: int, t: int, rank: int, heads=None) -> dict:
         if n_q <= 0 or n_kv <= 0 or d <= 0 or n_q % n_kv:
             raise PlanError("shape", f"heads {heads}")
         (q0, q1), (k0, k1), rep = _head_sets(t, rank, n_q, n_kv)
-        out.update(q_heads=(q0, q1), kv_heads=(k0, k1), kv_replicated=rep)
+        out.update(q_heads=(q0, q1), kv_heads=(k0, k1), kv_replicated=rep, heads=(n_q, n_kv, d))
         if kind == "qkv_col":
             if N != (n_q + 2 * n_kv) * d:
                 raise PlanError("shape", f"N={N} != (n_q + 2 n_kv) d")
@@ -484,3 +492,83 @@ def compare(got: np.ndarray, ref: np.ndarray) -> dict:
         max_ref=amax,
         max_rel=float(np.abs(diff).max() / amax) if amax > 0 else float(np.abs(diff).max() if diff.size else 0.0),
     )
+
+
+# --------------------------------------------------------------------------
+# Attention core on the rank's heads, with the rank's share of the KV cache
+# ("Tensor vs Pipeline Parallelism", "Tensor parallelism: split inside each
+# layer": attention heads are distributed among the GPUs, each computing its
+# slice, and each GPU keeps its heads' share of the KV cache; "AI
+# Infrastructure series, Part 5", "How does tensor parallelism split a
+# layer?": 1/N of the KV cache per GPU, and past the 8 key-value heads a
+# larger group repeats key-value heads, which wastes KV memory; "Step 1: does
+# it fit?": 320 KB of KV cache per token for Llama 3.1 70B in 16-bit).
+#
+# A batch is S sequences with q_len new tokens each: rows s q_len .. s q_len
+# + q_len - 1 of QKV [M x shard_n] (the rank's [Q_r | K_r | V_r]) belong to
+# sequence s, whose cache (slot slot[s]) holds kv_len[s] positions once the
+# new tokens are in; new token i sits at position kv_len[s] - q_len + i.
+# Cache arrays are [n_slots x n_kv_r x L_max x d] bf16 bits, K and V apart.
+# --------------------------------------------------------------------------
+
+def _attn_heads(p: dict):
+    """(n_q_r, n_kv_r, d, local kv head of each local query head)."""
+    assert p["kind"] == "qkv_col"
+    n_q, n_kv, d = p["heads"]
+    q0, q1 = p["q_heads"]
+    k0, k1 = p["kv_heads"]
+    group = n_q // n_kv
+    kv_of = [(q0 + h) // group - k0 for h in range(q1 - q0)]
+    return q1 - q0, k1 - k0, d, kv_of
+
+
+def kv_cache_new(p: dict, n_slots: int, L_max: int):
+    """Empty (zero) K and V cache arrays of a rank."""
+    _, nkv, d, _ = _attn_heads(p)
+    shape = (n_slots, nkv, L_max, d)
+    return np.zeros(shape, dtype=np.uint16), np.zeros(shape, dtype=np.uint16)
+
+
+def kv_append(QKV: np.ndarray, p: dict, q_len: int, kv_len, slot, Kc: np.ndarray, Vc: np.ndarray):
+    """Write the new tokens' K and V (bf16 bits, copied) into their slots."""
+    nq, nkv, d, _ = _attn_heads(p)
+    for s in range(len(kv_len)):
+        for i in range(q_len):
+            row, pos = s * q_len + i, kv_len[s] - q_len + i
+            for g in range(nkv):
+                Kc[slot[s], g, pos] = QKV[row, (nq + g) * d:(nq + g + 1) * d]
+                Vc[slot[s], g, pos] = QKV[row, (nq + nkv + g) * d:(nq + nkv + g + 1) * d]
+
+
+def attention_f64(QKV: np.ndarray, p: dict, q_len: int, kv_len, slot, Kc: np.ndarray, Vc: np.ndarray,
+                  rows=None) -> np.ndarray:
+    """The rank's attention output in fp64, [M x n_q_r d] (or only ``rows``),
+    from the queries in QKV and the keys and values in the cache."""
+    nq, _, d, kv_of = _attn_heads(p)
+    S = len(kv_len)
+    want = range(S * q_len) if rows is None else rows
+    out = np.zeros((len(want), nq * d))
+    for o, row in enumerate(want):
+        s, i = divmod(row, q_len)
+        pos = kv_len[s] - q_len + i
+        for h in range(nq):
+            q = bf16_to_f64(QKV[row, h * d:(h + 1) * d])
+            K = bf16_to_f64(Kc[slot[s], kv_of[h], :pos + 1])
+            V = bf16_to_f64(Vc[slot[s], kv_of[h], :pos + 1])
+            sc = K @ q / np.sqrt(d)
+            w = np.exp(sc - sc.max())
+            out[o, h * d:(h + 1) * d] = (w @ V) / w.sum()
+    return out
+
+
+def attention(QKV: np.ndarray, p: dict, q_len: int, kv_len, slot, Kc: np.ndarray, Vc: np.ndarray,
+              rows=None) -> np.ndarray:
+    """bf16 bits of the rank's attention output, rounded once from fp64."""
+    return round_bf16(attention_f64(QKV, p, q_len, kv_len, slot, Kc, Vc, rows))
+
+
+def kv_bytes_per_token(p: dict, layers: int) -> int:
+    """KV cache bytes a rank keeps per token over ``layers`` layers (bf16 K
+    and V of its key-value heads)."""
+    _, nkv, d, _ = _attn_heads(p)
+    return 2 * nkv * d * 2 * layers
