@@ -334,6 +334,75 @@ TP_API tp_status tp_swiglu_backward(const uint16_t* GU, int64_t ldgu, const floa
                              int64_t M, int64_t w, uint16_t* dGU, int64_t lddgu,
                              hipStream_t stream);
 
+/*
+ * Attention core on the rank's heads, with the rank's share of the KV cache
+ * ("Tensor vs Pipeline Parallelism", "Tensor parallelism: split inside each
+ * layer": attention heads are distributed among the GPUs, each computing its
+ * slice and keeping its heads' share of the KV cache; "AI Infrastructure
+ * series, Part 5", "How does tensor parallelism split a layer?": each GPU
+ * holds 1/N of the KV cache, and past the key-value head count a larger
+ * group repeats key-value heads; "How do you choose a layout for serving?":
+ * 320 KB of KV cache per token for Llama 3.1 70B in 16-bit). The pages give
+ * no formula; the one computed is, per query head of the rank,
+ *   softmax(q k^T / sqrt(d)) v
+ * over the positions 0..p of its sequence, p its own position (causal), with
+ * the key-value head of its group: query head q (global) reads key-value head
+ * floor(q / (n_q / n_kv)), which the rank holds (a repeated head when
+ * kv_replicated). No position encoding, no bias, no dropout.
+ *
+ * All of these take the TP_QKV_COL descriptor of the rank; its head
+ * dimension d = shard_n / (n_q_r + 2 n_kv_r) must be 64 or 128 (TP_ERR_SHAPE).
+ *
+ * A batch is S sequences with q_len new tokens each (M = S q_len rows):
+ * rows s q_len .. s q_len + q_len - 1 of QKV (the rank's [Q_r | K_r | V_r],
+ * bf16, leading dim ldqkv, e.g. tp_col_linear's output) belong to sequence s.
+ * kv_len[s] and slot[s] are device int32 arrays: sequence s uses cache slot
+ * slot[s] and holds kv_len[s] positions once its new tokens are in, new
+ * token i at position kv_len[s] - q_len + i. Slots must be distinct within a
+ * call. A sequence with kv_len[s] < q_len, kv_len[s] > max_kv (L_max for the
+ * append) or slot[s] outside [0, n_slots) is skipped by tp_kv_append and
+ * gets zero output rows from tp_attention; nothing outside the buffers is
+ * touched.
+ *
+ * The caches (K and V apart, caller-allocated, device, 16-byte aligned) are
+ * [n_slots x n_kv_r x L_max x d] bf16, position-major per key-value head;
+ * L_max d 2 must stay below 2^31 (TP_ERR_SHAPE).
+ */
+
+/* Bytes of one cache array (K or V): n_slots n_kv_r L_max d 2; 0 when the
+ * descriptor or sizes are invalid. */
+TP_API size_t tp_kv_cache_bytes(const tp_shard_desc* qkv, int64_t n_slots, int64_t L_max);
+
+/* Copies the new tokens' K and V rows (the rank's key-value heads) into
+ * their positions of their slots. S == 0 is a no-op. */
+TP_API tp_status tp_kv_append(const tp_shard_desc* qkv, const uint16_t* QKV, int64_t ldqkv,
+                       int32_t S, int32_t q_len, const int32_t* kv_len, const int32_t* slot,
+                       uint16_t* Kc, uint16_t* Vc, int64_t n_slots, int64_t L_max,
+                       hipStream_t stream);
+
+/*
+ * A [M x n_q_r d] bf16 (leading dim lda, a multiple of 8): the rank's query
+ * heads side by side, each row the attention of its token over its
+ * sequence's cache (which must already hold the new tokens: tp_kv_append
+ * first). max_kv (q_len <= max_kv <= L_max) bounds every kv_len entry.
+ * Scores and softmax in fp32; the probabilities enter the product with V as
+ * two bf16 terms (hi + lo); output rounded once to bf16.
+ * When (n_q_r / n_kv_r) q_len <= 16 (decode) the cache is read in chunks of
+ * 256 positions, each once per key-value head, and the chunks' partials
+ * (fp32) go to the workspace: tp_attention_workspace_bytes bytes
+ * (TP_ERR_WORKSPACE if short); otherwise no workspace is used.
+ */
+TP_API tp_status tp_attention(const tp_shard_desc* qkv, const uint16_t* QKV, int64_t ldqkv,
+                       int32_t S, int32_t q_len, const int32_t* kv_len, const int32_t* slot,
+                       int32_t max_kv, const uint16_t* Kc, const uint16_t* Vc, int64_t n_slots,
+                       int64_t L_max, uint16_t* A, int64_t lda, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Workspace tp_attention needs for these sizes (0 for the prefill form or
+ * invalid arguments). */
+TP_API size_t tp_attention_workspace_bytes(const tp_shard_desc* qkv, int32_t S, int32_t q_len,
+                                    int32_t max_kv);
+
 /* Bytes of device workspace tp_col_linear / tp_row_linear need for this
  * shard at this M: fp32 partial sums when K is split over workgroups (decode
  * batches of 17..64 tokens with few output tiles; prefill shapes whose output

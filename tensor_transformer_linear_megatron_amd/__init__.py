@@ -26,7 +26,8 @@ from ._lib import (  # noqa: F401
 
 __all__ = ["tp_shard_plan", "tp_shard_set_wformat", "tp_shard_pack", "tp_col_linear", "tp_row_linear", "tp_ffn_shard",
            "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows", "tp_shard_plan_dgrad",
-           "tp_weight_grad", "tp_swiglu_backward", "tp_workspace_bytes", "tp_status_str", "TpError",
+           "tp_weight_grad", "tp_swiglu_backward", "tp_kv_cache_bytes", "tp_kv_cache_new", "tp_kv_append",
+           "tp_attention", "tp_attention_workspace_bytes", "tp_workspace_bytes", "tp_status_str", "TpError",
            "TpShardDesc"]
 
 
@@ -278,3 +279,86 @@ def tp_swiglu_backward(GU: torch.Tensor, dH: torch.Tensor, dGU: torch.Tensor | N
     _check(_lib.load().tp_swiglu_backward(gp, ldg, hp, ldh, M, w, op, ldo, _stream(stream)),
            "tp_swiglu_backward")
     return dGU
+
+
+def _heads(qkv: TpShardDesc):
+    nq = qkv.q_head_end - qkv.q_head_begin
+    nkv = qkv.kv_head_end - qkv.kv_head_begin
+    return nq, nkv, qkv.shard_n // (nq + 2 * nkv) if nq + 2 * nkv else 0
+
+
+def tp_kv_cache_bytes(qkv: TpShardDesc, n_slots: int, L_max: int) -> int:
+    return int(_lib.load().tp_kv_cache_bytes(ctypes.byref(qkv), n_slots, L_max))
+
+
+def tp_kv_cache_new(qkv: TpShardDesc, n_slots: int, L_max: int, device="cuda"):
+    """Zeroed K and V caches of the rank: [n_slots x n_kv_r x L_max x d] bf16."""
+    if tp_kv_cache_bytes(qkv, n_slots, L_max) == 0:
+        raise ValueError("invalid descriptor or cache sizes")
+    _, nkv, d = _heads(qkv)
+    shape = (n_slots, nkv, L_max, d)
+    return (torch.zeros(shape, dtype=torch.bfloat16, device=device),
+            torch.zeros(shape, dtype=torch.bfloat16, device=device))
+
+
+def _seq(kv_len: torch.Tensor, slot: torch.Tensor):
+    for name, t in (("kv_len", kv_len), ("slot", slot)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous int32 device tensor")
+    if kv_len.numel() != slot.numel():
+        raise ValueError("kv_len and slot differ in length")
+    return kv_len.numel(), ctypes.c_void_p(kv_len.data_ptr()), ctypes.c_void_p(slot.data_ptr())
+
+
+def _cache(Kc: torch.Tensor, Vc: torch.Tensor):
+    for name, t in (("Kc", Kc), ("Vc", Vc)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() \
+                or t.dim() != 4:
+            raise TypeError(f"{name} must be a contiguous 4-D bf16 device tensor")
+    if Kc.shape != Vc.shape:
+        raise ValueError("K and V caches differ in shape")
+    return Kc.size(0), Kc.size(2)
+
+
+def tp_kv_append(qkv: TpShardDesc, QKV: torch.Tensor, q_len: int, kv_len: torch.Tensor, slot: torch.Tensor,
+                 Kc: torch.Tensor, Vc: torch.Tensor, stream=None):
+    """Write the new tokens' K and V rows into their cache slots."""
+    qp, ldq = _mat(QKV, torch.bfloat16, "QKV")
+    S, kp, sp = _seq(kv_len, slot)
+    n_slots, L_max = _cache(Kc, Vc)
+    if QKV.size(0) != S * q_len:
+        raise ValueError(f"QKV has {QKV.size(0)} rows, {S} sequences x {q_len} tokens expected")
+    _check(_lib.load().tp_kv_append(ctypes.byref(qkv), qp, ldq, S, q_len, kp, sp, ctypes.c_void_p(Kc.data_ptr()),
+                                    ctypes.c_void_p(Vc.data_ptr()), n_slots, L_max, _stream(stream)),
+           "tp_kv_append")
+
+
+def tp_attention_workspace_bytes(qkv: TpShardDesc, S: int, q_len: int, max_kv: int) -> int:
+    return int(_lib.load().tp_attention_workspace_bytes(ctypes.byref(qkv), S, q_len, max_kv))
+
+
+def tp_attention(qkv: TpShardDesc, QKV: torch.Tensor, q_len: int, kv_len: torch.Tensor, slot: torch.Tensor,
+                 Kc: torch.Tensor, Vc: torch.Tensor, max_kv: int, A: torch.Tensor | None = None,
+                 ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The rank's attention output A [S q_len x n_q_r d] bf16 over the caches
+    (the new tokens already appended)."""
+    qp, ldq = _mat(QKV, torch.bfloat16, "QKV")
+    S, kp, sp = _seq(kv_len, slot)
+    n_slots, L_max = _cache(Kc, Vc)
+    nq, _, d = _heads(qkv)
+    if QKV.size(0) != S * q_len:
+        raise ValueError(f"QKV has {QKV.size(0)} rows, {S} sequences x {q_len} tokens expected")
+    if A is None:
+        A = torch.empty((S * q_len, nq * d), dtype=torch.bfloat16, device=QKV.device)
+    ap, lda = _mat(A, torch.bfloat16, "A")
+    if ws is None:
+        need = tp_attention_workspace_bytes(qkv, S, q_len, max_kv)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=QKV.device) if need else None
+        if ws is not None and stream is not None:
+            ws.record_stream(stream)
+    wsp = ctypes.c_void_p(ws.data_ptr()) if ws is not None else ctypes.c_void_p(0)
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_lib.load().tp_attention(ctypes.byref(qkv), qp, ldq, S, q_len, kp, sp, max_kv,
+                                    ctypes.c_void_p(Kc.data_ptr()), ctypes.c_void_p(Vc.data_ptr()), n_slots, L_max,
+                                    ap, lda, wsp, wsb, _stream(stream)), "tp_attention")
+    return A

@@ -32,7 +32,8 @@ KIND_NAMES = {"col": TP_COL, "row": TP_ROW, "gateup_col": TP_GATEUP_COL,
 
 EXPORTS = ("tp_shard_plan", "tp_shard_set_wformat", "tp_shard_pack", "tp_col_linear", "tp_row_linear", "tp_ffn_shard",
            "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows", "tp_shard_plan_dgrad",
-           "tp_weight_grad", "tp_swiglu_backward", "tp_workspace_bytes", "tp_status_str")
+           "tp_weight_grad", "tp_swiglu_backward", "tp_kv_cache_bytes", "tp_kv_append", "tp_attention",
+           "tp_attention_workspace_bytes", "tp_workspace_bytes", "tp_status_str")
 
 
 class TpHeads(ctypes.Structure):
@@ -99,13 +100,19 @@ def load() -> ctypes.CDLL:
     lib.tp_shard_plan_dgrad.argtypes = [D, D]
     lib.tp_weight_grad.argtypes = [D, P, I64, P, I64, I64, P, I64, P]
     lib.tp_swiglu_backward.argtypes = [P, I64, P, I64, I64, I64, P, I64, P]
+    lib.tp_kv_cache_bytes.argtypes = [D, I64, I64]
+    lib.tp_kv_cache_bytes.restype = SZ
+    lib.tp_kv_append.argtypes = [D, P, I64, I32, I32, P, P, P, P, I64, I64, P]
+    lib.tp_attention.argtypes = [D, P, I64, I32, I32, P, P, I32, P, P, I64, I64, P, I64, P, SZ, P]
+    lib.tp_attention_workspace_bytes.argtypes = [D, I32, I32, I32]
+    lib.tp_attention_workspace_bytes.restype = SZ
     lib.tp_workspace_bytes.argtypes = [D, I64]
     lib.tp_workspace_bytes.restype = SZ
     lib.tp_status_str.argtypes = [I32]
     lib.tp_status_str.restype = ctypes.c_char_p
     for name in ("tp_shard_plan", "tp_shard_set_wformat", "tp_shard_pack", "tp_col_linear", "tp_row_linear",
                  "tp_ffn_shard", "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows",
-                 "tp_shard_plan_dgrad", "tp_weight_grad", "tp_swiglu_backward"):
+                 "tp_shard_plan_dgrad", "tp_weight_grad", "tp_swiglu_backward", "tp_kv_append", "tp_attention"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib

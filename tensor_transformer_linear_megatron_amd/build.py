@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "tpshard")
 LIB = os.path.join(PKG, "libtpshard.so")
 
-SOURCES = ["plan.cpp", "api.cpp", "pack.hip", "gemv.hip", "gemm.hip", "reduce.hip", "backward.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "pack.hip", "gemv.hip", "gemm.hip", "reduce.hip", "backward.hip", "attention.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,5 +1,6 @@
 // The C-ABI entry points: host-side validation and kernel dispatch. Nothing
 // here allocates device memory or keeps state between calls.
+#include <cmath>
 #include <cstdint>
 
 #include "tp_internal.h"
@@ -313,4 +314,133 @@ extern "C" tp_status tp_swiglu_backward(const uint16_t* GU, int64_t ldgu, const 
   return tpk::launch_swiglu_bwd(GU, ldgu, dH, lddh, M, w, dGU, lddgu, stream) == hipSuccess
              ? TP_OK
              : TP_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Attention core on the rank's heads and its KV-cache share.
+
+namespace {
+
+// Heads of a TP_QKV_COL shard: query heads, key-value heads, head dimension
+// and query heads per key-value head (all of them when the key-value head is
+// repeated).
+tp_status attn_heads(const tp_shard_desc* d, int& nq, int& nkv, int& D, int& G) {
+  tp_status st = check_desc(d);
+  if (st != TP_OK) return st;
+  if (d->kind != TP_QKV_COL) return TP_ERR_KIND;
+  nq = d->q_head_end - d->q_head_begin;
+  nkv = d->kv_head_end - d->kv_head_begin;
+  if (nq <= 0 || nkv <= 0 || nq % nkv) return TP_ERR_SHAPE;
+  const int64_t width = nq + 2 * nkv;
+  if (d->shard_n % width) return TP_ERR_SHAPE;
+  D = (int)(d->shard_n / width);
+  if (D != 64 && D != 128) return TP_ERR_SHAPE;
+  G = nq / nkv;
+  return TP_OK;
+}
+
+// One key-value head's cache rows are addressed with 32-bit byte offsets.
+bool cache_ok(int D, int64_t n_slots, int64_t L_max) {
+  return n_slots >= 1 && L_max >= 1 && L_max <= INT32_MAX / (2 * D);
+}
+
+bool attn_decode(int G, int32_t q_len) { return (int64_t)G * q_len <= tpk::kAttnDecodeRows; }
+
+int64_t attn_chunks(int32_t max_kv) {
+  return ((int64_t)max_kv + tpk::kAttnDecodeChunk - 1) / tpk::kAttnDecodeChunk;
+}
+
+// Checks shared by the append and the attention; fills the arguments.
+tp_status attn_args(const tp_shard_desc* qkv, const uint16_t* QKV, int64_t ldqkv, int32_t S,
+                    int32_t q_len, const int32_t* kv_len, const int32_t* slot, const void* Kc,
+                    const void* Vc, int64_t n_slots, int64_t L_max, int32_t max_kv,
+                    tpk::AttnArgs& a) {
+  int nq, nkv, D, G;
+  tp_status st = attn_heads(qkv, nq, nkv, D, G);
+  if (st != TP_OK) return st;
+  if (S < 0 || q_len < 1 || ldqkv < qkv->shard_n || !cache_ok(D, n_slots, L_max) ||
+      max_kv < q_len || max_kv > L_max)
+    return TP_ERR_SHAPE;
+  if (S > 0 && (QKV == nullptr || kv_len == nullptr || slot == nullptr || Kc == nullptr ||
+                Vc == nullptr))
+    return TP_ERR_NULL;
+  if (S > 0 && (!aligned16(QKV) || !aligned16(Kc) || !aligned16(Vc) || ldqkv % 8 ||
+                (reinterpret_cast<uintptr_t>(kv_len) & 3u) || (reinterpret_cast<uintptr_t>(slot) & 3u)))
+    return TP_ERR_ALIGN;
+  a = tpk::AttnArgs{};
+  a.QKV = QKV;
+  a.ldqkv = ldqkv;
+  a.kv_len = kv_len;
+  a.slot = slot;
+  a.Kc = static_cast<const uint16_t*>(Kc);
+  a.Vc = static_cast<const uint16_t*>(Vc);
+  a.n_slots = n_slots;
+  a.L_max = L_max;
+  a.S = S;
+  a.q_len = q_len;
+  a.nq = nq;
+  a.nkv = nkv;
+  a.G = G;
+  a.D = D;
+  a.max_kv = max_kv;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)D));
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" size_t tp_kv_cache_bytes(const tp_shard_desc* qkv, int64_t n_slots, int64_t L_max) {
+  int nq, nkv, D, G;
+  if (attn_heads(qkv, nq, nkv, D, G) != TP_OK || !cache_ok(D, n_slots, L_max)) return 0;
+  return (size_t)n_slots * (size_t)nkv * (size_t)L_max * (size_t)D * 2;
+}
+
+extern "C" tp_status tp_kv_append(const tp_shard_desc* qkv, const uint16_t* QKV, int64_t ldqkv,
+                                  int32_t S, int32_t q_len, const int32_t* kv_len,
+                                  const int32_t* slot, uint16_t* Kc, uint16_t* Vc, int64_t n_slots,
+                                  int64_t L_max, hipStream_t stream) {
+  tpk::AttnArgs a;
+  const int32_t max_kv = L_max < INT32_MAX ? (int32_t)L_max : INT32_MAX;
+  tp_status st = attn_args(qkv, QKV, ldqkv, S, q_len, kv_len, slot, Kc, Vc, n_slots, L_max,
+                           q_len > max_kv ? q_len : max_kv, a);
+  if (st != TP_OK || S == 0) return st;
+  a.Kw = Kc;
+  a.Vw = Vc;
+  return tpk::launch_kv_append(a, stream) == hipSuccess ? TP_OK : TP_ERR_HIP;
+}
+
+extern "C" size_t tp_attention_workspace_bytes(const tp_shard_desc* qkv, int32_t S, int32_t q_len,
+                                               int32_t max_kv) {
+  int nq, nkv, D, G;
+  if (attn_heads(qkv, nq, nkv, D, G) != TP_OK || S < 0 || q_len < 1 || max_kv < q_len) return 0;
+  if (!attn_decode(G, q_len)) return 0;
+  return tpk::attn_decode_ws_bytes(S, nkv, attn_chunks(max_kv), D);
+}
+
+extern "C" tp_status tp_attention(const tp_shard_desc* qkv, const uint16_t* QKV, int64_t ldqkv,
+                                  int32_t S, int32_t q_len, const int32_t* kv_len,
+                                  const int32_t* slot, int32_t max_kv, const uint16_t* Kc,
+                                  const uint16_t* Vc, int64_t n_slots, int64_t L_max, uint16_t* A,
+                                  int64_t lda, void* ws, size_t ws_bytes, hipStream_t stream) {
+  tpk::AttnArgs a;
+  tp_status st = attn_args(qkv, QKV, ldqkv, S, q_len, kv_len, slot, Kc, Vc, n_slots, L_max, max_kv, a);
+  if (st != TP_OK) return st;
+  if (lda < (int64_t)a.nq * a.D) return TP_ERR_SHAPE;
+  if (S == 0) return TP_OK;
+  if (A == nullptr) return TP_ERR_NULL;
+  if (!aligned16(A) || lda % 8) return TP_ERR_ALIGN;
+  a.A = A;
+  a.lda = lda;
+  const bool decode = attn_decode(a.G, q_len);
+  if (decode) {
+    a.nchunk = (int32_t)attn_chunks(max_kv);
+    if (a.nchunk > 65535) return TP_ERR_SHAPE;
+    const size_t need = tpk::attn_decode_ws_bytes(S, a.nkv, a.nchunk, a.D);
+    if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return TP_ERR_WORKSPACE;
+    a.ws = static_cast<float*>(ws);
+  } else if ((q_len + 127) / 128 > 65535 * 16) {
+    return TP_ERR_SHAPE;
+  }
+  if (S > 65535) return TP_ERR_SHAPE;
+  return tpk::launch_attention(a, decode, stream) == hipSuccess ? TP_OK : TP_ERR_HIP;
 }

@@ -1,0 +1,516 @@
+// Attention core on one tensor-parallel rank's heads, with the rank's share of
+// the KV cache ("Tensor vs Pipeline Parallelism", "Tensor parallelism: split
+// inside each layer": attention heads are distributed among the GPUs, each
+// computing its slice, each keeping its heads' share of the KV cache; "AI
+// Infrastructure series, Part 5", "How does tensor parallelism split a
+// layer?": past the key-value head count a larger group repeats key-value
+// heads). Per query head: softmax(q k^T / sqrt(D)) v over the positions of
+// its sequence up to its own (causal), with the rank's key-value head of its
+// group. No position encoding, no bias.
+//
+// Kernels:
+//  * kv_append_kernel: the new tokens' K and V rows into their cache slots.
+//  * attn_decode_kernel + attn_combine_kernel: few new tokens per sequence
+//    (the rank's query heads of one key-value head times the new tokens fit
+//    in 16 rows). The cache is split into chunks of 256 positions; each
+//    workgroup reads its chunk of one key-value head once for all those rows,
+//    and the combine kernel merges the chunks' softmax partials.
+//  * attn_prefill_kernel: many new tokens. 128 query tokens of one head per
+//    workgroup, key-value blocks of 64 positions shared through LDS, online
+//    softmax.
+//
+// Precision: q k^T accumulates in fp32 from bf16; the softmax runs in fp32
+// (exp2 with log2(e) folded into the scale). The probabilities enter the
+// p v product as two bf16 terms, hi = bf16(p) and lo = bf16(p - hi), so that
+// their rounding (about 2^-9 relative for one bf16 term, which alone would
+// put the output about 1e-3 from the exact value) drops to about 2^-17. The
+// output is rounded once to bf16.
+//
+// Operand layouts (v_mfma 16x16x32 and 32x32x16, bf16): lane (g, i) supplies
+// A[i][8g .. 8g + 7] and B[8g .. 8g + 7][i]; the 16x16 result lands as
+// D[4g + r][i], the 32x32 one as D[8q + 4g + r][i] in element 4q + r.
+// Scores are computed transposed, S^T = K Q^T, so that a lane holds one
+// query's scores. The p v product then runs as O^T = V^T P^T with its
+// contraction over positions taken in the order those registers hold them:
+// element e of lane group g is position 4g + e for e < 4 and 4g + 8 + (e - 4)
+// (32x32x16; 16 + 4g + (e - 4) for 16x16x32 over two 16-position blocks).
+// V^T comes out of LDS with ds_read_b64_tr_b16: within each 16-lane group,
+// output lane j, element q is element j % 4 of the 8 bytes addressed by lane
+// 4q + j / 4, so a lane addressing row base + j / 4 at column c0 + 4 (j % 4)
+// yields V[base + q][c0 + j].
+#include "tp_internal.h"
+
+namespace tpk {
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_p;
+
+constexpr int kWaitVm0 = 0x0F70;    // s_waitcnt vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0)
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint2 tr_read(const char* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)p));
+}
+
+__device__ __forceinline__ uint4 tr_pair(const char* p0, const char* p1) {
+  const uint2 a = tr_read(p0), b = tr_read(p1);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// Two bf16 terms of 8 probabilities, packed as MFMA operands.
+__device__ __forceinline__ void split8(const float (&p)[8], uint4& hi, uint4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint16_t b = f32_to_bf16(p[e]);
+    h[e] = b;
+    l[e] = f32_to_bf16(p[e] - __uint_as_float((uint32_t)b << 16));
+  }
+  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+}
+
+// A sequence's cache length, or 0 when its kv_len or slot is out of range
+// (max_kv <= L_max, checked on the host).
+__device__ __forceinline__ int seq_len(const AttnArgs& a, int s, int& sl) {
+  const int kl = a.kv_len[s];
+  sl = a.slot[s];
+  const bool ok = kl >= a.q_len && kl <= a.max_kv && sl >= 0 && sl < a.n_slots;
+  return ok ? kl : 0;
+}
+
+// The key-value head's cache rows [0, kl) as a buffer resource: positions
+// past kl read as zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* C, const AttnArgs& a, int sl, int g,
+                                                            int kl, int D) {
+  const uint64_t base = (uint64_t)(C + (kl > 0 ? ((int64_t)sl * a.nkv + g) * a.L_max * D : 0));
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0,
+                                           __builtin_amdgcn_readfirstlane(kl * D * 2), 0x00020000);
+}
+
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void kv_append_kernel(AttnArgs a, int64_t total) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int cpr = a.D / 8;
+  const int per_row = 2 * a.nkv * cpr;
+  const int64_t m = idx / per_row;
+  const int c = (int)(idx - m * per_row);
+  const int s = (int)(m / a.q_len), i = (int)(m - (int64_t)s * a.q_len);
+  int sl;
+  const int kl = seq_len(a, s, sl);
+  if (kl == 0) return;
+  const bool isv = c >= a.nkv * cpr;
+  const int cc = isv ? c - a.nkv * cpr : c;
+  const int g = cc / cpr, col = (cc - g * cpr) * 8;
+  const uint4 v = *reinterpret_cast<const uint4*>(a.QKV + m * a.ldqkv +
+                                                  (int64_t)(a.nq + (isv ? a.nkv : 0) + g) * a.D + col);
+  const int64_t pos = kl - a.q_len + i;
+  uint16_t* dst = (isv ? a.Vw : a.Kw) + (((int64_t)sl * a.nkv + g) * a.L_max + pos) * a.D + col;
+  *reinterpret_cast<uint4*>(dst) = v;
+}
+
+// ---------------------------------------------------------------------------
+// Decode. Workgroup (chunk, g, s) of 4 wavefronts; wavefront w takes positions
+// [256 chunk + 64 w, + 64). Row rho (< 16) of the 16x16x32 operands is query
+// head g G + rho / q_len of token rho % q_len. K fragments come straight from
+// the cache into registers (A operand rows = positions); V lands in the
+// wavefront's own LDS region by DMA at a pitch of D/8 + 2 16-byte slots, which
+// puts the four rows each 16-lane group reads on distinct banks. The four
+// wavefronts' partials merge through LDS into one per workgroup:
+// m[rho] (log2 domain), l[rho] and the unnormalised output [rho][D].
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;     // 32-deep k-steps of q k^T
+  constexpr int DB = D / 16;     // 16-column output blocks
+  constexpr int CPR = D / 8;     // 16-byte chunks per cache row
+  constexpr int PITCH = CPR + 2;
+  constexpr int WPOS = 64;
+  constexpr int RED = kAttnDecodeRows * D + 2 * kAttnDecodeRows;
+  static_assert(RED * 4 <= WPOS * PITCH * 16, "a wave's partial fits in its V region");
+  __shared__ uint4 Vs[4][WPOS * PITCH];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g4 = lane >> 4, i = lane & 15;
+  const int chunk = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  int sl;
+  const int kl = seq_len(a, s, sl);
+  const int R = a.G * a.q_len;
+  const int p0 = chunk * kAttnDecodeChunk + wave * WPOS;
+  const bool active = p0 < kl;
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.Kc, a, sl, g, kl, D);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.Vc, a, sl, g, kl, D);
+
+  if (active) {
+#pragma unroll
+    for (int u = 0; u < PITCH; ++u) {
+      const int q = u * 64 + lane, row = q / PITCH, c = q - row * PITCH;
+      const unsigned off = c < CPR ? (unsigned)(((p0 + row) * D + 8 * c) * 2) : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&Vs[wave][u * 64], 16, off, 0, 0, 0);
+    }
+  }
+
+  const int rho = i;
+  const int hh = rho / a.q_len, tok = rho - hh * a.q_len;
+  const bool row_ok = kl > 0 && rho < R;
+  const int pos_r = kl - a.q_len + tok;
+  float mx = -INFINITY, l = 0.f;
+  f32x4_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (active) {
+    uint4 qf[KS];
+    const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + tok) * a.ldqkv + (int64_t)(g * a.G + hh) * D + 8 * g4;
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      qf[k] = row_ok ? *reinterpret_cast<const uint4*>(qp + 32 * k) : make_uint4(0, 0, 0, 0);
+    f32x4_t sc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      sc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const unsigned off = (unsigned)(((p0 + 16 * b + i) * D + 32 * k + 8 * g4) * 2);
+        const uint4 kf = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+        sc[b] = mfma_16x16x32(kf, qf[k], sc[b]);
+      }
+    }
+    // Lane (g4, i) holds the scores of row i at positions p0 + 16 b + 4 g4 + r.
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = p0 + 16 * b + 4 * g4 + r;
+        sc[b][r] = (p < kl && p <= pos_r) ? sc[b][r] * a.qscale : -INFINITY;
+        mx = fmaxf(mx, sc[b][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = sc[b][r] == -INFINITY ? 0.f : exp2f(sc[b][r] - mx);
+        sc[b][r] = e;
+        l += e;
+      }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's V has landed
+    const char* vb = (const char*)Vs[wave] + ((4 * g4 + (i >> 2)) * PITCH + ((i & 3) >> 1)) * 16 + (i & 1) * 8;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const float pe[8] = {sc[2 * t2][0],     sc[2 * t2][1],     sc[2 * t2][2],     sc[2 * t2][3],
+                           sc[2 * t2 + 1][0], sc[2 * t2 + 1][1], sc[2 * t2 + 1][2], sc[2 * t2 + 1][3]};
+      uint4 ph, pl;
+      split8(pe, ph, pl);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint4 vf = tr_pair(vb + (32 * t2 * PITCH + 2 * db) * 16, vb + ((32 * t2 + 16) * PITCH + 2 * db) * 16);
+        o[db] = mfma_16x16x32(vf, ph, o[db]);
+        o[db] = mfma_16x16x32(vf, pl, o[db]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  }
+
+  // This wave's partial into its own region (its reads of V are complete).
+  float* red = reinterpret_cast<float*>(Vs[wave]);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[rho * D + 16 * db + 4 * g4 + r] = o[db][r];
+  if (g4 == 0) {
+    red[kAttnDecodeRows * D + i] = mx;
+    red[kAttnDecodeRows * D + kAttnDecodeRows + i] = l;
+  }
+  __syncthreads();
+
+  // Merge the four waves: thread t owns row t / 16, columns (t % 16) D / 16 ...
+  constexpr int CW = D / 16;
+  const int t = threadIdx.x, row = t >> 4, c0 = (t & 15) * CW;
+  float mw[4], M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    mw[w] = reinterpret_cast<const float*>(Vs[w])[kAttnDecodeRows * D + row];
+    M = fmaxf(M, mw[w]);
+  }
+  float L = 0.f, f[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f[w] = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - M);
+    L += f[w] * reinterpret_cast<const float*>(Vs[w])[kAttnDecodeRows * D + kAttnDecodeRows + row];
+  }
+  float* P = a.ws + (((int64_t)s * a.nkv + g) * a.nchunk + chunk) * RED;
+  if ((t & 15) == 0) {
+    P[kAttnDecodeRows * D + row] = M;
+    P[kAttnDecodeRows * D + kAttnDecodeRows + row] = L;
+  }
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc += f[w] * reinterpret_cast<const float*>(Vs[w])[row * D + c0 + c];
+    P[row * D + c0 + c] = acc;
+  }
+}
+
+// Workgroup (rho, g, s), thread c: output column c of row rho, merged over
+// the chunks in chunk order.
+template <int D>
+__global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
+  constexpr int RED = kAttnDecodeRows * D + 2 * kAttnDecodeRows;
+  const int rho = blockIdx.x, g = blockIdx.y, s = blockIdx.z, c = threadIdx.x;
+  int sl;
+  const int kl = seq_len(a, s, sl);
+  const float* P0 = a.ws + ((int64_t)s * a.nkv + g) * a.nchunk * RED;
+  float M = -INFINITY;
+  for (int ch = 0; ch < a.nchunk; ++ch) M = fmaxf(M, P0[(int64_t)ch * RED + kAttnDecodeRows * D + rho]);
+  float L = 0.f, acc = 0.f;
+  for (int ch = 0; ch < a.nchunk; ++ch) {
+    const float* P = P0 + (int64_t)ch * RED;
+    const float m = P[kAttnDecodeRows * D + rho];
+    if (m == -INFINITY) continue;
+    const float f = exp2f(m - M);
+    L += f * P[kAttnDecodeRows * D + kAttnDecodeRows + rho];
+    acc += f * P[rho * D + c];
+  }
+  const int hh = rho / a.q_len, tok = rho - hh * a.q_len;
+  a.A[((int64_t)s * a.q_len + tok) * a.lda + (int64_t)(g * a.G + hh) * D + c] =
+      f32_to_bf16(kl > 0 && L > 0.f ? acc / L : 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill. Workgroup (qb, h, s) of 4 wavefronts: query head h, tokens
+// [128 qb', + 128) with qb' = nqb - 1 - qb (the longest rows start first);
+// wavefront w takes tokens 128 qb' + 32 w + j, j = lane % 32 (the B operand
+// column). Key-value blocks of 64 positions land in LDS by DMA, double
+// buffered: K rows at a pitch of D/8 + 1 slots (the A operand of S^T is read
+// whole, 32 rows per half-wave), V rows at D/8 + 2 (transposed reads); a
+// stage's DMA instructions are padded to a multiple of 4 so that every wave
+// issues the same count (the padding fills a spare kilobyte with zeros).
+
+template <int D>
+struct PrefillCfg {
+  static constexpr int KP = D / 8 + 1, VP = D / 8 + 2;
+  static constexpr int KSL = 64 * KP, VSL = 64 * VP;
+  static constexpr int NDMA = (KSL + VSL) / 64;
+  static constexpr int NU = (NDMA + 3) / 4;  // DMA instructions per wave and stage
+  static constexpr int STAGE = NU * 4 * 64;  // slots, with the padding
+  static_assert(KSL % 64 == 0 && VSL % 64 == 0, "a DMA instruction stays within K or V");
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a, int nqb) {
+  using C = PrefillCfg<D>;
+  constexpr int KS = D / 16;  // 16-deep k-steps of q k^T
+  constexpr int DB = D / 32;  // 32-column output blocks
+  constexpr int CPR = D / 8;
+  __shared__ uint4 Ls[2][C::STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h2 = lane >> 5, j = lane & 31;
+  const int qb = nqb - 1 - (int)blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int g = h / a.G;
+  int sl;
+  const int kl = seq_len(a, s, sl);
+  const int tok0 = qb * 128 + wave * 32;
+  const int tok = tok0 + j;
+  const bool row_ok = tok < a.q_len;
+  uint16_t* out = a.A + ((int64_t)s * a.q_len + tok) * a.lda + (int64_t)h * D;
+  if (kl == 0) {  // the whole workgroup: a sequence out of range gives zeros
+    if (row_ok)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) store_bf16x4(out + 32 * db + 8 * q + 4 * h2, 0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int base_pos = kl - a.q_len;  // position of token 0
+  const int last_tok = qb * 128 + 127 < a.q_len - 1 ? qb * 128 + 127 : a.q_len - 1;
+  const int nblk = (base_pos + last_tok) / 64 + 1;
+  const int wlast = tok0 + 31 < a.q_len - 1 ? tok0 + 31 : a.q_len - 1;
+  const int wblk = tok0 < a.q_len ? (base_pos + wlast) / 64 + 1 : 0;  // blocks this wave multiplies
+  const int wfirst_pos = base_pos + tok0;
+  const int pos_j = base_pos + tok;
+
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.Kc, a, sl, g, kl, D);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.Vc, a, sl, g, kl, D);
+  // DMA: instruction n = 4 u + wave of a stage fills slots 64 n + lane.
+  unsigned off[C::NU];
+#pragma unroll
+  for (int u = 0; u < C::NU; ++u) {
+    const int n = 4 * u + wave;
+    int q = n * 64 + lane;
+    unsigned o = 0x80000000u;
+    if (n * 64 < C::KSL) {
+      const int row = q / C::KP, c = q - row * C::KP;
+      if (c < CPR) o = (unsigned)((row * D + 8 * c) * 2);
+    } else if (n < C::NDMA) {
+      q -= C::KSL;
+      const int row = q / C::VP, c = q - row * C::VP;
+      if (c < CPR) o = (unsigned)((row * D + 8 * c) * 2);
+    }
+    off[u] = o;
+  }
+#define AP_ISSUE(BUF, BLK)                                                                         \
+  {                                                                                                \
+    const unsigned bo_ = (unsigned)((BLK) * 64 * D * 2);                                           \
+    _Pragma("unroll") for (int u = 0; u < C::NU; ++u) {                                            \
+      const int n = 4 * u + wave;                                                                  \
+      const unsigned o_ = off[u] >= 0x80000000u ? off[u] : off[u] + bo_;                           \
+      if (n * 64 < C::KSL) /* wave-uniform */                                                      \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&Ls[BUF][n * 64], 16, o_, 0, 0, 0); \
+      else                                                                                         \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&Ls[BUF][n * 64], 16, o_, 0, 0, 0); \
+    }                                                                                              \
+  }
+
+  uint4 qf[KS];
+  {
+    const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + tok) * a.ldqkv + (int64_t)h * D + 8 * h2;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) qf[k] = row_ok ? *reinterpret_cast<const uint4*>(qp + 16 * k) : make_uint4(0, 0, 0, 0);
+  }
+  f32x16_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
+  float m = -INFINITY, l = 0.f;
+
+  // Fragment bases: K row 32 b + j, slot 2 k + h2; V (transposed reads) row
+  // 16 k' + 4 h2 + jj / 4 (+ 8), slot 4 db + 2 u + (jj % 4) / 2, half jj % 2,
+  // where the lane is 32 h2 + 16 u + jj.
+  const int jj = j & 15, uu = j >> 4;
+  const int kfb = (j * C::KP + h2) * 16;
+  const int vfb = C::KSL * 16 + ((4 * h2 + (jj >> 2)) * C::VP + 2 * uu + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
+
+  AP_ISSUE(0, 0)
+  if (nblk > 1) AP_ISSUE(1, 1)
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int buf = blk & 1;
+    if (blk + 1 < nblk)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | C::NU);  // vmcnt(NU): block blk has landed, blk + 1 may fly
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_barrier();
+    if (blk < wblk) {
+      const char* L = (const char*)Ls[buf];
+      f32x16_t sa[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const uint4 kf = *reinterpret_cast<const uint4*>(L + kfb + (32 * b * C::KP + 2 * k) * 16);
+          sa[b] = mfma_32x32x16(kf, qf[k], sa[b]);
+        }
+      // Lane (h2, j), element 4 q + r of block b: position 64 blk + 32 b + 8 q + 4 h2 + r.
+      const bool diag = blk * 64 + 63 > wfirst_pos;
+      float bm = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int p = blk * 64 + 32 * b + 8 * (e >> 2) + 4 * h2 + (e & 3);
+          const float v = (!diag || p <= pos_j) ? sa[b][e] * a.qscale : -INFINITY;
+          sa[b][e] = v;
+          bm = fmaxf(bm, v);
+        }
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float mn = fmaxf(m, bm);
+      const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+      float rs = 0.f;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float pe = sa[b][e] == -INFINITY ? 0.f : exp2f(sa[b][e] - mn);
+          sa[b][e] = pe;
+          rs += pe;
+        }
+      rs += __shfl_xor(rs, 32);
+      l = l * alpha + rs;
+      m = mn;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int b = kk >> 1, q0 = 2 * (kk & 1);
+        const float pe[8] = {sa[b][4 * q0],     sa[b][4 * q0 + 1], sa[b][4 * q0 + 2], sa[b][4 * q0 + 3],
+                             sa[b][4 * q0 + 4], sa[b][4 * q0 + 5], sa[b][4 * q0 + 6], sa[b][4 * q0 + 7]};
+        uint4 ph, pl;
+        split8(pe, ph, pl);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const char* v0 = L + vfb + (16 * kk * C::VP + 4 * db) * 16;
+          const uint4 vf = tr_pair(v0, v0 + 8 * C::VP * 16);
+          o[db] = mfma_32x32x16(vf, ph, o[db]);
+          o[db] = mfma_32x32x16(vf, pl, o[db]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();  // every wave is done with buffer buf
+    if (blk + 2 < nblk) AP_ISSUE(buf, blk + 2)
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#undef AP_ISSUE
+
+  if (row_ok) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    // Lane (h2, j), element 4 q + r of block db: column 32 db + 8 q + 4 h2 + r of token j.
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        store_bf16x4(out + 32 * db + 8 * q + 4 * h2, o[db][4 * q] * inv, o[db][4 * q + 1] * inv,
+                     o[db][4 * q + 2] * inv, o[db][4 * q + 3] * inv);
+  }
+}
+
+template <int D>
+hipError_t launch_attention_d(const AttnArgs& a, bool decode, hipStream_t s) {
+  if (decode) {
+    hipLaunchKernelGGL(attn_decode_kernel<D>, dim3(a.nchunk, a.nkv, a.S), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(a.G * a.q_len, a.nkv, a.S), dim3(D), 0, s, a);
+  } else {
+    const int nqb = (a.q_len + 127) / 128;
+    hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(nqb, a.nq, a.S), dim3(256), 0, s, a, nqb);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_decode_ws_bytes(int64_t S, int64_t nkv, int64_t nchunk, int D) {
+  return (size_t)(S * nkv * nchunk) * (size_t)(kAttnDecodeRows * D + 2 * kAttnDecodeRows) * sizeof(float);
+}
+
+hipError_t launch_kv_append(const AttnArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.S * a.q_len * 2 * a.nkv * (a.D / 8);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& a, bool decode, hipStream_t s) {
+  if (a.S == 0) return hipSuccess;
+  return a.D == 128 ? launch_attention_d<128>(a, decode, s) : launch_attention_d<64>(a, decode, s);
+}
+
+}  // namespace tpk

@@ -105,6 +105,35 @@ hipError_t launch_reduce(const float* P, int64_t stride, int32_t t, int64_t M, i
 hipError_t launch_gather(const uint16_t* Xs, int64_t stride, int32_t t, int64_t Mt, int64_t N,
                          int64_t ldb, uint16_t* X, int64_t ldx, hipStream_t s);
 
+// Attention core on a rank's heads (attention.hip). Rows s q_len .. s q_len +
+// q_len - 1 of QKV (the rank's [Q_r | K_r | V_r]) and of A belong to sequence
+// s; its cache is slot slot[s] and holds kv_len[s] positions once its new
+// tokens are in. Caches are [n_slots x nkv x L_max x D] bf16, K and V apart.
+struct AttnArgs {
+  const uint16_t* QKV;
+  int64_t ldqkv;
+  const int32_t* kv_len;
+  const int32_t* slot;
+  const uint16_t* Kc;
+  const uint16_t* Vc;
+  uint16_t* Kw;  // append: the caches written
+  uint16_t* Vw;
+  int64_t n_slots, L_max;
+  int32_t S, q_len, nq, nkv, G, D;  // G: query heads per key-value head of the rank
+  int32_t max_kv;                   // kv_len entries above it (or below q_len) mark a sequence invalid
+  uint16_t* A;
+  int64_t lda;
+  float* ws;       // decode: per-chunk partials
+  int32_t nchunk;  // decode: chunks of positions per (sequence, key-value head)
+  float qscale;    // log2(e) / sqrt(D)
+};
+
+constexpr int kAttnDecodeRows = 16;    // query rows (heads x tokens) of one decode workgroup
+constexpr int kAttnDecodeChunk = 256;  // positions per decode workgroup
+size_t attn_decode_ws_bytes(int64_t S, int64_t nkv, int64_t nchunk, int D);
+hipError_t launch_kv_append(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, bool decode, hipStream_t s);
+
 }  // namespace tpk
 
 #ifdef __HIPCC__

@@ -357,3 +357,71 @@ def test_backward_argument_errors():
     assert sb(MIS, 128, B, 64, 4, 64, C, 128, S) == _lib.TP_ERR_ALIGN
     assert sb(A, 128, B, 66, 4, 64, C, 128, S) == _lib.TP_ERR_ALIGN  # lddh % 4
     assert sb(NUL, 128, NUL, 64, 0, 64, NUL, 128, S) == _lib.TP_OK  # M == 0
+
+
+H70 = (64, 8, 128)
+
+
+def _qkv70(t, r):
+    return tp.tp_shard_plan("qkv_col", 8192, (64 + 16) * 128, t, r, heads=H70)
+
+
+def test_kv_cache_and_attention_workspace_sizes():
+    """Cache bytes: n_slots x n_kv_r x L_max x d x 2 per array; the rank's
+    share is 1/t of the layer's key-value heads up to t = n_kv, then one
+    repeated head. The decode form needs one partial (16 rows x (d + 2) fp32)
+    per sequence, key-value head and 256-position chunk."""
+    for t, nkv in ((1, 8), (2, 4), (8, 1), (16, 1)):
+        assert tp.tp_kv_cache_bytes(_qkv70(t, t - 1), 4, 4096) == 4 * nkv * 4096 * 128 * 2
+    assert tp.tp_kv_cache_bytes(tp.tp_shard_plan("col", 64, 64, 1, 0), 1, 16) == 0
+    assert tp.tp_kv_cache_bytes(tp.tp_shard_plan("qkv_col", 32, 12 * 16, 1, 0, heads=(8, 2, 16)), 1, 16) == 0  # d = 16
+    assert tp.tp_kv_cache_bytes(_qkv70(8, 0), 1, 2 ** 23) == 0  # one head past 2^31 bytes
+    q = _qkv70(8, 0)  # 8 query heads on one key-value head
+    assert tp.tp_attention_workspace_bytes(q, 32, 1, 4096) == 32 * 16 * (16 * 128 + 32) * 4
+    assert tp.tp_attention_workspace_bytes(q, 32, 2, 4097) == 32 * 17 * (16 * 128 + 32) * 4
+    assert tp.tp_attention_workspace_bytes(q, 1, 3, 4096) == 0  # 24 rows: the prefill form
+    q16 = _qkv70(16, 5)  # 4 query heads, repeated key-value head
+    assert tp.tp_attention_workspace_bytes(q16, 2, 4, 300) == 2 * 2 * (16 * 128 + 32) * 4
+    assert tp.tp_attention_workspace_bytes(q16, 2, 5, 300) == 0
+
+
+def test_attention_argument_errors():
+    """Every refusal happens on the host, before any launch."""
+    lib = _lib.load()
+    S_ = ctypes.c_void_p(0)
+    q = _qkv70(8, 0)
+    qb = ctypes.byref(q)
+    W = 10 * 128  # QKV row width of the rank
+    KL, SL = ctypes.c_void_p(0x400000), ctypes.c_void_p(0x500000)
+    ws_need = tp.tp_attention_workspace_bytes(q, 2, 1, 64)
+    att = lib.tp_attention
+    app = lib.tp_kv_append
+    col = tp.tp_shard_plan("col", 64, 64, 1, 0)
+    assert att(ctypes.byref(col), A, W, 2, 1, KL, SL, 64, B, C, 2, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_KIND
+    assert att(None, A, W, 2, 1, KL, SL, 64, B, C, 2, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_NULL
+    assert att(qb, NUL, W, 2, 1, KL, SL, 64, B, C, 2, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_NULL
+    assert att(qb, A, W, 2, 1, NUL, SL, 64, B, C, 2, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_NULL
+    assert att(qb, A, W, 2, 1, KL, SL, 64, B, NUL, 2, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_NULL
+    assert att(qb, A, W, 2, 1, KL, SL, 64, B, C, 2, 64, NUL, 1024, A, ws_need, S_) == _lib.TP_ERR_NULL
+    assert att(qb, A, W - 8, 2, 1, KL, SL, 64, B, C, 2, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_SHAPE  # ldqkv
+    assert att(qb, A, W, 2, 0, KL, SL, 64, B, C, 2, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_SHAPE  # q_len 0
+    assert att(qb, A, W, -1, 1, KL, SL, 64, B, C, 2, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_SHAPE
+    assert att(qb, A, W, 2, 1, KL, SL, 65, B, C, 2, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_SHAPE  # max_kv > L_max
+    assert att(qb, A, W, 2, 4, KL, SL, 3, B, C, 2, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_SHAPE  # max_kv < q_len
+    assert att(qb, A, W, 2, 1, KL, SL, 64, B, C, 0, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_SHAPE  # no slot
+    assert att(qb, A, W, 2, 1, KL, SL, 64, B, C, 2, 2 ** 23, A, 1024, A, ws_need, S_) == _lib.TP_ERR_SHAPE
+    assert att(qb, A, W, 2, 1, KL, SL, 64, B, C, 2, 64, A, 1016, A, ws_need, S_) == _lib.TP_ERR_SHAPE  # lda
+    assert att(qb, MIS, W, 2, 1, KL, SL, 64, B, C, 2, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_ALIGN
+    assert att(qb, A, W + 4, 2, 1, KL, SL, 64, B, C, 2, 64, A, 1024, A, ws_need, S_) == _lib.TP_ERR_ALIGN
+    assert att(qb, A, W, 2, 1, ctypes.c_void_p(0x400002), SL, 64, B, C, 2, 64, A, 1024, A, ws_need, S_) == \
+        _lib.TP_ERR_ALIGN
+    assert att(qb, A, W, 2, 1, KL, SL, 64, B, C, 2, 64, MIS, 1024, A, ws_need, S_) == _lib.TP_ERR_ALIGN
+    assert att(qb, A, W, 2, 1, KL, SL, 64, B, C, 2, 64, A, 1024, A, ws_need - 4, S_) == _lib.TP_ERR_WORKSPACE
+    assert att(qb, A, W, 2, 1, KL, SL, 64, B, C, 2, 64, A, 1024, NUL, ws_need, S_) == _lib.TP_ERR_WORKSPACE
+    assert att(qb, NUL, W, 0, 1, NUL, NUL, 64, NUL, NUL, 2, 64, NUL, 1024, NUL, 0, S_) == _lib.TP_OK  # S == 0
+    assert app(qb, NUL, W, 2, 1, KL, SL, B, C, 2, 64, S_) == _lib.TP_ERR_NULL
+    assert app(qb, A, W, 2, 1, KL, SL, B, NUL, 2, 64, S_) == _lib.TP_ERR_NULL
+    assert app(qb, A, W, 2, 1, KL, SL, MIS, C, 2, 64, S_) == _lib.TP_ERR_ALIGN
+    assert app(qb, A, W, 2, 65, KL, SL, B, C, 2, 64, S_) == _lib.TP_ERR_SHAPE  # q_len > L_max
+    assert app(ctypes.byref(col), A, W, 2, 1, KL, SL, B, C, 2, 64, S_) == _lib.TP_ERR_KIND
+    assert app(qb, NUL, W, 0, 1, NUL, NUL, NUL, NUL, 2, 64, S_) == _lib.TP_OK  # S == 0
