@@ -606,6 +606,99 @@ def config_sequence_parallel(timer):
                             frac=round(b_g / us_g / 1e3 / HBM_PEAK_GBS, 4)))
 
 
+def config_70b_attention_block(timer):
+    """Llama-3.1-70B attention block at TP = 8 (8 query heads and 1 key-value
+    head per rank, d = 128). Decode: 32 sequences with 4096 cached positions
+    each, one new token; the core alone on rank 0 (HBM GB/s of the KV cache it
+    reads), and the whole block for all 8 ranks in turn (QKV slice, KV append,
+    attention, O slice) plus the sum of the 8 partials. Prefill: rank 0's
+    attention core on one 4096-token sequence (causal FLOPs)."""
+    import torch
+    import tensor_transformer_linear_megatron_amd as tp
+    from seeded_inputs import workloads as wl
+    lib, VP, ref, stream = _abi()
+    c = wl.LLAMA70B
+    H, t = c["hidden"], 8
+    heads = (c["n_q"], c["n_kv"], c["head_dim"])
+    d = heads[2]
+    S, L = 32, 4096
+    dq = [tp.tp_shard_plan("qkv_col", H, (heads[0] + 2 * heads[1]) * d, t, r, heads=heads) for r in range(t)]
+    do = [tp.tp_shard_plan("o_row", heads[0] * d, H, t, r, heads=heads) for r in range(t)]
+    Wq = to_dev(wl.qkv_weight(H, *heads, c["sigma"]))
+    qp = [tp.tp_shard_pack(x, Wq) for x in dq]
+    del Wq
+    Wo = to_dev(wl.o_weight(heads[0], d, H, c["sigma"]))
+    op = [tp.tp_shard_pack(x, Wo) for x in do]
+    del Wo
+    g = torch.Generator(device="cuda").manual_seed(70)
+    caches = []
+    for r in range(t):
+        Kc, Vc = tp.tp_kv_cache_new(dq[r], S, L)
+        Kc.copy_(torch.randn(Kc.shape, generator=g, device="cuda"))
+        Vc.copy_(torch.randn(Vc.shape, generator=g, device="cuda"))
+        caches.append((Kc, Vc))
+    X = (torch.randn((S, H), generator=g, device="cuda")).to(torch.bfloat16)
+    kv_len = torch.full((S,), L, dtype=torch.int32, device="cuda")
+    slot = torch.arange(S, dtype=torch.int32, device="cuda")
+    nq, w = dq[0].q_head_end - dq[0].q_head_begin, dq[0].shard_n
+    QKV = torch.empty((S, w), dtype=torch.bfloat16, device="cuda")
+    A = torch.empty((S, nq * d), dtype=torch.bfloat16, device="cuda")
+    P = torch.empty((t, S, H), dtype=torch.float32, device="cuda")
+    out = torch.empty((S, H), dtype=torch.float32, device="cuda")
+    wsn = max([tp.tp_attention_workspace_bytes(dq[0], S, 1, L)] + [tp.tp_workspace_bytes(x, S) for x in dq + do] + [16])
+    ws = torch.empty(wsn, dtype=torch.uint8, device="cuda")
+    KL, SLP = VP(kv_len.data_ptr()), VP(slot.data_ptr())
+
+    def attn_call(r):
+        Kc, Vc = caches[r]
+        return (lib.tp_attention, (ref(dq[r]), VP(QKV.data_ptr()), w, S, 1, KL, SLP, L, VP(Kc.data_ptr()),
+                                   VP(Vc.data_ptr()), S, L, VP(A.data_ptr()), nq * d, VP(ws.data_ptr()), wsn, stream))
+
+    block = []
+    for r in range(t):
+        Kc, Vc = caches[r]
+        block += [(lib.tp_col_linear, (ref(dq[r]), VP(X.data_ptr()), S, H, VP(qp[r].data_ptr()), VP(QKV.data_ptr()), w,
+                                       VP(ws.data_ptr()), wsn, stream)),
+                  (lib.tp_kv_append, (ref(dq[r]), VP(QKV.data_ptr()), w, S, 1, KL, SLP, VP(Kc.data_ptr()),
+                                      VP(Vc.data_ptr()), S, L, stream)),
+                  attn_call(r),
+                  (lib.tp_row_linear, (ref(do[r]), VP(A.data_ptr()), S, nq * d, VP(op[r].data_ptr()),
+                                       VP(P[r].data_ptr()), H, VP(ws.data_ptr()), wsn, stream))]
+    block.append((lib.tp_reduce_partials, (VP(P.data_ptr()), S * H, t, S, H, H, VP(out.data_ptr()), H, stream)))
+    _run(block)
+    core = [attn_call(0)]
+    us_core = time_steps(timer, lambda i: _run(core), 20)
+    us_block = time_steps(timer, lambda i: _run(block), 10)
+    kv_bytes = S * L * 1 * d * 2 * 2  # one key-value head per rank
+    core_bytes = kv_bytes + S * w * 2 + S * nq * d * 2
+    wq, wo = H * w * 2, nq * d * H * 2
+    block_bytes = t * (wq + wo + kv_bytes + S * H * 2 + S * w * 2 * 2 + S * nq * d * 2 * 2) + (t + 1) * S * H * 4
+    # prefill core, rank 0, one 4096-token sequence
+    T = 4096
+    Kp, Vp = tp.tp_kv_cache_new(dq[0], 1, T)
+    QKVp = (torch.randn((T, w), generator=g, device="cuda")).to(torch.bfloat16)
+    Ap = torch.empty((T, nq * d), dtype=torch.bfloat16, device="cuda")
+    klp = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    slp = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    tp.tp_kv_append(dq[0], QKVp, T, klp, slp, Kp, Vp)
+    pre = [(lib.tp_attention, (ref(dq[0]), VP(QKVp.data_ptr()), w, 1, T, VP(klp.data_ptr()), VP(slp.data_ptr()), T,
+                               VP(Kp.data_ptr()), VP(Vp.data_ptr()), 1, T, VP(Ap.data_ptr()), nq * d, VP(0), 0,
+                               stream))]
+    us_pre = time_steps(timer, lambda i: _run(pre), 10)
+    flops = 4 * nq * d * T * (T + 1) // 2
+    return dict(config="llama3.1-70b attention, TP=8 (8 query heads + 1 KV head per rank, d=128)",
+                decode=dict(batch=S, context=L,
+                            core_rank0=dict(us=round(us_core, 2), kv_bytes=kv_bytes,
+                                            value=round(core_bytes / us_core / 1e3, 1), unit="GB/s",
+                                            frac=round(core_bytes / us_core / 1e3 / HBM_PEAK_GBS, 4)),
+                            block_8_ranks=dict(us=round(us_block, 1), bytes=block_bytes,
+                                               value=round(block_bytes / us_block / 1e3, 1), unit="GB/s",
+                                               frac=round(block_bytes / us_block / 1e3 / HBM_PEAK_GBS, 4))),
+                prefill_core_rank0=dict(tokens=T, us=round(us_pre, 1), flops=flops,
+                                        value=round(flops / us_pre / 1e6, 1), unit="TFLOP/s",
+                                        frac=round(flops / us_pre / 1e6 / MFMA_BF16_PEAK_TFS, 4)))
+
+
 def config_405b_ffn_backward(timer):
     """Backward of rank 0's Llama-3.1-405B feed-forward share at TP = 8 and
     8192 tokens (the prefill workload above): dH through the down projection's
@@ -662,7 +755,7 @@ def config_405b_ffn_backward(timer):
 
 CONFIGS = {"worked_tp2": config_worked_tp2, "70b_ffn_decode": config_70b_ffn_decode,
            "70b_attention_prefill": config_70b_attention_prefill, "sequence_parallel": config_sequence_parallel,
-           "405b_ffn_backward": config_405b_ffn_backward}
+           "405b_ffn_backward": config_405b_ffn_backward, "70b_attention_block": config_70b_attention_block}
 
 
 def main():
@@ -674,7 +767,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (worked TP=2 split, 70B decode and attention prefill, "
-                         "sequence-parallel partial sum, 405B feed-forward backward)")
+                         "sequence-parallel partial sum, 405B feed-forward backward, 70B attention block)")
     ap.add_argument("--config", choices=sorted(CONFIGS),
                     help="only run this one workload and print its line (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",

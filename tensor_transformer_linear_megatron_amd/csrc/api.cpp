@@ -438,7 +438,7 @@ extern "C" tp_status tp_attention(const tp_shard_desc* qkv, const uint16_t* QKV,
     const size_t need = tpk::attn_decode_ws_bytes(S, a.nkv, a.nchunk, a.D);
     if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return TP_ERR_WORKSPACE;
     a.ws = static_cast<float*>(ws);
-  } else if ((q_len + 127) / 128 > 65535 * 16) {
+  } else if ((int64_t)((q_len + 63) / 64) * a.nq * S > INT32_MAX) {
     return TP_ERR_SHAPE;
   }
   if (S > 65535) return TP_ERR_SHAPE;

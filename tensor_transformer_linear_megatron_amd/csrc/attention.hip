@@ -15,7 +15,7 @@
 //    in 16 rows). The cache is split into chunks of 256 positions; each
 //    workgroup reads its chunk of one key-value head once for all those rows,
 //    and the combine kernel merges the chunks' softmax partials.
-//  * attn_prefill_kernel: many new tokens. 128 query tokens of one head per
+//  * attn_prefill_kernel: many new tokens. 64 query tokens of one head per
 //    workgroup, key-value blocks of 64 positions shared through LDS, online
 //    softmax.
 //
@@ -154,15 +154,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.Kc, a, sl, g, kl, D);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.Vc, a, sl, g, kl, D);
 
-  if (active) {
-#pragma unroll
-    for (int u = 0; u < PITCH; ++u) {
-      const int q = u * 64 + lane, row = q / PITCH, c = q - row * PITCH;
-      const unsigned off = c < CPR ? (unsigned)(((p0 + row) * D + 8 * c) * 2) : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&Vs[wave][u * 64], 16, off, 0, 0, 0);
-    }
-  }
-
   const int rho = i;
   const int hh = rho / a.q_len, tok = rho - hh * a.q_len;
   const bool row_ok = kl > 0 && rho < R;
@@ -173,6 +164,20 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   if (active) {
+    // K fragments first (the first MFMAs wait on them alone), then V's DMA.
+    uint4 kf[4][KS];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        kf[b][k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rk, (unsigned)(((p0 + 16 * b + i) * D + 32 * k + 8 * g4) * 2), 0, 0));
+#pragma unroll
+    for (int u = 0; u < PITCH; ++u) {
+      const int q = u * 64 + lane, row = q / PITCH, c = q - row * PITCH;
+      const unsigned off = c < CPR ? (unsigned)(((p0 + row) * D + 8 * c) * 2) : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&Vs[wave][u * 64], 16, off, 0, 0, 0);
+    }
     uint4 qf[KS];
     const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + tok) * a.ldqkv + (int64_t)(g * a.G + hh) * D + 8 * g4;
 #pragma unroll
@@ -183,28 +188,27 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     for (int b = 0; b < 4; ++b) {
       sc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const unsigned off = (unsigned)(((p0 + 16 * b + i) * D + 32 * k + 8 * g4) * 2);
-        const uint4 kf = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-        sc[b] = mfma_16x16x32(kf, qf[k], sc[b]);
-      }
+      for (int k = 0; k < KS; ++k) sc[b] = mfma_16x16x32(kf[b][k], qf[k], sc[b]);
     }
-    // Lane (g4, i) holds the scores of row i at positions p0 + 16 b + 4 g4 + r.
+    // Lane (g4, i) holds row i's raw scores at positions p0 + 16 b + 4 g4 + r.
+    float bm = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int p = p0 + 16 * b + 4 * g4 + r;
-        sc[b][r] = (p < kl && p <= pos_r) ? sc[b][r] * a.qscale : -INFINITY;
-        mx = fmaxf(mx, sc[b][r]);
+        if (!(p < kl && p <= pos_r)) sc[b][r] = -INFINITY;
+        bm = fmaxf(bm, sc[b][r]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    mx = bm * a.qscale;  // -inf when the row sees none of these positions
+    const float ms = mx == -INFINITY ? 0.f : mx;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = sc[b][r] == -INFINITY ? 0.f : exp2f(sc[b][r] - mx);
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], a.qscale, -ms));
         sc[b][r] = e;
         l += e;
       }
@@ -219,12 +223,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
                            sc[2 * t2 + 1][0], sc[2 * t2 + 1][1], sc[2 * t2 + 1][2], sc[2 * t2 + 1][3]};
       uint4 ph, pl;
       split8(pe, ph, pl);
+      uint4 vf[DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint4 vf = tr_pair(vb + (32 * t2 * PITCH + 2 * db) * 16, vb + ((32 * t2 + 16) * PITCH + 2 * db) * 16);
-        o[db] = mfma_16x16x32(vf, ph, o[db]);
-        o[db] = mfma_16x16x32(vf, pl, o[db]);
-      }
+      for (int db = 0; db < DB; ++db)
+        vf[db] = tr_pair(vb + (32 * t2 * PITCH + 2 * db) * 16, vb + ((32 * t2 + 16) * PITCH + 2 * db) * 16);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = mfma_16x16x32(vf[db], ph, o[db]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = mfma_16x16x32(vf[db], pl, o[db]);
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   }
@@ -271,39 +277,70 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
 }
 
 // Workgroup (rho, g, s), thread c: output column c of row rho, merged over
-// the chunks in chunk order.
+// the chunks in chunk order. The chunks' maxima and sums are fetched a tile
+// of D chunks at a time, one per thread, and shared through LDS.
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   constexpr int RED = kAttnDecodeRows * D + 2 * kAttnDecodeRows;
+  __shared__ float wgt[D];
+  __shared__ float red[D];
   const int rho = blockIdx.x, g = blockIdx.y, s = blockIdx.z, c = threadIdx.x;
   int sl;
   const int kl = seq_len(a, s, sl);
   const float* P0 = a.ws + ((int64_t)s * a.nkv + g) * a.nchunk * RED;
   float M = -INFINITY;
-  for (int ch = 0; ch < a.nchunk; ++ch) M = fmaxf(M, P0[(int64_t)ch * RED + kAttnDecodeRows * D + rho]);
-  float L = 0.f, acc = 0.f;
-  for (int ch = 0; ch < a.nchunk; ++ch) {
-    const float* P = P0 + (int64_t)ch * RED;
-    const float m = P[kAttnDecodeRows * D + rho];
-    if (m == -INFINITY) continue;
-    const float f = exp2f(m - M);
-    L += f * P[kAttnDecodeRows * D + kAttnDecodeRows + rho];
-    acc += f * P[rho * D + c];
+  for (int ch = c; ch < a.nchunk; ch += D) M = fmaxf(M, P0[(int64_t)ch * RED + kAttnDecodeRows * D + rho]);
+  red[c] = M;
+  __syncthreads();
+  for (int w = D / 2; w > 0; w >>= 1) {
+    if (c < w) red[c] = fmaxf(red[c], red[c + w]);
+    __syncthreads();
   }
+  M = red[0];
+  __syncthreads();
+  float Lp = 0.f, acc = 0.f;
+  for (int t0 = 0; t0 < a.nchunk; t0 += D) {
+    const int ch = t0 + c;
+    float f = 0.f;
+    if (ch < a.nchunk) {
+      const float* P = P0 + (int64_t)ch * RED;
+      const float mc = P[kAttnDecodeRows * D + rho];
+      f = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+      Lp += f * P[kAttnDecodeRows * D + kAttnDecodeRows + rho];
+    }
+    wgt[c] = f;
+    __syncthreads();
+    const int n = a.nchunk - t0 < D ? a.nchunk - t0 : D;
+    const float* Pc = P0 + (int64_t)t0 * RED + rho * D + c;
+    for (int j = 0; j < n; ++j) acc += wgt[j] * Pc[(int64_t)j * RED];
+    __syncthreads();
+  }
+  red[c] = Lp;
+  __syncthreads();
+  for (int w = D / 2; w > 0; w >>= 1) {
+    if (c < w) red[c] += red[c + w];
+    __syncthreads();
+  }
+  const float L = red[0];
   const int hh = rho / a.q_len, tok = rho - hh * a.q_len;
   a.A[((int64_t)s * a.q_len + tok) * a.lda + (int64_t)(g * a.G + hh) * D + c] =
       f32_to_bf16(kl > 0 && L > 0.f ? acc / L : 0.f);
 }
 
 // ---------------------------------------------------------------------------
-// Prefill. Workgroup (qb, h, s) of 4 wavefronts: query head h, tokens
-// [128 qb', + 128) with qb' = nqb - 1 - qb (the longest rows start first);
-// wavefront w takes tokens 128 qb' + 32 w + j, j = lane % 32 (the B operand
-// column). Key-value blocks of 64 positions land in LDS by DMA, double
-// buffered: K rows at a pitch of D/8 + 1 slots (the A operand of S^T is read
-// whole, 32 rows per half-wave), V rows at D/8 + 2 (transposed reads); a
-// stage's DMA instructions are padded to a multiple of 4 so that every wave
-// issues the same count (the padding fills a spare kilobyte with zeros).
+// Prefill. A workgroup of 4 wavefronts takes 64 query tokens of one query
+// head; wavefront w takes tokens 64 qb + 16 w + i, i = lane % 16, the column
+// of its 16x16x32 operands (the decode kernel's layout, one head per column
+// set instead of a group). Key-value blocks of 64 positions land in LDS by
+// DMA, double buffered: K rows at a pitch of D/8 + 1 16-byte slots (the A
+// operand of S^T read whole: 16 rows per instruction on distinct banks), V
+// rows at D/8 + 2 (transposed reads, as in decode). A stage's DMA
+// instructions are padded to a multiple of 4 so that every wave issues the
+// same count; the padding fills a spare kilobyte with zeros.
+// Work order: units (query block, head, sequence) sorted by causal length,
+// longest first; workgroup b < half takes unit b and workgroup half + b unit
+// total - 1 - b, so a CU that runs workgroups b and half + b together gets
+// one long and one short unit.
 
 template <int D>
 struct PrefillCfg {
@@ -316,39 +353,41 @@ struct PrefillCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a, int nqb) {
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int nqb) {
   using C = PrefillCfg<D>;
-  constexpr int KS = D / 16;  // 16-deep k-steps of q k^T
-  constexpr int DB = D / 32;  // 32-column output blocks
+  constexpr int KS = D / 32;  // 32-deep k-steps of q k^T
+  constexpr int DB = D / 16;  // 16-column output blocks
   constexpr int CPR = D / 8;
   __shared__ uint4 Ls[2][C::STAGE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h2 = lane >> 5, j = lane & 31;
-  const int qb = nqb - 1 - (int)blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int g4 = lane >> 4, i = lane & 15;
+  const int total = (int)gridDim.x, half = (total + 1) / 2;
+  const int bid = (int)blockIdx.x;
+  const int unit = bid < half ? bid : total - 1 - (bid - half);
+  const int per = a.nq * a.S;
+  const int qb = nqb - 1 - unit / per, h = (unit % per) % a.nq, s = (unit % per) / a.nq;
   const int g = h / a.G;
   int sl;
   const int kl = seq_len(a, s, sl);
-  const int tok0 = qb * 128 + wave * 32;
-  const int tok = tok0 + j;
+  const int tok0 = qb * 64 + wave * 16;
+  const int tok = tok0 + i;
   const bool row_ok = tok < a.q_len;
   uint16_t* out = a.A + ((int64_t)s * a.q_len + tok) * a.lda + (int64_t)h * D;
-  if (kl == 0) {  // the whole workgroup: a sequence out of range gives zeros
+  if (kl == 0) {  // uniform over the workgroup: a sequence out of range gives zeros
     if (row_ok)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) store_bf16x4(out + 32 * db + 8 * q + 4 * h2, 0.f, 0.f, 0.f, 0.f);
+      for (int db = 0; db < DB; ++db) store_bf16x4(out + 16 * db + 4 * g4, 0.f, 0.f, 0.f, 0.f);
     return;
   }
   const int base_pos = kl - a.q_len;  // position of token 0
-  const int last_tok = qb * 128 + 127 < a.q_len - 1 ? qb * 128 + 127 : a.q_len - 1;
+  const int last_tok = qb * 64 + 63 < a.q_len - 1 ? qb * 64 + 63 : a.q_len - 1;
   const int nblk = (base_pos + last_tok) / 64 + 1;
-  const int wlast = tok0 + 31 < a.q_len - 1 ? tok0 + 31 : a.q_len - 1;
+  const int wlast = tok0 + 15 < a.q_len - 1 ? tok0 + 15 : a.q_len - 1;
   const int wblk = tok0 < a.q_len ? (base_pos + wlast) / 64 + 1 : 0;  // blocks this wave multiplies
   const int wfirst_pos = base_pos + tok0;
-  const int pos_j = base_pos + tok;
+  const int pos_i = base_pos + tok;
 
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.Kc, a, sl, g, kl, D);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.Vc, a, sl, g, kl, D);
@@ -384,21 +423,21 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a, int nqb) 
 
   uint4 qf[KS];
   {
-    const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + tok) * a.ldqkv + (int64_t)h * D + 8 * h2;
+    const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + tok) * a.ldqkv + (int64_t)h * D + 8 * g4;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) qf[k] = row_ok ? *reinterpret_cast<const uint4*>(qp + 16 * k) : make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < KS; ++k) qf[k] = row_ok ? *reinterpret_cast<const uint4*>(qp + 32 * k) : make_uint4(0, 0, 0, 0);
   }
-  f32x16_t o[DB];
+  f32x4_t o[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
+  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Running max of the scaled scores (log2 domain) and sum, per token column.
+  // Block 0 always holds position 0, visible to every token, so m is finite
+  // from the first block on and exp2 of a masked (-inf) score is exactly 0.
   float m = -INFINITY, l = 0.f;
+  const float c = a.qscale;
 
-  // Fragment bases: K row 32 b + j, slot 2 k + h2; V (transposed reads) row
-  // 16 k' + 4 h2 + jj / 4 (+ 8), slot 4 db + 2 u + (jj % 4) / 2, half jj % 2,
-  // where the lane is 32 h2 + 16 u + jj.
-  const int jj = j & 15, uu = j >> 4;
-  const int kfb = (j * C::KP + h2) * 16;
-  const int vfb = C::KSL * 16 + ((4 * h2 + (jj >> 2)) * C::VP + 2 * uu + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
+  const int kfb = (i * C::KP + g4) * 16;
+  const int vfb = C::KSL * 16 + ((4 * g4 + (i >> 2)) * C::VP + ((i & 3) >> 1)) * 16 + (i & 1) * 8;
 
   AP_ISSUE(0, 0)
   if (nblk > 1) AP_ISSUE(1, 1)
@@ -411,57 +450,65 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a, int nqb) 
     __builtin_amdgcn_s_barrier();
     if (blk < wblk) {
       const char* L = (const char*)Ls[buf];
-      f32x16_t sa[2] = {f32x16_t{}, f32x16_t{}};
+      f32x4_t sc[4];
 #pragma unroll
-      for (int k = 0; k < KS; ++k)
+      for (int b = 0; b < 4; ++b) {
+        sc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const uint4 kf = *reinterpret_cast<const uint4*>(L + kfb + (32 * b * C::KP + 2 * k) * 16);
-          sa[b] = mfma_32x32x16(kf, qf[k], sa[b]);
+        for (int k = 0; k < KS; ++k) {
+          const uint4 kf = *reinterpret_cast<const uint4*>(L + kfb + (16 * b * C::KP + 4 * k) * 16);
+          sc[b] = mfma_16x16x32(kf, qf[k], sc[b]);
         }
-      // Lane (h2, j), element 4 q + r of block b: position 64 blk + 32 b + 8 q + 4 h2 + r.
-      const bool diag = blk * 64 + 63 > wfirst_pos;
+      }
+      // Lane (g4, i) holds token i's raw scores at positions 64 blk + 16 b + 4 g4 + r.
+      if (blk * 64 + 63 > wfirst_pos) {  // a diagonal block: mask what lies past the token
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (blk * 64 + 16 * b + 4 * g4 + r > pos_i) sc[b][r] = -INFINITY;
+      }
       float bm = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int p = blk * 64 + 32 * b + 8 * (e >> 2) + 4 * h2 + (e & 3);
-          const float v = (!diag || p <= pos_j) ? sa[b][e] * a.qscale : -INFINITY;
-          sa[b][e] = v;
-          bm = fmaxf(bm, v);
-        }
+      for (int b = 0; b < 4; ++b) bm = fmaxf(bm, fmaxf(fmaxf(sc[b][0], sc[b][1]), fmaxf(sc[b][2], sc[b][3])));
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m, bm);
-      const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+      const float mn = fmaxf(m, bm * c);
       float rs = 0.f;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float pe = sa[b][e] == -INFINITY ? 0.f : exp2f(sa[b][e] - mn);
-          sa[b][e] = pe;
+        for (int r = 0; r < 4; ++r) {
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], c, -mn));
+          sc[b][r] = pe;
           rs += pe;
         }
+      rs += __shfl_xor(rs, 16);
       rs += __shfl_xor(rs, 32);
-      l = l * alpha + rs;
+      if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {  // some token's max moved: rescale
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
+      l += rs;
       m = mn;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int b = kk >> 1, q0 = 2 * (kk & 1);
-        const float pe[8] = {sa[b][4 * q0],     sa[b][4 * q0 + 1], sa[b][4 * q0 + 2], sa[b][4 * q0 + 3],
-                             sa[b][4 * q0 + 4], sa[b][4 * q0 + 5], sa[b][4 * q0 + 6], sa[b][4 * q0 + 7]};
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const float pe[8] = {sc[2 * t2][0],     sc[2 * t2][1],     sc[2 * t2][2],     sc[2 * t2][3],
+                             sc[2 * t2 + 1][0], sc[2 * t2 + 1][1], sc[2 * t2 + 1][2], sc[2 * t2 + 1][3]};
         uint4 ph, pl;
         split8(pe, ph, pl);
+        uint4 vf[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const char* v0 = L + vfb + (16 * kk * C::VP + 4 * db) * 16;
-          const uint4 vf = tr_pair(v0, v0 + 8 * C::VP * 16);
-          o[db] = mfma_32x32x16(vf, ph, o[db]);
-          o[db] = mfma_32x32x16(vf, pl, o[db]);
+          const char* v0 = L + vfb + (32 * t2 * C::VP + 2 * db) * 16;
+          vf[db] = tr_pair(v0, v0 + 16 * C::VP * 16);
         }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = mfma_16x16x32(vf[db], ph, o[db]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = mfma_16x16x32(vf[db], pl, o[db]);
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -473,13 +520,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a, int nqb) 
 
   if (row_ok) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    // Lane (h2, j), element 4 q + r of block db: column 32 db + 8 q + 4 h2 + r of token j.
+    // Lane (g4, i), element r of block db: column 16 db + 4 g4 + r of token i.
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        store_bf16x4(out + 32 * db + 8 * q + 4 * h2, o[db][4 * q] * inv, o[db][4 * q + 1] * inv,
-                     o[db][4 * q + 2] * inv, o[db][4 * q + 3] * inv);
+      store_bf16x4(out + 16 * db + 4 * g4, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
   }
 }
 
@@ -489,8 +533,8 @@ hipError_t launch_attention_d(const AttnArgs& a, bool decode, hipStream_t s) {
     hipLaunchKernelGGL(attn_decode_kernel<D>, dim3(a.nchunk, a.nkv, a.S), dim3(256), 0, s, a);
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(a.G * a.q_len, a.nkv, a.S), dim3(D), 0, s, a);
   } else {
-    const int nqb = (a.q_len + 127) / 128;
-    hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(nqb, a.nq, a.S), dim3(256), 0, s, a, nqb);
+    const int nqb = (a.q_len + 63) / 64;
+    hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(nqb * a.nq * a.S), dim3(256), 0, s, a, nqb);
   }
   return hipGetLastError();
 }
