@@ -16,8 +16,9 @@
 //    workgroup reads its chunk of one key-value head once for all those rows,
 //    and the combine kernel merges the chunks' softmax partials.
 //  * attn_prefill_kernel: many new tokens. 64 query tokens of one head per
-//    workgroup, key-value blocks of 64 positions shared through LDS, online
-//    softmax.
+//    workgroup of two wavefront groups that split the causal chain of
+//    64-position key-value blocks (shared through LDS) between them, online
+//    softmax, merged at the end.
 //
 // Precision: q k^T accumulates in fp32 from bf16; the softmax runs in fp32
 // (exp2 with log2(e) folded into the scale). The probabilities enter the
@@ -76,6 +77,27 @@ __device__ __forceinline__ void split8(const float (&p)[8], uint4& hi, uint4& lo
   }
   hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
   lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+}
+
+// Max / sum of x over lanes l and l ^ 16, and over l and l ^ 32: gfx950's
+// v_permlane16_swap / v_permlane32_swap of x with itself leave {x[l],
+// x[l ^ 16]} (resp. ^ 32) in the pair of results, in the same order on both
+// lanes, so partners get bit-identical values.
+__device__ __forceinline__ float max16(float x) {
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float max32(float x) {
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float sum16(float x) {
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+__device__ __forceinline__ float sum32(float x) {
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 // A sequence's cache length, or 0 when its kv_len or slot is out of range
@@ -200,8 +222,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
         if (!(p < kl && p <= pos_r)) sc[b][r] = -INFINITY;
         bm = fmaxf(bm, sc[b][r]);
       }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    bm = max32(max16(bm));
     mx = bm * a.qscale;  // -inf when the row sees none of these positions
     const float ms = mx == -INFINITY ? 0.f : mx;
 #pragma unroll
@@ -212,8 +233,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
         sc[b][r] = e;
         l += e;
       }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = sum32(sum16(l));
 
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's V has landed
     const char* vb = (const char*)Vs[wave] + ((4 * g4 + (i >> 2)) * PITCH + ((i & 3) >> 1)) * 16 + (i & 1) * 8;
@@ -328,19 +348,19 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill. A workgroup of 4 wavefronts takes 64 query tokens of one query
-// head; wavefront w takes tokens 64 qb + 16 w + i, i = lane % 16, the column
-// of its 16x16x32 operands (the decode kernel's layout, one head per column
-// set instead of a group). Key-value blocks of 64 positions land in LDS by
-// DMA, double buffered: K rows at a pitch of D/8 + 1 16-byte slots (the A
-// operand of S^T read whole: 16 rows per instruction on distinct banks), V
-// rows at D/8 + 2 (transposed reads, as in decode). A stage's DMA
-// instructions are padded to a multiple of 4 so that every wave issues the
-// same count; the padding fills a spare kilobyte with zeros.
-// Work order: units (query block, head, sequence) sorted by causal length,
-// longest first; workgroup b < half takes unit b and workgroup half + b unit
-// total - 1 - b, so a CU that runs workgroups b and half + b together gets
-// one long and one short unit.
+// Prefill. A workgroup of 8 wavefronts takes 64 query tokens of one query
+// head. Wavefront w belongs to group w / 4 and takes tokens 64 qb + 16 (w % 4)
+// + i, i = lane % 16, the column of its 16x16x32 operands (the decode
+// kernel's layout). Group gr multiplies key-value blocks gr, gr + 2, ... of 64
+// positions, so each group runs half of the causal chain; at the end group 1
+// hands its (max, sum, output) to group 0 through LDS and group 0 merges and
+// stores. Each group has its own pair of LDS stages, filled by DMA: K rows at
+// a pitch of D/8 + 1 16-byte slots (the A operand of S^T read whole: 16 rows
+// per instruction on distinct banks), V rows at D/8 + 2 (transposed reads,
+// as in decode). A stage's DMA instructions are padded to a multiple of 4 so
+// that every wave issues the same count; the padding fills a spare kilobyte
+// with zeros. Workgroups take units (query block, head, sequence) longest
+// first.
 
 template <int D>
 struct PrefillCfg {
@@ -350,33 +370,33 @@ struct PrefillCfg {
   static constexpr int NU = (NDMA + 3) / 4;  // DMA instructions per wave and stage
   static constexpr int STAGE = NU * 4 * 64;  // slots, with the padding
   static_assert(KSL % 64 == 0 && VSL % 64 == 0, "a DMA instruction stays within K or V");
+  static_assert(4 * 16 * (D + 2) * 4 <= 2 * STAGE * 16, "group 1's partials fit in its stages");
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int nqb) {
+__global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nqb) {
   using C = PrefillCfg<D>;
   constexpr int KS = D / 32;  // 32-deep k-steps of q k^T
   constexpr int DB = D / 16;  // 16-column output blocks
   constexpr int CPR = D / 8;
-  __shared__ uint4 Ls[2][C::STAGE];
+  __shared__ uint4 Ls[2][2][C::STAGE];  // [group][stage]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gr = wave >> 2, wq = wave & 3;
   const int g4 = lane >> 4, i = lane & 15;
-  const int total = (int)gridDim.x, half = (total + 1) / 2;
-  const int bid = (int)blockIdx.x;
-  const int unit = bid < half ? bid : total - 1 - (bid - half);
+  const int unit = (int)blockIdx.x;
   const int per = a.nq * a.S;
   const int qb = nqb - 1 - unit / per, h = (unit % per) % a.nq, s = (unit % per) / a.nq;
   const int g = h / a.G;
   int sl;
   const int kl = seq_len(a, s, sl);
-  const int tok0 = qb * 64 + wave * 16;
+  const int tok0 = qb * 64 + wq * 16;
   const int tok = tok0 + i;
   const bool row_ok = tok < a.q_len;
   uint16_t* out = a.A + ((int64_t)s * a.q_len + tok) * a.lda + (int64_t)h * D;
   if (kl == 0) {  // uniform over the workgroup: a sequence out of range gives zeros
-    if (row_ok)
+    if (row_ok && gr == 0)
 #pragma unroll
       for (int db = 0; db < DB; ++db) store_bf16x4(out + 16 * db + 4 * g4, 0.f, 0.f, 0.f, 0.f);
     return;
@@ -384,18 +404,19 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int nq
   const int base_pos = kl - a.q_len;  // position of token 0
   const int last_tok = qb * 64 + 63 < a.q_len - 1 ? qb * 64 + 63 : a.q_len - 1;
   const int nblk = (base_pos + last_tok) / 64 + 1;
+  const int nstep = (nblk + 1) / 2;
   const int wlast = tok0 + 15 < a.q_len - 1 ? tok0 + 15 : a.q_len - 1;
-  const int wblk = tok0 < a.q_len ? (base_pos + wlast) / 64 + 1 : 0;  // blocks this wave multiplies
+  const int wblk = tok0 < a.q_len ? (base_pos + wlast) / 64 + 1 : 0;  // blocks this wave's tokens see
   const int wfirst_pos = base_pos + tok0;
   const int pos_i = base_pos + tok;
 
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.Kc, a, sl, g, kl, D);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.Vc, a, sl, g, kl, D);
-  // DMA: instruction n = 4 u + wave of a stage fills slots 64 n + lane.
+  // DMA: instruction n = 4 u + wq of a stage fills slots 64 n + lane.
   unsigned off[C::NU];
 #pragma unroll
   for (int u = 0; u < C::NU; ++u) {
-    const int n = 4 * u + wave;
+    const int n = 4 * u + wq;
     int q = n * 64 + lane;
     unsigned o = 0x80000000u;
     if (n * 64 < C::KSL) {
@@ -408,16 +429,18 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int nq
     }
     off[u] = o;
   }
-#define AP_ISSUE(BUF, BLK)                                                                         \
+  // Step t of this group: block 2 t + gr into stage t & 1 (blocks past the
+  // end read as zeros: their offsets pass the range, and nothing uses them).
+#define AP_ISSUE(ST, T)                                                                            \
   {                                                                                                \
-    const unsigned bo_ = (unsigned)((BLK) * 64 * D * 2);                                           \
+    const unsigned bo_ = (unsigned)((2 * (T) + gr) * 64 * D * 2);                                  \
     _Pragma("unroll") for (int u = 0; u < C::NU; ++u) {                                            \
-      const int n = 4 * u + wave;                                                                  \
+      const int n = 4 * u + wq;                                                                    \
       const unsigned o_ = off[u] >= 0x80000000u ? off[u] : off[u] + bo_;                           \
       if (n * 64 < C::KSL) /* wave-uniform */                                                      \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&Ls[BUF][n * 64], 16, o_, 0, 0, 0); \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&Ls[gr][ST][n * 64], 16, o_, 0, 0, 0); \
       else                                                                                         \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&Ls[BUF][n * 64], 16, o_, 0, 0, 0); \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&Ls[gr][ST][n * 64], 16, o_, 0, 0, 0); \
     }                                                                                              \
   }
 
@@ -431,8 +454,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int nq
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // Running max of the scaled scores (log2 domain) and sum, per token column.
-  // Block 0 always holds position 0, visible to every token, so m is finite
-  // from the first block on and exp2 of a masked (-inf) score is exactly 0.
+  // Group 1 starts at block 1, which tokens before position 64 do not see:
+  // while a token's max is still -inf the exponents subtract 0 instead, so a
+  // masked (-inf) score gives exp2 = 0 and no -inf - -inf arises.
   float m = -INFINITY, l = 0.f;
   const float c = a.qscale;
 
@@ -440,16 +464,16 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int nq
   const int vfb = C::KSL * 16 + ((4 * g4 + (i >> 2)) * C::VP + ((i & 3) >> 1)) * 16 + (i & 1) * 8;
 
   AP_ISSUE(0, 0)
-  if (nblk > 1) AP_ISSUE(1, 1)
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int buf = blk & 1;
-    if (blk + 1 < nblk)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | C::NU);  // vmcnt(NU): block blk has landed, blk + 1 may fly
+  if (nstep > 1) AP_ISSUE(1, 1)
+  for (int t = 0; t < nstep; ++t) {
+    const int st = t & 1, blk = 2 * t + gr;
+    if (t + 1 < nstep)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | C::NU);  // vmcnt(NU): step t has landed, t + 1 may fly
     else
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __builtin_amdgcn_s_barrier();
     if (blk < wblk) {
-      const char* L = (const char*)Ls[buf];
+      const char* L = (const char*)Ls[gr][st];
       f32x4_t sc[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
@@ -471,22 +495,21 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int nq
       float bm = -INFINITY;
 #pragma unroll
       for (int b = 0; b < 4; ++b) bm = fmaxf(bm, fmaxf(fmaxf(sc[b][0], sc[b][1]), fmaxf(sc[b][2], sc[b][3])));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      bm = max32(max16(bm));
       const float mn = fmaxf(m, bm * c);
+      const float ms = mn == -INFINITY ? 0.f : mn;
       float rs = 0.f;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], c, -mn));
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], c, -ms));
           sc[b][r] = pe;
           rs += pe;
         }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
+      rs = sum32(sum16(rs));
       if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {  // some token's max moved: rescale
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        const float alpha = __builtin_amdgcn_exp2f(m - ms);
         l *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
@@ -512,18 +535,39 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int nq
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();  // every wave is done with buffer buf
-    if (blk + 2 < nblk) AP_ISSUE(buf, blk + 2)
+    __builtin_amdgcn_s_barrier();  // every wave is done with stage st
+    if (t + 2 < nstep) AP_ISSUE(st, t + 2)
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #undef AP_ISSUE
 
-  if (row_ok) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    // Lane (g4, i), element r of block db: column 16 db + 4 g4 + r of token i.
+  // Group 1's partials into its own stages ([wq][16 tokens][D] then m, l),
+  // then group 0 merges. Lane (g4, i), element r of block db: column
+  // 16 db + 4 g4 + r of token i.
+  float* red = reinterpret_cast<float*>(Ls[1][0]) + wq * 16 * (D + 2);
+  if (gr == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      store_bf16x4(out + 16 * db + 4 * g4, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[i * D + 16 * db + 4 * g4 + r] = o[db][r];
+    if (g4 == 0) {
+      red[16 * D + i] = m;
+      red[16 * D + 16 + i] = l;
+    }
+  }
+  __syncthreads();
+  if (gr == 0 && row_ok) {
+    const float m1 = red[16 * D + i], l1 = red[16 * D + 16 + i];
+    const float M = fmaxf(m, m1);
+    const float f0 = __builtin_amdgcn_exp2f(m - M), f1 = __builtin_amdgcn_exp2f(m1 - M);
+    const float L = f0 * l + f1 * l1;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const float* o1 = red + i * D + 16 * db + 4 * g4;
+      store_bf16x4(out + 16 * db + 4 * g4, (f0 * o[db][0] + f1 * o1[0]) * inv, (f0 * o[db][1] + f1 * o1[1]) * inv,
+                   (f0 * o[db][2] + f1 * o1[2]) * inv, (f0 * o[db][3] + f1 * o1[3]) * inv);
+    }
   }
 }
 
@@ -534,7 +578,7 @@ hipError_t launch_attention_d(const AttnArgs& a, bool decode, hipStream_t s) {
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(a.G * a.q_len, a.nkv, a.S), dim3(D), 0, s, a);
   } else {
     const int nqb = (a.q_len + 63) / 64;
-    hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(nqb * a.nq * a.S), dim3(256), 0, s, a, nqb);
+    hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(nqb * a.nq * a.S), dim3(512), 0, s, a, nqb);
   }
   return hipGetLastError();
 }
