@@ -388,7 +388,7 @@ TP_API tp_status tp_kv_append(const tp_shard_desc* qkv, const uint16_t* QKV, int
  * Scores and softmax in fp32; the probabilities enter the product with V as
  * two bf16 terms (hi + lo); output rounded once to bf16.
  * When (n_q_r / n_kv_r) q_len <= 16 (decode) the cache is read in chunks of
- * 256 positions, each once per key-value head, and the chunks' partials
+ * 512 positions, each once per key-value head, and the chunks' partials
  * (fp32) go to the workspace: tp_attention_workspace_bytes bytes
  * (TP_ERR_WORKSPACE if short); otherwise no workspace is used.
  */

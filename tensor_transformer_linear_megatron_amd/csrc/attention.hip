@@ -12,7 +12,7 @@
 //  * kv_append_kernel: the new tokens' K and V rows into their cache slots.
 //  * attn_decode_kernel + attn_combine_kernel: few new tokens per sequence
 //    (the rank's query heads of one key-value head times the new tokens fit
-//    in 16 rows). The cache is split into chunks of 256 positions; each
+//    in 16 rows). The cache is split into chunks of 512 positions; each
 //    workgroup reads its chunk of one key-value head once for all those rows,
 //    and the combine kernel merges the chunks' softmax partials.
 //  * attn_prefill_kernel: many new tokens. 64 query tokens of one head per
@@ -144,14 +144,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AttnArgs a, int64_t tota
 }
 
 // ---------------------------------------------------------------------------
-// Decode. Workgroup (chunk, g, s) of 4 wavefronts; wavefront w takes positions
-// [256 chunk + 64 w, + 64). Row rho (< 16) of the 16x16x32 operands is query
-// head g G + rho / q_len of token rho % q_len. K fragments come straight from
-// the cache into registers (A operand rows = positions); V lands in the
-// wavefront's own LDS region by DMA at a pitch of D/8 + 2 16-byte slots, which
-// puts the four rows each 16-lane group reads on distinct banks. The four
-// wavefronts' partials merge through LDS into one per workgroup:
-// m[rho] (log2 domain), l[rho] and the unnormalised output [rho][D].
+// Decode. Workgroup (chunk, g, s) of 4 wavefronts; wavefront w takes the two
+// 64-position halves [512 chunk + 64 (4 hb + w), + 64), hb = 0, 1. Row rho
+// (< 16) of the 16x16x32 operands is query head g G + rho / q_len of token
+// rho % q_len. K fragments come straight from the cache into registers (A
+// operand rows = positions); V lands in the wavefront's own LDS region by DMA
+// at a pitch of D/8 + 2 16-byte slots, which puts the four rows each 16-lane
+// group reads on distinct banks. Loads go out as Q, K0, V0, K1, V1, so half 0
+// is multiplied while half 1 is still arriving (online softmax across the
+// two). The four wavefronts' partials merge through LDS into one per
+// workgroup: m[rho] (log2 domain), l[rho] and the unnormalised output
+// [rho][D].
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
@@ -159,10 +162,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   constexpr int DB = D / 16;     // 16-column output blocks
   constexpr int CPR = D / 8;     // 16-byte chunks per cache row
   constexpr int PITCH = CPR + 2;
-  constexpr int WPOS = 64;
+  constexpr int HPOS = 64;       // positions per half
+  constexpr int HSL = HPOS * PITCH;  // LDS slots per half (a multiple of 64)
   constexpr int RED = kAttnDecodeRows * D + 2 * kAttnDecodeRows;
-  static_assert(RED * 4 <= WPOS * PITCH * 16, "a wave's partial fits in its V region");
-  __shared__ uint4 Vs[4][WPOS * PITCH];
+  static_assert(kAttnDecodeChunk == 2 * 4 * HPOS, "two halves per wavefront");
+  static_assert(RED * 4 <= HSL * 16, "a wave's partial fits in its half-0 V region");
+  // One array per half: the compiler then tracks the two halves' DMA apart
+  // and lets half 1 fly while half 0's V is read.
+  __shared__ uint4 Vs0[4][HSL], Vs1[4][HSL];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -171,8 +178,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   int sl;
   const int kl = seq_len(a, s, sl);
   const int R = a.G * a.q_len;
-  const int p0 = chunk * kAttnDecodeChunk + wave * WPOS;
-  const bool active = p0 < kl;
+  const int pc = chunk * kAttnDecodeChunk + wave * HPOS;  // half hb starts at pc + 256 hb
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.Kc, a, sl, g, kl, D);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.Vc, a, sl, g, kl, D);
 
@@ -180,89 +186,126 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   const int hh = rho / a.q_len, tok = rho - hh * a.q_len;
   const bool row_ok = kl > 0 && rho < R;
   const int pos_r = kl - a.q_len + tok;
-  float mx = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;
   f32x4_t o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (active) {
-    // K fragments first (the first MFMAs wait on them alone), then V's DMA.
-    uint4 kf[4][KS];
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int k = 0; k < KS; ++k)
-        kf[b][k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rk, (unsigned)(((p0 + 16 * b + i) * D + 32 * k + 8 * g4) * 2), 0, 0));
-#pragma unroll
-    for (int u = 0; u < PITCH; ++u) {
-      const int q = u * 64 + lane, row = q / PITCH, c = q - row * PITCH;
-      const unsigned off = c < CPR ? (unsigned)(((p0 + row) * D + 8 * c) * 2) : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&Vs[wave][u * 64], 16, off, 0, 0, 0);
-    }
+  if (pc < kl) {  // wave-uniform: at least half 0 holds positions
+    uint4 kf[2][4][KS];
+#define AD_KLOAD(HB)                                                                               \
+  _Pragma("unroll") for (int b = 0; b < 4; ++b) _Pragma("unroll") for (int k = 0; k < KS; ++k)    \
+      kf[HB][b][k] = __builtin_bit_cast(                                                           \
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(                                            \
+                     rk, (unsigned)(((pc + 4 * HPOS * (HB) + 16 * b + i) * D + 32 * k + 8 * g4) * 2), 0, 0));
+#define AD_VLOAD(HB, VS)                                                                           \
+  _Pragma("unroll") for (int u = 0; u < PITCH; ++u) {                                              \
+    const int q = u * 64 + lane, row = q / PITCH, c = q - row * PITCH;                             \
+    const unsigned off = c < CPR ? (unsigned)(((pc + 4 * HPOS * (HB) + row) * D + 8 * c) * 2) : 0x80000000u; \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&VS[wave][u * 64], 16, off, 0, 0, 0); \
+  }
+    // Issue order Q, K0, V0, K1, V1 (kept by the scheduling barriers): the
+    // wait before half 0's V leaves exactly K1 and V1 in flight. Q rows past
+    // R read row 0 (always in range) and are zeroed after the load, so no
+    // load sits behind a branch.
     uint4 qf[KS];
-    const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + tok) * a.ldqkv + (int64_t)(g * a.G + hh) * D + 8 * g4;
+    const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + (row_ok ? tok : 0)) * a.ldqkv +
+                         (int64_t)(g * a.G + (row_ok ? hh : 0)) * D + 8 * g4;
 #pragma unroll
-    for (int k = 0; k < KS; ++k)
-      qf[k] = row_ok ? *reinterpret_cast<const uint4*>(qp + 32 * k) : make_uint4(0, 0, 0, 0);
-    f32x4_t sc[4];
+    for (int k = 0; k < KS; ++k) qf[k] = *reinterpret_cast<const uint4*>(qp + 32 * k);
+    __builtin_amdgcn_sched_barrier(0);
+    AD_KLOAD(0)
+    __builtin_amdgcn_sched_barrier(0);
+    AD_VLOAD(0, Vs0)
+    __builtin_amdgcn_sched_barrier(0);
+    // Half 1 unconditionally: past the cache its loads return zeros without
+    // touching memory and its scores are masked, and straight-line code keeps
+    // the compiler's own wait counts exact.
+    AD_KLOAD(1)
+    __builtin_amdgcn_sched_barrier(0);
+    AD_VLOAD(1, Vs1)
+    __builtin_amdgcn_sched_barrier(0);
+#undef AD_KLOAD
+#undef AD_VLOAD
+    const uint32_t qm = row_ok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      sc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < KS; ++k) qf[k] = make_uint4(qf[k].x & qm, qf[k].y & qm, qf[k].z & qm, qf[k].w & qm);
+    const int vfo = ((4 * g4 + (i >> 2)) * PITCH + ((i & 3) >> 1)) * 16 + (i & 1) * 8;
 #pragma unroll
-      for (int k = 0; k < KS; ++k) sc[b] = mfma_16x16x32(kf[b][k], qf[k], sc[b]);
-    }
-    // Lane (g4, i) holds row i's raw scores at positions p0 + 16 b + 4 g4 + r.
-    float bm = -INFINITY;
+    for (int hb = 0; hb < 2; ++hb) {
+      const int p0 = pc + 4 * HPOS * hb;
+      f32x4_t sc[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 4; ++b) {
+        sc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = p0 + 16 * b + 4 * g4 + r;
-        if (!(p < kl && p <= pos_r)) sc[b][r] = -INFINITY;
-        bm = fmaxf(bm, sc[b][r]);
+        for (int k = 0; k < KS; ++k) sc[b] = mfma_16x16x32(kf[hb][b][k], qf[k], sc[b]);
       }
-    bm = max32(max16(bm));
-    mx = bm * a.qscale;  // -inf when the row sees none of these positions
-    const float ms = mx == -INFINITY ? 0.f : mx;
+      // Lane (g4, i) holds row i's raw scores at positions p0 + 16 b + 4 g4 + r.
+      float bm = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], a.qscale, -ms));
-        sc[b][r] = e;
-        l += e;
+        for (int r = 0; r < 4; ++r) {
+          const int p = p0 + 16 * b + 4 * g4 + r;
+          if (!(p < kl && p <= pos_r)) sc[b][r] = -INFINITY;
+          bm = fmaxf(bm, sc[b][r]);
+        }
+      bm = max32(max16(bm));
+      const float mn = fmaxf(m, bm * a.qscale);  // -inf while the row has seen no position
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      float rs = 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], a.qscale, -ms));
+          sc[b][r] = e;
+          rs += e;
+        }
+      rs = sum32(sum16(rs));
+      if (hb == 1) {
+        const float alpha = __builtin_amdgcn_exp2f(m - ms);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
       }
-    l = sum32(sum16(l));
-
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's V has landed
-    const char* vb = (const char*)Vs[wave] + ((4 * g4 + (i >> 2)) * PITCH + ((i & 3) >> 1)) * 16 + (i & 1) * 8;
+      l += rs;
+      m = mn;
+      // V of this half has landed: after half 0 only K1 and V1 may still fly.
+      if (hb == 0)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * KS + PITCH) & 15) | (((4 * KS + PITCH) >> 4) << 14));
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      const char* vh = (const char*)(hb == 0 ? Vs0[wave] : Vs1[wave]) + vfo;
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const float pe[8] = {sc[2 * t2][0],     sc[2 * t2][1],     sc[2 * t2][2],     sc[2 * t2][3],
-                           sc[2 * t2 + 1][0], sc[2 * t2 + 1][1], sc[2 * t2 + 1][2], sc[2 * t2 + 1][3]};
-      uint4 ph, pl;
-      split8(pe, ph, pl);
-      uint4 vf[DB];
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const float pe[8] = {sc[2 * t2][0],     sc[2 * t2][1],     sc[2 * t2][2],     sc[2 * t2][3],
+                             sc[2 * t2 + 1][0], sc[2 * t2 + 1][1], sc[2 * t2 + 1][2], sc[2 * t2 + 1][3]};
+        uint4 ph, pl;
+        split8(pe, ph, pl);
+        uint4 vf[DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        vf[db] = tr_pair(vb + (32 * t2 * PITCH + 2 * db) * 16, vb + ((32 * t2 + 16) * PITCH + 2 * db) * 16);
+        for (int db = 0; db < DB; ++db)
+          vf[db] = tr_pair(vh + (32 * t2 * PITCH + 2 * db) * 16, vh + ((32 * t2 + 16) * PITCH + 2 * db) * 16);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] = mfma_16x16x32(vf[db], ph, o[db]);
+        for (int db = 0; db < DB; ++db) o[db] = mfma_16x16x32(vf[db], ph, o[db]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] = mfma_16x16x32(vf[db], pl, o[db]);
+        for (int db = 0; db < DB; ++db) o[db] = mfma_16x16x32(vf[db], pl, o[db]);
+      }
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   }
 
-  // This wave's partial into its own region (its reads of V are complete).
-  float* red = reinterpret_cast<float*>(Vs[wave]);
+  // This wave's partial into its own half-0 region (its reads of V are complete).
+  float* red = reinterpret_cast<float*>(Vs0[wave]);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[rho * D + 16 * db + 4 * g4 + r] = o[db][r];
   if (g4 == 0) {
-    red[kAttnDecodeRows * D + i] = mx;
+    red[kAttnDecodeRows * D + i] = m;
     red[kAttnDecodeRows * D + kAttnDecodeRows + i] = l;
   }
   __syncthreads();
@@ -273,14 +316,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   float mw[4], M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    mw[w] = reinterpret_cast<const float*>(Vs[w])[kAttnDecodeRows * D + row];
+    mw[w] = reinterpret_cast<const float*>(Vs0[w])[kAttnDecodeRows * D + row];
     M = fmaxf(M, mw[w]);
   }
   float L = 0.f, f[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    f[w] = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - M);
-    L += f[w] * reinterpret_cast<const float*>(Vs[w])[kAttnDecodeRows * D + kAttnDecodeRows + row];
+    f[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+    L += f[w] * reinterpret_cast<const float*>(Vs0[w])[kAttnDecodeRows * D + kAttnDecodeRows + row];
   }
   float* P = a.ws + (((int64_t)s * a.nkv + g) * a.nchunk + chunk) * RED;
   if ((t & 15) == 0) {
@@ -291,14 +334,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   for (int c = 0; c < CW; ++c) {
     float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) acc += f[w] * reinterpret_cast<const float*>(Vs[w])[row * D + c0 + c];
+    for (int w = 0; w < 4; ++w) acc += f[w] * reinterpret_cast<const float*>(Vs0[w])[row * D + c0 + c];
     P[row * D + c0 + c] = acc;
   }
 }
 
 // Workgroup (rho, g, s), thread c: output column c of row rho, merged over
-// the chunks in chunk order. The chunks' maxima and sums are fetched a tile
-// of D chunks at a time, one per thread, and shared through LDS.
+// the chunks in chunk order. Up to kCombineRegs chunks, every load goes out in
+// one batch (each thread holds the chunks' maxima, sums and its column);
+// beyond that the chunks' maxima and sums are fetched a tile of D chunks at a
+// time, one per thread, and shared through LDS.
+constexpr int kCombineRegs = 32;
+
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   constexpr int RED = kAttnDecodeRows * D + 2 * kAttnDecodeRows;
@@ -308,6 +355,34 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   int sl;
   const int kl = seq_len(a, s, sl);
   const float* P0 = a.ws + ((int64_t)s * a.nkv + g) * a.nchunk * RED;
+  const int hh = rho / a.q_len, tok = rho - hh * a.q_len;
+  uint16_t* dst = a.A + ((int64_t)s * a.q_len + tok) * a.lda + (int64_t)(g * a.G + hh) * D + c;
+  if (a.nchunk <= kCombineRegs) {  // uniform
+    float mc[kCombineRegs], lc[kCombineRegs], oc[kCombineRegs];
+#pragma unroll
+    for (int j = 0; j < kCombineRegs; ++j) {
+      if (j < a.nchunk) {
+        const float* Pj = P0 + (int64_t)j * RED;
+        mc[j] = Pj[kAttnDecodeRows * D + rho];
+        lc[j] = Pj[kAttnDecodeRows * D + kAttnDecodeRows + rho];
+        oc[j] = Pj[rho * D + c];
+      }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kCombineRegs; ++j)
+      if (j < a.nchunk) M = fmaxf(M, mc[j]);
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kCombineRegs; ++j)
+      if (j < a.nchunk && mc[j] != -INFINITY) {
+        const float f = __builtin_amdgcn_exp2f(mc[j] - M);
+        L += f * lc[j];
+        acc += f * oc[j];
+      }
+    *dst = f32_to_bf16(kl > 0 && L > 0.f ? acc / L : 0.f);
+    return;
+  }
   float M = -INFINITY;
   for (int ch = c; ch < a.nchunk; ch += D) M = fmaxf(M, P0[(int64_t)ch * RED + kAttnDecodeRows * D + rho]);
   red[c] = M;
@@ -323,10 +398,10 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
     const int ch = t0 + c;
     float f = 0.f;
     if (ch < a.nchunk) {
-      const float* P = P0 + (int64_t)ch * RED;
-      const float mc = P[kAttnDecodeRows * D + rho];
+      const float* Pj = P0 + (int64_t)ch * RED;
+      const float mc = Pj[kAttnDecodeRows * D + rho];
       f = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-      Lp += f * P[kAttnDecodeRows * D + kAttnDecodeRows + rho];
+      Lp += f * Pj[kAttnDecodeRows * D + kAttnDecodeRows + rho];
     }
     wgt[c] = f;
     __syncthreads();
@@ -342,9 +417,7 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
     __syncthreads();
   }
   const float L = red[0];
-  const int hh = rho / a.q_len, tok = rho - hh * a.q_len;
-  a.A[((int64_t)s * a.q_len + tok) * a.lda + (int64_t)(g * a.G + hh) * D + c] =
-      f32_to_bf16(kl > 0 && L > 0.f ? acc / L : 0.f);
+  *dst = f32_to_bf16(kl > 0 && L > 0.f ? acc / L : 0.f);
 }
 
 // ---------------------------------------------------------------------------

@@ -129,7 +129,7 @@ struct AttnArgs {
 };
 
 constexpr int kAttnDecodeRows = 16;    // query rows (heads x tokens) of one decode workgroup
-constexpr int kAttnDecodeChunk = 256;  // positions per decode workgroup
+constexpr int kAttnDecodeChunk = 512;  // positions per decode workgroup
 size_t attn_decode_ws_bytes(int64_t S, int64_t nkv, int64_t nchunk, int D);
 hipError_t launch_kv_append(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, bool decode, hipStream_t s);

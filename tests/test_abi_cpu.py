@@ -370,18 +370,18 @@ def test_kv_cache_and_attention_workspace_sizes():
     """Cache bytes: n_slots x n_kv_r x L_max x d x 2 per array; the rank's
     share is 1/t of the layer's key-value heads up to t = n_kv, then one
     repeated head. The decode form needs one partial (16 rows x (d + 2) fp32)
-    per sequence, key-value head and 256-position chunk."""
+    per sequence, key-value head and 512-position chunk."""
     for t, nkv in ((1, 8), (2, 4), (8, 1), (16, 1)):
         assert tp.tp_kv_cache_bytes(_qkv70(t, t - 1), 4, 4096) == 4 * nkv * 4096 * 128 * 2
     assert tp.tp_kv_cache_bytes(tp.tp_shard_plan("col", 64, 64, 1, 0), 1, 16) == 0
     assert tp.tp_kv_cache_bytes(tp.tp_shard_plan("qkv_col", 32, 12 * 16, 1, 0, heads=(8, 2, 16)), 1, 16) == 0  # d = 16
     assert tp.tp_kv_cache_bytes(_qkv70(8, 0), 1, 2 ** 23) == 0  # one head past 2^31 bytes
     q = _qkv70(8, 0)  # 8 query heads on one key-value head
-    assert tp.tp_attention_workspace_bytes(q, 32, 1, 4096) == 32 * 16 * (16 * 128 + 32) * 4
-    assert tp.tp_attention_workspace_bytes(q, 32, 2, 4097) == 32 * 17 * (16 * 128 + 32) * 4
+    assert tp.tp_attention_workspace_bytes(q, 32, 1, 4096) == 32 * 8 * (16 * 128 + 32) * 4
+    assert tp.tp_attention_workspace_bytes(q, 32, 2, 4097) == 32 * 9 * (16 * 128 + 32) * 4
     assert tp.tp_attention_workspace_bytes(q, 1, 3, 4096) == 0  # 24 rows: the prefill form
     q16 = _qkv70(16, 5)  # 4 query heads, repeated key-value head
-    assert tp.tp_attention_workspace_bytes(q16, 2, 4, 300) == 2 * 2 * (16 * 128 + 32) * 4
+    assert tp.tp_attention_workspace_bytes(q16, 2, 4, 300) == 2 * 1 * (16 * 128 + 32) * 4
     assert tp.tp_attention_workspace_bytes(q16, 2, 5, 300) == 0
 
 

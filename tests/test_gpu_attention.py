@@ -1,7 +1,7 @@
 """GPU parity of the attention core on a rank's heads and its KV-cache share:
 tp_kv_append against the oracle's append (bit-exact), tp_attention against
 the fp64 oracle (both rounded once to bf16) on the decode form (split over
-256-position chunks) and the prefill form, on several head layouts: grouped
+512-position chunks) and the prefill form, on several head layouts: grouped
 query heads at t = 2 and 8, a repeated key-value head at t = 16, d = 64 and
 128; ragged lengths, a prefill on top of an earlier cache, out-of-range
 sequences, and the 70B TP = 8 rank-0 shapes the benchmark times.
@@ -195,6 +195,16 @@ def test_out_of_range_sequence_gives_zero_rows(q_len):
     assert not A[q_len:].any()
     np.testing.assert_allclose(oracle.bf16_to_f64(A[:q_len]), oracle.bf16_to_f64(c.ref(range(q_len))),
                                rtol=1e-2, atol=1e-2)
+
+
+def test_decode_long_cache_merges_many_chunks():
+    """More chunks than the merge keeps in registers (17000 positions = 34
+    chunks of 512): the tiled merge path."""
+    say("decode long cache")
+    c = Case((64, 8, 128), 8, 0, 1, [17000, 300], [1, 0], 2, 17024, 497)
+    c.append()
+    rows = [0, 1]
+    assert_parity(host_f64(c.run())[rows], oracle.bf16_to_f64(c.ref(rows)), "long cache")
 
 
 def test_max_kv_above_every_length():
