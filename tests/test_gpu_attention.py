@@ -242,3 +242,67 @@ def test_llama70b_tp8_prefill_4096():
     A = host_bits(c.run())
     rows = [0, 1, 127, 128, 2047, 4000, 4095]
     assert_parity(oracle.bf16_to_f64(A[rows]), oracle.bf16_to_f64(c.ref(rows)), "70b prefill")
+
+
+# ---------------------------------------------------------------------------
+# The whole attention block of a layer, each rank's share through the
+# library, on a prefill chunk and then two decode steps.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("t", [2, 4])
+def test_attention_block_all_ranks(t):
+    """X -> QKV slice -> append -> attention -> O slice (fp32 partial), for
+    every rank, then the sum over the ranks; on a 40-token prefill of two
+    sequences and two decode steps after it. Compared with the oracle taking
+    the same steps, and with the unsharded block (t = 1) computed the same way
+    by the oracle."""
+    heads, hidden = (8, 2, 64), 192
+    n_q, n_kv, d = heads
+    S, T0, L = 2, 40, 64
+    Wq = si.normal_bf16(600, (hidden, (n_q + 2 * n_kv) * d), 0.08)
+    Wo = si.normal_bf16(601, (n_q * d, hidden), 0.08)
+    steps = [(T0, si.normal_bf16(602, (S * T0, hidden), 1.0)),
+             (1, si.normal_bf16(603, (S, hidden), 1.0)),
+             (1, si.normal_bf16(604, (S, hidden), 1.0))]
+    Wqd, Wod = dev(Wq), dev(Wo)
+    ranks = []
+    for r in range(t):
+        q = tp.tp_shard_plan("qkv_col", hidden, Wq.shape[1], t, r, heads=heads)
+        o = tp.tp_shard_plan("o_row", n_q * d, hidden, t, r, heads=heads)
+        pq = oracle.plan("qkv_col", hidden, Wq.shape[1], t, r, heads=heads)
+        po = oracle.plan("o_row", n_q * d, hidden, t, r, heads=heads)
+        Kd, Vd = tp.tp_kv_cache_new(q, S, L)
+        Kh, Vh = oracle.kv_cache_new(pq, S, L)
+        ranks.append(dict(q=q, o=o, pq=pq, po=po, qp=tp.tp_shard_pack(q, Wqd), op=tp.tp_shard_pack(o, Wod),
+                          Kd=Kd, Vd=Vd, Kh=Kh, Vh=Vh))
+    p1 = oracle.plan("qkv_col", hidden, Wq.shape[1], 1, 0, heads=heads)
+    o1 = oracle.plan("o_row", n_q * d, hidden, 1, 0, heads=heads)
+    K1, V1 = oracle.kv_cache_new(p1, S, L)
+    slot = [1, 0]
+    pos = 0
+    for q_len, X in steps:
+        say("attention block", t, q_len)
+        pos += q_len
+        kv_len = [pos] * S
+        P = torch.empty((t, S * q_len, hidden), dtype=torch.float32, device="cuda")
+        ref = np.zeros((S * q_len, hidden))
+        Xd = dev(X)
+        for r, R in enumerate(ranks):
+            QKV = tp.tp_col_linear(R["q"], Xd, R["qp"])
+            tp.tp_kv_append(R["q"], QKV, q_len, i32(kv_len), i32(slot), R["Kd"], R["Vd"])
+            A = tp.tp_attention(R["q"], QKV, q_len, i32(kv_len), i32(slot), R["Kd"], R["Vd"], L)
+            tp.tp_row_linear(R["o"], A, R["op"], P=P[r])
+            # the oracle, step by step
+            QKVh = oracle.col_linear_bf16(X, Wq, R["pq"])
+            oracle.kv_append(QKVh, R["pq"], q_len, kv_len, slot, R["Kh"], R["Vh"])
+            Ah = oracle.attention(QKVh, R["pq"], q_len, kv_len, slot, R["Kh"], R["Vh"])
+            ref += oracle.row_linear(Ah, Wo, R["po"])
+            assert_parity(host_f64(QKV), oracle.bf16_to_f64(QKVh), f"QKV_{r}")
+            assert_parity(host_f64(A), oracle.bf16_to_f64(Ah), f"A_{r}")
+        Y = host_f64(tp.tp_reduce_partials(P))
+        assert_parity(Y, ref, f"block t={t} q_len={q_len}")
+        # the unsharded layer: the heads concatenate, so the block is the same
+        QKV1 = oracle.col_linear_bf16(X, Wq, p1)
+        oracle.kv_append(QKV1, p1, q_len, kv_len, slot, K1, V1)
+        Y1 = oracle.row_linear(oracle.attention(QKV1, p1, q_len, kv_len, slot, K1, V1), Wo, o1)
+        assert_parity(Y, Y1, f"block t={t} vs unsharded")
