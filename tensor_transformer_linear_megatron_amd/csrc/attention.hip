@@ -16,8 +16,8 @@
 //    workgroup reads its chunk of one key-value head once for all those rows,
 //    and the combine kernel merges the chunks' softmax partials.
 //  * attn_prefill_kernel: many new tokens. 64 query tokens of one head per
-//    workgroup of two wavefront groups that split the causal chain of
-//    64-position key-value blocks (shared through LDS) between them, online
+//    workgroup of four wavefront groups that split the causal chain of
+//    32-position key-value blocks (shared through LDS) between them, online
 //    softmax, merged at the end.
 //
 // Precision: q k^T accumulates in fp32 from bf16; the softmax runs in fp32
@@ -166,7 +166,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   constexpr int HSL = HPOS * PITCH;  // LDS slots per half (a multiple of 64)
   constexpr int RED = kAttnDecodeRows * D + 2 * kAttnDecodeRows;
   static_assert(kAttnDecodeChunk == 2 * 4 * HPOS, "two halves per wavefront");
-  static_assert(RED * 4 <= HSL * 16, "a wave's partial fits in its half-0 V region");
+  static_assert((D * (kAttnDecodeRows + 1) + 2 * kAttnDecodeRows) * 4 <= HSL * 16,
+                "a wave's partial fits in its half-0 V region");
   // One array per half: the compiler then tracks the two halves' DMA apart
   // and lets half 1 fly while half 0's V is read.
   __shared__ uint4 Vs0[4][HSL], Vs1[4][HSL];
@@ -298,35 +299,39 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   }
 
-  // This wave's partial into its own half-0 region (its reads of V are complete).
+  // This wave's partial into its own half-0 region (its reads of V are
+  // complete), [D columns][17] (row rho at rho: the pitch of 17 keeps a
+  // column's 16 rows and the other lane groups' columns on distinct banks),
+  // then m, l.
+  constexpr int RP = kAttnDecodeRows + 1;
   float* red = reinterpret_cast<float*>(Vs0[wave]);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[rho * D + 16 * db + 4 * g4 + r] = o[db][r];
+    for (int r = 0; r < 4; ++r) red[(16 * db + 4 * g4 + r) * RP + rho] = o[db][r];
   if (g4 == 0) {
-    red[kAttnDecodeRows * D + i] = m;
-    red[kAttnDecodeRows * D + kAttnDecodeRows + i] = l;
+    red[D * RP + i] = m;
+    red[D * RP + kAttnDecodeRows + i] = l;
   }
   __syncthreads();
 
-  // Merge the four waves: thread t owns row t / 16, columns (t % 16) D / 16 ...
+  // Merge the four waves: thread t owns row t % 16, columns (t / 16) D / 16 ...
   constexpr int CW = D / 16;
-  const int t = threadIdx.x, row = t >> 4, c0 = (t & 15) * CW;
+  const int t = threadIdx.x, row = t & 15, c0 = (t >> 4) * CW;
   float mw[4], M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    mw[w] = reinterpret_cast<const float*>(Vs0[w])[kAttnDecodeRows * D + row];
+    mw[w] = reinterpret_cast<const float*>(Vs0[w])[D * RP + row];
     M = fmaxf(M, mw[w]);
   }
   float L = 0.f, f[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     f[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
-    L += f[w] * reinterpret_cast<const float*>(Vs0[w])[kAttnDecodeRows * D + kAttnDecodeRows + row];
+    L += f[w] * reinterpret_cast<const float*>(Vs0[w])[D * RP + kAttnDecodeRows + row];
   }
   float* P = a.ws + (((int64_t)s * a.nkv + g) * a.nchunk + chunk) * RED;
-  if ((t & 15) == 0) {
+  if (t < kAttnDecodeRows) {
     P[kAttnDecodeRows * D + row] = M;
     P[kAttnDecodeRows * D + kAttnDecodeRows + row] = L;
   }
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   for (int c = 0; c < CW; ++c) {
     float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) acc += f[w] * reinterpret_cast<const float*>(Vs0[w])[row * D + c0 + c];
+    for (int w = 0; w < 4; ++w) acc += f[w] * reinterpret_cast<const float*>(Vs0[w])[(c0 + c) * RP + row];
     P[row * D + c0 + c] = acc;
   }
 }
@@ -422,79 +427,83 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Prefill. A workgroup of 8 wavefronts takes 64 query tokens of one query
-// head. Wavefront w belongs to group w / 4 and takes tokens 64 qb + 16 (w % 4)
-// + i, i = lane % 16, the column of its 16x16x32 operands (the decode
-// kernel's layout). Group gr multiplies key-value blocks gr, gr + 2, ... of 64
-// positions, so each group runs half of the causal chain; at the end group 1
-// hands its (max, sum, output) to group 0 through LDS and group 0 merges and
-// stores. Each group has its own pair of LDS stages, filled by DMA: K rows at
-// a pitch of D/8 + 1 16-byte slots (the A operand of S^T read whole: 16 rows
-// per instruction on distinct banks), V rows at D/8 + 2 (transposed reads,
-// as in decode). A stage's DMA instructions are padded to a multiple of 4 so
-// that every wave issues the same count; the padding fills a spare kilobyte
-// with zeros. Workgroups take units (query block, head, sequence) longest
-// first.
+// head. Wavefront w belongs to group w / 2 and takes tokens 64 qb + 32 (w % 2)
+// + j, j = lane % 32, the column of its 32x32x16 operands. Group gr multiplies
+// key-value blocks gr, gr + 4, ... of 32 positions, so each group runs a
+// quarter of the causal chain; at the end groups 1..3 hand their (max, sum,
+// output) to group 0 through LDS and group 0 merges and stores. Each group has
+// its own pair of LDS stages, filled by DMA: 32 K rows at a pitch of D/8 + 1
+// 16-byte slots (the A operand of S^T read whole, 32 rows per half-wavefront
+// on distinct banks) in a region padded to whole DMA instructions, then 32 V
+// rows at D/8 + 4 (transposed reads). Workgroups take units (query block,
+// head, sequence) longest first.
 
 template <int D>
 struct PrefillCfg {
-  static constexpr int KP = D / 8 + 1, VP = D / 8 + 2;
-  static constexpr int KSL = 64 * KP, VSL = 64 * VP;
-  static constexpr int NDMA = (KSL + VSL) / 64;
-  static constexpr int NU = (NDMA + 3) / 4;  // DMA instructions per wave and stage
-  static constexpr int STAGE = NU * 4 * 64;  // slots, with the padding
-  static_assert(KSL % 64 == 0 && VSL % 64 == 0, "a DMA instruction stays within K or V");
-  static_assert(4 * 16 * (D + 2) * 4 <= 2 * STAGE * 16, "group 1's partials fit in its stages");
+  // V's pitch of D/8 + 4 slots puts the 8 row segments of a half-wavefront's
+  // transposed read (4 rows x 2 column halves) on distinct banks.
+  static constexpr int KP = D / 8 + 1, VP = D / 8 + 4;
+  static constexpr int BK = 32;                                 // positions per block
+  static constexpr int KSL = (BK * KP + 63) / 64 * 64;          // K region, whole instructions
+  static constexpr int VSL = BK * VP;
+  static constexpr int NDMA = (KSL + VSL) / 64;                 // DMA instructions per stage
+  static constexpr int NU = (NDMA + 1) / 2;                     // per wave (2 wavefronts per group)
+  static constexpr int STAGE = NU * 2 * 64;                     // slots, with the padding
+  static_assert(VSL % 64 == 0, "a DMA instruction stays within K or V");
+  static_assert(6 * (D * 33 + 64) * 4 <= 4 * 2 * STAGE * 16, "groups 1..3's partials fit in LDS");
 };
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nqb) {
   using C = PrefillCfg<D>;
-  constexpr int KS = D / 32;  // 32-deep k-steps of q k^T
-  constexpr int DB = D / 16;  // 16-column output blocks
+  constexpr int KS = D / 16;  // 16-deep k-steps of q k^T
+  constexpr int DB = D / 32;  // 32-column output blocks
   constexpr int CPR = D / 8;
-  __shared__ uint4 Ls[2][2][C::STAGE];  // [group][stage]
+  __shared__ uint4 Ls[4][2][C::STAGE];  // [group][stage]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gr = wave >> 2, wq = wave & 3;
-  const int g4 = lane >> 4, i = lane & 15;
+  const int gr = wave >> 1, wq = wave & 1;
+  const int h2 = lane >> 5, j = lane & 31;
   const int unit = (int)blockIdx.x;
   const int per = a.nq * a.S;
   const int qb = nqb - 1 - unit / per, h = (unit % per) % a.nq, s = (unit % per) / a.nq;
   const int g = h / a.G;
   int sl;
   const int kl = seq_len(a, s, sl);
-  const int tok0 = qb * 64 + wq * 16;
-  const int tok = tok0 + i;
+  const int tok0 = qb * 64 + wq * 32;
+  const int tok = tok0 + j;
   const bool row_ok = tok < a.q_len;
   uint16_t* out = a.A + ((int64_t)s * a.q_len + tok) * a.lda + (int64_t)h * D;
   if (kl == 0) {  // uniform over the workgroup: a sequence out of range gives zeros
     if (row_ok && gr == 0)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) store_bf16x4(out + 16 * db + 4 * g4, 0.f, 0.f, 0.f, 0.f);
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) store_bf16x4(out + 32 * db + 8 * q + 4 * h2, 0.f, 0.f, 0.f, 0.f);
     return;
   }
   const int base_pos = kl - a.q_len;  // position of token 0
   const int last_tok = qb * 64 + 63 < a.q_len - 1 ? qb * 64 + 63 : a.q_len - 1;
-  const int nblk = (base_pos + last_tok) / 64 + 1;
-  const int nstep = (nblk + 1) / 2;
-  const int wlast = tok0 + 15 < a.q_len - 1 ? tok0 + 15 : a.q_len - 1;
-  const int wblk = tok0 < a.q_len ? (base_pos + wlast) / 64 + 1 : 0;  // blocks this wave's tokens see
+  const int nblk = (base_pos + last_tok) / C::BK + 1;
+  const int nstep = (nblk + 3) / 4;
+  const int wlast = tok0 + 31 < a.q_len - 1 ? tok0 + 31 : a.q_len - 1;
+  const int wblk = tok0 < a.q_len ? (base_pos + wlast) / C::BK + 1 : 0;  // blocks this wave's tokens see
   const int wfirst_pos = base_pos + tok0;
-  const int pos_i = base_pos + tok;
+  const int pos_j = base_pos + tok;
 
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.Kc, a, sl, g, kl, D);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.Vc, a, sl, g, kl, D);
-  // DMA: instruction n = 4 u + wq of a stage fills slots 64 n + lane.
+  // DMA: instruction n = 2 u + wq of a stage fills slots 64 n + lane.
   unsigned off[C::NU];
 #pragma unroll
   for (int u = 0; u < C::NU; ++u) {
-    const int n = 4 * u + wq;
+    const int n = 2 * u + wq;
     int q = n * 64 + lane;
     unsigned o = 0x80000000u;
     if (n * 64 < C::KSL) {
       const int row = q / C::KP, c = q - row * C::KP;
-      if (c < CPR) o = (unsigned)((row * D + 8 * c) * 2);
+      if (row < C::BK && c < CPR) o = (unsigned)((row * D + 8 * c) * 2);
     } else if (n < C::NDMA) {
       q -= C::KSL;
       const int row = q / C::VP, c = q - row * C::VP;
@@ -502,13 +511,13 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nq
     }
     off[u] = o;
   }
-  // Step t of this group: block 2 t + gr into stage t & 1 (blocks past the
-  // end read as zeros: their offsets pass the range, and nothing uses them).
+  // Step t of this group: block 4 t + gr into stage t & 1 (blocks past the
+  // end read as zeros and nothing uses them).
 #define AP_ISSUE(ST, T)                                                                            \
   {                                                                                                \
-    const unsigned bo_ = (unsigned)((2 * (T) + gr) * 64 * D * 2);                                  \
+    const unsigned bo_ = (unsigned)((4 * (T) + gr) * C::BK * D * 2);                               \
     _Pragma("unroll") for (int u = 0; u < C::NU; ++u) {                                            \
-      const int n = 4 * u + wq;                                                                    \
+      const int n = 2 * u + wq;                                                                    \
       const unsigned o_ = off[u] >= 0x80000000u ? off[u] : off[u] + bo_;                           \
       if (n * 64 < C::KSL) /* wave-uniform */                                                      \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&Ls[gr][ST][n * 64], 16, o_, 0, 0, 0); \
@@ -519,27 +528,35 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nq
 
   uint4 qf[KS];
   {
-    const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + tok) * a.ldqkv + (int64_t)h * D + 8 * g4;
+    const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + (row_ok ? tok : 0)) * a.ldqkv + (int64_t)h * D + 8 * h2;
+    const uint32_t qm = row_ok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) qf[k] = row_ok ? *reinterpret_cast<const uint4*>(qp + 32 * k) : make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < KS; ++k) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + 16 * k);
+      qf[k] = make_uint4(v.x & qm, v.y & qm, v.z & qm, v.w & qm);
+    }
   }
-  f32x4_t o[DB];
+  f32x16_t o[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
   // Running max of the scaled scores (log2 domain) and sum, per token column.
-  // Group 1 starts at block 1, which tokens before position 64 do not see:
-  // while a token's max is still -inf the exponents subtract 0 instead, so a
-  // masked (-inf) score gives exp2 = 0 and no -inf - -inf arises.
+  // Groups 1..3 start at blocks that early tokens do not see: while a token's
+  // max is still -inf the exponents subtract 0 instead, so a masked (-inf)
+  // score gives exp2 = 0 and no -inf - -inf arises.
   float m = -INFINITY, l = 0.f;
   const float c = a.qscale;
 
-  const int kfb = (i * C::KP + g4) * 16;
-  const int vfb = C::KSL * 16 + ((4 * g4 + (i >> 2)) * C::VP + ((i & 3) >> 1)) * 16 + (i & 1) * 8;
+  // Fragment bases: K row j, slot 2 k + h2; V (transposed reads) row
+  // 16 k' + 4 h2 + jj / 4 (+ 8), slot 4 db + 2 uu + (jj % 4) / 2, half jj % 2,
+  // where the lane is 32 h2 + 16 uu + jj.
+  const int jj = j & 15, uu = j >> 4;
+  const int kfb = (j * C::KP + h2) * 16;
+  const int vfb = C::KSL * 16 + ((4 * h2 + (jj >> 2)) * C::VP + 2 * uu + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
 
   AP_ISSUE(0, 0)
   if (nstep > 1) AP_ISSUE(1, 1)
   for (int t = 0; t < nstep; ++t) {
-    const int st = t & 1, blk = 2 * t + gr;
+    const int st = t & 1, blk = 4 * t + gr;
     if (t + 1 < nstep)
       __builtin_amdgcn_s_waitcnt(0x0F70 | C::NU);  // vmcnt(NU): step t has landed, t + 1 may fly
     else
@@ -547,40 +564,32 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nq
     __builtin_amdgcn_s_barrier();
     if (blk < wblk) {
       const char* L = (const char*)Ls[gr][st];
-      f32x4_t sc[4];
+      f32x16_t sa = f32x16_t{};
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        sc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          const uint4 kf = *reinterpret_cast<const uint4*>(L + kfb + (16 * b * C::KP + 4 * k) * 16);
-          sc[b] = mfma_16x16x32(kf, qf[k], sc[b]);
-        }
+      for (int k = 0; k < KS; ++k) {
+        const uint4 kf = *reinterpret_cast<const uint4*>(L + kfb + 2 * k * 16);
+        sa = mfma_32x32x16(kf, qf[k], sa);
       }
-      // Lane (g4, i) holds token i's raw scores at positions 64 blk + 16 b + 4 g4 + r.
-      if (blk * 64 + 63 > wfirst_pos) {  // a diagonal block: mask what lies past the token
+      // Lane (h2, j), element 4 q + r: position 32 blk + 8 q + 4 h2 + r.
+      if (blk * C::BK + C::BK - 1 > wfirst_pos) {  // a diagonal block: mask what lies past the token
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (blk * 64 + 16 * b + 4 * g4 + r > pos_i) sc[b][r] = -INFINITY;
+        for (int e = 0; e < 16; ++e)
+          if (blk * C::BK + 8 * (e >> 2) + 4 * h2 + (e & 3) > pos_j) sa[e] = -INFINITY;
       }
       float bm = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bm = fmaxf(bm, fmaxf(fmaxf(sc[b][0], sc[b][1]), fmaxf(sc[b][2], sc[b][3])));
-      bm = max32(max16(bm));
+      for (int e = 0; e < 16; e += 4) bm = fmaxf(bm, fmaxf(fmaxf(sa[e], sa[e + 1]), fmaxf(sa[e + 2], sa[e + 3])));
+      bm = max32(bm);
       const float mn = fmaxf(m, bm * c);
       const float ms = mn == -INFINITY ? 0.f : mn;
       float rs = 0.f;
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], c, -ms));
-          sc[b][r] = pe;
-          rs += pe;
-        }
-      rs = sum32(sum16(rs));
+      for (int e = 0; e < 16; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], c, -ms));
+        sa[e] = pe;
+        rs += pe;
+      }
+      rs = sum32(rs);
       if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {  // some token's max moved: rescale
         const float alpha = __builtin_amdgcn_exp2f(m - ms);
         l *= alpha;
@@ -590,21 +599,22 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nq
       l += rs;
       m = mn;
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const float pe[8] = {sc[2 * t2][0],     sc[2 * t2][1],     sc[2 * t2][2],     sc[2 * t2][3],
-                             sc[2 * t2 + 1][0], sc[2 * t2 + 1][1], sc[2 * t2 + 1][2], sc[2 * t2 + 1][3]};
+      for (int kk = 0; kk < 2; ++kk) {
+        const int q0 = 2 * kk;
+        const float pe[8] = {sa[4 * q0],     sa[4 * q0 + 1], sa[4 * q0 + 2], sa[4 * q0 + 3],
+                             sa[4 * q0 + 4], sa[4 * q0 + 5], sa[4 * q0 + 6], sa[4 * q0 + 7]};
         uint4 ph, pl;
         split8(pe, ph, pl);
         uint4 vf[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const char* v0 = L + vfb + (32 * t2 * C::VP + 2 * db) * 16;
-          vf[db] = tr_pair(v0, v0 + 16 * C::VP * 16);
+          const char* v0 = L + vfb + (16 * kk * C::VP + 4 * db) * 16;
+          vf[db] = tr_pair(v0, v0 + 8 * C::VP * 16);
         }
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = mfma_16x16x32(vf[db], ph, o[db]);
+        for (int db = 0; db < DB; ++db) o[db] = mfma_32x32x16(vf[db], ph, o[db]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = mfma_16x16x32(vf[db], pl, o[db]);
+        for (int db = 0; db < DB; ++db) o[db] = mfma_32x32x16(vf[db], pl, o[db]);
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -614,33 +624,57 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nq
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #undef AP_ISSUE
 
-  // Group 1's partials into its own stages ([wq][16 tokens][D] then m, l),
-  // then group 0 merges. Lane (g4, i), element r of block db: column
-  // 16 db + 4 g4 + r of token i.
-  float* red = reinterpret_cast<float*>(Ls[1][0]) + wq * 16 * (D + 2);
-  if (gr == 1) {
+  // Groups 1..3: partials into LDS, per wave [D columns][33] (token j at
+  // j, a pitch of 33 keeps a column's 32 tokens and the other half-wave's
+  // columns on distinct banks) then m, l; then group 0 merges the four in
+  // group order. Lane (h2, j), element 4 q + r of block db: column
+  // 32 db + 8 q + 4 h2 + r of token j.
+  constexpr int TP = 33;
+  constexpr int WR = D * TP + 64;
+  float* red = reinterpret_cast<float*>(&Ls[0][0][0]);
+  if (gr > 0) {
+    float* rw = red + (wave - 2) * WR;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[i * D + 16 * db + 4 * g4 + r] = o[db][r];
-    if (g4 == 0) {
-      red[16 * D + i] = m;
-      red[16 * D + 16 + i] = l;
+      for (int e = 0; e < 16; ++e) rw[(32 * db + 8 * (e >> 2) + 4 * h2 + (e & 3)) * TP + j] = o[db][e];
+    if (h2 == 0) {
+      rw[D * TP + j] = m;
+      rw[D * TP + 32 + j] = l;
     }
   }
   __syncthreads();
   if (gr == 0 && row_ok) {
-    const float m1 = red[16 * D + i], l1 = red[16 * D + 16 + i];
-    const float M = fmaxf(m, m1);
-    const float f0 = __builtin_amdgcn_exp2f(m - M), f1 = __builtin_amdgcn_exp2f(m1 - M);
-    const float L = f0 * l + f1 * l1;
+    float mg[4], M = m;
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+      mg[q] = red[(2 * q + wq - 2) * WR + D * TP + j];
+      M = fmaxf(M, mg[q]);
+    }
+    float f[4];
+    f[0] = __builtin_amdgcn_exp2f(m - M);
+    float L = f[0] * l;
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+      f[q] = __builtin_amdgcn_exp2f(mg[q] - M);
+      L += f[q] * red[(2 * q + wq - 2) * WR + D * TP + 32 + j];
+    }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const float* o1 = red + i * D + 16 * db + 4 * g4;
-      store_bf16x4(out + 16 * db + 4 * g4, (f0 * o[db][0] + f1 * o1[0]) * inv, (f0 * o[db][1] + f1 * o1[1]) * inv,
-                   (f0 * o[db][2] + f1 * o1[2]) * inv, (f0 * o[db][3] + f1 * o1[3]) * inv);
-    }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int col = 32 * db + 8 * q + 4 * h2 + r;
+          float acc = f[0] * o[db][4 * q + r];
+#pragma unroll
+          for (int gq = 1; gq < 4; ++gq) acc += f[gq] * red[(2 * gq + wq - 2) * WR + col * TP + j];
+          v[r] = acc * inv;
+        }
+        store_bf16x4(out + 32 * db + 8 * q + 4 * h2, v[0], v[1], v[2], v[3]);
+      }
   }
 }
 
