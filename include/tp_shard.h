@@ -388,9 +388,11 @@ TP_API tp_status tp_kv_append(const tp_shard_desc* qkv, const uint16_t* QKV, int
  * Scores and softmax in fp32; the probabilities enter the product with V as
  * two bf16 terms (hi + lo); output rounded once to bf16.
  * When (n_q_r / n_kv_r) q_len <= 16 (decode) the cache is read in chunks of
- * 512 positions, each once per key-value head, and the chunks' partials
- * (fp32) go to the workspace: tp_attention_workspace_bytes bytes
- * (TP_ERR_WORKSPACE if short); otherwise no workspace is used.
+ * 512, 1024, 2048 or 4096 positions (the longest that still leave 256 or more
+ * workgroups), each once per key-value head; with more than one chunk per
+ * sequence the chunks' partials (fp32) go to the workspace:
+ * tp_attention_workspace_bytes bytes (TP_ERR_WORKSPACE if short or not
+ * 16-byte aligned). Otherwise no workspace is used and ws may be null.
  */
 TP_API tp_status tp_attention(const tp_shard_desc* qkv, const uint16_t* QKV, int64_t ldqkv,
                        int32_t S, int32_t q_len, const int32_t* kv_len, const int32_t* slot,

@@ -346,9 +346,6 @@ bool cache_ok(int D, int64_t n_slots, int64_t L_max) {
 
 bool attn_decode(int G, int32_t q_len) { return (int64_t)G * q_len <= tpk::kAttnDecodeRows; }
 
-int64_t attn_chunks(int32_t max_kv) {
-  return ((int64_t)max_kv + tpk::kAttnDecodeChunk - 1) / tpk::kAttnDecodeChunk;
-}
 
 // Checks shared by the append and the attention; fills the arguments.
 tp_status attn_args(const tp_shard_desc* qkv, const uint16_t* QKV, int64_t ldqkv, int32_t S,
@@ -414,7 +411,9 @@ extern "C" size_t tp_attention_workspace_bytes(const tp_shard_desc* qkv, int32_t
   int nq, nkv, D, G;
   if (attn_heads(qkv, nq, nkv, D, G) != TP_OK || S < 0 || q_len < 1 || max_kv < q_len) return 0;
   if (!attn_decode(G, q_len)) return 0;
-  return tpk::attn_decode_ws_bytes(S, nkv, attn_chunks(max_kv), D);
+  int32_t nchunk, npw;
+  tpk::attn_decode_split(S, nkv, max_kv, nchunk, npw);
+  return tpk::attn_decode_ws_bytes(S, nkv, nchunk, D);
 }
 
 extern "C" tp_status tp_attention(const tp_shard_desc* qkv, const uint16_t* QKV, int64_t ldqkv,
@@ -433,10 +432,9 @@ extern "C" tp_status tp_attention(const tp_shard_desc* qkv, const uint16_t* QKV,
   a.lda = lda;
   const bool decode = attn_decode(a.G, q_len);
   if (decode) {
-    a.nchunk = (int32_t)attn_chunks(max_kv);
-    if (a.nchunk > 65535) return TP_ERR_SHAPE;
+    tpk::attn_decode_split(S, a.nkv, max_kv, a.nchunk, a.npw);
     const size_t need = tpk::attn_decode_ws_bytes(S, a.nkv, a.nchunk, a.D);
-    if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return TP_ERR_WORKSPACE;
+    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws))) return TP_ERR_WORKSPACE;
     a.ws = static_cast<float*>(ws);
   } else if ((int64_t)((q_len + 63) / 64) * a.nq * S > INT32_MAX) {
     return TP_ERR_SHAPE;

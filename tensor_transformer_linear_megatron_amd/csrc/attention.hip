@@ -12,9 +12,10 @@
 //  * kv_append_kernel: the new tokens' K and V rows into their cache slots.
 //  * attn_decode_kernel + attn_combine_kernel: few new tokens per sequence
 //    (the rank's query heads of one key-value head times the new tokens fit
-//    in 16 rows). The cache is split into chunks of 512 positions; each
-//    workgroup reads its chunk of one key-value head once for all those rows,
-//    and the combine kernel merges the chunks' softmax partials.
+//    in 16 rows). The cache is split into chunks of 512, 1024, 2048 or 4096
+//    positions, as few as still fill the GPU; each workgroup reads its chunk
+//    of one key-value head once for all those rows, and with more than one
+//    chunk the combine kernel merges the chunks' softmax partials.
 //  * attn_prefill_kernel: many new tokens. 64 query tokens of one head per
 //    workgroup of four wavefront groups that split the causal chain of
 //    32-position key-value blocks (shared through LDS) between them, online
@@ -144,32 +145,39 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AttnArgs a, int64_t tota
 }
 
 // ---------------------------------------------------------------------------
-// Decode. Workgroup (chunk, g, s) of 4 wavefronts; wavefront w takes the two
-// 64-position halves [512 chunk + 64 (4 hb + w), + 64), hb = 0, 1. Row rho
-// (< 16) of the 16x16x32 operands is query head g G + rho / q_len of token
-// rho % q_len. K fragments come straight from the cache into registers (A
-// operand rows = positions); V lands in the wavefront's own LDS region by DMA
-// at a pitch of D/8 + 2 16-byte slots, which puts the four rows each 16-lane
-// group reads on distinct banks. Loads go out as Q, K0, V0, K1, V1, so half 0
-// is multiplied while half 1 is still arriving (online softmax across the
-// two). The four wavefronts' partials merge through LDS into one per
-// workgroup: m[rho] (log2 domain), l[rho] and the unnormalised output
-// [rho][D].
+// Decode. Workgroup (chunk, g, s) of 4 wavefronts takes NPW passes of 512
+// positions of one (sequence, key-value head); in each pass wavefront w takes
+// two 64-position halves, half h of the chunk at [chunk 512 NPW + 64 (4 h + w),
+// + 64). Row rho (< 16) of the 16x16x32 operands is query head g G + rho /
+// q_len of token rho % q_len. K fragments come straight from the cache into
+// registers (A operand rows = positions); V lands in the wavefront's own LDS
+// region by DMA at a pitch of D/8 + 2 16-byte slots, which puts the four rows
+// each 16-lane group reads on distinct banks. Halves alternate between two
+// register sets and two LDS arrays: loads go out as Q, K0, V0, K1, V1, and
+// half h + 2's K and V as soon as half h has left them, so each half is
+// multiplied while the next two are arriving (online softmax across the
+// halves). The four wavefronts' results merge through LDS: with one chunk per
+// (sequence, key-value head) the workgroup normalises and writes the output
+// rows itself; otherwise it writes one partial, m[rho] (log2 domain), l[rho]
+// and the unnormalised output [rho][D], and attn_combine_kernel merges them.
 
-template <int D>
+template <int D, int NPW>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   constexpr int KS = D / 32;     // 32-deep k-steps of q k^T
   constexpr int DB = D / 16;     // 16-column output blocks
   constexpr int CPR = D / 8;     // 16-byte chunks per cache row
   constexpr int PITCH = CPR + 2;
   constexpr int HPOS = 64;       // positions per half
+  constexpr int NH = 2 * NPW;    // halves per wavefront
   constexpr int HSL = HPOS * PITCH;  // LDS slots per half (a multiple of 64)
   constexpr int RED = kAttnDecodeRows * D + 2 * kAttnDecodeRows;
-  static_assert(kAttnDecodeChunk == 2 * 4 * HPOS, "two halves per wavefront");
+  constexpr int KN = 4 * KS;     // K load instructions per half
+  static_assert(kAttnDecodePass == 2 * 4 * HPOS, "two halves per wavefront and pass");
   static_assert((D * (kAttnDecodeRows + 1) + 2 * kAttnDecodeRows) * 4 <= HSL * 16,
                 "a wave's partial fits in its half-0 V region");
-  // One array per half: the compiler then tracks the two halves' DMA apart
-  // and lets half 1 fly while half 0's V is read.
+  static_assert(2 * KN + PITCH <= 63, "the in-flight loads fit the wait counter");
+  // One array per parity of the half: the compiler then tracks their DMA
+  // apart and lets the other parity fly while one is read.
   __shared__ uint4 Vs0[4][HSL], Vs1[4][HSL];
 
   const int lane = threadIdx.x & 63;
@@ -179,7 +187,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   int sl;
   const int kl = seq_len(a, s, sl);
   const int R = a.G * a.q_len;
-  const int pc = chunk * kAttnDecodeChunk + wave * HPOS;  // half hb starts at pc + 256 hb
+  const int pc = chunk * kAttnDecodePass * NPW + wave * HPOS;  // half h starts at pc + 256 h
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.Kc, a, sl, g, kl, D);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.Vc, a, sl, g, kl, D);
 
@@ -194,21 +202,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
 
   if (pc < kl) {  // wave-uniform: at least half 0 holds positions
     uint4 kf[2][4][KS];
-#define AD_KLOAD(HB)                                                                               \
+#define AD_KLOAD(H)                                                                                \
   _Pragma("unroll") for (int b = 0; b < 4; ++b) _Pragma("unroll") for (int k = 0; k < KS; ++k)    \
-      kf[HB][b][k] = __builtin_bit_cast(                                                           \
+      kf[(H) & 1][b][k] = __builtin_bit_cast(                                                      \
           uint4, __builtin_amdgcn_raw_buffer_load_b128(                                            \
-                     rk, (unsigned)(((pc + 4 * HPOS * (HB) + 16 * b + i) * D + 32 * k + 8 * g4) * 2), 0, 0));
-#define AD_VLOAD(HB, VS)                                                                           \
+                     rk, (unsigned)(((pc + 4 * HPOS * (H) + 16 * b + i) * D + 32 * k + 8 * g4) * 2), 0, 0));
+#define AD_VLOAD(H)                                                                                \
   _Pragma("unroll") for (int u = 0; u < PITCH; ++u) {                                              \
     const int q = u * 64 + lane, row = q / PITCH, c = q - row * PITCH;                             \
-    const unsigned off = c < CPR ? (unsigned)(((pc + 4 * HPOS * (HB) + row) * D + 8 * c) * 2) : 0x80000000u; \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&VS[wave][u * 64], 16, off, 0, 0, 0); \
+    const unsigned off = c < CPR ? (unsigned)(((pc + 4 * HPOS * (H) + row) * D + 8 * c) * 2) : 0x80000000u; \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&(((H) & 1) ? Vs1 : Vs0)[wave][u * 64], 16, off, 0, 0, 0); \
   }
-    // Issue order Q, K0, V0, K1, V1 (kept by the scheduling barriers): the
-    // wait before half 0's V leaves exactly K1 and V1 in flight. Q rows past
-    // R read row 0 (always in range) and are zeroed after the load, so no
-    // load sits behind a branch.
+    // Q rows past R read row 0 (always in range) and are zeroed after the
+    // load, so no load sits behind a branch. Halves past the cache are loaded
+    // and multiplied all the same: their loads return zeros without touching
+    // memory and their scores are masked, and straight-line code keeps the
+    // compiler's own wait counts exact.
     uint4 qf[KS];
     const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + (row_ok ? tok : 0)) * a.ldqkv +
                          (int64_t)(g * a.G + (row_ok ? hh : 0)) * D + 8 * g4;
@@ -217,31 +226,29 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     AD_KLOAD(0)
     __builtin_amdgcn_sched_barrier(0);
-    AD_VLOAD(0, Vs0)
+    AD_VLOAD(0)
     __builtin_amdgcn_sched_barrier(0);
-    // Half 1 unconditionally: past the cache its loads return zeros without
-    // touching memory and its scores are masked, and straight-line code keeps
-    // the compiler's own wait counts exact.
     AD_KLOAD(1)
     __builtin_amdgcn_sched_barrier(0);
-    AD_VLOAD(1, Vs1)
+    AD_VLOAD(1)
     __builtin_amdgcn_sched_barrier(0);
-#undef AD_KLOAD
-#undef AD_VLOAD
     const uint32_t qm = row_ok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int k = 0; k < KS; ++k) qf[k] = make_uint4(qf[k].x & qm, qf[k].y & qm, qf[k].z & qm, qf[k].w & qm);
     const int vfo = ((4 * g4 + (i >> 2)) * PITCH + ((i & 3) >> 1)) * 16 + (i & 1) * 8;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int p0 = pc + 4 * HPOS * hb;
+    for (int h = 0; h < NH; ++h) {
+      const int p0 = pc + 4 * HPOS * h;
       f32x4_t sc[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         sc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < KS; ++k) sc[b] = mfma_16x16x32(kf[hb][b][k], qf[k], sc[b]);
+        for (int k = 0; k < KS; ++k) sc[b] = mfma_16x16x32(kf[h & 1][b][k], qf[k], sc[b]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (h + 2 < NH) AD_KLOAD(h + 2)  // this half's K registers are free again
+      __builtin_amdgcn_sched_barrier(0);
       // Lane (g4, i) holds row i's raw scores at positions p0 + 16 b + 4 g4 + r.
       float bm = -INFINITY;
 #pragma unroll
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
           rs += e;
         }
       rs = sum32(sum16(rs));
-      if (hb == 1) {
+      if (h > 0) {
         const float alpha = __builtin_amdgcn_exp2f(m - ms);
         l *= alpha;
 #pragma unroll
@@ -273,12 +280,16 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
       }
       l += rs;
       m = mn;
-      // V of this half has landed: after half 0 only K1 and V1 may still fly.
-      if (hb == 0)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * KS + PITCH) & 15) | (((4 * KS + PITCH) >> 4) << 14));
+      // This half's V has landed; issued after it: K and V of half h + 1
+      // and K of half h + 2 (those that exist).
+      constexpr int kW2 = 2 * KN + PITCH, kW1 = KN + PITCH;
+      if (h + 2 < NH)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (kW2 & 15) | ((kW2 >> 4) << 14));
+      else if (h + 1 < NH)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (kW1 & 15) | ((kW1 >> 4) << 14));
       else
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      const char* vh = (const char*)(hb == 0 ? Vs0[wave] : Vs1[wave]) + vfo;
+      const char* vh = (const char*)((h & 1) ? Vs1[wave] : Vs0[wave]) + vfo;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const float pe[8] = {sc[2 * t2][0],     sc[2 * t2][1],     sc[2 * t2][2],     sc[2 * t2][3],
@@ -294,12 +305,20 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] = mfma_16x16x32(vf[db], pl, o[db]);
       }
+      if (h + 2 < NH) {  // this half's V region is free once its reads are done
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_sched_barrier(0);
+        AD_VLOAD(h + 2)
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+#undef AD_KLOAD
+#undef AD_VLOAD
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   }
 
-  // This wave's partial into its own half-0 region (its reads of V are
+  // This wave's result into its own half-0 region (its reads of V are
   // complete), [D columns][17] (row rho at rho: the pitch of 17 keeps a
   // column's 16 rows and the other lane groups' columns on distinct banks),
   // then m, l.
@@ -330,18 +349,32 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     f[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
     L += f[w] * reinterpret_cast<const float*>(Vs0[w])[D * RP + kAttnDecodeRows + row];
   }
+  float acc[CW];
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    acc[c] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc[c] += f[w] * reinterpret_cast<const float*>(Vs0[w])[(c0 + c) * RP + row];
+  }
+  if (a.nchunk == 1) {  // the whole cache was this workgroup's: write the output rows
+    if (row < R) {  // divided as the combine kernel divides, so both forms agree bit for bit
+      const bool ok = kl > 0 && L > 0.f;
+      const int hr = row / a.q_len, tr = row - hr * a.q_len;
+      uint16_t* dst = a.A + ((int64_t)s * a.q_len + tr) * a.lda + (int64_t)(g * a.G + hr) * D + c0;
+#pragma unroll
+      for (int q = 0; q < CW / 4; ++q)
+        store_bf16x4(dst + 4 * q, ok ? acc[4 * q] / L : 0.f, ok ? acc[4 * q + 1] / L : 0.f,
+                     ok ? acc[4 * q + 2] / L : 0.f, ok ? acc[4 * q + 3] / L : 0.f);
+    }
+    return;
+  }
   float* P = a.ws + (((int64_t)s * a.nkv + g) * a.nchunk + chunk) * RED;
   if (t < kAttnDecodeRows) {
     P[kAttnDecodeRows * D + row] = M;
     P[kAttnDecodeRows * D + kAttnDecodeRows + row] = L;
   }
 #pragma unroll
-  for (int c = 0; c < CW; ++c) {
-    float acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) acc += f[w] * reinterpret_cast<const float*>(Vs0[w])[(c0 + c) * RP + row];
-    P[row * D + c0 + c] = acc;
-  }
+  for (int c = 0; c < CW; ++c) P[row * D + c0 + c] = acc[c];
 }
 
 // Workgroup (rho, g, s), thread c: output column c of row rho, merged over
@@ -681,8 +714,15 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nq
 template <int D>
 hipError_t launch_attention_d(const AttnArgs& a, bool decode, hipStream_t s) {
   if (decode) {
-    hipLaunchKernelGGL(attn_decode_kernel<D>, dim3(a.nchunk, a.nkv, a.S), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(a.G * a.q_len, a.nkv, a.S), dim3(D), 0, s, a);
+    const dim3 grid(a.nchunk, a.nkv, a.S);
+    switch (a.npw) {
+      case 1: hipLaunchKernelGGL((attn_decode_kernel<D, 1>), grid, dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((attn_decode_kernel<D, 2>), grid, dim3(256), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((attn_decode_kernel<D, 4>), grid, dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL((attn_decode_kernel<D, 8>), grid, dim3(256), 0, s, a); break;
+    }
+    if (a.nchunk > 1)
+      hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(a.G * a.q_len, a.nkv, a.S), dim3(D), 0, s, a);
   } else {
     const int nqb = (a.q_len + 63) / 64;
     hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(nqb * a.nq * a.S), dim3(512), 0, s, a, nqb);
@@ -693,7 +733,19 @@ hipError_t launch_attention_d(const AttnArgs& a, bool decode, hipStream_t s) {
 }  // namespace
 
 size_t attn_decode_ws_bytes(int64_t S, int64_t nkv, int64_t nchunk, int D) {
+  if (nchunk <= 1) return 0;  // one chunk writes the output itself
   return (size_t)(S * nkv * nchunk) * (size_t)(kAttnDecodeRows * D + 2 * kAttnDecodeRows) * sizeof(float);
+}
+
+void attn_decode_split(int64_t S, int64_t nkv, int64_t max_kv, int32_t& nchunk, int32_t& npw) {
+  // The fewest chunks that still give about one workgroup per CU: passes of
+  // 512 positions per chunk double while the workgroups stay at 256 or more.
+  const int64_t full = (max_kv + kAttnDecodePass - 1) / kAttnDecodePass;
+  const int64_t pairs = S * nkv;
+  int64_t p = 1;
+  while (p < 8 && p < full && pairs * ((full + 2 * p - 1) / (2 * p)) >= 256) p *= 2;
+  npw = (int32_t)p;
+  nchunk = (int32_t)((full + p - 1) / p);
 }
 
 hipError_t launch_kv_append(const AttnArgs& a, hipStream_t s) {

@@ -125,12 +125,15 @@ struct AttnArgs {
   int64_t lda;
   float* ws;       // decode: per-chunk partials
   int32_t nchunk;  // decode: chunks of positions per (sequence, key-value head)
+  int32_t npw;     // decode: 512-position passes per chunk (1, 2, 4 or 8)
   float qscale;    // log2(e) / sqrt(D)
 };
 
 constexpr int kAttnDecodeRows = 16;    // query rows (heads x tokens) of one decode workgroup
-constexpr int kAttnDecodeChunk = 512;  // positions per decode workgroup
+constexpr int kAttnDecodePass = 512;   // positions per decode pass of a workgroup
 size_t attn_decode_ws_bytes(int64_t S, int64_t nkv, int64_t nchunk, int D);
+// Chunks per (sequence, key-value head) and passes per chunk for a decode call.
+void attn_decode_split(int64_t S, int64_t nkv, int64_t max_kv, int32_t& nchunk, int32_t& npw);
 hipError_t launch_kv_append(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, bool decode, hipStream_t s);
 

@@ -370,7 +370,9 @@ def test_kv_cache_and_attention_workspace_sizes():
     """Cache bytes: n_slots x n_kv_r x L_max x d x 2 per array; the rank's
     share is 1/t of the layer's key-value heads up to t = n_kv, then one
     repeated head. The decode form needs one partial (16 rows x (d + 2) fp32)
-    per sequence, key-value head and 512-position chunk."""
+    per sequence, key-value head and chunk, and none when each (sequence,
+    key-value head) is one chunk: chunks take 512 x 2^j positions (j <= 3),
+    as long as every chunk count still gives 256 or more workgroups."""
     for t, nkv in ((1, 8), (2, 4), (8, 1), (16, 1)):
         assert tp.tp_kv_cache_bytes(_qkv70(t, t - 1), 4, 4096) == 4 * nkv * 4096 * 128 * 2
     assert tp.tp_kv_cache_bytes(tp.tp_shard_plan("col", 64, 64, 1, 0), 1, 16) == 0
@@ -381,8 +383,16 @@ def test_kv_cache_and_attention_workspace_sizes():
     assert tp.tp_attention_workspace_bytes(q, 32, 2, 4097) == 32 * 9 * (16 * 128 + 32) * 4
     assert tp.tp_attention_workspace_bytes(q, 1, 3, 4096) == 0  # 24 rows: the prefill form
     q16 = _qkv70(16, 5)  # 4 query heads, repeated key-value head
-    assert tp.tp_attention_workspace_bytes(q16, 2, 4, 300) == 2 * 1 * (16 * 128 + 32) * 4
+    assert tp.tp_attention_workspace_bytes(q16, 2, 4, 300) == 0  # one chunk: no partials
+    assert tp.tp_attention_workspace_bytes(q16, 2, 4, 513) == 2 * 2 * (16 * 128 + 32) * 4
     assert tp.tp_attention_workspace_bytes(q16, 2, 5, 300) == 0
+    part = (16 * 128 + 32) * 4
+    assert tp.tp_attention_workspace_bytes(q, 64, 1, 4096) == 64 * 4 * part  # 1024-position chunks
+    assert tp.tp_attention_workspace_bytes(q, 128, 1, 4096) == 128 * 2 * part  # 2048-position chunks
+    assert tp.tp_attention_workspace_bytes(q, 256, 1, 4096) == 0  # one 4096-position chunk each
+    assert tp.tp_attention_workspace_bytes(q, 32, 1, 32768) == 32 * 8 * part  # 4096-position chunks
+    assert tp.tp_attention_workspace_bytes(q, 1, 1, 32768) == 1 * 64 * part  # too few to lengthen
+    assert tp.tp_attention_workspace_bytes(q, 300, 1, 1000) == 0  # 300 x 1: one 1024-position chunk
 
 
 def test_attention_argument_errors():
@@ -394,6 +404,8 @@ def test_attention_argument_errors():
     W = 10 * 128  # QKV row width of the rank
     KL, SL = ctypes.c_void_p(0x400000), ctypes.c_void_p(0x500000)
     ws_need = tp.tp_attention_workspace_bytes(q, 2, 1, 64)
+    ws_long = tp.tp_attention_workspace_bytes(q, 2, 1, 1024)
+    assert ws_need == 0 and ws_long > 0
     att = lib.tp_attention
     app = lib.tp_kv_append
     col = tp.tp_shard_plan("col", 64, 64, 1, 0)
@@ -416,8 +428,9 @@ def test_attention_argument_errors():
     assert att(qb, A, W, 2, 1, ctypes.c_void_p(0x400002), SL, 64, B, C, 2, 64, A, 1024, A, ws_need, S_) == \
         _lib.TP_ERR_ALIGN
     assert att(qb, A, W, 2, 1, KL, SL, 64, B, C, 2, 64, MIS, 1024, A, ws_need, S_) == _lib.TP_ERR_ALIGN
-    assert att(qb, A, W, 2, 1, KL, SL, 64, B, C, 2, 64, A, 1024, A, ws_need - 4, S_) == _lib.TP_ERR_WORKSPACE
-    assert att(qb, A, W, 2, 1, KL, SL, 64, B, C, 2, 64, A, 1024, NUL, ws_need, S_) == _lib.TP_ERR_WORKSPACE
+    assert att(qb, A, W, 2, 1, KL, SL, 1024, B, C, 2, 1024, A, 1024, A, ws_long - 4, S_) == _lib.TP_ERR_WORKSPACE
+    assert att(qb, A, W, 2, 1, KL, SL, 1024, B, C, 2, 1024, A, 1024, NUL, ws_long, S_) == _lib.TP_ERR_WORKSPACE
+    assert att(qb, A, W, 2, 1, KL, SL, 1024, B, C, 2, 1024, A, 1024, MIS, ws_long, S_) == _lib.TP_ERR_WORKSPACE
     assert att(qb, NUL, W, 0, 1, NUL, NUL, 64, NUL, NUL, 2, 64, NUL, 1024, NUL, 0, S_) == _lib.TP_OK  # S == 0
     assert app(qb, NUL, W, 2, 1, KL, SL, B, C, 2, 64, S_) == _lib.TP_ERR_NULL
     assert app(qb, A, W, 2, 1, KL, SL, B, NUL, 2, 64, S_) == _lib.TP_ERR_NULL

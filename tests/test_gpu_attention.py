@@ -1,7 +1,8 @@
 """GPU parity of the attention core on a rank's heads and its KV-cache share:
 tp_kv_append against the oracle's append (bit-exact), tp_attention against
-the fp64 oracle (both rounded once to bf16) on the decode form (split over
-512-position chunks) and the prefill form, on several head layouts: grouped
+the fp64 oracle (both rounded once to bf16) on the decode form (split into
+chunks of 512 to 4096 positions, merged when there are several) and the
+prefill form, on several head layouts: grouped
 query heads at t = 2 and 8, a repeated key-value head at t = 16, d = 64 and
 128; ragged lengths, a prefill on top of an earlier cache, out-of-range
 sequences, and the 70B TP = 8 rank-0 shapes the benchmark times.
@@ -208,13 +209,37 @@ def test_decode_long_cache_merges_many_chunks():
 
 
 def test_max_kv_above_every_length():
-    """A larger max_kv only adds empty chunks."""
+    """A larger max_kv only adds empty chunks; one chunk (the output written
+    by the chunk's own workgroup) and several (merged by the combine kernel)
+    give the same bits."""
     say("max_kv slack")
     c = Case((64, 8, 128), 8, 0, 1, [300, 17], [0, 1], 2, 2048, 495)
     c.append()
     a1 = host_bits(c.run(max_kv=300))
     a2 = host_bits(c.run(max_kv=2048))
     np.testing.assert_array_equal(a1, a2)
+
+
+@pytest.mark.parametrize("S,L,chunk", [(128, 2048, 1024), (64, 4096, 1024), (128, 4096, 2048), (256, 4096, 4096),
+                                       (32, 32768, 4096), (300, 700, 1024)])
+def test_decode_longer_chunks_for_large_batches(S, L, chunk):
+    """Many sequences: each workgroup takes 2, 4 or 8 passes of 512 positions,
+    or the whole cache (no combine); ragged lengths around the chunk edges.
+    Sampled rows."""
+    say("decode large batch", S, L)
+    part = (16 * 128 + 32) * 4
+    q = plans((64, 8, 128), 8, 0)[0]
+    n_chunks = -(-L // chunk)
+    assert tp.tp_attention_workspace_bytes(q, S, 1, L) == (S * n_chunks * part if n_chunks > 1 else 0)
+    rng = np.random.default_rng(S + L)
+    kv = [int(x) for x in rng.integers(1, L + 1, S)]
+    kv[0], kv[-1] = L, min(L, chunk + 1)
+    kv[1] = min(L, chunk)
+    c = Case((64, 8, 128), 8, 0, 1, kv, list(range(S)), S, L, 530)
+    c.append()
+    A = host_bits(c.run(max_kv=L))
+    rows = sorted({0, 1, S // 2, S - 1})
+    assert_parity(oracle.bf16_to_f64(A[rows]), oracle.bf16_to_f64(c.ref(rows)), f"decode {S} x {L}")
 
 
 # ---------------------------------------------------------------------------
