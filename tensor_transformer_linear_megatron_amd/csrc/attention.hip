@@ -17,9 +17,9 @@
 //    of one key-value head once for all those rows, and with more than one
 //    chunk the combine kernel merges the chunks' softmax partials.
 //  * attn_prefill_kernel: many new tokens. 64 query tokens of one head per
-//    workgroup of four wavefront groups that split the causal chain of
-//    32-position key-value blocks (shared through LDS) between them, online
-//    softmax, merged at the end.
+//    workgroup of two or four wavefront groups that split the causal chain
+//    of 32-position key-value blocks (shared through LDS) between them,
+//    online softmax, merged at the end.
 //
 // Precision: q k^T accumulates in fp32 from bf16; the softmax runs in fp32
 // (exp2 with log2(e) folded into the scale). The probabilities enter the
@@ -459,12 +459,13 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill. A workgroup of 8 wavefronts takes 64 query tokens of one query
-// head. Wavefront w belongs to group w / 2 and takes tokens 64 qb + 32 (w % 2)
-// + j, j = lane % 32, the column of its 32x32x16 operands. Group gr multiplies
-// key-value blocks gr, gr + 4, ... of 32 positions, so each group runs a
-// quarter of the causal chain; at the end groups 1..3 hand their (max, sum,
-// output) to group 0 through LDS and group 0 merges and stores. Each group has
+// Prefill. A workgroup of NG groups of 2 wavefronts (NG = 2 or 4) takes 64
+// query tokens of one query head. Wavefront w belongs to group w / 2 and
+// takes tokens 64 qb + 32 (w % 2) + j, j = lane % 32, the column of its
+// 32x32x16 operands. Group gr multiplies key-value blocks gr, gr + NG, ... of
+// 32 positions, so each group runs 1/NG of the causal chain; at the end
+// groups 1..NG-1 hand their (max, sum, output) to group 0 through LDS and
+// group 0 merges and stores. Each group has
 // its own pair of LDS stages, filled by DMA: 32 K rows at a pitch of D/8 + 1
 // 16-byte slots (the A operand of S^T read whole, 32 rows per half-wavefront
 // on distinct banks) in a region padded to whole DMA instructions, then 32 V
@@ -483,16 +484,17 @@ struct PrefillCfg {
   static constexpr int NU = (NDMA + 1) / 2;                     // per wave (2 wavefronts per group)
   static constexpr int STAGE = NU * 2 * 64;                     // slots, with the padding
   static_assert(VSL % 64 == 0, "a DMA instruction stays within K or V");
-  static_assert(6 * (D * 33 + 64) * 4 <= 4 * 2 * STAGE * 16, "groups 1..3's partials fit in LDS");
 };
 
-template <int D>
-__global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nqb) {
+template <int D, int NG>
+__global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs a, int nqb) {
   using C = PrefillCfg<D>;
+  static_assert(NG == 2 || NG == 4, "two or four groups");
+  static_assert(2 * (NG - 1) * (D * 33 + 64) * 4 <= NG * 2 * C::STAGE * 16, "groups 1..NG-1's partials fit in LDS");
   constexpr int KS = D / 16;  // 16-deep k-steps of q k^T
   constexpr int DB = D / 32;  // 32-column output blocks
   constexpr int CPR = D / 8;
-  __shared__ uint4 Ls[4][2][C::STAGE];  // [group][stage]
+  __shared__ uint4 Ls[NG][2][C::STAGE];  // [group][stage]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -519,7 +521,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nq
   const int base_pos = kl - a.q_len;  // position of token 0
   const int last_tok = qb * 64 + 63 < a.q_len - 1 ? qb * 64 + 63 : a.q_len - 1;
   const int nblk = (base_pos + last_tok) / C::BK + 1;
-  const int nstep = (nblk + 3) / 4;
+  const int nstep = (nblk + NG - 1) / NG;
   const int wlast = tok0 + 31 < a.q_len - 1 ? tok0 + 31 : a.q_len - 1;
   const int wblk = tok0 < a.q_len ? (base_pos + wlast) / C::BK + 1 : 0;  // blocks this wave's tokens see
   const int wfirst_pos = base_pos + tok0;
@@ -548,7 +550,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nq
   // end read as zeros and nothing uses them).
 #define AP_ISSUE(ST, T)                                                                            \
   {                                                                                                \
-    const unsigned bo_ = (unsigned)((4 * (T) + gr) * C::BK * D * 2);                               \
+    const unsigned bo_ = (unsigned)((NG * (T) + gr) * C::BK * D * 2);                               \
     _Pragma("unroll") for (int u = 0; u < C::NU; ++u) {                                            \
       const int n = 2 * u + wq;                                                                    \
       const unsigned o_ = off[u] >= 0x80000000u ? off[u] : off[u] + bo_;                           \
@@ -589,7 +591,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nq
   AP_ISSUE(0, 0)
   if (nstep > 1) AP_ISSUE(1, 1)
   for (int t = 0; t < nstep; ++t) {
-    const int st = t & 1, blk = 4 * t + gr;
+    const int st = t & 1, blk = NG * t + gr;
     if (t + 1 < nstep)
       __builtin_amdgcn_s_waitcnt(0x0F70 | C::NU);  // vmcnt(NU): step t has landed, t + 1 may fly
     else
@@ -678,17 +680,17 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nq
   }
   __syncthreads();
   if (gr == 0 && row_ok) {
-    float mg[4], M = m;
+    float mg[NG], M = m;
 #pragma unroll
-    for (int q = 1; q < 4; ++q) {
+    for (int q = 1; q < NG; ++q) {
       mg[q] = red[(2 * q + wq - 2) * WR + D * TP + j];
       M = fmaxf(M, mg[q]);
     }
-    float f[4];
+    float f[NG];
     f[0] = __builtin_amdgcn_exp2f(m - M);
     float L = f[0] * l;
 #pragma unroll
-    for (int q = 1; q < 4; ++q) {
+    for (int q = 1; q < NG; ++q) {
       f[q] = __builtin_amdgcn_exp2f(mg[q] - M);
       L += f[q] * red[(2 * q + wq - 2) * WR + D * TP + 32 + j];
     }
@@ -703,7 +705,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_kernel(AttnArgs a, int nq
           const int col = 32 * db + 8 * q + 4 * h2 + r;
           float acc = f[0] * o[db][4 * q + r];
 #pragma unroll
-          for (int gq = 1; gq < 4; ++gq) acc += f[gq] * red[(2 * gq + wq - 2) * WR + col * TP + j];
+          for (int gq = 1; gq < NG; ++gq) acc += f[gq] * red[(2 * gq + wq - 2) * WR + col * TP + j];
           v[r] = acc * inv;
         }
         store_bf16x4(out + 32 * db + 8 * q + 4 * h2, v[0], v[1], v[2], v[3]);
@@ -725,7 +727,16 @@ hipError_t launch_attention_d(const AttnArgs& a, bool decode, hipStream_t s) {
       hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(a.G * a.q_len, a.nkv, a.S), dim3(D), 0, s, a);
   } else {
     const int nqb = (a.q_len + 63) / 64;
-    hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(nqb * a.nq * a.S), dim3(512), 0, s, a, nqb);
+    // Two groups per workgroup (two workgroups per CU, which drift apart and
+    // overlap one's softmax with the other's products) when the units fill
+    // the CUs' two slots at least twice, or once with short chains; otherwise
+    // four groups (one workgroup per CU), which halves the longest chain.
+    const int64_t units = (int64_t)nqb * a.nq * a.S;
+    const dim3 grid((unsigned)units);
+    if (units >= 1024 || (units >= 512 && nqb <= 16))
+      hipLaunchKernelGGL((attn_prefill_kernel<D, 2>), grid, dim3(256), 0, s, a, nqb);
+    else
+      hipLaunchKernelGGL((attn_prefill_kernel<D, 4>), grid, dim3(512), 0, s, a, nqb);
   }
   return hipGetLastError();
 }

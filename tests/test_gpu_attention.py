@@ -139,6 +139,21 @@ def test_prefill_matches_oracle(heads, t, r, q_len, prior):
     assert_parity(host_f64(A), oracle.bf16_to_f64(c.ref()), f"prefill {heads} t={t} q={q_len}")
 
 
+@pytest.mark.parametrize("heads,t,r,S,q_len", [((64, 8, 128), 8, 0, 8, 1024), ((16, 4, 64), 2, 1, 4, 1000)])
+def test_prefill_two_group_form(heads, t, r, S, q_len):
+    """Enough query blocks for the two-group workgroups (1024 units of 64
+    tokens, or 512 with chains of at most 16 blocks), on top of ragged earlier
+    caches; sampled rows around the 64-token block edges and the ragged end."""
+    say("prefill two groups", heads, t, r, S, q_len)
+    prior = [0, 77, 300, 5, 64, 1, 200, 31][:S]
+    kv = [q_len + p for p in prior]
+    c = Case(heads, t, r, q_len, kv, list(range(S))[::-1], S, max(kv), 540 + S)
+    c.append()
+    A = host_bits(c.run())
+    rows = sorted({0, 63, 64, q_len - 1, q_len, q_len + 500, 2 * q_len + 127, S * q_len - 1, (S - 1) * q_len + 960})
+    assert_parity(oracle.bf16_to_f64(A[rows]), oracle.bf16_to_f64(c.ref(rows)), f"prefill two groups {heads}")
+
+
 @pytest.mark.parametrize("q_len", [1, 3, 40])
 def test_sharp_and_flat_attention(q_len):
     """Large query scale (nearly one-hot weights) and tiny scale (nearly
