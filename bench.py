@@ -611,8 +611,9 @@ def config_70b_attention_block(timer):
     head per rank, d = 128). Decode: 32 sequences with 4096 cached positions
     each, one new token; the core alone on rank 0 (HBM GB/s of the KV cache it
     reads), and the whole block for all 8 ranks in turn (QKV slice, KV append,
-    attention, O slice) plus the sum of the 8 partials. Prefill: rank 0's
-    attention core on one 4096-token sequence (causal FLOPs)."""
+    attention, O slice) plus the sum of the 8 partials; also the core at 256
+    sequences. Prefill: rank 0's attention core on one 4096-token and one
+    16384-token sequence (causal FLOPs)."""
     import torch
     import tensor_transformer_linear_megatron_amd as tp
     from seeded_inputs import workloads as wl
@@ -686,6 +687,37 @@ def config_70b_attention_block(timer):
                                stream))]
     us_pre = time_steps(timer, lambda i: _run(pre), 10)
     flops = 4 * nq * d * T * (T + 1) // 2
+    del Kp, Vp, QKVp, Ap, caches
+    # decode core at a serving batch (256 sequences x 4096 positions: one
+    # 4096-position chunk per workgroup, no merge) and the prefill core on one
+    # 16384-token sequence (the two-group form)
+    S2 = 256
+    K2, V2 = tp.tp_kv_cache_new(dq[0], S2, L)
+    K2.copy_(torch.randn(K2.shape, generator=g, device="cuda"))
+    V2.copy_(torch.randn(V2.shape, generator=g, device="cuda"))
+    Q2 = (torch.randn((S2, w), generator=g, device="cuda")).to(torch.bfloat16)
+    A2 = torch.empty((S2, nq * d), dtype=torch.bfloat16, device="cuda")
+    kl2 = torch.full((S2,), L, dtype=torch.int32, device="cuda")
+    sl2 = torch.arange(S2, dtype=torch.int32, device="cuda")
+    ws2n = max(16, tp.tp_attention_workspace_bytes(dq[0], S2, 1, L))
+    ws2 = torch.empty(ws2n, dtype=torch.uint8, device="cuda")
+    big = [(lib.tp_attention, (ref(dq[0]), VP(Q2.data_ptr()), w, S2, 1, VP(kl2.data_ptr()), VP(sl2.data_ptr()), L,
+                               VP(K2.data_ptr()), VP(V2.data_ptr()), S2, L, VP(A2.data_ptr()), nq * d,
+                               VP(ws2.data_ptr()), ws2n, stream))]
+    us_big = time_steps(timer, lambda i: _run(big), 20)
+    big_bytes = S2 * L * d * 2 * 2 + S2 * w * 2 + S2 * nq * d * 2
+    del K2, V2
+    T2 = 16384
+    Kq, Vq = tp.tp_kv_cache_new(dq[0], 1, T2)
+    Qq = (torch.randn((T2, w), generator=g, device="cuda")).to(torch.bfloat16)
+    Aq = torch.empty((T2, nq * d), dtype=torch.bfloat16, device="cuda")
+    klq = torch.full((1,), T2, dtype=torch.int32, device="cuda")
+    tp.tp_kv_append(dq[0], Qq, T2, klq, slp, Kq, Vq)
+    long_pre = [(lib.tp_attention, (ref(dq[0]), VP(Qq.data_ptr()), w, 1, T2, VP(klq.data_ptr()), VP(slp.data_ptr()),
+                                    T2, VP(Kq.data_ptr()), VP(Vq.data_ptr()), 1, T2, VP(Aq.data_ptr()), nq * d,
+                                    VP(0), 0, stream))]
+    us_long = time_steps(timer, lambda i: _run(long_pre), 5)
+    flops_long = 4 * nq * d * T2 * (T2 + 1) // 2
     return dict(config="llama3.1-70b attention, TP=8 (8 query heads + 1 KV head per rank, d=128)",
                 decode=dict(batch=S, context=L,
                             core_rank0=dict(us=round(us_core, 2), kv_bytes=kv_bytes,
@@ -694,9 +726,15 @@ def config_70b_attention_block(timer):
                             block_8_ranks=dict(us=round(us_block, 1), bytes=block_bytes,
                                                value=round(block_bytes / us_block / 1e3, 1), unit="GB/s",
                                                frac=round(block_bytes / us_block / 1e3 / HBM_PEAK_GBS, 4))),
+                decode_core_rank0_batch256=dict(batch=S2, context=L, us=round(us_big, 2),
+                                                value=round(big_bytes / us_big / 1e3, 1), unit="GB/s",
+                                                frac=round(big_bytes / us_big / 1e3 / HBM_PEAK_GBS, 4)),
                 prefill_core_rank0=dict(tokens=T, us=round(us_pre, 1), flops=flops,
                                         value=round(flops / us_pre / 1e6, 1), unit="TFLOP/s",
-                                        frac=round(flops / us_pre / 1e6 / MFMA_BF16_PEAK_TFS, 4)))
+                                        frac=round(flops / us_pre / 1e6 / MFMA_BF16_PEAK_TFS, 4)),
+                prefill_core_rank0_16384=dict(tokens=T2, us=round(us_long, 1), flops=flops_long,
+                                              value=round(flops_long / us_long / 1e6, 1), unit="TFLOP/s",
+                                              frac=round(flops_long / us_long / 1e6 / MFMA_BF16_PEAK_TFS, 4)))
 
 
 def config_405b_ffn_backward(timer):
