@@ -235,26 +235,30 @@ def test_max_kv_above_every_length():
     np.testing.assert_array_equal(a1, a2)
 
 
-@pytest.mark.parametrize("S,L,chunk", [(128, 2048, 1024), (64, 4096, 1024), (128, 4096, 2048), (256, 4096, 4096),
-                                       (32, 32768, 4096), (300, 700, 1024)])
-def test_decode_longer_chunks_for_large_batches(S, L, chunk):
-    """Many sequences: each workgroup takes 2, 4 or 8 passes of 512 positions,
-    or the whole cache (no combine); ragged lengths around the chunk edges.
-    Sampled rows."""
-    say("decode large batch", S, L)
-    part = (16 * 128 + 32) * 4
-    q = plans((64, 8, 128), 8, 0)[0]
+@pytest.mark.parametrize("heads,t,r,S,L,chunk", [
+    ((64, 8, 128), 8, 0, 128, 2048, 1024), ((64, 8, 128), 8, 0, 64, 4096, 1024),
+    ((64, 8, 128), 8, 0, 128, 4096, 2048), ((64, 8, 128), 8, 0, 256, 4096, 4096),
+    ((64, 8, 128), 8, 0, 32, 32768, 4096), ((64, 8, 128), 8, 0, 300, 700, 1024),
+    ((16, 4, 64), 2, 1, 128, 4096, 4096), ((16, 4, 64), 2, 1, 32, 4096, 1024)])
+def test_decode_longer_chunks_for_large_batches(heads, t, r, S, L, chunk):
+    """Many (sequence, key-value head) pairs: each workgroup takes 2, 4 or 8
+    passes of 512 positions, or the whole cache (no combine); ragged lengths
+    around the chunk edges; d = 128 and 64. Sampled rows."""
+    say("decode large batch", heads, S, L)
+    q, p = plans(heads, t, r)
+    nkv = p["kv_heads"][1] - p["kv_heads"][0]
+    part = (16 * heads[2] + 32) * 4
     n_chunks = -(-L // chunk)
-    assert tp.tp_attention_workspace_bytes(q, S, 1, L) == (S * n_chunks * part if n_chunks > 1 else 0)
+    assert tp.tp_attention_workspace_bytes(q, S, 1, L) == (S * nkv * n_chunks * part if n_chunks > 1 else 0)
     rng = np.random.default_rng(S + L)
     kv = [int(x) for x in rng.integers(1, L + 1, S)]
     kv[0], kv[-1] = L, min(L, chunk + 1)
     kv[1] = min(L, chunk)
-    c = Case((64, 8, 128), 8, 0, 1, kv, list(range(S)), S, L, 530)
+    c = Case(heads, t, r, 1, kv, list(range(S)), S, L, 530)
     c.append()
     A = host_bits(c.run(max_kv=L))
     rows = sorted({0, 1, S // 2, S - 1})
-    assert_parity(oracle.bf16_to_f64(A[rows]), oracle.bf16_to_f64(c.ref(rows)), f"decode {S} x {L}")
+    assert_parity(oracle.bf16_to_f64(A[rows]), oracle.bf16_to_f64(c.ref(rows)), f"decode {heads} {S} x {L}")
 
 
 # ---------------------------------------------------------------------------
