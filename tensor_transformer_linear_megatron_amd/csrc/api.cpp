@@ -90,7 +90,7 @@ size_t workspace_bytes(const tp_shard_desc* d, int64_t M, int64_t ldx) {
   const int64_t ntiles = d->packed_n / tpk::kTileN;
   if (is_fp8(d)) {
     if (path_of(d, M) == TP_PATH_DECODE)
-      return tpk::gemv_workspace_bytes(M, 2 * ksteps_of(d), ntiles, epilogue_of(d));
+      return tpk::gemv_workspace_bytes(M, 2 * ksteps_of(d), ntiles, epilogue_of(d), true);
     return dequant_bytes(d) + tpk::gemm_workspace_bytes(M, ldx, 2 * ksteps_of(d), ntiles);
   }
   if (path_of(d, M) == TP_PATH_DECODE)

@@ -17,6 +17,8 @@
 //    rows past M are read from a clamped address and zeroed by a lane mask.
 //    The S partial sums are reduced through LDS in wave order (deterministic)
 //    and the epilogue (bf16 rounding, SwiGLU or fp32) runs in registers.
+//    It also serves 17 to 32 tokens (two token blocks per wavefront) when
+//    the tile pairs fill the GPU and K is short, instead of a split.
 //  * gemv_shared (16 < M <= 64): at larger M every wavefront would re-read
 //    all the token fragments from L2 for its own tiles, which caps the rate.
 //    Here SN wavefronts of a workgroup own different 32-column blocks over
@@ -652,11 +654,25 @@ hipError_t launch_shared(const LinearArgs& a, float* ws, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 17 to 32 tokens over tile pairs that alone fill the GPU (256 or more),
+// where the shared-token kernel would have to split K: two token blocks per
+// wavefront in the streaming kernel, with no split and no fix-up launch. The
+// tokens are re-read from L2 by every wavefront, which costs less than the
+// fix-up only while K is short. Measured on the 70B TP = 8 shares at M = 24
+// and 32: the O slice (K = 1024) went from 10.2 to 7.1 us; the down share
+// (K = 3584) gained about 2 % alone and nothing inside the 8-rank step; every
+// shape whose pairs do not fill the GPU was slower.
+bool stream_two_blocks(int64_t M, int64_t ntiles, int64_t ksteps) {
+  return M > 16 && M <= 32 && ntiles >= 512 && ksteps <= 64 && plan_shared(ntiles, ksteps, 1).G > 1;
+}
+
 template <int T, int EPI>
 hipError_t launch_t(const LinearArgs& a, float* ws, hipStream_t s) {
   switch ((a.M + 15) / 16) {
     case 1: return launch_stream<1, T, EPI>(a, s);
-    case 2: return launch_shared<1, EPI>(a, ws, s);
+    case 2:
+      if (T == 2 && stream_two_blocks(a.M, a.ntiles, a.ksteps)) return launch_stream<2, T, EPI>(a, s);
+      return launch_shared<1, EPI>(a, ws, s);
     case 3:
     case 4: return launch_shared<2, EPI>(a, ws, s);
     default: return hipErrorInvalidValue;
@@ -730,8 +746,9 @@ hipError_t launch_split_fixup(const LinearArgs& a, Epilogue epi, const float* pa
   return hipGetLastError();
 }
 
-size_t gemv_workspace_bytes(int64_t M, int64_t ksteps, int64_t ntiles, Epilogue epi) {
+size_t gemv_workspace_bytes(int64_t M, int64_t ksteps, int64_t ntiles, Epilogue epi, bool f8) {
   if (M <= 16 || M > 64) return 0;
+  if (!f8 && stream_two_blocks(M, ntiles, ksteps)) return 0;  // tile pairs (ntiles >= 512) stream, no split
   (void)epi;
   const SharedPlan p = plan_shared(ntiles, ksteps, (int)((M + 31) / 32));
   return p.G > 1 ? (size_t)p.G * M * ntiles * kTileN * sizeof(float) : 0;

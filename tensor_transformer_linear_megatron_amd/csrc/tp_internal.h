@@ -86,12 +86,13 @@ hipError_t launch_wgrad(const uint16_t* A, int64_t lda, const uint16_t* dC, int6
 hipError_t launch_swiglu_bwd(const uint16_t* GU, int64_t ldgu, const float* dH, int64_t lddh,
                              int64_t M, int64_t w, uint16_t* dGU, int64_t lddgu, hipStream_t s);
 // Decode path for 8-bit shards, 1 <= M <= 64. `ws` as for launch_gemv, with
-// gemv_workspace_bytes(M, 2 ksteps, ntiles) (the plan counts bf16 k-steps).
+// gemv_workspace_bytes(M, 2 ksteps, ntiles, epi, true) (the plan counts bf16
+// k-steps).
 hipError_t launch_gemv8(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s);
 // Decode path. `ws` must hold gemv_workspace_bytes() bytes (fp32 split
 // partials) when that is non-zero.
 hipError_t launch_gemv(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s);
-size_t gemv_workspace_bytes(int64_t M, int64_t ksteps, int64_t ntiles, Epilogue epi);
+size_t gemv_workspace_bytes(int64_t M, int64_t ksteps, int64_t ntiles, Epilogue epi, bool f8 = false);
 // Prefill path. `ws` must hold gemm_workspace_bytes() bytes (fp32 split-K
 // partials, when the output tiles alone do not fill the GPU) when that is
 // non-zero.

@@ -165,6 +165,25 @@ def test_prefill_split_k_ragged(kind, K, N, t, r, M, heads):
     assert_parity(got, ref, f"{kind} K={K} N={N} t={t} r={r} M={M}")
 
 
+@pytest.mark.parametrize("M", [17, 24, 32])
+def test_decode_two_token_blocks_wide_shards(M):
+    """17 to 32 tokens over 256 or more tile pairs with a short K (the 70B
+    TP = 8 O slice and the like): the streaming kernel with two token blocks
+    per wavefront, with no split and no workspace; ragged K. Beyond 32 tokens
+    the split returns."""
+    say("decode two token blocks", M)
+    for kind, K, N, t, r, heads in (("o_row", 8192, 8192, 8, 3, (64, 8, 128)), ("row", 8 * 1000, 8192, 8, 2, None),
+                                    ("gateup_col", 2000, 2 * 4096, 1, 0, None), ("col", 1000, 8192, 1, 0, None)):
+        d = tp.tp_shard_plan(kind, K, N, t, r, heads=heads)
+        assert tp.tp_workspace_bytes(d, M) == 0
+        assert tp.tp_workspace_bytes(d, 33) > 0
+        if kind in ("row", "o_row"):
+            got, ref = _row_case(kind, K, N, t, r, M, tp.TP_PATH_AUTO, heads=heads)
+        else:
+            got, ref = _col_case(kind, K, N, t, r, M, tp.TP_PATH_AUTO, heads=heads)
+        assert_parity(got, ref, f"{kind} K={K} N={N} t={t} r={r} M={M}")
+
+
 @pytest.mark.parametrize("M", [17, 33, 50, 64])
 def test_decode_split_k_ragged(M):
     """Long ragged K with few output tiles: the decode path splits K over
