@@ -609,7 +609,9 @@ hipError_t launch_stream(const LinearArgs& a, hipStream_t s) {
 // How gemv_shared splits the work: SN waves (one 32-column block each) per
 // workgroup, G splits of the k-range of `per` k-steps each (a multiple of the
 // chunk), G the smallest power of two that gives ~200 workgroups while each
-// split keeps at least 2 chunks.
+// split keeps at least 2 chunks, and at most 16: beyond that the fix-up's
+// reads cost more than the extra workgroups gain (the 70B TP = 8 QKV slice,
+// 80 tiles, at M = 64: 32 splits 22 us, 16 splits 15.7 us, 8 splits 16.4 us).
 struct SharedPlan {
   int G;
   int64_t per, groups;
@@ -624,7 +626,7 @@ SharedPlan plan_shared(int64_t ntiles, int64_t ksteps, int MB32) {
   p.groups = (nblk + kSharedSN - 1) / kSharedSN;
   const int C = shared_chunk(MB32);
   int G = 1;
-  while (p.groups * G < 200 && ksteps / (2 * G) >= 2 * C) G <<= 1;
+  while (p.groups * G < 200 && G < 16 && ksteps / (2 * G) >= 2 * C) G <<= 1;
   p.per = ((ksteps + G - 1) / G + C - 1) / C * C;
   p.G = (int)((ksteps + p.per - 1) / p.per);
   return p;
