@@ -408,12 +408,58 @@ GemmPlan plan_gemm(int64_t M, int64_t ldx, int64_t ksteps, int64_t ntiles) {
   return p;
 }
 
+// The last round of big tiles, when it would run at most half full. If its
+// tiles (ids [full, nb) of gemm_big's grouped order) form a rectangle of
+// token tiles x column tiles, it runs as a sub-GEMM with K split G = 256 /
+// tiles ways (fp32 partials, then the split fix-up applies the epilogue), so
+// that whole 256 x 256 tiles fill the GPU; otherwise as 128-token half tiles.
+struct TailPlan {
+  bool split = false;
+  int64_t m0 = 0, rows = 0, nt0 = 0, nt = 0;  // token rows and packed tiles of the sub-GEMM
+  int G = 1;
+  int64_t kper = 0;
+};
+
+TailPlan plan_tail(int64_t M, int64_t ksteps, int64_t ntiles) {
+  TailPlan t;
+  const int64_t ntn = (ntiles + BIG_T - 1) / BIG_T, ntm = (M + BIG_MT * 16 - 1) / (BIG_MT * 16);
+  const int64_t nb = ntn * ntm, full = nb / 256 * 256, left = nb - full;
+  if (left == 0 || left > 128) return t;
+  int64_t G = 256 / left;
+  if (G > ksteps / 16) G = ksteps / 16;
+  if (G < 2) return t;
+  // gemm_big's tile of id b: groups of GM = 8 token tiles, column-major inside
+  constexpr int64_t GM = 8;
+  int64_t tm0 = ntm, tm1 = 0, tn0 = ntn, tn1 = 0;
+  for (int64_t b = full; b < nb; ++b) {
+    const int64_t first_m = b / (GM * ntn) * GM;
+    const int64_t gsize = ntm - first_m < GM ? ntm - first_m : GM;
+    const int64_t tm = first_m + (b % (GM * ntn)) % gsize, tn = (b % (GM * ntn)) / gsize;
+    tm0 = tm < tm0 ? tm : tm0;
+    tm1 = tm + 1 > tm1 ? tm + 1 : tm1;
+    tn0 = tn < tn0 ? tn : tn0;
+    tn1 = tn + 1 > tn1 ? tn + 1 : tn1;
+  }
+  if ((tm1 - tm0) * (tn1 - tn0) != left) return t;  // not a rectangle
+  t.m0 = tm0 * BIG_MT * 16;
+  t.rows = (tm1 * BIG_MT * 16 < M ? tm1 * BIG_MT * 16 : M) - t.m0;
+  t.nt0 = tn0 * BIG_T;
+  t.nt = (tn1 * BIG_T < ntiles ? tn1 * BIG_T : ntiles) - t.nt0;
+  t.kper = ((ksteps + G - 1) / G + 1) / 2 * 2;
+  t.G = (int)((ksteps + t.kper - 1) / t.kper);
+  t.split = t.G > 1;
+  return t;
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t M, int64_t ldx, int64_t ksteps, int64_t ntiles) {
   if (M <= 0) return 0;
   const GemmPlan p = plan_gemm(M, ldx, ksteps, ntiles);
-  return p.big && p.G > 1 ? (size_t)p.G * M * ntiles * kTileN * sizeof(float) : 0;
+  if (!p.big) return 0;
+  if (p.G > 1) return (size_t)p.G * M * ntiles * kTileN * sizeof(float);
+  const TailPlan t = plan_tail(M, ksteps, ntiles);
+  return t.split ? (size_t)t.G * t.rows * t.nt * kTileN * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s) {
@@ -430,11 +476,14 @@ hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t
   }
   if (p.big) {
     // One workgroup per CU at a time (128 KiB of LDS each). When the last
-    // round would run at most half full, its tiles are split into 128-token
-    // halves and run as a second launch that fills the GPU.
+    // round would run at most half full, it runs as a second launch that
+    // fills the GPU: a split-K sub-GEMM of whole tiles (plan_tail), or its
+    // tiles split into 128-token halves.
     const int64_t nb = ntn * ntm, full = nb / 256 * 256, left = nb - full;
     const bool split = left > 0 && left <= 128;
     const unsigned n1 = (unsigned)(split ? full : nb);
+    const TailPlan tp = plan_tail(a.M, a.ksteps, a.ntiles);
+    if (tp.split && ws == nullptr) return hipErrorInvalidValue;
     switch (epi) {
       case kEpiSwiglu: hipLaunchKernelGGL((gemm_big<kEpiSwiglu, 2, false>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0, 0, nullptr); break;
       case kEpiBf16: hipLaunchKernelGGL((gemm_big<kEpiBf16, 2, false>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0, 0, nullptr); break;
@@ -442,6 +491,25 @@ hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !split) return e;
+    if (tp.split) {
+      LinearArgs b = a;
+      b.X = a.X + tp.m0 * a.ldx;
+      b.M = tp.rows;
+      b.W = a.W + tp.nt0 * a.ksteps * kTileU4;
+      b.ntiles = tp.nt;
+      const int64_t col0 = epi == kEpiSwiglu ? tp.nt0 * kTileN / 2 : tp.nt0 * kTileN;
+      const int64_t width = epi == kEpiSwiglu ? tp.nt * kTileN / 2 : tp.nt * kTileN;
+      const size_t es = epi == kEpiF32 ? sizeof(float) : sizeof(uint16_t);
+      b.out = static_cast<char*>(a.out) + (size_t)(tp.m0 * a.ldo + col0) * es;
+      b.out_n = a.out_n - col0 < width ? a.out_n - col0 : width;
+      if (a.wscale != nullptr) b.wscale = a.wscale + tp.nt0 * kTileN;
+      const int64_t bn = (b.ntiles + BIG_T - 1) / BIG_T, bm = (b.M + BIG_MT * 16 - 1) / (BIG_MT * 16);
+      hipLaunchKernelGGL((gemm_big<kEpiF32, 2, true>), dim3((unsigned)(bn * bm), (unsigned)tp.G),
+                         dim3(BIG_THREADS), 0, s, b, (int)bn, (int)bm, 0, tp.kper, ws);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_split_fixup(b, epi, ws, tp.G, s);
+    }
     const dim3 g2((unsigned)(2 * left));
     switch (epi) {
       case kEpiSwiglu: hipLaunchKernelGGL((gemm_big<kEpiSwiglu, 1, false>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full, 0, nullptr); break;

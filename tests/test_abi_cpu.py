@@ -256,9 +256,11 @@ def _big_tiles(d, M):
 
 def test_workspace_bytes():
     """Decode batches of 17..64 tokens may split K over workgroups; the fp32
-    partials need G * M * packed_n * 4 bytes. Prefill splits K only when its
+    partials need G * M * packed_n * 4 bytes. Prefill splits K when its
     256 x 256 tiles cannot fill the 256 CUs: then G >= 2 splits of at least 16
-    k-steps with G * tiles <= 256. M <= 16 and invalid descriptors need none."""
+    k-steps with G * tiles <= 256. With 256 or more tiles only a last round
+    of at most 128 tiles may be split (see test_prefill_tail_workspace).
+    M <= 16 and invalid descriptors need none."""
     lib = _lib.load()
     for kind, K, N, t in (("col", 4096, 4096, 2), ("gateup_col", 8192, 57344, 8), ("row", 28672, 8192, 8),
                           ("row", 14336, 4096, 1), ("gateup_col", 4096, 28672, 1), ("row", 1024, 8192, 1)):
@@ -273,9 +275,17 @@ def test_workspace_bytes():
         for M in (32, 65, 300, 4096, 8192):
             dd = pre if M <= 64 else d
             ws = tp.tp_workspace_bytes(dd, M)
+            tiles, ksteps = _big_tiles(d, M), d.packed_k // 32
+            if tiles >= 256:
+                left = tiles % 256
+                if left == 0 or left > 128:
+                    assert ws == 0, (kind, K, N, M)
+                else:  # the last round's tiles, split at most 256 // left ways
+                    assert ws <= (256 // left) * M * d.packed_n * 4, (kind, K, N, M)
+                continue
             assert ws % (M * d.packed_n * 4) == 0
-            G, tiles, ksteps = ws // (M * d.packed_n * 4), _big_tiles(d, M), d.packed_k // 32
-            if tiles >= 256 or min(256 // tiles, ksteps // 16) < 2:
+            G = ws // (M * d.packed_n * 4)
+            if min(256 // tiles, ksteps // 16) < 2:
                 assert G == 0, (kind, K, N, M)
             else:
                 assert G >= 2 and G * tiles <= 256 and -(-ksteps // G) >= 16, (kind, K, N, M, G)
@@ -289,6 +299,33 @@ def test_workspace_bytes():
             == _lib.TP_ERR_WORKSPACE
         assert lib.tp_row_linear(ctypes.byref(d), A, 64, 14336, B, C, 4096, A, 16, ctypes.c_void_p(0)) \
             == _lib.TP_ERR_WORKSPACE
+
+
+def test_prefill_tail_workspace():
+    """A last round of at most 128 big tiles whose tiles (in the kernel's
+    grouped order: 8 token tiles deep, column-major inside a group) form a
+    rectangle runs as a sub-GEMM with K split 256 // tiles ways (at least 16
+    k-steps each), its fp32 partials in the workspace."""
+    part = 16 * 4  # bytes per packed tile column per token
+    # 405B gate/up, rank 0 of 8, 8192 tokens: 52 x 32 tiles, the last 128 are
+    # token tiles 24..31 x column tiles 36..51: 2 splits of 2048 x 256 tiles
+    d = tp.tp_shard_plan("gateup_col", 16384, 2 * 53248, 8, 0)
+    assert tp.tp_workspace_bytes(d, 8192) == 2 * 2048 * 256 * part
+    # 70B gate/up, rank 0 of 8: 28 x 32 tiles, the last 128 are 8 x 16
+    d = tp.tp_shard_plan("gateup_col", 8192, 57344, 8, 0)
+    assert tp.tp_workspace_bytes(d, 8192) == 2 * 2048 * 256 * part
+    # 17 x 16 tiles, ragged everywhere: the last 16 are token tiles 8..15 x
+    # column tiles 15, 16 (packed tiles 240 .. packed_n / 16), K = 1000 in 2 splits
+    d = tp.tp_shard_plan("col", 1000, 4328, 1, 0)
+    assert d.packed_n // 16 == 272
+    assert tp.tp_workspace_bytes(d, 4000) == 2 * (4000 - 2048) * (272 - 240) * part
+    # 21 x 13 tiles: the last 17 span column tiles 17..20 and token tiles
+    # 8..12 without filling them, so they run as half tiles with no workspace
+    d = tp.tp_shard_plan("col", 1024, 5376, 1, 0)
+    assert tp.tp_workspace_bytes(d, 3300) == 0
+    # 17 x 16 tiles with 1 k-step: too short to split
+    d = tp.tp_shard_plan("col", 32, 4352, 1, 0)
+    assert tp.tp_workspace_bytes(d, 4096) == 0
 
 
 @pytest.mark.parametrize("kind,K,N,t,r,heads", [("col", 4096, 1024, 4, 1, None), ("row", 1024, 4096, 4, 3, None),

@@ -142,6 +142,38 @@ def test_prefill_big_tile_ragged(kind, K, N, t, r, M):
     assert_parity(got, ref, f"{kind} K={K} N={N} t={t} r={r} M={M}")
 
 
+# 17 x 16 big tiles: 256 run whole, the last 16 (token tiles 8..15 x column
+# tiles 15 and 16) form a rectangle and run as a sub-GEMM with K split 2 ways
+# (fp32 partials, then the fix-up applies the epilogue). Ragged K, columns and
+# tokens; rows sampled from both parts (rows are independent).
+TAIL_CASES = [("col", 1000, 4328, 1, 0, 4000), ("gateup_col", 1000, 2 * 2168, 1, 0, 4000),
+              ("row", 1000, 4328, 1, 0, 4000)]
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,M", TAIL_CASES)
+def test_prefill_tail_split_k(kind, K, N, t, r, M):
+    say("prefill tail split-K", kind, K, N, t, r, M)
+    d, p = plan_both(kind, K, N, t, r)
+    d = with_path(d, tp.TP_PATH_PREFILL)
+    assert tp.tp_workspace_bytes(d, M) == 2 * (M - 2048) * (d.packed_n // 16 - 240) * 16 * 4
+    X = si.normal_bf16(90, (M, K), 1.0)
+    W = si.normal_bf16(91, (K, N), 0.05)
+    Wp = tp.tp_shard_pack(d, dev(W))
+    rows = [0, 1, 1000, 2047, 2048, 2049, 3000, 3998, 3999]
+    if kind == "row":
+        got = host_f64(tp.tp_row_linear(d, dev(X), Wp))[rows]
+        ref = oracle.row_linear(X[rows], W, p)
+    else:
+        got = host_f64(tp.tp_col_linear(d, dev(X), Wp))[rows]
+        if kind == "gateup_col":
+            ref = oracle.bf16_to_f64(oracle.gateup_swiglu(X[rows], W, p))
+        else:
+            ref = oracle.bf16_to_f64(oracle.col_linear_bf16(X[rows], W, p))
+    assert_parity(got, ref, f"{kind} K={K} N={N} M={M} (tail split)")
+    # the tail rectangle on its own, against the same rows' reference
+    assert_parity(got[4:], ref[4:], f"{kind} tail rows")
+
+
 # Few 256 x 256 output tiles and a long ragged K: the prefill path splits K
 # over workgroups (fp32 partials in the workspace, summed in split order by
 # the fix-up, which applies the epilogue). The last split has an odd number of
