@@ -408,8 +408,9 @@ TP_API size_t tp_attention_workspace_bytes(const tp_shard_desc* qkv, int32_t S, 
 /* Bytes of device workspace tp_col_linear / tp_row_linear need for this
  * shard at this M: fp32 partial sums when K is split over workgroups (decode
  * batches of 17..64 tokens with few output tiles; prefill shapes whose output
- * tiles alone cannot fill the GPU); 0 when the chosen kernels need none or
- * the descriptor is invalid. The value assumes X at its smallest leading
+ * tiles alone cannot fill the GPU, or whose last round of tiles would run at
+ * most half full), plus the dequantised copy of an 8-bit shard on the prefill
+ * path; 0 when the chosen kernels need none or the descriptor is invalid. The value assumes X at its smallest leading
  * dimension (shard_k); a wider one never needs more. tp_ffn_shard needs the
  * larger of its two descriptors' values. */
 TP_API size_t tp_workspace_bytes(const tp_shard_desc* desc, int64_t M);
