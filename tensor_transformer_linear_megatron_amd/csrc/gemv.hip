@@ -524,6 +524,15 @@ __global__ __launch_bounds__(64 * SN) void gemv_shared(LinearArgs a, int64_t per
   }
 }
 
+constexpr int FIX_U = 8;  // split partials loaded together by the fix-up
+
+__device__ __forceinline__ void add4(float4& a, const float4& b) {
+  a.x += b.x;
+  a.y += b.y;
+  a.z += b.z;
+  a.w += b.w;
+}
+
 // Adds the G split partials in split order and applies the epilogue. One
 // thread per 4 output columns of one token row.
 template <int EPI>
@@ -541,29 +550,39 @@ __global__ __launch_bounds__(256) void gemv_fixup(LinearArgs a, const float* par
     const float* pg = part + m * pld + gc;
     float4 gs = *reinterpret_cast<const float4*>(pg);
     float4 us = *reinterpret_cast<const float4*>(pg + kTileN);
-    for (int y = 1; y < G; ++y) {
-      const float4 a4 = *reinterpret_cast<const float4*>(pg + y * split);
-      const float4 b4 = *reinterpret_cast<const float4*>(pg + y * split + kTileN);
-      gs.x += a4.x;
-      gs.y += a4.y;
-      gs.z += a4.z;
-      gs.w += a4.w;
-      us.x += b4.x;
-      us.y += b4.y;
-      us.z += b4.z;
-      us.w += b4.w;
+    // Loads in groups of FIX_U, all in flight together (indices past the
+    // last split re-read the last one and are not added); the adds stay in
+    // split order.
+    for (int y0 = 1; y0 < G; y0 += FIX_U) {
+      float4 a4[FIX_U], b4[FIX_U];
+#pragma unroll
+      for (int u = 0; u < FIX_U; ++u) {
+        const int64_t y = y0 + u < G ? y0 + u : G - 1;
+        a4[u] = *reinterpret_cast<const float4*>(pg + y * split);
+        b4[u] = *reinterpret_cast<const float4*>(pg + y * split + kTileN);
+      }
+#pragma unroll
+      for (int u = 0; u < FIX_U; ++u)
+        if (y0 + u < G) {
+          add4(gs, a4[u]);
+          add4(us, b4[u]);
+        }
     }
     store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + c, swiglu(gs.x, us.x),
                  swiglu(gs.y, us.y), swiglu(gs.z, us.z), swiglu(gs.w, us.w));
   } else {
     const float* pp = part + m * pld + c;
     float4 s = *reinterpret_cast<const float4*>(pp);
-    for (int y = 1; y < G; ++y) {
-      const float4 b4 = *reinterpret_cast<const float4*>(pp + y * split);
-      s.x += b4.x;
-      s.y += b4.y;
-      s.z += b4.z;
-      s.w += b4.w;
+    for (int y0 = 1; y0 < G; y0 += FIX_U) {
+      float4 b4[FIX_U];
+#pragma unroll
+      for (int u = 0; u < FIX_U; ++u) {
+        const int64_t y = y0 + u < G ? y0 + u : G - 1;
+        b4[u] = *reinterpret_cast<const float4*>(pp + y * split);
+      }
+#pragma unroll
+      for (int u = 0; u < FIX_U; ++u)
+        if (y0 + u < G) add4(s, b4[u]);
     }
     if constexpr (EPI == kEpiBf16) {
       store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + c, s.x, s.y, s.z, s.w);
