@@ -379,10 +379,38 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
 
 // Workgroup (rho, g, s), thread c: output column c of row rho, merged over
 // the chunks in chunk order. Up to kCombineRegs chunks, every load goes out in
-// one batch (each thread holds the chunks' maxima, sums and its column);
-// beyond that the chunks' maxima and sums are fetched a tile of D chunks at a
-// time, one per thread, and shared through LDS.
+// one batch (each thread holds the chunks' maxima, sums and its column; the
+// loads take a clamped chunk index, so none sits behind a branch and the
+// entries past the last chunk are never used); beyond that the chunks' maxima
+// and sums are fetched a tile of D chunks at a time, one per thread, and
+// shared through LDS.
 constexpr int kCombineRegs = 32;
+
+template <int D, int NR>
+__device__ __forceinline__ float combine_regs(const AttnArgs& a, const float* P0, int rho, int c) {
+  constexpr int RED = kAttnDecodeRows * D + 2 * kAttnDecodeRows;
+  float mc[NR], lc[NR], oc[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const float* Pj = P0 + (int64_t)(j < a.nchunk ? j : a.nchunk - 1) * RED;
+    mc[j] = Pj[kAttnDecodeRows * D + rho];
+    lc[j] = Pj[kAttnDecodeRows * D + kAttnDecodeRows + rho];
+    oc[j] = Pj[rho * D + c];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+    if (j < a.nchunk) M = fmaxf(M, mc[j]);
+  float L = 0.f, acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+    if (j < a.nchunk && mc[j] != -INFINITY) {
+      const float f = __builtin_amdgcn_exp2f(mc[j] - M);
+      L += f * lc[j];
+      acc += f * oc[j];
+    }
+  return L > 0.f ? acc / L : 0.f;
+}
 
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
@@ -396,29 +424,10 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   const int hh = rho / a.q_len, tok = rho - hh * a.q_len;
   uint16_t* dst = a.A + ((int64_t)s * a.q_len + tok) * a.lda + (int64_t)(g * a.G + hh) * D + c;
   if (a.nchunk <= kCombineRegs) {  // uniform
-    float mc[kCombineRegs], lc[kCombineRegs], oc[kCombineRegs];
-#pragma unroll
-    for (int j = 0; j < kCombineRegs; ++j) {
-      if (j < a.nchunk) {
-        const float* Pj = P0 + (int64_t)j * RED;
-        mc[j] = Pj[kAttnDecodeRows * D + rho];
-        lc[j] = Pj[kAttnDecodeRows * D + kAttnDecodeRows + rho];
-        oc[j] = Pj[rho * D + c];
-      }
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kCombineRegs; ++j)
-      if (j < a.nchunk) M = fmaxf(M, mc[j]);
-    float L = 0.f, acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < kCombineRegs; ++j)
-      if (j < a.nchunk && mc[j] != -INFINITY) {
-        const float f = __builtin_amdgcn_exp2f(mc[j] - M);
-        L += f * lc[j];
-        acc += f * oc[j];
-      }
-    *dst = f32_to_bf16(kl > 0 && L > 0.f ? acc / L : 0.f);
+    const float v = a.nchunk <= 8    ? combine_regs<D, 8>(a, P0, rho, c)
+                    : a.nchunk <= 16 ? combine_regs<D, 16>(a, P0, rho, c)
+                                     : combine_regs<D, kCombineRegs>(a, P0, rho, c);
+    *dst = f32_to_bf16(kl > 0 ? v : 0.f);
     return;
   }
   float M = -INFINITY;
