@@ -812,8 +812,8 @@ def main():
                     help="only run a plain device copy of known size (the yardstick for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs every tensor-parallel rank in turn on a "
-              "single MI355X and has no multi-GPU path; run it with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: every tensor-parallel rank runs in turn on a single MI355X "
+              "and there is no multi-GPU path; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
