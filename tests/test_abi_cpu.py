@@ -328,6 +328,58 @@ def test_prefill_tail_workspace():
     assert tp.tp_workspace_bytes(d, 4096) == 0
 
 
+def _tail_ws(M, K, N):
+    """The documented rule, restated: 256 x 256 tiles in groups of 8 token
+    tiles, column-major inside a group; a last round of 1..128 tiles that form
+    a rectangle is split min(256 // tiles, ksteps // 16) >= 2 ways (k-steps per
+    split rounded up to even)."""
+    ntiles = -(-N // 32) * 2  # packed tiles: whole pairs
+    ksteps = -(-K // 32)
+    ntn, ntm = -(-ntiles // 16), -(-M // 256)
+    nb = ntn * ntm
+    full, left = nb // 256 * 256, nb % 256
+    if nb < 256 or left == 0 or left > 128:
+        return None
+    G = min(256 // left, ksteps // 16)
+    if G < 2:
+        return 0
+    cells = set()
+    for b in range(full, nb):
+        first = b // (8 * ntn) * 8
+        gsize = min(8, ntm - first)
+        cells.add((first + (b % (8 * ntn)) % gsize, (b % (8 * ntn)) // gsize))
+    tms = {c[0] for c in cells}
+    tns = {c[1] for c in cells}
+    if (max(tms) - min(tms) + 1) * (max(tns) - min(tns) + 1) != left:
+        return 0
+    kper = (-(-ksteps // G) + 1) // 2 * 2
+    G = -(-ksteps // kper)
+    if G < 2:
+        return 0
+    rows = min((max(tms) + 1) * 256, M) - min(tms) * 256
+    nt = min((max(tns) + 1) * 16, ntiles) - min(tns) * 16
+    return G * rows * nt * 16 * 4
+
+
+def test_prefill_tail_workspace_random_shapes():
+    """Seeded random column shards with 256 or more big tiles: the library's
+    workspace equals the rule restated above whenever the last round is at
+    most half full (rectangle or not)."""
+    rng = np.random.default_rng(5)
+    seen = {"split": 0, "none": 0}
+    for _ in range(300):
+        M = int(rng.integers(2049, 12000))
+        N = int(rng.integers(8, 600)) * 8 * 8
+        K = int(rng.integers(1, 64)) * 8 * 8
+        want = _tail_ws(M, K, N)
+        if want is None:
+            continue
+        d = tp.tp_shard_plan("col", K, N, 1, 0)
+        assert tp.tp_workspace_bytes(d, M) == want, (M, K, N)
+        seen["split" if want else "none"] += 1
+    assert seen["split"] >= 5 and seen["none"] >= 5, seen
+
+
 @pytest.mark.parametrize("kind,K,N,t,r,heads", [("col", 4096, 1024, 4, 1, None), ("row", 1024, 4096, 4, 3, None),
                                                  ("gateup_col", 8192, 2 * 28672, 8, 5, None),
                                                  ("qkv_col", 512, (8 + 2 * 2) * 64, 2, 1, (8, 2, 64)),
