@@ -2,19 +2,20 @@
  * tp_shard.h -- one tensor-parallel rank's linear share of a Megatron-style
  * transformer layer on an MI355X (gfx950) GPU.
  *
- * The method, as the pages state it:
- *   - "Tensor vs Pipeline Parallelism" (xingyuzhitong.com), section "Tensor
- *     parallelism: split inside each layer": the first linear layer of the
- *     feed-forward block is split by columns and the second by rows, attention
- *     heads are distributed among GPUs, and the partial results are combined
- *     by an all-reduce.
- *   - "AI Infrastructure series, Part 5" (drpranayjha.com), section "How does
- *     tensor parallelism split a layer?": the first matrix of each block by
- *     columns, the second by rows; each GPU holds and reads 1/N of every
- *     matrix; 64 query heads split over 2, 4 or 8 GPUs but not 3 or 6; past
- *     the 8 key-value heads a group repeats key-value heads.
+ * The method, after these pages (title, section):
+ *   - "Tensor vs Pipeline Parallelism" (xingyuzhitong.com), "Tensor
+ *     parallelism: split inside each layer": in the MLP the leading weight
+ *     matrix is cut along its output columns and the trailing one along its
+ *     input rows; the attention heads are shared out over the ranks; one
+ *     all-reduce then adds up the ranks' partial products.
+ *   - "AI Infrastructure series, Part 5" (drpranayjha.com), "How does tensor
+ *     parallelism split a layer?": attention and MLP are cut the same way
+ *     (columns, then rows), so a rank stores and streams 1/N of each matrix;
+ *     a 64-query-head model takes 2, 4 or 8 ranks, never 3 or 6, and a group
+ *     larger than the 8 key-value heads holds copies of key-value heads.
  *   - "Tensor Parallelism" glossary (aidolsgroup.com), "Full definition":
- *     activations are broadcast and partial outputs are summed.
+ *     every rank sees the same input and the ranks' partial products are
+ *     added.
  *   - "How do tensor parallelism (TP) and pipeline parallelism (PP) split large
  *     model weights ...?" (iloveeagents.com), "Detail" and "Example": a
  *     4096 x 4096 W cut column-wise into two 4096 x 2048 pieces; a
@@ -148,9 +149,9 @@ TP_API tp_status tp_shard_plan(tp_kind kind, int64_t K, int64_t N, int32_t t, in
 
 /*
  * Switches a planned shard to another weight storage before it is packed
- * ("AI Infrastructure series, Part 5", "Reason 2": in decode every token
- * reads every weight, so a 70B model in 8-bit reads 70.6 GB per token, half
- * its 16-bit bytes). Sets desc->wformat and recomputes packed_k and
+ * ("AI Infrastructure series, Part 5", "Reason 2": a decoded token streams
+ * all the weights, 70.6 GB for a 70B model stored in 8 bits, half of its
+ * 16-bit size). Sets desc->wformat and recomputes packed_k and
  * packed_bytes; everything else is unchanged.
  *   TP_W_BF16: packed_k = shard_k rounded up to 32, 2 bytes per weight.
  *   TP_W_FP8_E4M3: weight-only 8-bit storage; the activations stay bf16.
@@ -169,7 +170,7 @@ TP_API tp_status tp_shard_set_wformat(tp_shard_desc* desc, int32_t wformat);
 /*
  * Copies the rank's shard out of the full weight into the kernels' packed
  * layout ("AI Infrastructure series, Part 5", "What does it look like in vLLM
- * ...": the engine splits the weights as it loads them). Load-time work.
+ * ...": the shards are cut once, while the model is loaded). Load-time work.
  *   W        device, full logical [K x N] bf16, row-major, leading dim ldw >= N
  *   W_packed device, desc->packed_bytes bytes, 16-byte aligned; its layout is
  *            private to the library (tiles of 16 output columns x 32 k for
@@ -240,8 +241,8 @@ TP_API tp_status tp_ffn_shard(const tp_shard_desc* gateup, const tp_shard_desc* 
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * The sum that replaces the all-reduce ("Tensor Parallelism" glossary:
- * partial outputs are summed; "Tensor vs Pipeline Parallelism": two
+ * The sum that replaces the all-reduce ("Tensor Parallelism" glossary,
+ * "Full definition": the ranks' partial products are added; "Tensor vs Pipeline Parallelism": two
  * all-reduces per layer, after attention and after the feed-forward block):
  *   Y[m][n] = P_0[m][n] + P_1[m][n] + ... + P_{t-1}[m][n], added in fp32 in
  *   rank order, where P_r = P + r * stride_elems is [M x N] with leading dim
@@ -337,12 +338,12 @@ TP_API tp_status tp_swiglu_backward(const uint16_t* GU, int64_t ldgu, const floa
 /*
  * Attention core on the rank's heads, with the rank's share of the KV cache
  * ("Tensor vs Pipeline Parallelism", "Tensor parallelism: split inside each
- * layer": attention heads are distributed among the GPUs, each computing its
- * slice and keeping its heads' share of the KV cache; "AI Infrastructure
- * series, Part 5", "How does tensor parallelism split a layer?": each GPU
- * holds 1/N of the KV cache, and past the key-value head count a larger
- * group repeats key-value heads; "How do you choose a layout for serving?":
- * 320 KB of KV cache per token for Llama 3.1 70B in 16-bit). The pages give
+ * layer": the heads are shared out over the ranks, and a rank keeps the KV
+ * cache of its own heads only; "AI Infrastructure series, Part 5", "How does
+ * tensor parallelism split a layer?": a rank's KV cache is 1/N of the
+ * whole, and ranks beyond the key-value head count hold copies of a
+ * key-value head; "How do you choose a layout for serving?": Llama 3.1 70B
+ * in 16-bit needs 320 KB of KV cache per token). The pages give
  * no formula; the one computed is, per query head of the rank,
  *   softmax(q k^T / sqrt(d)) v
  * over the positions 0..p of its sequence, p its own position (causal), with

@@ -13,16 +13,18 @@ Sources (cited by page title and section):
   piece; "Example": a column-parallel linear keeps out_features / t output
   features and computes the local product x @ W_r.
 * "Tensor vs Pipeline Parallelism" (xingyuzhitong.com), "Tensor parallelism:
-  split inside each layer": first feed-forward matrix by columns, second by
-  rows, attention heads distributed, partial results combined by a sum; the
-  head and key-value head counts must divide evenly. "Common mistakes": a
-  degree that does not divide the key-value heads is refused.
+  split inside each layer": the MLP's leading matrix is cut by output
+  columns and its trailing one by input rows, the heads are shared out, and
+  the ranks' partial products are added; head and key-value head counts
+  have to be multiples of the degree. "Common mistakes": frameworks reject a
+  degree that the key-value heads do not divide.
 * "AI Infrastructure series, Part 5" (drpranayjha.com), "How does tensor
-  parallelism split a layer?": 64 query heads split over 2, 4 or 8 ranks, not
-  3 or 6; beyond the 8 key-value heads a group repeats key-value heads.
-  "Short answers": same maths, only the order of additions differs.
-* "Tensor Parallelism" glossary (aidolsgroup.com), "Full definition":
-  activations broadcast, partial outputs summed.
+  parallelism split a layer?": a 64-query-head model takes 2, 4 or 8 ranks,
+  never 3 or 6, and ranks beyond the 8 key-value heads hold copies of a
+  key-value head. "Short answers": the split changes only the order of the
+  additions, hence only the last digits.
+* "Tensor Parallelism" glossary (aidolsgroup.com), "Full definition": every
+  rank sees the same input; the partial products are added.
 
 Readings where the pages are silent (the same list is in the design notes):
 
@@ -61,7 +63,12 @@ Readings where the pages are silent (the same list is in the design notes):
   the next column-parallel product are the ranks' row blocks stacked in rank
   order (an all-gather); M must divide by t.
 
-Every function below is parity-pinned by ``tests/test_oracle_pins.py``.
+Every product below, whatever its operands (bf16 shards, dequantised 8-bit
+shards, gradients, attention scores), is the C core's in-order fp64 loop:
+one accumulator per output, the contraction index ascending, no BLAS.
+
+Every function below is parity-pinned by ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_attention_pins.py``.
 """
 from __future__ import annotations
 
@@ -92,6 +99,7 @@ def _load():
         lib.orc_shard_matmul.argtypes = [P, I64, I64, I64, P, I64, P, P, I64, P]
         lib.orc_swiglu.argtypes = [P, P, I64, P]
         lib.orc_sum_partials.argtypes = [P, I64, ctypes.c_int32, I64, P]
+        lib.orc_matmul_f64.argtypes = [P, I64, I64, I64, I64, P, I64, I64, I64, P]
         _lib = lib
     return _lib
 
@@ -237,6 +245,35 @@ def shard_matmul(X: np.ndarray, W: np.ndarray, rows: np.ndarray, cols: np.ndarra
     return Y
 
 
+def _f64_strided(a: np.ndarray) -> tuple[np.ndarray, int, int]:
+    """(array, row stride, column stride) in elements of a 2-D fp64 array;
+    transposed views are passed as they are, anything else is copied."""
+    a = np.asarray(a, dtype=np.float64)
+    assert a.ndim == 2
+    s0, s1 = a.strides
+    if s0 < 0 or s1 < 0 or s0 % 8 or s1 % 8:
+        a = np.ascontiguousarray(a)
+        s0, s1 = a.strides
+    return a, s0 // 8, s1 // 8
+
+
+def matmul_f64(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """C[m, n] = sum_k A[m, k] B[k, n] in fp64, k ascending, one accumulator
+    per output (the C core's in-order loop; no BLAS)."""
+    A, sam, sak = _f64_strided(A)
+    B, sbk, sbn = _f64_strided(B)
+    M, K = A.shape
+    assert B.shape[0] == K, (A.shape, B.shape)
+    N = B.shape[1]
+    C = np.empty((M, N), dtype=np.float64)
+    if M and N:
+        if K == 0:
+            C[:] = 0.0
+        else:
+            _load().orc_matmul_f64(_ptr(A), M, K, sam, sak, _ptr(B), N, sbk, sbn, _ptr(C))
+    return C
+
+
 def swiglu(G: np.ndarray, U: np.ndarray) -> np.ndarray:
     """bf16 bits of SiLU(G) * U, rounded once from fp64."""
     G = np.ascontiguousarray(G, dtype=np.float64)
@@ -287,8 +324,8 @@ def gather_rows(blocks) -> np.ndarray:
 
 # --------------------------------------------------------------------------
 # 8-bit weights for decode ("AI Infrastructure series, Part 5", "Reason 2":
-# in decode every token reads every weight, so a 70B model in 8-bit reads
-# 70.6 GB per token, half its 16-bit bytes). The pages fix no format. Reading
+# a decoded token streams all the weights, 70.6 GB for a 70B model stored in
+# 8 bits, half of its 16-bit size). The pages fix no format. Reading
 # taken: OCP FP8 E4M3 codes with one power-of-two scale per output column of
 # the rank's shard; the activations stay bf16 (weight-only quantisation).
 # --------------------------------------------------------------------------
@@ -364,7 +401,7 @@ def shard_weight_fp8(W: np.ndarray, p: dict) -> np.ndarray:
 def col_linear_fp8(X: np.ndarray, W: np.ndarray, p: dict) -> np.ndarray:
     """X W'_r in fp64, unrounded (W'_r: the dequantised 8-bit shard)."""
     assert p["kind"] in ("col", "qkv_col")
-    return bf16_to_f64(X) @ shard_weight_fp8(W, p)
+    return matmul_f64(bf16_to_f64(X), shard_weight_fp8(W, p))
 
 
 def gateup_swiglu_fp8(X: np.ndarray, Wgu: np.ndarray, p: dict) -> np.ndarray:
@@ -373,13 +410,13 @@ def gateup_swiglu_fp8(X: np.ndarray, Wgu: np.ndarray, p: dict) -> np.ndarray:
     Wq = shard_weight_fp8(Wgu, p)
     half = p["shard_n"] // 2
     Xf = bf16_to_f64(X)
-    return swiglu(Xf @ Wq[:, :half], Xf @ Wq[:, half:])
+    return swiglu(matmul_f64(Xf, Wq[:, :half]), matmul_f64(Xf, Wq[:, half:]))
 
 
 def row_linear_fp8(Z: np.ndarray, W: np.ndarray, p: dict) -> np.ndarray:
     """P_r = Z_r W'[rows_r, :] in fp64 with the 8-bit row shard."""
     assert p["kind"] in ("row", "o_row")
-    return bf16_to_f64(Z) @ shard_weight_fp8(W, p)
+    return matmul_f64(bf16_to_f64(Z), shard_weight_fp8(W, p))
 
 
 # --------------------------------------------------------------------------
@@ -400,13 +437,13 @@ def grad_input(dC: np.ndarray, W: np.ndarray, p: dict) -> np.ndarray:
     linear with respect to its input. dC_r (bf16 bits) is the gradient of the
     rank's output: [M x shard_n] in shard column order for the column kinds
     ([dG | dU] for gate/up), the full [M x N] output gradient for the row kinds."""
-    return bf16_to_f64(dC) @ _shard_weight_f64(W, p).T
+    return matmul_f64(bf16_to_f64(dC), _shard_weight_f64(W, p).T)
 
 
 def grad_weight(A: np.ndarray, dC: np.ndarray, p: dict) -> np.ndarray:
     """dW_r = A_r^T dC_r, fp64 [shard_k x shard_n]: A_r (bf16 bits) is the
     rank's input (X for the column kinds, its own Z_r for the row kinds)."""
-    return bf16_to_f64(A).T @ bf16_to_f64(dC)
+    return matmul_f64(bf16_to_f64(A).T, bf16_to_f64(dC))
 
 
 def gateup_preact(X: np.ndarray, Wgu: np.ndarray, p: dict):
@@ -480,9 +517,14 @@ def ffn_unsharded(X: np.ndarray, Wgu: np.ndarray, Wd: np.ndarray) -> np.ndarray:
 
 
 def compare(got: np.ndarray, ref: np.ndarray) -> dict:
-    """Relative Frobenius error and max element error against max |ref|."""
+    """The parity bar's two measures of ``got`` against ``ref`` (same shape):
+    rel_fro = ||got - ref||_F / ||ref||_F (||got - ref||_F when ref is all
+    zero), max_err = max |got - ref|, max_ref = max |ref| and max_rel =
+    max_err / max_ref. A shape mismatch is an error, not a broadcast."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:  # never let broadcasting stand in for a missing row
+        raise ValueError(f"compare: shapes differ, got {got.shape} and ref {ref.shape}")
     diff = got - ref
     nref = np.linalg.norm(ref)
     amax = float(np.abs(ref).max()) if ref.size else 0.0
@@ -497,12 +539,12 @@ def compare(got: np.ndarray, ref: np.ndarray) -> dict:
 # --------------------------------------------------------------------------
 # Attention core on the rank's heads, with the rank's share of the KV cache
 # ("Tensor vs Pipeline Parallelism", "Tensor parallelism: split inside each
-# layer": attention heads are distributed among the GPUs, each computing its
-# slice, and each GPU keeps its heads' share of the KV cache; "AI
-# Infrastructure series, Part 5", "How does tensor parallelism split a
-# layer?": 1/N of the KV cache per GPU, and past the 8 key-value heads a
-# larger group repeats key-value heads, which wastes KV memory; "Step 1: does
-# it fit?": 320 KB of KV cache per token for Llama 3.1 70B in 16-bit).
+# layer": the heads are shared out over the ranks and a rank keeps the KV
+# cache of its own heads; "AI Infrastructure series, Part 5", "How does
+# tensor parallelism split a layer?": a rank's KV cache is 1/N of the whole,
+# and ranks beyond the 8 key-value heads hold copies of a key-value head,
+# spending KV memory twice; "How do you choose a layout for serving?": Llama
+# 3.1 70B in 16-bit needs 320 KB of KV cache per token).
 #
 # A batch is S sequences with q_len new tokens each: rows s q_len .. s q_len
 # + q_len - 1 of QKV [M x shard_n] (the rank's [Q_r | K_r | V_r]) belong to
@@ -555,9 +597,10 @@ def attention_f64(QKV: np.ndarray, p: dict, q_len: int, kv_len, slot, Kc: np.nda
             q = bf16_to_f64(QKV[row, h * d:(h + 1) * d])
             K = bf16_to_f64(Kc[slot[s], kv_of[h], :pos + 1])
             V = bf16_to_f64(Vc[slot[s], kv_of[h], :pos + 1])
-            sc = K @ q / np.sqrt(d)
+            sc = matmul_f64(K, q[:, None])[:, 0] / np.sqrt(d)
             w = np.exp(sc - sc.max())
-            out[o, h * d:(h + 1) * d] = (w @ V) / w.sum()
+            total = matmul_f64(w[None, :], np.ones((len(w), 1)))[0, 0]
+            out[o, h * d:(h + 1) * d] = matmul_f64(w[None, :], V)[0] / total
     return out
 
 

@@ -9,14 +9,14 @@
  * What it computes (every function is the plain definition, no blocking,
  * no reordering of sums):
  *   - "Tensor vs Pipeline Parallelism" (xingyuzhitong.com), section "Tensor
- *     parallelism: split inside each layer": the first linear layer of the
- *     feed-forward block is split by columns, the second by rows, and the
- *     partial results are combined by a sum.
+ *     parallelism: split inside each layer": the MLP's leading matrix is cut
+ *     along output columns and its trailing matrix along input rows; the
+ *     ranks' partial products are then added.
  *   - "AI Infrastructure series, Part 5" (drpranayjha.com), section "How does
- *     tensor parallelism split a layer?": first matrix by columns, second by
- *     rows; each rank holds and reads 1/N of every matrix.
+ *     tensor parallelism split a layer?": the same column-then-row cut in
+ *     every block, so a rank stores and streams 1/N of each matrix.
  *   - "Tensor Parallelism" glossary (aidolsgroup.com), "Full definition":
- *     activations are broadcast and partial outputs are summed.
+ *     every rank sees the same input; the partial products are added.
  *   - Same page series, "Short answers": splitting computes the same maths;
  *     only the order of additions changes the last digits. The oracle
  *     therefore sums every dot product in ascending k, in fp64.
@@ -84,13 +84,17 @@ void orc_bf16_to_f64_array(const uint16_t* b, int64_t n, double* out) {
 void orc_shard_matmul(const uint16_t* X, int64_t M, int64_t ldx, int64_t Kr,
                       const uint16_t* W, int64_t ldw, const int64_t* rows,
                       const int64_t* cols, int64_t Nc, double* Y) {
-  const int64_t CH = 2048; /* columns per task: only splits work over threads */
+  /* Work split over threads only (each output is still one in-order sum):
+   * tasks of CH columns of one row, all rows of a column stripe before the
+   * next stripe, so threads working at the same time read the same stripe
+   * of W from the host's caches. */
+  const int64_t CH = 256;
   int64_t nch = (Nc + CH - 1) / CH;
   int64_t ntask = M * nch;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t task = 0; task < ntask; ++task) {
-    int64_t m = task / nch;
-    int64_t j0 = (task % nch) * CH;
+    int64_t m = task % M;
+    int64_t j0 = (task / M) * CH;
     int64_t j1 = j0 + CH < Nc ? j0 + CH : Nc;
     double* y = Y + m * Nc;
     for (int64_t j = j0; j < j1; ++j) y[j] = 0.0;
@@ -125,5 +129,34 @@ void orc_sum_partials(const double* P, int64_t stride, int32_t t, int64_t n, dou
     double s = 0.0;
     for (int32_t r = 0; r < t; ++r) s += P[(int64_t)r * stride + i];
     Y[i] = s;
+  }
+}
+
+/*
+ * The same product on fp64 operands (dequantised 8-bit weights, gradients,
+ * attention scores and probabilities):
+ *   C[m][n] = sum_{k = 0 .. K-1} A(m, k) * B(k, n)
+ * with A(m, k) = A[m * sam + k * sak] and B(k, n) = B[k * sbk + n * sbn]
+ * (element strides, so a transposed operand is read in place). C is [M x N]
+ * row-major. One fp64 accumulator per output, k ascending, no blocking: the
+ * plain definition, exactly as orc_shard_matmul sums.
+ */
+void orc_matmul_f64(const double* A, int64_t M, int64_t K, int64_t sam, int64_t sak,
+                    const double* B, int64_t N, int64_t sbk, int64_t sbn, double* C) {
+  const int64_t CH = 256; /* work split only, as in orc_shard_matmul */
+  int64_t nch = (N + CH - 1) / CH;
+  int64_t ntask = M * nch;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t task = 0; task < ntask; ++task) {
+    int64_t m = task % M;
+    int64_t j0 = (task / M) * CH;
+    int64_t j1 = j0 + CH < N ? j0 + CH : N;
+    double* y = C + m * N;
+    for (int64_t j = j0; j < j1; ++j) y[j] = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      double a = A[m * sam + k * sak];
+      const double* b = B + k * sbk;
+      for (int64_t j = j0; j < j1; ++j) y[j] += a * b[j * sbn];
+    }
   }
 }

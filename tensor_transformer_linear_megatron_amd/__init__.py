@@ -8,8 +8,9 @@ HIP kernels; torch supplies device memory and streams. Output tensors are
 allocated with torch when the caller does not pass them.
 
 The method ("Tensor vs Pipeline Parallelism" (xingyuzhitong.com), "Tensor
-parallelism: split inside each layer"): the first matrix of a block is split
-by columns, the second by rows, and the rows' partial outputs are summed.
+parallelism: split inside each layer"): a block's leading matrix is cut by
+output columns, its trailing one by input rows, and the row shards' partial
+products are added.
 """
 from __future__ import annotations
 
@@ -59,7 +60,19 @@ def _mat(x: torch.Tensor, dtype, name: str):
         raise TypeError(f"{name} must be {dtype}, got {x.dtype}")
     if x.dim() != 2 or (x.numel() > 0 and x.size(1) > 1 and x.stride(1) != 1):
         raise ValueError(f"{name} must be 2-D with unit column stride")
+    if x.size(0) > 1 and x.stride(0) < x.size(1):
+        raise ValueError(f"{name}'s rows overlap (row stride {x.stride(0)} < {x.size(1)} columns)")
     return ctypes.c_void_p(x.data_ptr()), max(x.stride(0), x.size(1))
+
+
+def _out_shape(x: torch.Tensor, rows: int, cols: int, name: str):
+    """An output the kernels write: exactly [rows x cols], so that no write
+    can land past the tensor (fewer rows) or in a neighbour's columns (a
+    narrower column slice of a wider buffer)."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(x.shape) != (rows, cols):
+        raise ValueError(f"{name} is {tuple(x.shape)}, the call writes [{rows} x {cols}]")
 
 
 def tp_shard_plan(kind, K: int, N: int, t: int, rank: int, heads=None) -> TpShardDesc:
@@ -137,6 +150,7 @@ def tp_col_linear(desc: TpShardDesc, X: torch.Tensor, W_packed: torch.Tensor,
         raise ValueError(f"X has {X.size(1)} columns, shard expects {desc.shard_k}")
     if Y is None:
         Y = torch.empty((M, desc.out_n), dtype=torch.bfloat16, device=X.device)
+    _out_shape(Y, M, desc.out_n, "Y")
     yp, ldy = _mat(Y, torch.bfloat16, "Y")
     wsp, wsb, _keep = _ws((desc,), M, ws, X.device, stream)
     _check(_lib.load().tp_col_linear(ctypes.byref(desc), xp, M, ldx,
@@ -156,6 +170,7 @@ def tp_row_linear(desc: TpShardDesc, Z: torch.Tensor, W_packed: torch.Tensor,
         raise ValueError(f"Z has {Z.size(1)} columns, shard expects {desc.shard_k}")
     if P is None:
         P = torch.empty((M, desc.out_n), dtype=torch.float32, device=Z.device)
+    _out_shape(P, M, desc.out_n, "P")
     pp, ldp = _mat(P, torch.float32, "P")
     wsp, wsb, _keep = _ws((desc,), M, ws, Z.device, stream)
     _check(_lib.load().tp_row_linear(ctypes.byref(desc), zp, M, ldz,
@@ -176,6 +191,7 @@ def tp_ffn_shard(gateup: TpShardDesc, down: TpShardDesc, X: torch.Tensor, Wgu_pa
         raise ValueError("H must be a contiguous bf16 [M x I/t] tensor")
     if P is None:
         P = torch.empty((M, down.N), dtype=torch.float32, device=X.device)
+    _out_shape(P, M, down.N, "P")
     pp, ldp = _mat(P, torch.float32, "P")
     wsp, wsb, _keep = _ws((gateup, down), M, ws, X.device, stream)
     _check(_lib.load().tp_ffn_shard(ctypes.byref(gateup), ctypes.byref(down), xp, M, ldx,
@@ -194,6 +210,7 @@ def tp_reduce_partials(P: torch.Tensor, Y: torch.Tensor | None = None, stream=No
     t, M, N = P.shape
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=P.device)
+    _out_shape(Y, M, N, "Y")
     yp, ldy = _mat(Y, torch.float32, "Y")
     _check(_lib.load().tp_reduce_partials(ctypes.c_void_p(P.data_ptr()), P.stride(0), t, M, N,
                                           max(P.stride(1), N), yp, ldy, _stream(stream)),
@@ -210,6 +227,7 @@ def tp_reduce_scatter_partials(P: torch.Tensor, rank: int, Y: torch.Tensor | Non
     t, M, N = P.shape
     if Y is None:
         Y = torch.empty((M // t if t else 0, N), dtype=torch.float32, device=P.device)
+    _out_shape(Y, M // t if t else 0, N, "Y")
     yp, ldy = _mat(Y, torch.float32, "Y")
     _check(_lib.load().tp_reduce_scatter_partials(ctypes.c_void_p(P.data_ptr()), P.stride(0), t, M, N,
                                                   max(P.stride(1), N), rank, yp, ldy, _stream(stream)),
@@ -225,6 +243,7 @@ def tp_gather_rows(Xs: torch.Tensor, X: torch.Tensor | None = None, stream=None)
     t, Mt, N = Xs.shape
     if X is None:
         X = torch.empty((t * Mt, N), dtype=torch.bfloat16, device=Xs.device)
+    _out_shape(X, t * Mt, N, "X")
     xp, ldx = _mat(X, torch.bfloat16, "X")
     _check(_lib.load().tp_gather_rows(ctypes.c_void_p(Xs.data_ptr()), Xs.stride(0), t, Mt, N,
                                       max(Xs.stride(1), N), xp, ldx, _stream(stream)),
@@ -350,6 +369,7 @@ def tp_attention(qkv: TpShardDesc, QKV: torch.Tensor, q_len: int, kv_len: torch.
         raise ValueError(f"QKV has {QKV.size(0)} rows, {S} sequences x {q_len} tokens expected")
     if A is None:
         A = torch.empty((S * q_len, nq * d), dtype=torch.bfloat16, device=QKV.device)
+    _out_shape(A, S * q_len, nq * d, "A")
     ap, lda = _mat(A, torch.bfloat16, "A")
     if ws is None:
         need = tp_attention_workspace_bytes(qkv, S, q_len, max_kv)

@@ -1,10 +1,9 @@
 // Attention core on one tensor-parallel rank's heads, with the rank's share of
 // the KV cache ("Tensor vs Pipeline Parallelism", "Tensor parallelism: split
-// inside each layer": attention heads are distributed among the GPUs, each
-// computing its slice, each keeping its heads' share of the KV cache; "AI
-// Infrastructure series, Part 5", "How does tensor parallelism split a
-// layer?": past the key-value head count a larger group repeats key-value
-// heads). Per query head: softmax(q k^T / sqrt(D)) v over the positions of
+// inside each layer": the heads are shared out over the ranks and a rank
+// keeps the KV cache of its own heads; "AI Infrastructure series, Part 5",
+// "How does tensor parallelism split a layer?": ranks beyond the key-value
+// head count hold copies of a key-value head). Per query head: softmax(q k^T / sqrt(D)) v over the positions of
 // its sequence up to its own (causal), with the rank's key-value head of its
 // group. No position encoding, no bias.
 //

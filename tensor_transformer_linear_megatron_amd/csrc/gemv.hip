@@ -1,7 +1,7 @@
 // Decode path (M <= 64 tokens): Y = X W_shard streams every weight byte once
 // and is bound by HBM bandwidth ("AI Infrastructure series, Part 5",
-// "Reason 2": in decode every token needs a read of every weight; a rank of t
-// reads 1/t of them).
+// "Reason 2": each decoded token streams the whole weight set once, and a
+// rank of t streams its 1/t share).
 //
 // Both kernels multiply on the matrix cores: the weight tile is the A operand
 // of v_mfma_f32_16x16x32_bf16 (16 output columns x 32 k, one packed 1 KiB

@@ -2,8 +2,9 @@
 // owns, and how big its packed copy is. Integer work only, no GPU calls.
 //
 // Rules: "Tensor vs Pipeline Parallelism" (xingyuzhitong.com), sections
-// "Tensor parallelism: split inside each layer" (first matrix by columns,
-// second by rows, heads distributed, counts must divide evenly) and "Common
+// "Tensor parallelism: split inside each layer" (leading matrix cut by output
+// columns, trailing one by input rows, heads shared out, head counts a
+// multiple of the degree) and "Common
 // mistakes" (a degree that does not divide the key-value heads is refused);
 // "AI Infrastructure series, Part 5" (drpranayjha.com), "How does tensor
 // parallelism split a layer?" (64 heads: 2, 4 or 8 ranks, not 3 or 6; past 8

@@ -36,6 +36,20 @@ def test_library_exports_every_declared_symbol():
     assert exported == set(names), exported ^ set(names)
 
 
+def test_binding_output_shape_rule():
+    """The binding's check on every output the kernels write: exactly the
+    [rows x cols] the call writes (host logic, no GPU)."""
+    import torch
+    from tensor_transformer_linear_megatron_amd import _out_shape
+    buf = torch.empty((6, 16))
+    _out_shape(buf[:4, :8], 4, 8, "Y")
+    for view in (buf[:3, :8], buf[:4, :4], buf[:4], buf[:5, :8], buf[:4, :8].reshape(8, 4)):
+        with pytest.raises(ValueError):
+            _out_shape(view, 4, 8, "Y")
+    with pytest.raises(TypeError):
+        _out_shape(None, 4, 8, "Y")
+
+
 def test_status_strings():
     for code in range(-8, 1):
         assert tp.tp_status_str(code) not in ("", "unknown status")

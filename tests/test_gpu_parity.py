@@ -578,34 +578,74 @@ def test_llama70b_attention_tp8_prefill():
     assert_parity(Y, ref, "O partials summed over 8 ranks vs unsharded")
 
 
-def test_llama405b_ffn_tp8_rank0_prefill():
-    """Rank 0's feed-forward share at 8192 tokens: gate/up 16384 x 13312 with
-    SwiGLU, down 6656 x 16384, fp32 partial; checked on sampled rows."""
-    say("llama405b ffn tp8 rank0 prefill")
+def _rows_405b(M=8192, tile=256, per_tile=4, seed=405):
+    """A seeded 128-row subset touching every one of the 32 token tiles of 256
+    rows: each tile's first and last row and two drawn rows in between."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for t0 in range(0, M, tile):
+        mid = rng.choice(np.arange(t0 + 1, t0 + tile - 1), per_tile - 2, replace=False)
+        rows += [t0, *sorted(int(x) for x in mid), t0 + tile - 1]
+    return rows
+
+
+@pytest.fixture(scope="module")
+def llama405b_ffn():
+    """The 405B feed-forward layer at 8192 tokens, TP = 8: all 8 rank shares
+    in turn (each packed from the full weights, in the launch configuration
+    the benchmark times), their partials kept, and their on-device sum."""
+    say("llama405b ffn tp8, 8 ranks at 8192 tokens: generating the full layer")
     c = wl.LLAMA405B
-    Hd, I, t, M, r = c["hidden"], c["inter"], 8, 8192, 0
-    w = I // t
+    Hd, I, t, M = c["hidden"], c["inter"], 8, 8192
     X = wl.activations(M, Hd)
-    gu, pgu = plan_both("gateup_col", Hd, 2 * I, t, r)
-    dn, pdn = plan_both("row", I, Hd, t, r)
-    assert (gu.shard_k, gu.shard_n, dn.shard_k, dn.shard_n) == (16384, 13312, 6656, 16384)
-    cols = range(r * w, (r + 1) * w)
-    Wgu_r = wl.gateup(Hd, I, c["sigma"], cols=cols)     # [Wg[:, cols] | Wu[:, cols]]
-    Wd_r = wl.down(I, Hd, c["sigma"], rows=cols)
-    Wgu_full = full_device((Hd, 2 * I), [(range(0, Hd), cols, Wgu_r[:, :w]),
-                                         (range(0, Hd), range(I + cols.start, I + cols.stop), Wgu_r[:, w:])])
-    gp = tp.tp_shard_pack(gu, Wgu_full)
-    del Wgu_full
-    Wd_full = full_device((I, Hd), [(cols, range(0, Hd), Wd_r)])
-    dp = tp.tp_shard_pack(dn, Wd_full)
-    del Wd_full
-    H, P = tp.tp_ffn_shard(gu, dn, dev(X), gp, dp)
-    rows = [0, 1, 127, 128, 4095, 4096, 8190, 8191]
-    local = oracle.plan("gateup_col", Hd, 2 * w, 1, 0)  # the rank's block, columns in shard order
-    Href = oracle.gateup_swiglu(X[rows], Wgu_r, local)
-    Pref = oracle.row_linear(Href, Wd_r, oracle.plan("row", w, Hd, 1, 0))
-    assert_parity(host_f64(H)[rows], oracle.bf16_to_f64(Href), "H_0")
-    assert_parity(host_f64(P)[rows], Pref, "P_0")
+    Wgu = wl.gateup(Hd, I, c["sigma"])   # the full [Wg | Wu], 16384 x 106496
+    Wd = wl.down(I, Hd, c["sigma"])      # 53248 x 16384
+    Xd, Wgud, Wdd = dev(X), dev(Wgu), dev(Wd)
+    P = torch.empty((t, M, Hd), dtype=torch.float32, device="cuda")
+    H0 = None
+    for r in range(t):
+        say(f"llama405b ffn tp8 rank {r}")
+        gu = tp.tp_shard_plan("gateup_col", Hd, 2 * I, t, r)
+        dn = tp.tp_shard_plan("row", I, Hd, t, r)
+        assert (gu.shard_k, gu.shard_n, dn.shard_k, dn.shard_n) == (16384, 13312, 6656, 16384)
+        gp, dp = tp.tp_shard_pack(gu, Wgud), tp.tp_shard_pack(dn, Wdd)
+        Hr, _ = tp.tp_ffn_shard(gu, dn, Xd, gp, dp, P=P[r])
+        if r == 0:
+            H0 = Hr
+        del gp, dp
+    del Wgud, Wdd
+    say("llama405b ffn tp8: sum of 8 partials")
+    Y = tp.tp_reduce_partials(P)
+    rows = _rows_405b(M)
+    torch.cuda.synchronize()
+    out = dict(X=X, Wgu=Wgu, Wd=Wd, rows=rows, Hd=Hd, I=I, t=t,
+               H0=host_f64(H0)[rows], P0=host_f64(P[0])[rows], Y=host_f64(Y)[rows])
+    del P, Y, H0
+    torch.cuda.empty_cache()
+    return out
+
+
+def test_llama405b_ffn_tp8_rank0_prefill(llama405b_ffn):
+    """Rank 0's share (gate/up 16384 x 13312 with SwiGLU, down 6656 x 16384,
+    fp32 partial) on the 128 sampled rows, against its share of the oracle."""
+    f = llama405b_ffn
+    Hd, I, t, rows = f["Hd"], f["I"], f["t"], f["rows"]
+    pgu, pdn = oracle.plan("gateup_col", Hd, 2 * I, t, 0), oracle.plan("row", I, Hd, t, 0)
+    Xs = np.ascontiguousarray(f["X"][rows])
+    Href = oracle.gateup_swiglu(Xs, f["Wgu"], pgu)
+    assert_parity(f["H0"], oracle.bf16_to_f64(Href), "H_0")
+    assert_parity(f["P0"], oracle.row_linear(Href, f["Wd"], pdn), "P_0")
+
+
+def test_llama405b_ffn_tp8_all_ranks_sum_to_unsharded(llama405b_ffn):
+    """The invariant at prefill size ("Tensor Parallelism" glossary, "Full
+    definition"; "Tensor vs Pipeline Parallelism", "Tensor parallelism: split
+    inside each layer"): the 8 ranks' partials, summed on the GPU, equal the
+    unsharded feed-forward layer (t = 1) on the 128 sampled rows."""
+    f = llama405b_ffn
+    say("llama405b ffn: unsharded oracle on 128 rows")
+    ref = oracle.ffn_unsharded(np.ascontiguousarray(f["X"][f["rows"]]), f["Wgu"], f["Wd"])
+    assert_parity(f["Y"], ref, "405B FFN: 8 partials summed vs unsharded")
 
 
 def test_binding_rejects_short_packed_buffer():
@@ -616,6 +656,66 @@ def test_binding_rejects_short_packed_buffer():
     short = torch.empty(d.packed_bytes - 16, dtype=torch.uint8, device="cuda")
     with pytest.raises(ValueError):
         tp.tp_col_linear(d, X, short)
+
+
+def test_binding_rejects_wrong_output_shapes():
+    """Every output the kernels write is checked against the shape the call
+    writes before anything is queued: too few rows (writes past the tensor),
+    a narrower column slice of a wider buffer (writes into the neighbour's
+    columns), and rows that overlap (row stride below the width)."""
+    M, K, N, t = 4, 256, 256, 2
+    X = dev(si.normal_bf16(63, (M, K), 1.0))
+    dc = tp.tp_shard_plan("col", K, N, t, 0)
+    dr = tp.tp_shard_plan("row", K, N, t, 0)
+    gu = tp.tp_shard_plan("gateup_col", K, 2 * N, t, 0)
+    dn = tp.tp_shard_plan("row", N, K, t, 0)
+    cp, rp = tp.tp_shard_pack(dc, dev(si.normal_bf16(64, (K, N), 0.05))), \
+        tp.tp_shard_pack(dr, dev(si.normal_bf16(65, (K, N), 0.05)))
+    gp, np_ = tp.tp_shard_pack(gu, dev(si.normal_bf16(66, (K, 2 * N), 0.05))), \
+        tp.tp_shard_pack(dn, dev(si.normal_bf16(67, (N, K), 0.05)))
+    bf, f32 = torch.bfloat16, torch.float32
+    wide_bf = torch.zeros((M, 4 * N), dtype=bf, device="cuda")
+    wide_f = torch.zeros((M, 4 * N), dtype=f32, device="cuda")
+    Z = dev(si.normal_bf16(68, (M, dr.shard_k), 1.0))
+    bad = [
+        lambda: tp.tp_col_linear(dc, X, cp, Y=torch.empty((M - 1, dc.out_n), dtype=bf, device="cuda")),
+        lambda: tp.tp_col_linear(dc, X, cp, Y=wide_bf[:, :dc.out_n // 2]),
+        lambda: tp.tp_col_linear(dc, X, cp, Y=torch.empty((1, dc.out_n), dtype=bf, device="cuda").expand(M, -1)),
+        lambda: tp.tp_row_linear(dr, Z, rp, P=torch.empty((M - 1, N), dtype=f32, device="cuda")),
+        lambda: tp.tp_row_linear(dr, Z, rp, P=wide_f[:, :N - 8]),
+        lambda: tp.tp_ffn_shard(gu, dn, X, gp, np_, P=torch.empty((M, K - 8), dtype=f32, device="cuda")),
+        lambda: tp.tp_ffn_shard(gu, dn, X, gp, np_, P=torch.empty((M - 1, K), dtype=f32, device="cuda")),
+        lambda: tp.tp_reduce_partials(torch.zeros((t, M, N), dtype=f32, device="cuda"), Y=wide_f[:M - 1, :N]),
+        lambda: tp.tp_reduce_partials(torch.zeros((t, M, N), dtype=f32, device="cuda"), Y=wide_f[:, :N // 2]),
+        lambda: tp.tp_reduce_scatter_partials(torch.zeros((t, M, N), dtype=f32, device="cuda"), 1,
+                                              Y=wide_f[:M // t - 1, :N]),
+        lambda: tp.tp_reduce_scatter_partials(torch.zeros((t, M, N), dtype=f32, device="cuda"), 1,
+                                              Y=wide_f[:M // t, :N - 4]),
+        lambda: tp.tp_gather_rows(torch.zeros((t, 2, N), dtype=bf, device="cuda"), X=wide_bf[:3, :N]),
+        lambda: tp.tp_gather_rows(torch.zeros((t, 2, N), dtype=bf, device="cuda"), X=wide_bf[:, :N - 8]),
+    ]
+    torch.cuda.synchronize()
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
+    torch.cuda.synchronize()
+    assert not wide_bf.any() and not wide_f.any(), "a rejected call wrote into its output"
+
+
+def test_binding_rejects_wrong_attention_output_shape():
+    heads, t = (16, 4, 64), 2
+    q = tp.tp_shard_plan("qkv_col", 256, (16 + 8) * 64, t, 0, heads=heads)
+    QKV = dev(si.normal_bf16(69, (2, q.shard_n), 1.0))
+    Kc, Vc = tp.tp_kv_cache_new(q, 2, 16)
+    kl = torch.tensor([3, 5], dtype=torch.int32, device="cuda")
+    sl = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    nqd = (q.q_head_end - q.q_head_begin) * 64
+    wide = torch.zeros((2, 2 * nqd), dtype=torch.bfloat16, device="cuda")
+    for A in (wide[:1, :nqd], wide[:, :nqd - 8]):
+        with pytest.raises(ValueError):
+            tp.tp_attention(q, QKV, 1, kl, sl, Kc, Vc, 16, A=A)
+    torch.cuda.synchronize()
+    assert not wide.any()
 
 
 @pytest.mark.parametrize("M", [3, 40, 200])

@@ -384,17 +384,6 @@ def test_fp8_shards_follow_the_plan():
         assert np.all(np.abs(P - Xf @ Wst) <= bound + 1e-300)
 
 
-def test_pages_8bit_decode_closed_forms():
-    # 70B in 8-bit: 70.6 GB per token; at 3.35 TB/s about 21 ms; a TP = 4 rank
-    # reads a quarter, about 5.3 ms ("Reason 2")
-    assert round(70.6e9 / 3.35e12 * 1e3) == 21
-    assert round(70.6e9 / 4 / 3.35e12 * 1e3, 1) == 5.3
-    # one code byte per weight: an 8-bit shard is half its bf16 bytes, plus 4
-    # bytes of scale per column (the 70B feed-forward rank share of TP = 8)
-    K, N = 8192, 7168
-    assert K * N + 4 * N < (K * N * 2) // 2 * 1.001
-
-
 def test_planted_round_toward_zero_is_caught():
     # truncating the scaled weights instead of rounding them moves many codes
     bits = np.arange(0, 65536, 7, dtype=np.uint32)
@@ -502,18 +491,201 @@ def test_swiglu_backward_closed_forms_and_differences():
     np.testing.assert_allclose(dU[0], dh * (hfun(g, u + eps) - hfun(g, u - eps)) / (2 * eps), rtol=1e-7, atol=1e-9)
 
 
-def test_training_flops_closed_form():
-    # 6 x parameters x tokens ("AI Infrastructure series, Part 5"): the forward is
-    # 2 x parameters x tokens, so the backward (input and weight gradients) is 4
-    M, K, N = 4096, 8192, 1280
-    fwd = 2 * M * K * N
-    assert 2 * M * N * K + 2 * K * M * N == 2 * fwd
+def _swiglu_backward_autograd_bits(G, U, dH):
+    """[dG | dU] from torch's fp64 autograd of H = silu(G) * U (a library
+    routine, no oracle code), each element rounded once by exact rational
+    arithmetic."""
+    Gt = torch.tensor(G, dtype=torch.float64, requires_grad=True)
+    Ut = torch.tensor(U, dtype=torch.float64, requires_grad=True)
+    (torch.nn.functional.silu(Gt) * Ut).backward(torch.tensor(dH, dtype=torch.float64))
+    both = np.concatenate([Gt.grad.numpy(), Ut.grad.numpy()], axis=1)
+    return np.array([[exact_round_bf16(float(v)) for v in row] for row in both], dtype=np.uint16)
+
+
+def _swiglu_backward_cases():
+    rng = np.random.default_rng(21)
+    G = decode(si.normal_bf16(50, (7, 12), 3.0))
+    G[0, :6] = [0.0, 40.0, -40.0, 89.0, -100.0, 1e-3]  # saturated and near-zero pre-activations
+    U = decode(si.normal_bf16(51, (7, 12), 1.0))
+    dH = rng.standard_normal((7, 12))
+    return G, U, dH
+
+
+def test_swiglu_backward_bits_match_torch_autograd():
+    """oracle.swiglu_backward: the [dG | dU] order (gate half first, the
+    order of [Wg | Wu]) and a single bf16 rounding of each fp64 gradient."""
+    G, U, dH = _swiglu_backward_cases()
+    np.testing.assert_array_equal(oracle.swiglu_backward(G, U, dH), _swiglu_backward_autograd_bits(G, U, dH))
 
 
 def test_planted_swapped_swiglu_gradients_are_caught():
-    g, u, dh = np.array([[0.7, -1.3]]), np.array([[0.4, 2.0]]), np.array([[1.0, -0.5]])
-    dG, dU = oracle.swiglu_backward_f64(g, u, dh)
-    assert not np.allclose(dG, dU)  # a mix-up of the two halves would show
+    """A planted [dU | dG] order in a copy of the oracle fails the pin above."""
+    def swapped(G, U, dH):
+        dG, dU = oracle.swiglu_backward_f64(G, U, dH)
+        return oracle.round_bf16(np.concatenate([dU, dG], axis=1))
+
+    G, U, dH = _swiglu_backward_cases()
+    assert not np.array_equal(swapped(G, U, dH), _swiglu_backward_autograd_bits(G, U, dH))
+
+
+# ---------------------------------------------------------------------------
+# The oracle's in-order fp64 product (8-bit shards, gradients, attention).
+# ---------------------------------------------------------------------------
+
+def test_matmul_f64_is_the_in_order_sum():
+    """Bit for bit a pure-Python loop that adds the products in ascending k
+    from 0.0 (Python floats are IEEE fp64 without fused multiply-add), also
+    for transposed operands read in place."""
+    rng = np.random.default_rng(31)
+    A, B = rng.standard_normal((5, 19)), rng.standard_normal((19, 7))
+    want = np.empty((5, 7))
+    for m in range(5):
+        for n in range(7):
+            acc = 0.0
+            for k in range(19):
+                acc += float(A[m, k]) * float(B[k, n])
+            want[m, n] = acc
+    np.testing.assert_array_equal(oracle.matmul_f64(A, B), want)
+    np.testing.assert_array_equal(oracle.matmul_f64(np.ascontiguousarray(A.T).T, np.asfortranarray(B)), want)
+    np.testing.assert_array_equal(oracle.matmul_f64(B.T, A.T), want.T)
+
+
+def test_matmul_f64_exact_integers():
+    Ai, Bi = si.int_bf16(52, (9, 300), -3, 3), si.int_bf16(53, (300, 11), -3, 3)
+    Ai, Bi = decode(Ai).astype(np.int64), decode(Bi).astype(np.int64)
+    assert np.array_equal(oracle.matmul_f64(Ai.astype(np.float64), Bi.astype(np.float64)),
+                          (Ai @ Bi).astype(np.float64))
+    assert np.array_equal(oracle.matmul_f64(np.zeros((3, 0)), np.zeros((0, 4))), np.zeros((3, 4)))
+
+
+# ---------------------------------------------------------------------------
+# 8-bit gate/up with SwiGLU (oracle.gateup_swiglu_fp8).
+# ---------------------------------------------------------------------------
+
+def _gateup_fp8_onehot(K=40, inter=12):
+    """[Wg | Wu] whose columns each hold one nonzero weight of at most 3
+    significant bits (exact in E4M3 after any power-of-two scale), gate and
+    up columns on different rows with different values."""
+    rng = np.random.default_rng(22)
+    a, b = rng.integers(0, K, inter), rng.integers(0, K, inter)
+    b = np.where(a == b, (b + 1) % K, b)
+    vals = np.array([1.0, -1.5, 0.75, 1.25, -1.75, 0.5, 3.0, -0.625])
+    va, vb = vals[rng.integers(0, len(vals), inter)], vals[rng.integers(0, len(vals), inter)] * 2.0
+    W = np.zeros((K, 2 * inter))
+    W[a, np.arange(inter)] = va
+    W[b, inter + np.arange(inter)] = vb
+    bits = np.array([[exact_round_bf16(float(v)) for v in row] for row in W], dtype=np.uint16)
+    return bits, a, b, va, vb
+
+
+def test_gateup_swiglu_fp8_onehot_against_high_precision():
+    """With one-hot columns the 8-bit shard is exact, so H[m, j] must be
+    bf16(SiLU(x[m, a_j] va_j) * x[m, b_j] vb_j), SiLU on the gate half, for
+    every rank's share."""
+    K, inter, M = 40, 12, 5
+    X = normal(23, (M, K), 2.0)
+    Wgu, a, b, va, vb = _gateup_fp8_onehot(K, inter)
+    Xf = decode(X)
+    for t in (1, 2, 3):
+        w = inter // t
+        for r in range(t):
+            p = oracle.plan("gateup_col", K, 2 * inter, t, r)
+            js = range(r * w, (r + 1) * w)
+            want = np.array([[_silu_times_u_highprec(Xf[m, a[j]] * va[j], Xf[m, b[j]] * vb[j]) for j in js]
+                             for m in range(M)], dtype=np.uint16)
+            np.testing.assert_array_equal(oracle.gateup_swiglu_fp8(X, Wgu, p), want)
+
+
+def _fp8_shard_torch(Wf: np.ndarray) -> np.ndarray:
+    """Independent quantiser: scale 2^e per column from Python's frexp, codes
+    from torch's float8_e4m3fn cast (round to nearest even), decoded by torch."""
+    out = np.empty_like(Wf)
+    for n in range(Wf.shape[1]):
+        amax = float(np.abs(Wf[:, n]).max())
+        e = 0
+        if amax > 0:
+            f, x = math.frexp(amax)
+            e = x - 9 if f <= 0.875 else x - 8
+        q = torch.tensor(Wf[:, n] * 2.0 ** -e, dtype=torch.float64).to(torch.float8_e4m3fn)
+        out[:, n] = q.to(torch.float64).numpy() * 2.0 ** e
+    return out
+
+
+def _gateup_fp8_reference(X, Wgu, t, r):
+    """H of rank r from the independent quantiser, per-half columns, exact
+    integer sums (small integers times dyadic weights), decimal SwiGLU."""
+    K, N2 = Wgu.shape
+    inter = N2 // 2
+    w = inter // t
+    cols = list(range(r * w, (r + 1) * w))
+    Wf = decode(Wgu)
+    Wg = _fp8_shard_torch(Wf[:, cols])
+    Wu = _fp8_shard_torch(Wf[:, [inter + c for c in cols]])
+    Xf = decode(X)
+    G = [[math.fsum(Xf[m, k] * Wg[k, j] for k in range(K)) for j in range(w)] for m in range(X.shape[0])]
+    U = [[math.fsum(Xf[m, k] * Wu[k, j] for k in range(K)) for j in range(w)] for m in range(X.shape[0])]
+    return np.array([[_silu_times_u_highprec(G[m][j], U[m][j]) for j in range(w)] for m in range(X.shape[0])],
+                    dtype=np.uint16)
+
+
+def _gateup_fp8_inputs():
+    """Integer activations and weights whose columns need real rounding
+    (values that are not E4M3 codes after their column's scale), with gate
+    and up columns of very different ranges."""
+    X = si.int_bf16(24, (4, 32), -3, 3)
+    Wg = si.normal_bf16(25, (32, 8), 0.3)
+    Wu = si.normal_bf16(26, (32, 8), 5.0)
+    return X, np.concatenate([Wg, Wu], axis=1)
+
+
+def test_gateup_swiglu_fp8_against_torch_float8():
+    X, Wgu = _gateup_fp8_inputs()
+    for t, r in ((1, 0), (2, 1), (4, 2)):
+        p = oracle.plan("gateup_col", 32, 16, t, r)
+        np.testing.assert_array_equal(oracle.gateup_swiglu_fp8(X, Wgu, p), _gateup_fp8_reference(X, Wgu, t, r))
+
+
+def test_planted_gateup_fp8_half_swap_is_caught():
+    """A copy of the oracle's 8-bit gate/up with the halves swapped (SiLU on
+    the up products) fails both 8-bit gate/up pins."""
+    def swapped(X, Wgu, p):
+        Wq = oracle.shard_weight_fp8(Wgu, p)
+        half = p["shard_n"] // 2
+        Xf = oracle.bf16_to_f64(X)
+        return oracle.swiglu(oracle.matmul_f64(Xf, Wq[:, half:]), oracle.matmul_f64(Xf, Wq[:, :half]))
+
+    X, Wgu = _gateup_fp8_inputs()
+    p = oracle.plan("gateup_col", 32, 16, 2, 1)
+    assert not np.array_equal(swapped(X, Wgu, p), _gateup_fp8_reference(X, Wgu, 2, 1))
+    Xo = normal(23, (5, 40), 2.0)
+    Wo, a, b, va, vb = _gateup_fp8_onehot()
+    po = oracle.plan("gateup_col", 40, 24, 1, 0)
+    Xf = decode(Xo)
+    want = np.array([[_silu_times_u_highprec(Xf[m, a[j]] * va[j], Xf[m, b[j]] * vb[j]) for j in range(12)]
+                     for m in range(5)], dtype=np.uint16)
+    assert not np.array_equal(swapped(Xo, Wo, po), want)
+
+
+# ---------------------------------------------------------------------------
+# The parity measure (oracle.compare).
+# ---------------------------------------------------------------------------
+
+def test_compare_closed_forms():
+    s = oracle.compare(np.array([[3.0, 4.5]]), np.array([[3.0, 4.0]]))
+    # diff (0, 0.5): ||diff|| / ||(3, 4)|| = 0.5 / 5
+    assert s == dict(rel_fro=0.1, max_err=0.5, max_ref=4.0, max_rel=0.125)
+    s = oracle.compare(np.array([1.0, -2.0, 2.0]), np.array([0.0, 0.0, 0.0]))
+    assert s["rel_fro"] == 3.0 and s["max_err"] == 2.0 and s["max_ref"] == 0.0
+    s = oracle.compare(np.arange(12.0).reshape(3, 4), np.arange(12.0).reshape(3, 4))
+    assert s["rel_fro"] == 0.0 and s["max_err"] == 0.0 and s["max_ref"] == 11.0
+
+
+def test_compare_refuses_shape_mismatch():
+    """One row must not stand in for M rows by broadcasting."""
+    ref = np.ones((4, 8))
+    for got in (np.ones((1, 8)), np.ones(8), np.ones((4, 8, 1)), np.ones((8, 4))):
+        with pytest.raises(ValueError):
+            oracle.compare(got, ref)
 
 
 # ---------------------------------------------------------------------------
@@ -743,15 +915,6 @@ def test_planted_contiguous_gateup_cut_is_caught():
     X, Wgu, Wd = normal(0, (4, 64)), normal(1, (64, 96), 0.1), normal(3, (48, 64), 0.1)
     with pytest.raises(AssertionError):
         _ffn_invariant(_mutant(plan=bad_plan, ffn_shard=ffn_shard), X, Wgu, Wd, 2)
-
-
-def test_planted_transposed_operand_is_caught():
-    def bad_matmul(X, W, rows, cols):  # W read transposed
-        return oracle.shard_matmul(X, np.ascontiguousarray(W.T), rows, cols)
-
-    X, W = si.int_bf16(11, (7, 48), -3, 3), si.int_bf16(12, (48, 48), -3, 3)
-    Xi, Wi = decode(X).astype(np.int64), decode(W).astype(np.int64)
-    assert not np.array_equal(bad_matmul(X, W, np.arange(48), np.arange(48)), Xi @ Wi)
 
 
 def test_planted_truncating_round_is_caught():
