@@ -362,7 +362,7 @@ def run_prefill(args):
     for _ in range(2):
         tp.tp_col_linear(gu, X, gp, Y=Hb)
         tp.tp_row_linear(dn, Hb, dp, P=P)
-    steps = max(3, args.steps // 4)
+    steps = max(10, args.steps // 4)
     timer = Timer(torch.cuda.current_stream().cuda_stream)
     ev = [[timer.event() for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
@@ -373,7 +373,8 @@ def run_prefill(args):
         tp.tp_row_linear(dn, Hb, dp, P=P)
         timer.record(e[2])
     torch.cuda.synchronize()
-    d = np.array([[timer.ms(e[0], e[1]), timer.ms(e[1], e[2])] for e in ev]).mean(axis=0)  # ms
+    # median per op over the steps (ms-scale launches: the events' own cost is negligible)
+    d = np.median(np.array([[timer.ms(e[0], e[1]), timer.ms(e[1], e[2])] for e in ev]), axis=0)  # ms
     fg = 2 * M * Hd * 2 * w
     fd = 2 * M * w * Hd
     tf = (fg + fd) / d.sum() / 1e9
@@ -382,7 +383,7 @@ def run_prefill(args):
                 value=round(tf, 1), frac=round(tf / MFMA_BF16_PEAK_TFS, 4), peak=MFMA_BF16_PEAK_TFS,
                 gateup_ms=round(float(d[0]), 3), gateup_TFs=round(fg / d[0] / 1e9, 1),
                 down_ms=round(float(d[1]), 3), down_TFs=round(fd / d[1] / 1e9, 1), steps=steps,
-                cpu_baseline=cpu)
+                statistic="median", cpu_baseline=cpu)
 
 
 COPY_BYTES = 1 << 30
@@ -449,7 +450,7 @@ def config_worked_tp2(timer):
     Xd, Wd, W2d = to_dev(X), to_dev(W), to_dev(W2)
     cols = [tp.tp_shard_plan("col", H, H, t, r) for r in range(t)]
     rows = [tp.tp_shard_plan("row", H, H, t, r) for r in range(t)]
-    copies = 8  # 8 x 64 MiB of packed shards, past the 256 MB last-level cache
+    copies = 16  # 16 x 64 MiB = 1 GiB of packed shards, far past the 256 MB last-level cache
     packs = [[(tp.tp_shard_pack(cols[r], Wd), tp.tp_shard_pack(rows[r], W2d)) for r in range(t)]
              for _ in range(copies)]
     Y = [torch.empty((M, H // t), dtype=torch.bfloat16, device="cuda") for _ in range(t)]
@@ -791,9 +792,17 @@ def config_405b_ffn_backward(timer):
                 peak=MFMA_BF16_PEAK_TFS, per_op=per)
 
 
+def config_405b_ffn_prefill(timer):
+    """The prefill workload alone (rank 0 of the 405B feed-forward layer at
+    TP = 8, 8192 tokens), without the CPU baseline: for profiler runs."""
+    return run_prefill(argparse.Namespace(steps=40, no_cpu_baseline=True))
+
+
 CONFIGS = {"worked_tp2": config_worked_tp2, "70b_ffn_decode": config_70b_ffn_decode,
            "70b_attention_prefill": config_70b_attention_prefill, "sequence_parallel": config_sequence_parallel,
            "405b_ffn_backward": config_405b_ffn_backward, "70b_attention_block": config_70b_attention_block}
+# run only with --config (the default line already carries the prefill workload)
+PROFILE_ONLY = {"405b_ffn_prefill": config_405b_ffn_prefill}
 
 
 def main():
@@ -806,7 +815,7 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (worked TP=2 split, 70B decode and attention prefill, "
                          "sequence-parallel partial sum, 405B feed-forward backward, 70B attention block)")
-    ap.add_argument("--config", choices=sorted(CONFIGS),
+    ap.add_argument("--config", choices=sorted({**CONFIGS, **PROFILE_ONLY}),
                     help="only run this one workload and print its line (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (the yardstick for HBM byte counters)")
@@ -825,7 +834,7 @@ def main():
         return
     if args.config:
         timer = Timer(torch.cuda.current_stream().cuda_stream)
-        print(json.dumps(CONFIGS[args.config](timer)), flush=True)
+        print(json.dumps({**CONFIGS, **PROFILE_ONLY}[args.config](timer)), flush=True)
         return
     dec = run_decode(args)
     pre = None if args.no_prefill else run_prefill(args)

@@ -625,6 +625,7 @@ def llama405b_ffn():
     return out
 
 
+@pytest.mark.timeout(900)
 def test_llama405b_ffn_tp8_rank0_prefill(llama405b_ffn):
     """Rank 0's share (gate/up 16384 x 13312 with SwiGLU, down 6656 x 16384,
     fp32 partial) on the 128 sampled rows, against its share of the oracle."""
@@ -637,6 +638,7 @@ def test_llama405b_ffn_tp8_rank0_prefill(llama405b_ffn):
     assert_parity(f["P0"], oracle.row_linear(Href, f["Wd"], pdn), "P_0")
 
 
+@pytest.mark.timeout(900)
 def test_llama405b_ffn_tp8_all_ranks_sum_to_unsharded(llama405b_ffn):
     """The invariant at prefill size ("Tensor Parallelism" glossary, "Full
     definition"; "Tensor vs Pipeline Parallelism", "Tensor parallelism: split
