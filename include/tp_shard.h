@@ -241,6 +241,27 @@ TP_API tp_status tp_ffn_shard(const tp_shard_desc* gateup, const tp_shard_desc* 
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * tp_ffn_shard for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc. Same
+ * arguments, results and errors as tp_ffn_shard, without ws / ws_bytes: the
+ * kernels' scratch (split-K fp32 partials) lives in one static device array
+ * of TP_NOALLOC_SCRATCH_BYTES per GPU, which the library's code object
+ * holds from its first use on that GPU until the process ends. This call
+ * allocates nothing. A call whose scratch (the larger of
+ * tp_workspace_bytes(gateup, M) and tp_workspace_bytes(down, M)) exceeds
+ * TP_NOALLOC_SCRATCH_BYTES returns TP_ERR_WORKSPACE and queues nothing.
+ * Every call on one GPU uses that GPU's one array and leaves its contents
+ * behind: calls that may overlap on one GPU (several streams, several host
+ * threads) race and must be serialised by the caller. The stream's device
+ * must be the calling thread's current device (TP_ERR_HIP otherwise).
+ */
+#define TP_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+TP_API tp_status tp_ffn_shard_noalloc(const tp_shard_desc* gateup, const tp_shard_desc* down,
+                               const uint16_t* X, int64_t M, int64_t ldx, const void* Wgu_packed,
+                               const void* Wd_packed, uint16_t* H_ws, float* P, int64_t ldp,
+                               hipStream_t stream);
+
+/*
  * The sum that replaces the all-reduce ("Tensor Parallelism" glossary,
  * "Full definition": the ranks' partial products are added; "Tensor vs Pipeline Parallelism": two
  * all-reduces per layer, after attention and after the feed-forward block):

@@ -33,7 +33,8 @@ KIND_NAMES = {"col": TP_COL, "row": TP_ROW, "gateup_col": TP_GATEUP_COL,
 EXPORTS = ("tp_shard_plan", "tp_shard_set_wformat", "tp_shard_pack", "tp_col_linear", "tp_row_linear", "tp_ffn_shard",
            "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows", "tp_shard_plan_dgrad",
            "tp_weight_grad", "tp_swiglu_backward", "tp_kv_cache_bytes", "tp_kv_append", "tp_attention",
-           "tp_attention_workspace_bytes", "tp_workspace_bytes", "tp_status_str")
+           "tp_attention_workspace_bytes", "tp_workspace_bytes", "tp_status_str", "tp_ffn_shard_noalloc")
+NOALLOC_SCRATCH_BYTES = 16 << 20  # TP_NOALLOC_SCRATCH_BYTES
 
 
 class TpHeads(ctypes.Structure):
@@ -94,6 +95,7 @@ def load() -> ctypes.CDLL:
     lib.tp_col_linear.argtypes = [D, P, I64, I64, P, P, I64, P, SZ, P]
     lib.tp_row_linear.argtypes = [D, P, I64, I64, P, P, I64, P, SZ, P]
     lib.tp_ffn_shard.argtypes = [D, D, P, I64, I64, P, P, P, P, I64, P, SZ, P]
+    lib.tp_ffn_shard_noalloc.argtypes = [D, D, P, I64, I64, P, P, P, P, I64, P]
     lib.tp_reduce_partials.argtypes = [P, I64, I32, I64, I64, I64, P, I64, P]
     lib.tp_reduce_scatter_partials.argtypes = [P, I64, I32, I64, I64, I64, I32, P, I64, P]
     lib.tp_gather_rows.argtypes = [P, I64, I32, I64, I64, I64, P, I64, P]
@@ -112,7 +114,8 @@ def load() -> ctypes.CDLL:
     lib.tp_status_str.restype = ctypes.c_char_p
     for name in ("tp_shard_plan", "tp_shard_set_wformat", "tp_shard_pack", "tp_col_linear", "tp_row_linear",
                  "tp_ffn_shard", "tp_reduce_partials", "tp_reduce_scatter_partials", "tp_gather_rows",
-                 "tp_shard_plan_dgrad", "tp_weight_grad", "tp_swiglu_backward", "tp_kv_append", "tp_attention"):
+                 "tp_shard_plan_dgrad", "tp_weight_grad", "tp_swiglu_backward", "tp_kv_append", "tp_attention",
+                 "tp_ffn_shard_noalloc"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib

@@ -1,7 +1,9 @@
 // The C-ABI entry points: host-side validation and kernel dispatch. Nothing
 // here allocates device memory or keeps state between calls.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "tp_internal.h"
 
@@ -238,6 +240,64 @@ extern "C" tp_status tp_ffn_shard(const tp_shard_desc* gu, const tp_shard_desc* 
   st = tp_col_linear(gu, X, M, ldx, Wgu_packed, H_ws, gu->out_n, ws, ws_bytes, stream);
   if (st != TP_OK) return st;
   return tp_row_linear(dn, H_ws, M, gu->out_n, Wd_packed, P, ldp, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The feed-forward share without a caller workspace: the split-K partials go
+// to a static device array. In host code `scratch` is only a host-side
+// stand-in for the symbol; its device address (one per GPU) comes from
+// hipGetSymbolAddress and is the only form ever passed to a kernel.
+
+static __device__ __align__(256) unsigned char scratch[TP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of this GPU's scratch array, looked up once per device
+// with that device current.
+tp_status scratch_of(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TP_ERR_HIP;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return TP_ERR_HIP;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return TP_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" tp_status tp_ffn_shard_noalloc(const tp_shard_desc* gu, const tp_shard_desc* dn,
+                                          const uint16_t* X, int64_t M, int64_t ldx,
+                                          const void* Wgu_packed, const void* Wd_packed,
+                                          uint16_t* H_ws, float* P, int64_t ldp, hipStream_t stream) {
+  tp_status st = check_desc(gu);
+  if (st != TP_OK) return st;
+  st = check_desc(dn);
+  if (st != TP_OK) return st;
+  if (M < 0) return TP_ERR_SHAPE;
+  const size_t need_gu = workspace_bytes(gu, M), need_dn = workspace_bytes(dn, M);
+  if ((need_gu > need_dn ? need_gu : need_dn) > TP_NOALLOC_SCRATCH_BYTES) return TP_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (M > 0) {
+    st = scratch_of(stream, &ws);
+    if (st != TP_OK) return st;
+  }
+  return tp_ffn_shard(gu, dn, X, M, ldx, Wgu_packed, Wd_packed, H_ws, P, ldp, ws,
+                      TP_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 extern "C" tp_status tp_reduce_partials(const float* P, int64_t stride_elems, int32_t t, int64_t M,
