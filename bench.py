@@ -52,10 +52,11 @@ def log(*a):
 def decode_bytes(M, H, I, t=1):
     """Algorithmic HBM bytes of one rank's feed-forward share at batch M:
     weights once, X once, H written and read once (bf16), the fp32 partial
-    written once, and the partial sum reading t partials and writing Y."""
+    written once, and the partial sum reading t partials and writing Y (at
+    t = 1 the sum is taken in place, Y = P_0: nothing moves)."""
     gateup = H * 2 * (I // t) * 2 + M * H * 2 + M * (I // t) * 2
     down = (I // t) * H * 2 + M * (I // t) * 2 + M * H * 4
-    reduce = (t + 1) * M * H * 4
+    reduce = (t + 1) * M * H * 4 if t > 1 else 0
     return gateup, down, reduce
 
 
@@ -130,7 +131,6 @@ def run_decode(args):
     Xd = to_dev(X)
     bufs = {M: dict(X=Xd[:M], H=torch.empty((M, I), dtype=torch.bfloat16, device="cuda"),
                     P=torch.empty((1, M, H), dtype=torch.float32, device="cuda"),
-                    Y=torch.empty((M, H), dtype=torch.float32, device="cuda"),
                     ws=torch.empty(max(16, tp.tp_workspace_bytes(gu, M), tp.tp_workspace_bytes(dn, M)),
                                    dtype=torch.uint8, device="cuda")) for M in DECODE_MS}
     torch.cuda.synchronize()
@@ -153,7 +153,8 @@ def run_decode(args):
             row.append((
                 (gub, VP(b["X"].data_ptr()), M, H, VP(gp.data_ptr()), VP(b["H"].data_ptr()), I, ws, wsb, stream),
                 (dnb, VP(b["H"].data_ptr()), M, I, VP(dp.data_ptr()), VP(b["P"].data_ptr()), H, ws, wsb, stream),
-                (VP(b["P"].data_ptr()), M * H, 1, M, H, H, VP(b["Y"].data_ptr()), H, stream)))
+                # t = 1: the sum of the one partial, in place (Y = P_0)
+                (VP(b["P"].data_ptr()), M * H, 1, M, H, H, VP(b["P"].data_ptr()), H, stream)))
         calls.append(row)
 
     timer = Timer(torch.cuda.current_stream().cuda_stream)

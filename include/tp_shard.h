@@ -268,7 +268,8 @@ TP_API tp_status tp_ffn_shard_noalloc(const tp_shard_desc* gateup, const tp_shar
  *   Y[m][n] = P_0[m][n] + P_1[m][n] + ... + P_{t-1}[m][n], added in fp32 in
  *   rank order, where P_r = P + r * stride_elems is [M x N] with leading dim
  *   ldp. Y [M x N] fp32 with leading dim ldy may be P_0 itself (in place);
- *   it must not overlap P_1 ... P_{t-1}.
+ *   it must not overlap P_1 ... P_{t-1}. With t == 1 in place (Y == P,
+ *   ldy == ldp) the sum is already there and nothing is queued.
  */
 TP_API tp_status tp_reduce_partials(const float* P, int64_t stride_elems, int32_t t, int64_t M,
                              int64_t N, int64_t ldp, float* Y, int64_t ldy, hipStream_t stream);

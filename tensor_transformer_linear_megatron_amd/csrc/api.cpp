@@ -309,6 +309,8 @@ extern "C" tp_status tp_reduce_partials(const float* P, int64_t stride_elems, in
   if (t > 1 && stride_elems < M * ldp) return TP_ERR_SHAPE;
   if (!aligned16(P) || !aligned16(Y) || N % 4 || ldp % 4 || ldy % 4 || stride_elems % 4)
     return TP_ERR_ALIGN;
+  // One partial summed into itself: the result is already in place.
+  if (t == 1 && Y == P && ldy == ldp) return TP_OK;
   return tpk::launch_reduce(P, stride_elems, t, M, N, ldp, Y, ldy, stream) == hipSuccess
              ? TP_OK
              : TP_ERR_HIP;
