@@ -43,6 +43,7 @@ METRIC = "TP-shard linear: decode HBM GB/s, prefill bf16 TFLOP/s (% of roofline)
 DECODE_MS = (1, 8, 32, 64)
 COPIES = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+PREFILL_COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_counters.json")
 
 
 def log(*a):
@@ -277,6 +278,21 @@ def load_traffic(key, src_hash):
     return e.get("bytes_per_launch")
 
 
+def load_prefill_counters(workload):
+    """Per-kernel MFMA utilisation, sustained clock and TFLOP/s of a prefill
+    workload from the committed rocprofv3 counter summary (MfmaUtil =
+    SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs' active cycles), or None if it is
+    missing or the GEMM source changed since the counters were taken."""
+    try:
+        with open(PREFILL_COUNTERS_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash", {}).get("gemm.hip") != source_hash("gemm.hip"):
+        return None
+    return t.get("workloads", {}).get(workload)
+
+
 def host_cpu():
     """The host's CPU model, as the kernel reports it."""
     try:
@@ -384,7 +400,7 @@ def run_prefill(args):
                 value=round(tf, 1), frac=round(tf / MFMA_BF16_PEAK_TFS, 4), peak=MFMA_BF16_PEAK_TFS,
                 gateup_ms=round(float(d[0]), 3), gateup_TFs=round(fg / d[0] / 1e9, 1),
                 down_ms=round(float(d[1]), 3), down_TFs=round(fd / d[1] / 1e9, 1), steps=steps,
-                statistic="median", cpu_baseline=cpu)
+                statistic="median", mfma_counters=load_prefill_counters("405b_ffn_prefill"), cpu_baseline=cpu)
 
 
 COPY_BYTES = 1 << 30
