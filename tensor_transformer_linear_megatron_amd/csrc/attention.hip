@@ -66,17 +66,28 @@ __device__ __forceinline__ uint4 tr_pair(const char* p0, const char* p1) {
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 
-// Two bf16 terms of 8 probabilities, packed as MFMA operands.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// a and b rounded to bf16 (to nearest, ties to even) in one v_cvt_pk_bf16_f32,
+// a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+// Two bf16 terms of 8 probabilities, packed as MFMA operands: hi = bf16(p),
+// lo = bf16(p - hi) (the difference is exact in fp32). Per pair: two
+// conversions, the two hi values back in fp32 by a shift and a mask, and two
+// subtractions.
 __device__ __forceinline__ void split8(const float (&p)[8], uint4& hi, uint4& lo) {
-  uint32_t h[8], l[8];
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint16_t b = f32_to_bf16(p[e]);
-    h[e] = b;
-    l[e] = f32_to_bf16(p[e] - __uint_as_float((uint32_t)b << 16));
+  for (int e = 0; e < 4; ++e) {
+    h[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+    l[e] = pack_bf16x2(p[2 * e] - __uint_as_float(h[e] << 16), p[2 * e + 1] - __uint_as_float(h[e] & 0xFFFF0000u));
   }
-  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 // Max / sum of x over lanes l and l ^ 16, and over l and l ^ 32: gfx950's
@@ -474,7 +485,10 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 // 32 positions, so each group runs 1/NG of the causal chain; at the end
 // groups 1..NG-1 hand their (max, sum, output) to group 0 through LDS and
 // group 0 merges and stores. Each group has
-// its own pair of LDS stages, filled by DMA: 32 K rows at a pitch of D/8 + 1
+// its own pair of LDS stages (one in the array of even steps, one in that of
+// odd steps: with two arrays the compiler tells the DMA into one stage apart
+// from the reads of the other, and lets the next stage's DMA fly while this
+// one is multiplied), filled by DMA: 32 K rows at a pitch of D/8 + 1
 // 16-byte slots (the A operand of S^T read whole, 32 rows per half-wavefront
 // on distinct banks) in a region padded to whole DMA instructions, then 32 V
 // rows at D/8 + 4 (transposed reads). Workgroups take units (query block,
@@ -498,11 +512,10 @@ template <int D, int NG>
 __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs a, int nqb) {
   using C = PrefillCfg<D>;
   static_assert(NG == 2 || NG == 4, "two or four groups");
-  static_assert(2 * (NG - 1) * (D * 33 + 64) * 4 <= NG * 2 * C::STAGE * 16, "groups 1..NG-1's partials fit in LDS");
   constexpr int KS = D / 16;  // 16-deep k-steps of q k^T
   constexpr int DB = D / 32;  // 32-column output blocks
   constexpr int CPR = D / 8;
-  __shared__ uint4 Ls[NG][2][C::STAGE];  // [group][stage]
+  __shared__ uint4 Ls0[NG][C::STAGE], Ls1[NG][C::STAGE];  // [group]: stages of even, odd steps
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -554,18 +567,18 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
     }
     off[u] = o;
   }
-  // Step t of this group: block 4 t + gr into stage t & 1 (blocks past the
-  // end read as zeros and nothing uses them).
-#define AP_ISSUE(ST, T)                                                                            \
+  // Step t of this group: block NG t + gr into its stage of Ls0 (t even) or
+  // Ls1 (t odd); blocks past the end read as zeros and nothing uses them.
+#define AP_ISSUE(LB, T)                                                                            \
   {                                                                                                \
     const unsigned bo_ = (unsigned)((NG * (T) + gr) * C::BK * D * 2);                               \
     _Pragma("unroll") for (int u = 0; u < C::NU; ++u) {                                            \
       const int n = 2 * u + wq;                                                                    \
       const unsigned o_ = off[u] >= 0x80000000u ? off[u] : off[u] + bo_;                           \
       if (n * 64 < C::KSL) /* wave-uniform */                                                      \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&Ls[gr][ST][n * 64], 16, o_, 0, 0, 0); \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&LB[gr][n * 64], 16, o_, 0, 0, 0); \
       else                                                                                         \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&Ls[gr][ST][n * 64], 16, o_, 0, 0, 0); \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&LB[gr][n * 64], 16, o_, 0, 0, 0); \
     }                                                                                              \
   }
 
@@ -582,12 +595,14 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
   f32x16_t o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
-  // Running max of the scaled scores (log2 domain) and sum, per token column.
-  // Groups 1..3 start at blocks that early tokens do not see: while a token's
-  // max is still -inf the exponents subtract 0 instead, so a masked (-inf)
-  // score gives exp2 = 0 and no -inf - -inf arises.
+  // Reference max m of the scaled scores (log2 domain; it trails the running
+  // max by at most kSlack) and sum, per token column. Groups 1..NG-1 start at
+  // blocks that early tokens do not see: while a token's m is still -inf the
+  // exponents subtract 0 instead, so a masked (-inf) score gives exp2 = 0 and
+  // no -inf - -inf arises.
   float m = -INFINITY, l = 0.f;
   const float c = a.qscale;
+  constexpr float kSlack = 8.f;
 
   // Fragment bases: K row j, slot 2 k + h2; V (transposed reads) row
   // 16 k' + 4 h2 + jj / 4 (+ 8), slot 4 db + 2 uu + (jj % 4) / 2, half jj % 2,
@@ -596,17 +611,14 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
   const int kfb = (j * C::KP + h2) * 16;
   const int vfb = C::KSL * 16 + ((4 * h2 + (jj >> 2)) * C::VP + 2 * uu + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
 
-  AP_ISSUE(0, 0)
-  if (nstep > 1) AP_ISSUE(1, 1)
-  for (int t = 0; t < nstep; ++t) {
-    const int st = t & 1, blk = NG * t + gr;
-    if (t + 1 < nstep)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | C::NU);  // vmcnt(NU): step t has landed, t + 1 may fly
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  // Step t on the stages LB (Ls0 for even t, Ls1 for odd t). Called with
+  // each array by name, so that the compiler sees which one is read.
+  auto step = [&](uint4 (&LB)[NG][C::STAGE], const int t) __attribute__((always_inline)) {
+    const int blk = NG * t + gr;
+    __builtin_amdgcn_s_waitcnt(0x0F70 | C::NU);  // vmcnt(NU): step t has landed, t + 1 may fly
     __builtin_amdgcn_s_barrier();
     if (blk < wblk) {
-      const char* L = (const char*)Ls[gr][st];
+      const char* L = (const char*)LB[gr];
       f32x16_t sa = f32x16_t{};
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
@@ -623,17 +635,23 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
 #pragma unroll
       for (int e = 0; e < 16; e += 4) bm = fmaxf(bm, fmaxf(fmaxf(sa[e], sa[e + 1]), fmaxf(sa[e + 2], sa[e + 3])));
       bm = max32(bm);
-      const float mn = fmaxf(m, bm * c);
+      // The subtracted reference mn moves only when the block's max passes
+      // it by more than kSlack (log2 units), so the probabilities stay below
+      // 2^kSlack and the output's rescale runs a few times per chain instead
+      // of at nearly every step. Softmax does not depend on the constant
+      // subtracted: only rounding changes.
+      const float mb = bm * c;
+      const float mn = mb > m + kSlack ? mb : m;
       const float ms = mn == -INFINITY ? 0.f : mn;
-      float rs = 0.f;
+      float r4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], c, -ms));
         sa[e] = pe;
-        rs += pe;
+        r4[e & 3] += pe;
       }
-      rs = sum32(rs);
-      if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {  // some token's max moved: rescale
+      const float rs = sum32((r4[0] + r4[1]) + (r4[2] + r4[3]));
+      if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {  // some token's reference moved: rescale
         const float alpha = __builtin_amdgcn_exp2f(m - ms);
         l *= alpha;
 #pragma unroll
@@ -661,22 +679,45 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();  // every wave is done with stage st
-    if (t + 2 < nstep) AP_ISSUE(st, t + 2)
+    __builtin_amdgcn_s_barrier();  // every wave is done with this stage
+    AP_ISSUE(LB, t + 2)
+  };
+
+  // Every step waits for its own stage and leaves the next one in flight,
+  // so every step issues one: the last two fetch blocks that nothing uses
+  // (past this query block's chain, or zeros past the cache). With
+  // conditional issues the compiler could not tell which array's DMA is the
+  // newer one and waited for both.
+  AP_ISSUE(Ls0, 0)
+  AP_ISSUE(Ls1, 1)
+  // Whole pairs of steps in the loop, so that its back edge always follows
+  // an odd step: then the compiler knows Ls1's DMA to be the newer one at
+  // the top of the loop and lets it fly while Ls0 is read.
+  int t = 0;
+  for (; t + 1 < nstep; t += 2) {
+    step(Ls0, t);
+    step(Ls1, t + 1);
   }
+  if (t < nstep) step(Ls0, t);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __builtin_amdgcn_s_barrier();  // no DMA is still landing when the stages become the merge's regions
 #undef AP_ISSUE
 
-  // Groups 1..3: partials into LDS, per wave [D columns][33] (token j at
+  // Groups 1..NG-1: partials into LDS, per wave [D columns][33] (token j at
   // j, a pitch of 33 keeps a column's 32 tokens and the other half-wave's
-  // columns on distinct banks) then m, l; then group 0 merges the four in
+  // columns on distinct banks) then m, l; then group 0 merges them in
   // group order. Lane (h2, j), element 4 q + r of block db: column
-  // 32 db + 8 q + 4 h2 + r of token j.
+  // 32 db + 8 q + 4 h2 + r of token j. Region r of the 2 (NG - 1) lies in
+  // Ls0 for r < RA, else in Ls1.
   constexpr int TP = 33;
   constexpr int WR = D * TP + 64;
-  float* red = reinterpret_cast<float*>(&Ls[0][0][0]);
+  constexpr int RA = NG * C::STAGE * 16 / (WR * 4);  // regions per array
+  static_assert(2 * RA >= 2 * (NG - 1), "groups 1..NG-1's partials fit in LDS");
+  auto region = [&](const int r) -> float* {
+    return r < RA ? reinterpret_cast<float*>(&Ls0[0][0]) + r * WR : reinterpret_cast<float*>(&Ls1[0][0]) + (r - RA) * WR;
+  };
   if (gr > 0) {
-    float* rw = red + (wave - 2) * WR;
+    float* rw = region(wave - 2);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -689,9 +730,11 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
   __syncthreads();
   if (gr == 0 && row_ok) {
     float mg[NG], M = m;
+    const float* rg[NG];
 #pragma unroll
     for (int q = 1; q < NG; ++q) {
-      mg[q] = red[(2 * q + wq - 2) * WR + D * TP + j];
+      rg[q] = region(2 * q + wq - 2);
+      mg[q] = rg[q][D * TP + j];
       M = fmaxf(M, mg[q]);
     }
     float f[NG];
@@ -700,7 +743,7 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
 #pragma unroll
     for (int q = 1; q < NG; ++q) {
       f[q] = __builtin_amdgcn_exp2f(mg[q] - M);
-      L += f[q] * red[(2 * q + wq - 2) * WR + D * TP + 32 + j];
+      L += f[q] * rg[q][D * TP + 32 + j];
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
@@ -713,7 +756,7 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
           const int col = 32 * db + 8 * q + 4 * h2 + r;
           float acc = f[0] * o[db][4 * q + r];
 #pragma unroll
-          for (int gq = 1; gq < NG; ++gq) acc += f[gq] * red[(2 * gq + wq - 2) * WR + col * TP + j];
+          for (int gq = 1; gq < NG; ++gq) acc += f[gq] * rg[gq][col * TP + j];
           v[r] = acc * inv;
         }
         store_bf16x4(out + 32 * db + 8 * q + 4 * h2, v[0], v[1], v[2], v[3]);
