@@ -122,13 +122,28 @@ __device__ __forceinline__ int seq_len(const AttnArgs& a, int s, int& sl) {
 
 // The key-value head's cache rows [0, kl) as a buffer resource: positions
 // past kl read as zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* C, const AttnArgs& a, int sl, int g,
-                                                            int kl, int D) {
+__device__ __forceinline__ uint64_t head_base(const uint16_t* C, const AttnArgs& a, int sl, int g, int kl, int D) {
   const uint64_t base = (uint64_t)(C + (kl > 0 ? ((int64_t)sl * a.nkv + g) * a.L_max * D : 0));
   const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
   const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0,
+  return lo | (hi << 32);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* C, const AttnArgs& a, int sl, int g,
+                                                            int kl, int D) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)head_base(C, a, sl, g, kl, D), (short)0,
                                            __builtin_amdgcn_readfirstlane(kl * D * 2), 0x00020000);
+}
+
+// A head's cache from byte bo on (bo and the head's byte count nb uniform):
+// the base moves in scalar registers, the range check still ends at the
+// head's last position, and nothing at all is in range once bo >= nb.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tail_rsrc(uint64_t base, unsigned nb, unsigned bo) {
+  const uint64_t p = base + bo;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)(nb > bo ? nb - bo : 0u)), 0x00020000);
 }
 
 // ---------------------------------------------------------------------------
@@ -494,6 +509,19 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 // rows at D/8 + 4 (transposed reads). Workgroups take units (query block,
 // head, sequence) longest first.
 
+// One stage of the prefill kernel's DMA: instruction n = 2 u + wq of the
+// stage fills 16-byte slots 64 n + lane of dst from byte off[u] of the block
+// at byte bo of the head's K (slots below KSL) or V cache.
+__device__ __forceinline__ void prefill_dma(int NU, int KSL, uint64_t kbase, uint64_t vbase, unsigned nb, unsigned bo,
+                                            uint4* dst, const unsigned* off, int wq) {
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int n = 2 * u + wq;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tail_rsrc(n * 64 < KSL ? kbase : vbase, nb, bo), (lds_void_t*)(dst + n * 64),
+                                             16, off[u], 0, 0, 0);
+  }
+}
+
 template <int D>
 struct PrefillCfg {
   // V's pitch of D/8 + 4 slots puts the 8 row segments of a half-wavefront's
@@ -548,9 +576,10 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
   const int wfirst_pos = base_pos + tok0;
   const int pos_j = base_pos + tok;
 
-  const __amdgpu_buffer_rsrc_t rk = head_rsrc(a.Kc, a, sl, g, kl, D);
-  const __amdgpu_buffer_rsrc_t rv = head_rsrc(a.Vc, a, sl, g, kl, D);
-  // DMA: instruction n = 2 u + wq of a stage fills slots 64 n + lane.
+  const uint64_t kbase = head_base(a.Kc, a, sl, g, kl, D), vbase = head_base(a.Vc, a, sl, g, kl, D);
+  const unsigned nb = (unsigned)__builtin_amdgcn_readfirstlane(kl * D * 2);
+  // DMA: instruction n = 2 u + wq of a stage fills slots 64 n + lane, from
+  // byte off[u] of the step's block (0x80000000: a padding slot, out of range).
   unsigned off[C::NU];
 #pragma unroll
   for (int u = 0; u < C::NU; ++u) {
@@ -568,19 +597,10 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
     off[u] = o;
   }
   // Step t of this group: block NG t + gr into its stage of Ls0 (t even) or
-  // Ls1 (t odd); blocks past the end read as zeros and nothing uses them.
-#define AP_ISSUE(LB, T)                                                                            \
-  {                                                                                                \
-    const unsigned bo_ = (unsigned)((NG * (T) + gr) * C::BK * D * 2);                               \
-    _Pragma("unroll") for (int u = 0; u < C::NU; ++u) {                                            \
-      const int n = 2 * u + wq;                                                                    \
-      const unsigned o_ = off[u] >= 0x80000000u ? off[u] : off[u] + bo_;                           \
-      if (n * 64 < C::KSL) /* wave-uniform */                                                      \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&LB[gr][n * 64], 16, o_, 0, 0, 0); \
-      else                                                                                         \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&LB[gr][n * 64], 16, o_, 0, 0, 0); \
-    }                                                                                              \
-  }
+  // Ls1 (t odd), through buffer resources that start at the block; blocks
+  // past the end read as zeros and nothing uses them.
+#define AP_ISSUE(LB, T) \
+  prefill_dma(C::NU, C::KSL, kbase, vbase, nb, (unsigned)((NG * (T) + gr) * C::BK * D * 2), LB[gr], off, wq);
 
   uint4 qf[KS];
   {
@@ -619,12 +639,16 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
     __builtin_amdgcn_s_barrier();
     if (blk < wblk) {
       const char* L = (const char*)LB[gr];
+      // All of the block's K fragments are read before the chain of
+      // products starts, so that one LDS latency is exposed, not KS / 2.
+      uint4 kf[KS];
+#pragma unroll
+      for (int k = 0; k < KS; ++k) kf[k] = *reinterpret_cast<const uint4*>(L + kfb + 2 * k * 16);
       f32x16_t sa = f32x16_t{};
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const uint4 kf = *reinterpret_cast<const uint4*>(L + kfb + 2 * k * 16);
-        sa = mfma_32x32x16(kf, qf[k], sa);
-      }
+      for (int k = 0; k < KS; ++k) sa = mfma_32x32x16(kf[k], qf[k], sa);
+      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // the DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);  // then the MFMAs
       // Lane (h2, j), element 4 q + r: position 32 blk + 8 q + 4 h2 + r.
       if (blk * C::BK + C::BK - 1 > wfirst_pos) {  // a diagonal block: mask what lies past the token
 #pragma unroll
