@@ -631,20 +631,25 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
   const int kfb = (j * C::KP + h2) * 16;
   const int vfb = C::KSL * 16 + ((4 * h2 + (jj >> 2)) * C::VP + 2 * uu + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
 
-  // Step t on the stages LB (Ls0 for even t, Ls1 for odd t). Called with
-  // each array by name, so that the compiler sees which one is read.
+  // Step t on the stages LB (Ls0 for even t, Ls1 for odd t; called with
+  // each array by name, so that the compiler sees which one is read) in two
+  // halves, each ended by a barrier: the scores and softmax, then the
+  // probabilities' two bf16 terms and P V. With four groups, groups 2 and
+  // 3 run one half behind groups 0 and 1, so the two wavefronts that share
+  // a SIMD (w and w + 4) are always in different halves: one's softmax
+  // overlaps the other's products.
   auto step = [&](uint4 (&LB)[NG][C::STAGE], const int t) __attribute__((always_inline)) {
     const int blk = NG * t + gr;
-    __builtin_amdgcn_s_waitcnt(0x0F70 | C::NU);  // vmcnt(NU): step t has landed, t + 1 may fly
-    __builtin_amdgcn_s_barrier();
-    if (blk < wblk) {
-      const char* L = (const char*)LB[gr];
+    const bool live = blk < wblk;
+    const char* L = (const char*)LB[gr];
+    f32x16_t sa;  // the scores, then the block's probabilities
+    if (live) {
       // All of the block's K fragments are read before the chain of
       // products starts, so that one LDS latency is exposed, not KS / 2.
       uint4 kf[KS];
 #pragma unroll
       for (int k = 0; k < KS; ++k) kf[k] = *reinterpret_cast<const uint4*>(L + kfb + 2 * k * 16);
-      f32x16_t sa = f32x16_t{};
+      sa = f32x16_t{};
 #pragma unroll
       for (int k = 0; k < KS; ++k) sa = mfma_32x32x16(kf[k], qf[k], sa);
       __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // the DS reads
@@ -683,6 +688,9 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
       }
       l += rs;
       m = mn;
+    }
+    __builtin_amdgcn_s_barrier();  // end of the first half
+    if (live) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int q0 = 2 * kk;
@@ -703,7 +711,8 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();  // every wave is done with this stage
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // step t + 1 (issued a step ago) has landed
+    __builtin_amdgcn_s_barrier();          // end of the second half: every wave is done with stage t
     AP_ISSUE(LB, t + 2)
   };
 
@@ -714,6 +723,10 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
   // newer one and waited for both.
   AP_ISSUE(Ls0, 0)
   AP_ISSUE(Ls1, 1)
+  __builtin_amdgcn_s_waitcnt(0x0F70 | C::NU);  // vmcnt(NU): step 0 has landed, step 1 may fly
+  __builtin_amdgcn_s_barrier();
+  const bool late = NG == 4 && gr >= 2;  // wave-uniform
+  if (late) __builtin_amdgcn_s_barrier();  // the half that groups 0 and 1 spend on step 0's scores
   // Whole pairs of steps in the loop, so that its back edge always follows
   // an odd step: then the compiler knows Ls1's DMA to be the newer one at
   // the top of the loop and lets it fly while Ls0 is read.
@@ -723,6 +736,7 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
     step(Ls1, t + 1);
   }
   if (t < nstep) step(Ls0, t);
+  if (!late) __builtin_amdgcn_s_barrier();  // the half that groups 2 and 3 spend on their last P V
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __builtin_amdgcn_s_barrier();  // no DMA is still landing when the stages become the merge's regions
 #undef AP_ISSUE
