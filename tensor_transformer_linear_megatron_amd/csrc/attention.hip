@@ -597,10 +597,12 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
     off[u] = o;
   }
   // Step t of this group: block NG t + gr into its stage of Ls0 (t even) or
-  // Ls1 (t odd), through buffer resources that start at the block; blocks
-  // past the end read as zeros and nothing uses them.
+  // Ls1 (t odd), through buffer resources that start at the block (blocks
+  // past the cache read as zeros). Steps t >= nstep, which the loop issues
+  // as well, get an empty range: all out of range, they write zeros without
+  // a memory access and land sooner than a fetch.
 #define AP_ISSUE(LB, T) \
-  prefill_dma(C::NU, C::KSL, kbase, vbase, nb, (unsigned)((NG * (T) + gr) * C::BK * D * 2), LB[gr], off, wq);
+  prefill_dma(C::NU, C::KSL, kbase, vbase, nb, (T) < nstep ? (unsigned)((NG * (T) + gr) * C::BK * D * 2) : nb, LB[gr], off, wq);
 
   uint4 qf[KS];
   {
@@ -717,8 +719,7 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
   };
 
   // Every step waits for its own stage and leaves the next one in flight,
-  // so every step issues one: the last two fetch blocks that nothing uses
-  // (past this query block's chain, or zeros past the cache). With
+  // so every step issues one; the last two have empty ranges. With
   // conditional issues the compiler could not tell which array's DMA is the
   // newer one and waited for both.
   AP_ISSUE(Ls0, 0)
