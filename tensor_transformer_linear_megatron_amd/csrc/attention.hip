@@ -499,15 +499,14 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 // 32x32x16 operands. Group gr multiplies key-value blocks gr, gr + NG, ... of
 // 32 positions, so each group runs 1/NG of the causal chain; at the end
 // groups 1..NG-1 hand their (max, sum, output) to group 0 through LDS and
-// group 0 merges and stores. Each group has
-// its own pair of LDS stages (one in the array of even steps, one in that of
-// odd steps: with two arrays the compiler tells the DMA into one stage apart
-// from the reads of the other, and lets the next stage's DMA fly while this
-// one is multiplied), filled by DMA: 32 K rows at a pitch of D/8 + 1
-// 16-byte slots (the A operand of S^T read whole, 32 rows per half-wavefront
-// on distinct banks) in a region padded to whole DMA instructions, then 32 V
-// rows at D/8 + 4 (transposed reads). Workgroups take units (query block,
-// head, sequence) longest first.
+// group 0 merges and stores. Each group has its own pair of LDS stages (one
+// in the array of even steps, one in that of odd steps: with two arrays the
+// compiler tells the DMA into one stage apart from the reads of the other,
+// and lets the next stage's DMA fly while this one is multiplied), filled by
+// DMA: 32 K rows at a pitch of D/8 + 1 16-byte slots (the A operand of S^T
+// read whole, 32 rows per half-wavefront on distinct banks) in a region
+// padded to whole DMA instructions, then 32 V rows at D/8 + 4 (transposed
+// reads). Workgroups take units (query block, head, sequence) longest first.
 
 // One stage of the prefill kernel's DMA: instruction n = 2 u + wq of the
 // stage fills 16-byte slots 64 n + lane of dst from byte off[u] of the block
