@@ -499,26 +499,34 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 // 32x32x16 operands. Group gr multiplies key-value blocks gr, gr + NG, ... of
 // 32 positions, so each group runs 1/NG of the causal chain; at the end
 // groups 1..NG-1 hand their (max, sum, output) to group 0 through LDS and
-// group 0 merges and stores. Each group has its own pair of LDS stages (one
-// in the array of even steps, one in that of odd steps: with two arrays the
-// compiler tells the DMA into one stage apart from the reads of the other,
-// and lets the next stage's DMA fly while this one is multiplied), filled by
-// DMA: 32 K rows at a pitch of D/8 + 1 16-byte slots (the A operand of S^T
-// read whole, 32 rows per half-wavefront on distinct banks) in a region
-// padded to whole DMA instructions, then 32 V rows at D/8 + 4 (transposed
-// reads). Workgroups take units (query block, head, sequence) longest first.
+// group 0 merges and stores. Workgroups take units (query block, head,
+// sequence) longest first.
+//
+// Each group stages its blocks in LDS by DMA, K and V apart, each double
+// buffered in two arrays (even and odd blocks of its chain): 32 K rows at a
+// pitch of D/8 + 1 16-byte slots (the A operand of S^T read whole, 32 rows
+// per half-wavefront on distinct banks), 32 V rows at D/8 + 4 (transposed
+// reads), each region padded to whole DMA instructions. With separate arrays
+// read by name the compiler tells the DMA into one buffer apart from the
+// reads of another and lets it fly.
+//
+// A step of the chain is two halves, each ended by a barrier: (1) the softmax
+// of block t's scores and the probabilities' two bf16 terms, vector ALU only;
+// (2) P V of block t and the scores S^T of block t + 1, matrix cores and LDS
+// reads. K of block t + 1 is fetched two steps before it is used, V of block
+// t two steps before. With four groups, groups 2 and 3 run one half behind
+// groups 0 and 1: the two wavefronts that share a SIMD (w and w + 4) are then
+// always in different halves, one on the vector ALU while the other keeps the
+// matrix cores busy.
 
-// One stage of the prefill kernel's DMA: instruction n = 2 u + wq of the
-// stage fills 16-byte slots 64 n + lane of dst from byte off[u] of the block
-// at byte bo of the head's K (slots below KSL) or V cache.
-__device__ __forceinline__ void prefill_dma(int NU, int KSL, uint64_t kbase, uint64_t vbase, unsigned nb, unsigned bo,
-                                            uint4* dst, const unsigned* off, int wq) {
+// One buffer's DMA: instruction n = 2 u + wq fills 16-byte slots 64 n + lane
+// of dst from byte off[u] of the block at byte bo of the head's cache (base).
+__device__ __forceinline__ void prefill_dma(int NU, uint64_t base, unsigned nb, unsigned bo, uint4* dst,
+                                            const unsigned* off, int wq) {
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int n = 2 * u + wq;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(tail_rsrc(n * 64 < KSL ? kbase : vbase, nb, bo), (lds_void_t*)(dst + n * 64),
-                                             16, off[u], 0, 0, 0);
-  }
+  for (int u = 0; u < NU; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tail_rsrc(base, nb, bo), (lds_void_t*)(dst + (2 * u + wq) * 64), 16,
+                                             off[u], 0, 0, 0);
 }
 
 template <int D>
@@ -526,13 +534,11 @@ struct PrefillCfg {
   // V's pitch of D/8 + 4 slots puts the 8 row segments of a half-wavefront's
   // transposed read (4 rows x 2 column halves) on distinct banks.
   static constexpr int KP = D / 8 + 1, VP = D / 8 + 4;
-  static constexpr int BK = 32;                                 // positions per block
-  static constexpr int KSL = (BK * KP + 63) / 64 * 64;          // K region, whole instructions
-  static constexpr int VSL = BK * VP;
-  static constexpr int NDMA = (KSL + VSL) / 64;                 // DMA instructions per stage
-  static constexpr int NU = (NDMA + 1) / 2;                     // per wave (2 wavefronts per group)
-  static constexpr int STAGE = NU * 2 * 64;                     // slots, with the padding
-  static_assert(VSL % 64 == 0, "a DMA instruction stays within K or V");
+  static constexpr int BK = 32;                       // positions per block
+  static constexpr int NUK = (BK * KP + 127) / 128;   // K DMA instructions per wave
+  static constexpr int NUV = (BK * VP + 127) / 128;   // V DMA instructions per wave
+  static constexpr int KST = NUK * 128, VST = NUV * 128;  // slots of a K / V buffer, with the padding
+  static_assert(NUK + 2 * NUV <= 15, "the prologue's wait fits the low vmcnt field");
 };
 
 template <int D, int NG>
@@ -542,7 +548,8 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
   constexpr int KS = D / 16;  // 16-deep k-steps of q k^T
   constexpr int DB = D / 32;  // 32-column output blocks
   constexpr int CPR = D / 8;
-  __shared__ uint4 Ls0[NG][C::STAGE], Ls1[NG][C::STAGE];  // [group]: stages of even, odd steps
+  // [group]: K of even and odd blocks of the group's chain, V of even and odd blocks
+  __shared__ uint4 Ks0[NG][C::KST], Ks1[NG][C::KST], Vs0[NG][C::VST], Vs1[NG][C::VST];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -577,42 +584,37 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
 
   const uint64_t kbase = head_base(a.Kc, a, sl, g, kl, D), vbase = head_base(a.Vc, a, sl, g, kl, D);
   const unsigned nb = (unsigned)__builtin_amdgcn_readfirstlane(kl * D * 2);
-  // DMA: instruction n = 2 u + wq of a stage fills slots 64 n + lane, from
-  // byte off[u] of the step's block (0x80000000: a padding slot, out of range).
-  unsigned off[C::NU];
+  // DMA offsets of this lane: slot 64 (2 u + wq) + lane of a buffer holds
+  // byte offk[u] (offv[u]) of its block; 0x80000000 marks a padding slot
+  // (out of range: zeros).
+  unsigned offk[C::NUK], offv[C::NUV];
 #pragma unroll
-  for (int u = 0; u < C::NU; ++u) {
-    const int n = 2 * u + wq;
-    int q = n * 64 + lane;
-    unsigned o = 0x80000000u;
-    if (n * 64 < C::KSL) {
-      const int row = q / C::KP, c = q - row * C::KP;
-      if (row < C::BK && c < CPR) o = (unsigned)((row * D + 8 * c) * 2);
-    } else if (n < C::NDMA) {
-      q -= C::KSL;
-      const int row = q / C::VP, c = q - row * C::VP;
-      if (c < CPR) o = (unsigned)((row * D + 8 * c) * 2);
-    }
-    off[u] = o;
+  for (int u = 0; u < C::NUK; ++u) {
+    const int q = (2 * u + wq) * 64 + lane, row = q / C::KP, c = q - row * C::KP;
+    offk[u] = row < C::BK && c < CPR ? (unsigned)((row * D + 8 * c) * 2) : 0x80000000u;
   }
-  // Step t of this group: block NG t + gr into its stage of Ls0 (t even) or
-  // Ls1 (t odd), through buffer resources that start at the block (blocks
-  // past the cache read as zeros). Steps t >= nstep, which the loop issues
-  // as well, get an empty range: all out of range, they write zeros without
-  // a memory access and land sooner than a fetch.
-#define AP_ISSUE(LB, T) \
-  prefill_dma(C::NU, C::KSL, kbase, vbase, nb, (T) < nstep ? (unsigned)((NG * (T) + gr) * C::BK * D * 2) : nb, LB[gr], off, wq);
+#pragma unroll
+  for (int u = 0; u < C::NUV; ++u) {
+    const int q = (2 * u + wq) * 64 + lane, row = q / C::VP, c = q - row * C::VP;
+    offv[u] = row < C::BK && c < CPR ? (unsigned)((row * D + 8 * c) * 2) : 0x80000000u;
+  }
+  // Block NG t + gr of this group's chain (t = its step) into a K or V
+  // buffer; steps t >= nstep, which the loop issues as well, get an empty
+  // range: all out of range, they write zeros without a memory access.
+#define AP_BO(T) ((T) < nstep ? (unsigned)((NG * (T) + gr) * C::BK * D * 2) : nb)
+#define AP_K(KB, T) prefill_dma(C::NUK, kbase, nb, AP_BO(T), KB[gr], offk, wq);
+#define AP_V(VB, T) prefill_dma(C::NUV, vbase, nb, AP_BO(T), VB[gr], offv, wq);
 
+  // Q fragments. Tokens past q_len read token 0's row: their columns of S^T
+  // are finite and independent of the others', and nothing stores them.
   uint4 qf[KS];
   {
     const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + (row_ok ? tok : 0)) * a.ldqkv + (int64_t)h * D + 8 * h2;
-    const uint32_t qm = row_ok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qp + 16 * k);
-      qf[k] = make_uint4(v.x & qm, v.y & qm, v.z & qm, v.w & qm);
-    }
+    for (int k = 0; k < KS; ++k) qf[k] = *reinterpret_cast<const uint4*>(qp + 16 * k);
   }
+  // The explicit DMA wait counts below assume the Q loads went out first.
+  __builtin_amdgcn_sched_barrier(0);
   f32x16_t o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
@@ -630,31 +632,28 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
   // where the lane is 32 h2 + 16 uu + jj.
   const int jj = j & 15, uu = j >> 4;
   const int kfb = (j * C::KP + h2) * 16;
-  const int vfb = C::KSL * 16 + ((4 * h2 + (jj >> 2)) * C::VP + 2 * uu + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
+  const int vfb = ((4 * h2 + (jj >> 2)) * C::VP + 2 * uu + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
 
-  // Step t on the stages LB (Ls0 for even t, Ls1 for odd t; called with
-  // each array by name, so that the compiler sees which one is read) in two
-  // halves, each ended by a barrier: the scores and softmax, then the
-  // probabilities' two bf16 terms and P V. With four groups, groups 2 and
-  // 3 run one half behind groups 0 and 1, so the two wavefronts that share
-  // a SIMD (w and w + 4) are always in different halves: one's softmax
-  // overlaps the other's products.
-  auto step = [&](uint4 (&LB)[NG][C::STAGE], const int t) __attribute__((always_inline)) {
+  // The scores S^T of block blk (this wave's 32 tokens x its 32 positions)
+  // from the K buffer KB, all K fragments read before the chain of products.
+  auto scores = [&](const uint4* KB, f32x16_t& sa) __attribute__((always_inline)) {
+    const char* L = (const char*)KB;
+    uint4 kf[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) kf[k] = *reinterpret_cast<const uint4*>(L + kfb + 2 * k * 16);
+    sa = f32x16_t{};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) sa = mfma_32x32x16(kf[k], qf[k], sa);
+  };
+
+  // Step t: V of block t is in VB, K of block t + 1 in KB (so VB is the
+  // array of t's parity and KB the other); sa holds block t's scores.
+  f32x16_t sa;
+  auto step = [&](uint4 (&VB)[NG][C::VST], uint4 (&KB)[NG][C::KST], const int t) __attribute__((always_inline)) {
     const int blk = NG * t + gr;
-    const bool live = blk < wblk;
-    const char* L = (const char*)LB[gr];
-    f32x16_t sa;  // the scores, then the block's probabilities
+    const bool live = blk < wblk, live1 = blk + NG < wblk;
+    uint4 ph[2], pl[2];
     if (live) {
-      // All of the block's K fragments are read before the chain of
-      // products starts, so that one LDS latency is exposed, not KS / 2.
-      uint4 kf[KS];
-#pragma unroll
-      for (int k = 0; k < KS; ++k) kf[k] = *reinterpret_cast<const uint4*>(L + kfb + 2 * k * 16);
-      sa = f32x16_t{};
-#pragma unroll
-      for (int k = 0; k < KS; ++k) sa = mfma_32x32x16(kf[k], qf[k], sa);
-      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // the DS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);  // then the MFMAs
       // Lane (h2, j), element 4 q + r: position 32 blk + 8 q + 4 h2 + r.
       if (blk * C::BK + C::BK - 1 > wfirst_pos) {  // a diagonal block: mask what lies past the token
 #pragma unroll
@@ -689,16 +688,22 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
       }
       l += rs;
       m = mn;
-    }
-    __builtin_amdgcn_s_barrier();  // end of the first half
-    if (live) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int q0 = 2 * kk;
         const float pe[8] = {sa[4 * q0],     sa[4 * q0 + 1], sa[4 * q0 + 2], sa[4 * q0 + 3],
                              sa[4 * q0 + 4], sa[4 * q0 + 5], sa[4 * q0 + 6], sa[4 * q0 + 7]};
-        uint4 ph, pl;
-        split8(pe, ph, pl);
+        split8(pe, ph[kk], pl[kk]);
+      }
+    }
+    // V of block t and K of block t + 1 have landed; after them only V of
+    // t + 1 and K of t + 2 may be in flight.
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (C::NUV + C::NUK));
+    __builtin_amdgcn_s_barrier();  // end of the first half
+    if (live) {
+      const char* L = (const char*)VB[gr];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
         uint4 vf[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -706,53 +711,66 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
           vf[db] = tr_pair(v0, v0 + 8 * C::VP * 16);
         }
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = mfma_32x32x16(vf[db], ph, o[db]);
+        for (int db = 0; db < DB; ++db) o[db] = mfma_32x32x16(vf[db], ph[kk], o[db]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = mfma_32x32x16(vf[db], pl, o[db]);
+        for (int db = 0; db < DB; ++db) o[db] = mfma_32x32x16(vf[db], pl[kk], o[db]);
       }
     }
+    if (live1) scores(KB[gr], sa);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // step t + 1 (issued a step ago) has landed
-    __builtin_amdgcn_s_barrier();          // end of the second half: every wave is done with stage t
-    AP_ISSUE(LB, t + 2)
+    __builtin_amdgcn_s_barrier();  // end of the second half: V of t and K of t + 1 are read
+    AP_V(VB, t + 2)
+    AP_K(KB, t + 3)
   };
 
-  // Every step waits for its own stage and leaves the next one in flight,
-  // so every step issues one; the last two have empty ranges. With
-  // conditional issues the compiler could not tell which array's DMA is the
-  // newer one and waited for both.
-  AP_ISSUE(Ls0, 0)
-  AP_ISSUE(Ls1, 1)
-  __builtin_amdgcn_s_waitcnt(0x0F70 | C::NU);  // vmcnt(NU): step 0 has landed, step 1 may fly
+  // Prologue: K and V of steps 0 and 1 in flight, then step 0's scores; K of
+  // step 2 follows once step 0's K buffer is free. Every DMA issue is
+  // unconditional (the last ones have empty ranges): with conditional
+  // issues the compiler could not tell which buffer's DMA is the newest and
+  // would wait for all of them before a fragment read.
+  AP_K(Ks0, 0)
+  AP_V(Vs0, 0)
+  AP_K(Ks1, 1)
+  AP_V(Vs1, 1)
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * C::NUV + C::NUK));  // K of step 0 has landed
   __builtin_amdgcn_s_barrier();
   const bool late = NG == 4 && gr >= 2;  // wave-uniform
   if (late) __builtin_amdgcn_s_barrier();  // the half that groups 0 and 1 spend on step 0's scores
-  // Whole pairs of steps in the loop, so that its back edge always follows
-  // an odd step: then the compiler knows Ls1's DMA to be the newer one at
-  // the top of the loop and lets it fly while Ls0 is read.
-  int t = 0;
-  for (; t + 1 < nstep; t += 2) {
-    step(Ls0, t);
-    step(Ls1, t + 1);
+  if (gr < wblk) scores(Ks0[gr], sa);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  AP_K(Ks0, 2)
+  // Whole pairs of steps (an odd count gets one step that multiplies
+  // nothing), so that the loop's back edge always follows an odd step and the
+  // compiler knows which buffers' DMAs are the newer ones at its top.
+  const int npair = (nstep + 1) / 2;
+  for (int tp = 0; tp < npair; ++tp) {
+    step(Vs0, Ks1, 2 * tp);
+    step(Vs1, Ks0, 2 * tp + 1);
   }
-  if (t < nstep) step(Ls0, t);
-  if (!late) __builtin_amdgcn_s_barrier();  // the half that groups 2 and 3 spend on their last P V
+  if (!late) __builtin_amdgcn_s_barrier();  // the half that groups 2 and 3 spend on their last step
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __builtin_amdgcn_s_barrier();  // no DMA is still landing when the stages become the merge's regions
-#undef AP_ISSUE
+  __builtin_amdgcn_s_barrier();  // no DMA is still landing when the buffers become the merge's regions
+#undef AP_BO
+#undef AP_K
+#undef AP_V
 
   // Groups 1..NG-1: partials into LDS, per wave [D columns][33] (token j at
   // j, a pitch of 33 keeps a column's 32 tokens and the other half-wave's
   // columns on distinct banks) then m, l; then group 0 merges them in
   // group order. Lane (h2, j), element 4 q + r of block db: column
-  // 32 db + 8 q + 4 h2 + r of token j. Region r of the 2 (NG - 1) lies in
-  // Ls0 for r < RA, else in Ls1.
+  // 32 db + 8 q + 4 h2 + r of token j. Region r of the 2 (NG - 1) is region
+  // r % RK of Ks0, Ks1 (r < 2 RK), else of Vs0, Vs1.
   constexpr int TP = 33;
   constexpr int WR = D * TP + 64;
-  constexpr int RA = NG * C::STAGE * 16 / (WR * 4);  // regions per array
-  static_assert(2 * RA >= 2 * (NG - 1), "groups 1..NG-1's partials fit in LDS");
+  constexpr int RK = NG * C::KST * 16 / (WR * 4);  // regions per K buffer
+  constexpr int RV = NG * C::VST * 16 / (WR * 4);  // regions per V buffer
+  static_assert(RK >= 1 && RV >= 1 && 2 * RK + 2 * RV >= 2 * (NG - 1), "groups 1..NG-1's partials fit in LDS");
   auto region = [&](const int r) -> float* {
-    return r < RA ? reinterpret_cast<float*>(&Ls0[0][0]) + r * WR : reinterpret_cast<float*>(&Ls1[0][0]) + (r - RA) * WR;
+    if (r < RK) return reinterpret_cast<float*>(&Ks0[0][0]) + r * WR;
+    if (r < 2 * RK) return reinterpret_cast<float*>(&Ks1[0][0]) + (r - RK) * WR;
+    if (r < 2 * RK + RV) return reinterpret_cast<float*>(&Vs0[0][0]) + (r - 2 * RK) * WR;
+    return reinterpret_cast<float*>(&Vs1[0][0]) + (r - 2 * RK - RV) * WR;
   };
   if (gr > 0) {
     float* rw = region(wave - 2);
