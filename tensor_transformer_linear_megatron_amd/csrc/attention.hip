@@ -755,25 +755,27 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
 #undef AP_K
 #undef AP_V
 
-  // Groups 1..NG-1: partials into LDS, per wave [D columns][33] (token j at
-  // j, a pitch of 33 keeps a column's 32 tokens and the other half-wave's
-  // columns on distinct banks) then m, l; then group 0 merges them in
-  // group order. Lane (h2, j), element 4 q + r of block db: column
-  // 32 db + 8 q + 4 h2 + r of token j. Region r of the 2 (NG - 1) is region
-  // r % RK of Ks0, Ks1 (r < 2 RK), else of Vs0, Vs1.
+  // Every wave's partial into LDS, region w = the wave: [D columns][33]
+  // (token j at j; a pitch of 33 keeps a column's 32 tokens and the other
+  // half-wave's columns on distinct banks), then m and l. Lane (h2, j),
+  // element 4 q + r of block db: column 32 db + 8 q + 4 h2 + r of token j.
+  // Then wave (gr, wq) merges columns [gr D/NG, (gr + 1) D/NG) of its 32
+  // tokens over the NG groups in group order, each half-wavefront half of
+  // them, and stores them. Region r is region r % RK of Ks0, Ks1 (r < 2 RK),
+  // else of Vs0, Vs1.
   constexpr int TP = 33;
   constexpr int WR = D * TP + 64;
   constexpr int RK = NG * C::KST * 16 / (WR * 4);  // regions per K buffer
   constexpr int RV = NG * C::VST * 16 / (WR * 4);  // regions per V buffer
-  static_assert(RK >= 1 && RV >= 1 && 2 * RK + 2 * RV >= 2 * (NG - 1), "groups 1..NG-1's partials fit in LDS");
+  static_assert(RK >= 1 && RV >= 1 && 2 * RK + 2 * RV >= 2 * NG, "every wave's partial fits in LDS");
   auto region = [&](const int r) -> float* {
     if (r < RK) return reinterpret_cast<float*>(&Ks0[0][0]) + r * WR;
     if (r < 2 * RK) return reinterpret_cast<float*>(&Ks1[0][0]) + (r - RK) * WR;
     if (r < 2 * RK + RV) return reinterpret_cast<float*>(&Vs0[0][0]) + (r - 2 * RK) * WR;
     return reinterpret_cast<float*>(&Vs1[0][0]) + (r - 2 * RK - RV) * WR;
   };
-  if (gr > 0) {
-    float* rw = region(wave - 2);
+  {
+    float* rw = region(wave);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -784,39 +786,38 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
     }
   }
   __syncthreads();
-  if (gr == 0 && row_ok) {
-    float mg[NG], M = m;
+  if (row_ok) {
+    constexpr int CW = D / NG / 2;  // columns per lane
+    static_assert(CW % 4 == 0, "whole 4-column stores");
     const float* rg[NG];
+    float mg[NG], M = -INFINITY;
 #pragma unroll
-    for (int q = 1; q < NG; ++q) {
-      rg[q] = region(2 * q + wq - 2);
+    for (int q = 0; q < NG; ++q) {
+      rg[q] = region(2 * q + wq);
       mg[q] = rg[q][D * TP + j];
       M = fmaxf(M, mg[q]);
     }
-    float f[NG];
-    f[0] = __builtin_amdgcn_exp2f(m - M);
-    float L = f[0] * l;
+    float f[NG], L = 0.f;
 #pragma unroll
-    for (int q = 1; q < NG; ++q) {
+    for (int q = 0; q < NG; ++q) {
       f[q] = __builtin_amdgcn_exp2f(mg[q] - M);
       L += f[q] * rg[q][D * TP + 32 + j];
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
+    const int c0 = gr * (D / NG) + h2 * CW;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int i = 0; i < CW; i += 4) {
+      float v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v[4];
+      for (int r = 0; r < 4; ++r) {
+        const int col = c0 + i + r;
+        float acc = f[0] * rg[0][col * TP + j];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int col = 32 * db + 8 * q + 4 * h2 + r;
-          float acc = f[0] * o[db][4 * q + r];
-#pragma unroll
-          for (int gq = 1; gq < NG; ++gq) acc += f[gq] * rg[gq][col * TP + j];
-          v[r] = acc * inv;
-        }
-        store_bf16x4(out + 32 * db + 8 * q + 4 * h2, v[0], v[1], v[2], v[3]);
+        for (int q = 1; q < NG; ++q) acc += f[q] * rg[q][col * TP + j];
+        v[r] = acc * inv;
       }
+      store_bf16x4(out + c0 + i, v[0], v[1], v[2], v[3]);
+    }
   }
 }
 
