@@ -498,9 +498,9 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 // takes tokens 64 qb + 32 (w % 2) + j, j = lane % 32, the column of its
 // 32x32x16 operands. Group gr multiplies key-value blocks gr, gr + NG, ... of
 // 32 positions, so each group runs 1/NG of the causal chain; at the end
-// groups 1..NG-1 hand their (max, sum, output) to group 0 through LDS and
-// group 0 merges and stores. Workgroups take units (query block, head,
-// sequence) longest first.
+// every wavefront writes its (max, sum, output) to LDS, then merges and
+// stores its own slice of columns over the NG groups. Workgroups take units
+// (query block, head, sequence) longest first.
 //
 // Each group stages its blocks in LDS by DMA, K and V apart, each double
 // buffered in two arrays (even and odd blocks of its chain): 32 K rows at a
