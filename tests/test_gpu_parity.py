@@ -316,7 +316,7 @@ def test_permutation_weight_bit_exact():
 # Reduction.
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("t", [1, 2, 3, 8])
+@pytest.mark.parametrize("t", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("M,N", [(1, 8), (7, 4100), (64, 8192)])
 def test_reduce_partials(t, M, N):
     say("reduce", t, M, N)
@@ -334,7 +334,7 @@ def test_reduce_partials(t, M, N):
     np.testing.assert_array_equal(host_f64(Pd[0]), got)
 
 
-@pytest.mark.parametrize("t", [1, 2, 3, 8])
+@pytest.mark.parametrize("t", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("Mt,N", [(1, 8), (3, 4100), (8, 8192)])
 def test_reduce_scatter_partials(t, Mt, N):
     """Sequence-parallel partial sum: each rank's token rows of the rank-order
@@ -362,7 +362,7 @@ def test_reduce_scatter_partials(t, Mt, N):
     assert not wide[:, :4].any() and not wide[:, 4 + N:].any()
 
 
-@pytest.mark.parametrize("t", [1, 2, 3, 8])
+@pytest.mark.parametrize("t", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("Mt,N", [(1, 8), (5, 4104), (64, 8192)])
 def test_gather_rows(t, Mt, N):
     """The row gather: the ranks' bf16 row blocks stacked in rank order, bit-exact."""
