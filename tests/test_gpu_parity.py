@@ -548,9 +548,10 @@ SAMPLE_ROWS_4096 = [0, 1, 15, 16, 127, 128, 129, 1000, 2047, 2048, 3071, 4094, 4
 
 
 def test_llama70b_attention_tp8_prefill():
-    """Rank 0's QKV column slice (8 Q + 1 K + 1 V head: 8192 x 1280) and O row
-    slice (1024 x 8192) at 4096 tokens; the O partials of all 8 ranks summed
-    against the unsharded projection, on sampled rows."""
+    """Every rank's QKV column slice (8 Q + 1 K + 1 V head: 8192 x 1280) and O
+    row slice (1024 x 8192) at 4096 tokens, each against its share of the
+    oracle, and the O partials of all 8 ranks summed against the unsharded
+    projection, on sampled rows."""
     say("llama70b attention tp8 prefill")
     c = wl.LLAMA70B
     heads = (c["n_q"], c["n_kv"], c["head_dim"])
@@ -569,10 +570,9 @@ def test_llama70b_attention_tp8_prefill():
         QKV = tp.tp_col_linear(dq, Xd, tp.tp_shard_pack(dq, Wqkv_d))
         Ar = Ad[:, do.row_begin:do.row_end].contiguous()
         tp.tp_row_linear(do, Ar, tp.tp_shard_pack(do, Wo_d), P=P[r])
-        if r in (0, 7):
-            got = host_f64(QKV)[rows]
-            assert_parity(got, oracle.bf16_to_f64(oracle.col_linear_bf16(X[rows], Wqkv, pq)), f"QKV_{r}")
-            assert_parity(host_f64(P[r])[rows], oracle.row_linear(A[rows][:, po["rows"]], Wo, po), f"O_{r}")
+        got = host_f64(QKV)[rows]
+        assert_parity(got, oracle.bf16_to_f64(oracle.col_linear_bf16(X[rows], Wqkv, pq)), f"QKV_{r}")
+        assert_parity(host_f64(P[r])[rows], oracle.row_linear(A[rows][:, po["rows"]], Wo, po), f"O_{r}")
     Y = host_f64(tp.tp_reduce_partials(P))[rows]
     ref = oracle.row_linear(A[rows], Wo, oracle.plan("o_row", 8192, 8192, 1, 0, heads=heads))
     assert_parity(Y, ref, "O partials summed over 8 ranks vs unsharded")
