@@ -5,10 +5,11 @@ partials of the decode split-K, the prefill split-K, the prefill's split last
 round and the attention decode's chunks; the 8-bit prefill's dequantised bf16
 copy of the shard) with a workspace of exactly the reported size. That
 workspace is filled with NaN bit patterns beforehand and sits at the start of
-a larger buffer whose tail holds a canary. The result must match the oracle
-(so no kernel reads workspace bytes that no kernel of the call wrote: a NaN
-would spread to the output) and the canary must come back intact (so no
-kernel writes past the reported size).
+a larger buffer whose tail holds a canary. The whole output must be finite
+and the sampled rows must match the oracle (so no kernel reads workspace
+bytes that no kernel of the call wrote: a NaN would spread to the output),
+and the canary must come back intact (so no kernel writes past the reported
+size).
 """
 from __future__ import annotations
 
@@ -61,6 +62,12 @@ LINEAR_CASES = [
     ("row", 3088, 1000, 2, 1, 257, tp.TP_PATH_PREFILL),
     ("col", 1000, 4328, 1, 0, 4000, tp.TP_PATH_PREFILL),
     ("gateup_col", 1000, 2 * 2168, 1, 0, 4000, tp.TP_PATH_PREFILL),
+    # drawn by a seeded search over random shapes for ones whose last round
+    # of big tiles runs as a split-K sub-GEMM (ragged token counts)
+    ("gateup_col", 2048, 5760, 1, 0, 2979, tp.TP_PATH_PREFILL),
+    ("col", 2112, 15744, 1, 0, 8591, tp.TP_PATH_PREFILL),
+    ("gateup_col", 1536, 9088, 1, 0, 8971, tp.TP_PATH_PREFILL),
+    ("row", 2432, 5184, 1, 0, 6307, tp.TP_PATH_PREFILL),
 ]
 
 
@@ -76,15 +83,20 @@ def test_linear_workspace_is_exactly_enough(kind, K, N, t, r, M, path):
     W = si.normal_bf16(71, (K, N), 0.05)
     Wp = tp.tp_shard_pack(d, dev(W))
     buf, ws = _buffer(need)
-    rows = sorted({0, 1, M // 3, M // 2, M - 2, M - 1})
+    # one row in every 256-token tile, plus the edges
+    rows = sorted({0, 1, M // 3, M // 2, M - 2, M - 1} | {min(M - 1, t0 + 131) for t0 in range(0, M, 256)})
     if kind == "row":
         Zr = X[:, p["rows"]]
-        got = host_f64(tp.tp_row_linear(d, dev(Zr), Wp, ws=ws))[rows]
+        out = tp.tp_row_linear(d, dev(Zr), Wp, ws=ws)
         ref = oracle.row_linear(Zr[rows], W, p)
     else:
-        got = host_f64(tp.tp_col_linear(d, dev(X), Wp, ws=ws))[rows]
+        out = tp.tp_col_linear(d, dev(X), Wp, ws=ws)
         fn = oracle.gateup_swiglu if kind == "gateup_col" else oracle.col_linear_bf16
         ref = oracle.bf16_to_f64(fn(X[rows], W, p))
+    # a workspace byte read before any kernel of the call wrote it is NaN, and
+    # would leave a non-finite value somewhere in the output
+    assert bool(torch.isfinite(out.float()).all()), f"{kind} K={K} N={N} M={M}: non-finite output"
+    got = host_f64(out)[rows]
     _canary_intact(buf, need, f"{kind} K={K} N={N} M={M}")
     assert_parity(got, ref, f"{kind} K={K} N={N} M={M} with an exact workspace")
 
@@ -111,14 +123,16 @@ def test_fp8_workspace_is_exactly_enough(kind, K, N, t, r, M, path):
     rows = sorted({0, 1, M // 2, M - 1})
     if kind == "row":
         Zr = X[:, p["rows"]]
-        got = host_f64(tp.tp_row_linear(d, dev(Zr), Wp, ws=ws))[rows]
+        out = tp.tp_row_linear(d, dev(Zr), Wp, ws=ws)
         ref = oracle.row_linear_fp8(Zr[rows], W, p)
     else:
-        got = host_f64(tp.tp_col_linear(d, dev(X), Wp, ws=ws))[rows]
+        out = tp.tp_col_linear(d, dev(X), Wp, ws=ws)
         if kind == "gateup_col":
             ref = oracle.bf16_to_f64(oracle.gateup_swiglu_fp8(X[rows], W, p))
         else:
             ref = oracle.bf16_to_f64(oracle.round_bf16(oracle.col_linear_fp8(X[rows], W, p)))
+    assert bool(torch.isfinite(out.float()).all()), f"fp8 {kind} K={K} N={N} M={M}: non-finite output"
+    got = host_f64(out)[rows]
     _canary_intact(buf, need, f"fp8 {kind} K={K} N={N} M={M}")
     assert_parity(got, ref, f"fp8 {kind} K={K} N={N} M={M} with an exact workspace")
 
