@@ -500,7 +500,9 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 // 32 positions, so each group runs 1/NG of the causal chain; at the end
 // every wavefront writes its (max, sum, output) to LDS, then merges and
 // stores its own slice of columns over the NG groups. Workgroups take units
-// (query block, head, sequence) longest first.
+// (query block, head, sequence) longest first; with four groups and nearly
+// two rounds of units, each workgroup takes a pair, the longest with the
+// shortest.
 //
 // Each group stages its blocks in LDS by DMA, K and V apart, each double
 // buffered in two arrays (even and odd blocks of its chain): 32 K rows at a
@@ -542,7 +544,7 @@ struct PrefillCfg {
 };
 
 template <int D, int NG>
-__global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs a, int nqb) {
+__global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs a, int nqb, int units, int paired) {
   using C = PrefillCfg<D>;
   static_assert(NG == 2 || NG == 4, "two or four groups");
   constexpr int KS = D / 16;  // 16-deep k-steps of q k^T
@@ -555,270 +557,278 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void attn_prefill_kernel(AttnArgs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gr = wave >> 1, wq = wave & 1;
   const int h2 = lane >> 5, j = lane & 31;
-  const int unit = (int)blockIdx.x;
-  const int per = a.nq * a.S;
-  const int qb = nqb - 1 - unit / per, h = (unit % per) % a.nq, s = (unit % per) / a.nq;
-  const int g = h / a.G;
-  int sl;
-  const int kl = seq_len(a, s, sl);
-  const int tok0 = qb * 64 + wq * 32;
-  const int tok = tok0 + j;
-  const bool row_ok = tok < a.q_len;
-  uint16_t* out = a.A + ((int64_t)s * a.q_len + tok) * a.lda + (int64_t)h * D;
-  if (kl == 0) {  // uniform over the workgroup: a sequence out of range gives zeros
-    if (row_ok && gr == 0)
+  // Paired (four groups only): workgroup b also takes unit units - 1 - b
+  // after unit b, the longest chains with the shortest, so each CU runs one
+  // workgroup for two units instead of two workgroups in turn.
+  const int bid = (int)blockIdx.x;
+  const int npass = NG == 4 && paired && units - 1 - bid > bid ? 2 : 1;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int unit = pass == 0 ? bid : units - 1 - bid;
+    const int per = a.nq * a.S;
+    const int qb = nqb - 1 - unit / per, h = (unit % per) % a.nq, s = (unit % per) / a.nq;
+    const int g = h / a.G;
+    int sl;
+    const int kl = seq_len(a, s, sl);
+    const int tok0 = qb * 64 + wq * 32;
+    const int tok = tok0 + j;
+    const bool row_ok = tok < a.q_len;
+    uint16_t* out = a.A + ((int64_t)s * a.q_len + tok) * a.lda + (int64_t)h * D;
+    if (kl == 0) {  // uniform over the workgroup: a sequence out of range gives zeros
+      if (row_ok && gr == 0)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) store_bf16x4(out + 32 * db + 8 * q + 4 * h2, 0.f, 0.f, 0.f, 0.f);
-    return;
-  }
-  const int base_pos = kl - a.q_len;  // position of token 0
-  const int last_tok = qb * 64 + 63 < a.q_len - 1 ? qb * 64 + 63 : a.q_len - 1;
-  const int nblk = (base_pos + last_tok) / C::BK + 1;
-  const int nstep = (nblk + NG - 1) / NG;
-  const int wlast = tok0 + 31 < a.q_len - 1 ? tok0 + 31 : a.q_len - 1;
-  const int wblk = tok0 < a.q_len ? (base_pos + wlast) / C::BK + 1 : 0;  // blocks this wave's tokens see
-  const int wfirst_pos = base_pos + tok0;
-  const int pos_j = base_pos + tok;
+          for (int q = 0; q < 4; ++q) store_bf16x4(out + 32 * db + 8 * q + 4 * h2, 0.f, 0.f, 0.f, 0.f);
+    } else {
+      const int base_pos = kl - a.q_len;  // position of token 0
+      const int last_tok = qb * 64 + 63 < a.q_len - 1 ? qb * 64 + 63 : a.q_len - 1;
+      const int nblk = (base_pos + last_tok) / C::BK + 1;
+      const int nstep = (nblk + NG - 1) / NG;
+      const int wlast = tok0 + 31 < a.q_len - 1 ? tok0 + 31 : a.q_len - 1;
+      const int wblk = tok0 < a.q_len ? (base_pos + wlast) / C::BK + 1 : 0;  // blocks this wave's tokens see
+      const int wfirst_pos = base_pos + tok0;
+      const int pos_j = base_pos + tok;
 
-  const uint64_t kbase = head_base(a.Kc, a, sl, g, kl, D), vbase = head_base(a.Vc, a, sl, g, kl, D);
-  const unsigned nb = (unsigned)__builtin_amdgcn_readfirstlane(kl * D * 2);
-  // DMA offsets of this lane: slot 64 (2 u + wq) + lane of a buffer holds
-  // byte offk[u] (offv[u]) of its block; 0x80000000 marks a padding slot
-  // (out of range: zeros).
-  unsigned offk[C::NUK], offv[C::NUV];
+      const uint64_t kbase = head_base(a.Kc, a, sl, g, kl, D), vbase = head_base(a.Vc, a, sl, g, kl, D);
+      const unsigned nb = (unsigned)__builtin_amdgcn_readfirstlane(kl * D * 2);
+      // DMA offsets of this lane: slot 64 (2 u + wq) + lane of a buffer holds
+      // byte offk[u] (offv[u]) of its block; 0x80000000 marks a padding slot
+      // (out of range: zeros).
+      unsigned offk[C::NUK], offv[C::NUV];
 #pragma unroll
-  for (int u = 0; u < C::NUK; ++u) {
-    const int q = (2 * u + wq) * 64 + lane, row = q / C::KP, c = q - row * C::KP;
-    offk[u] = row < C::BK && c < CPR ? (unsigned)((row * D + 8 * c) * 2) : 0x80000000u;
-  }
-#pragma unroll
-  for (int u = 0; u < C::NUV; ++u) {
-    const int q = (2 * u + wq) * 64 + lane, row = q / C::VP, c = q - row * C::VP;
-    offv[u] = row < C::BK && c < CPR ? (unsigned)((row * D + 8 * c) * 2) : 0x80000000u;
-  }
-  // Block NG t + gr of this group's chain (t = its step) into a K or V
-  // buffer; steps t >= nstep, which the loop issues as well, get an empty
-  // range: all out of range, they write zeros without a memory access.
-#define AP_BO(T) ((T) < nstep ? (unsigned)((NG * (T) + gr) * C::BK * D * 2) : nb)
-#define AP_K(KB, T) prefill_dma(C::NUK, kbase, nb, AP_BO(T), KB[gr], offk, wq);
-#define AP_V(VB, T) prefill_dma(C::NUV, vbase, nb, AP_BO(T), VB[gr], offv, wq);
-
-  // Q fragments. Tokens past q_len read token 0's row: their columns of S^T
-  // are finite and independent of the others', and nothing stores them.
-  uint4 qf[KS];
-  {
-    const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + (row_ok ? tok : 0)) * a.ldqkv + (int64_t)h * D + 8 * h2;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) qf[k] = *reinterpret_cast<const uint4*>(qp + 16 * k);
-  }
-  // The explicit DMA wait counts below assume the Q loads went out first.
-  __builtin_amdgcn_sched_barrier(0);
-  f32x16_t o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
-  // Reference max m of the scaled scores (log2 domain; it trails the running
-  // max by at most kSlack) and sum, per token column. Groups 1..NG-1 start at
-  // blocks that early tokens do not see: while a token's m is still -inf the
-  // exponents subtract 0 instead, so a masked (-inf) score gives exp2 = 0 and
-  // no -inf - -inf arises.
-  float m = -INFINITY, l = 0.f;
-  const float c = a.qscale;
-  constexpr float kSlack = 8.f;
-
-  // Fragment bases: K row j, slot 2 k + h2; V (transposed reads) row
-  // 16 k' + 4 h2 + jj / 4 (+ 8), slot 4 db + 2 uu + (jj % 4) / 2, half jj % 2,
-  // where the lane is 32 h2 + 16 uu + jj.
-  const int jj = j & 15, uu = j >> 4;
-  const int kfb = (j * C::KP + h2) * 16;
-  const int vfb = ((4 * h2 + (jj >> 2)) * C::VP + 2 * uu + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
-
-  // The scores S^T of block blk (this wave's 32 tokens x its 32 positions)
-  // from the K buffer KB, all K fragments read before the chain of products.
-  auto scores = [&](const uint4* KB, f32x16_t& sa) __attribute__((always_inline)) {
-    const char* L = (const char*)KB;
-    uint4 kf[KS];
-#pragma unroll
-    for (int k = 0; k < KS; ++k) kf[k] = *reinterpret_cast<const uint4*>(L + kfb + 2 * k * 16);
-    sa = f32x16_t{};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) sa = mfma_32x32x16(kf[k], qf[k], sa);
-  };
-
-  // Step t: V of block t is in VB, K of block t + 1 in KB (so VB is the
-  // array of t's parity and KB the other); sa holds block t's scores.
-  f32x16_t sa;
-  auto step = [&](uint4 (&VB)[NG][C::VST], uint4 (&KB)[NG][C::KST], const int t) __attribute__((always_inline)) {
-    const int blk = NG * t + gr;
-    const bool live = blk < wblk, live1 = blk + NG < wblk;
-    uint4 ph[2], pl[2];
-    if (live) {
-      // Lane (h2, j), element 4 q + r: position 32 blk + 8 q + 4 h2 + r.
-      if (blk * C::BK + C::BK - 1 > wfirst_pos) {  // a diagonal block: mask what lies past the token
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (blk * C::BK + 8 * (e >> 2) + 4 * h2 + (e & 3) > pos_j) sa[e] = -INFINITY;
+      for (int u = 0; u < C::NUK; ++u) {
+        const int q = (2 * u + wq) * 64 + lane, row = q / C::KP, c = q - row * C::KP;
+        offk[u] = row < C::BK && c < CPR ? (unsigned)((row * D + 8 * c) * 2) : 0x80000000u;
       }
-      float bm = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; e += 4) bm = fmaxf(bm, fmaxf(fmaxf(sa[e], sa[e + 1]), fmaxf(sa[e + 2], sa[e + 3])));
-      bm = max32(bm);
-      // The subtracted reference mn moves only when the block's max passes
-      // it by more than kSlack (log2 units), so the probabilities stay below
-      // 2^kSlack and the output's rescale runs a few times per chain instead
-      // of at nearly every step. Softmax does not depend on the constant
-      // subtracted: only rounding changes.
-      const float mb = bm * c;
-      const float mn = mb > m + kSlack ? mb : m;
-      const float ms = mn == -INFINITY ? 0.f : mn;
-      float r4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], c, -ms));
-        sa[e] = pe;
-        r4[e & 3] += pe;
+      for (int u = 0; u < C::NUV; ++u) {
+        const int q = (2 * u + wq) * 64 + lane, row = q / C::VP, c = q - row * C::VP;
+        offv[u] = row < C::BK && c < CPR ? (unsigned)((row * D + 8 * c) * 2) : 0x80000000u;
       }
-      const float rs = sum32((r4[0] + r4[1]) + (r4[2] + r4[3]));
-      if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {  // some token's reference moved: rescale
-        const float alpha = __builtin_amdgcn_exp2f(m - ms);
-        l *= alpha;
+      // Block NG t + gr of this group's chain (t = its step) into a K or V
+      // buffer; steps t >= nstep, which the loop issues as well, get an empty
+      // range: all out of range, they write zeros without a memory access.
+    #define AP_BO(T) ((T) < nstep ? (unsigned)((NG * (T) + gr) * C::BK * D * 2) : nb)
+    #define AP_K(KB, T) prefill_dma(C::NUK, kbase, nb, AP_BO(T), KB[gr], offk, wq);
+    #define AP_V(VB, T) prefill_dma(C::NUV, vbase, nb, AP_BO(T), VB[gr], offv, wq);
+
+      // Q fragments. Tokens past q_len read token 0's row: their columns of S^T
+      // are finite and independent of the others', and nothing stores them.
+      uint4 qf[KS];
+      {
+        const uint16_t* qp = a.QKV + ((int64_t)s * a.q_len + (row_ok ? tok : 0)) * a.ldqkv + (int64_t)h * D + 8 * h2;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        for (int k = 0; k < KS; ++k) qf[k] = *reinterpret_cast<const uint4*>(qp + 16 * k);
       }
-      l += rs;
-      m = mn;
+      // The explicit DMA wait counts below assume the Q loads went out first.
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16_t o[DB];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int q0 = 2 * kk;
-        const float pe[8] = {sa[4 * q0],     sa[4 * q0 + 1], sa[4 * q0 + 2], sa[4 * q0 + 3],
-                             sa[4 * q0 + 4], sa[4 * q0 + 5], sa[4 * q0 + 6], sa[4 * q0 + 7]};
-        split8(pe, ph[kk], pl[kk]);
-      }
-    }
-    // V of block t and K of block t + 1 have landed; after them only V of
-    // t + 1 and K of t + 2 may be in flight.
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (C::NUV + C::NUK));
-    __builtin_amdgcn_s_barrier();  // end of the first half
-    if (live) {
-      const char* L = (const char*)VB[gr];
+      for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
+      // Reference max m of the scaled scores (log2 domain; it trails the running
+      // max by at most kSlack) and sum, per token column. Groups 1..NG-1 start at
+      // blocks that early tokens do not see: while a token's m is still -inf the
+      // exponents subtract 0 instead, so a masked (-inf) score gives exp2 = 0 and
+      // no -inf - -inf arises.
+      float m = -INFINITY, l = 0.f;
+      const float c = a.qscale;
+      constexpr float kSlack = 8.f;
+
+      // Fragment bases: K row j, slot 2 k + h2; V (transposed reads) row
+      // 16 k' + 4 h2 + jj / 4 (+ 8), slot 4 db + 2 uu + (jj % 4) / 2, half jj % 2,
+      // where the lane is 32 h2 + 16 uu + jj.
+      const int jj = j & 15, uu = j >> 4;
+      const int kfb = (j * C::KP + h2) * 16;
+      const int vfb = ((4 * h2 + (jj >> 2)) * C::VP + 2 * uu + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
+
+      // The scores S^T of block blk (this wave's 32 tokens x its 32 positions)
+      // from the K buffer KB, all K fragments read before the chain of products.
+      auto scores = [&](const uint4* KB, f32x16_t& sa) __attribute__((always_inline)) {
+        const char* L = (const char*)KB;
+        uint4 kf[KS];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        uint4 vf[DB];
+        for (int k = 0; k < KS; ++k) kf[k] = *reinterpret_cast<const uint4*>(L + kfb + 2 * k * 16);
+        sa = f32x16_t{};
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const char* v0 = L + vfb + (16 * kk * C::VP + 4 * db) * 16;
-          vf[db] = tr_pair(v0, v0 + 8 * C::VP * 16);
+        for (int k = 0; k < KS; ++k) sa = mfma_32x32x16(kf[k], qf[k], sa);
+      };
+
+      // Step t: V of block t is in VB, K of block t + 1 in KB (so VB is the
+      // array of t's parity and KB the other); sa holds block t's scores.
+      f32x16_t sa;
+      auto step = [&](uint4 (&VB)[NG][C::VST], uint4 (&KB)[NG][C::KST], const int t) __attribute__((always_inline)) {
+        const int blk = NG * t + gr;
+        const bool live = blk < wblk, live1 = blk + NG < wblk;
+        uint4 ph[2], pl[2];
+        if (live) {
+          // Lane (h2, j), element 4 q + r: position 32 blk + 8 q + 4 h2 + r.
+          if (blk * C::BK + C::BK - 1 > wfirst_pos) {  // a diagonal block: mask what lies past the token
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (blk * C::BK + 8 * (e >> 2) + 4 * h2 + (e & 3) > pos_j) sa[e] = -INFINITY;
+          }
+          float bm = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 16; e += 4) bm = fmaxf(bm, fmaxf(fmaxf(sa[e], sa[e + 1]), fmaxf(sa[e + 2], sa[e + 3])));
+          bm = max32(bm);
+          // The subtracted reference mn moves only when the block's max passes
+          // it by more than kSlack (log2 units), so the probabilities stay below
+          // 2^kSlack and the output's rescale runs a few times per chain instead
+          // of at nearly every step. Softmax does not depend on the constant
+          // subtracted: only rounding changes.
+          const float mb = bm * c;
+          const float mn = mb > m + kSlack ? mb : m;
+          const float ms = mn == -INFINITY ? 0.f : mn;
+          float r4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], c, -ms));
+            sa[e] = pe;
+            r4[e & 3] += pe;
+          }
+          const float rs = sum32((r4[0] + r4[1]) + (r4[2] + r4[3]));
+          if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {  // some token's reference moved: rescale
+            const float alpha = __builtin_amdgcn_exp2f(m - ms);
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db] *= alpha;
+          }
+          l += rs;
+          m = mn;
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const int q0 = 2 * kk;
+            const float pe[8] = {sa[4 * q0],     sa[4 * q0 + 1], sa[4 * q0 + 2], sa[4 * q0 + 3],
+                                 sa[4 * q0 + 4], sa[4 * q0 + 5], sa[4 * q0 + 6], sa[4 * q0 + 7]};
+            split8(pe, ph[kk], pl[kk]);
+          }
         }
+        // V of block t and K of block t + 1 have landed; after them only V of
+        // t + 1 and K of t + 2 may be in flight.
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (C::NUV + C::NUK));
+        __builtin_amdgcn_s_barrier();  // end of the first half
+        if (live) {
+          const char* L = (const char*)VB[gr];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = mfma_32x32x16(vf[db], ph[kk], o[db]);
+          for (int kk = 0; kk < 2; ++kk) {
+            uint4 vf[DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = mfma_32x32x16(vf[db], pl[kk], o[db]);
-      }
-    }
-    if (live1) scores(KB[gr], sa);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();  // end of the second half: V of t and K of t + 1 are read
-    AP_V(VB, t + 2)
-    AP_K(KB, t + 3)
-  };
+            for (int db = 0; db < DB; ++db) {
+              const char* v0 = L + vfb + (16 * kk * C::VP + 4 * db) * 16;
+              vf[db] = tr_pair(v0, v0 + 8 * C::VP * 16);
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db] = mfma_32x32x16(vf[db], ph[kk], o[db]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db] = mfma_32x32x16(vf[db], pl[kk], o[db]);
+          }
+        }
+        if (live1) scores(KB[gr], sa);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();  // end of the second half: V of t and K of t + 1 are read
+        AP_V(VB, t + 2)
+        AP_K(KB, t + 3)
+      };
 
-  // Prologue: K and V of steps 0 and 1 in flight, then step 0's scores; K of
-  // step 2 follows once step 0's K buffer is free. Every DMA issue is
-  // unconditional (the last ones have empty ranges): with conditional
-  // issues the compiler could not tell which buffer's DMA is the newest and
-  // would wait for all of them before a fragment read.
-  AP_K(Ks0, 0)
-  AP_V(Vs0, 0)
-  AP_K(Ks1, 1)
-  AP_V(Vs1, 1)
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * C::NUV + C::NUK));  // K of step 0 has landed
-  __builtin_amdgcn_s_barrier();
-  const bool late = NG == 4 && gr >= 2;  // wave-uniform
-  if (late) __builtin_amdgcn_s_barrier();  // the half that groups 0 and 1 spend on step 0's scores
-  if (gr < wblk) scores(Ks0[gr], sa);
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_barrier();
-  AP_K(Ks0, 2)
-  // Whole pairs of steps (an odd count gets one step that multiplies
-  // nothing), so that the loop's back edge always follows an odd step and the
-  // compiler knows which buffers' DMAs are the newer ones at its top.
-  const int npair = (nstep + 1) / 2;
-  for (int tp = 0; tp < npair; ++tp) {
-    step(Vs0, Ks1, 2 * tp);
-    step(Vs1, Ks0, 2 * tp + 1);
-  }
-  if (!late) __builtin_amdgcn_s_barrier();  // the half that groups 2 and 3 spend on their last step
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __builtin_amdgcn_s_barrier();  // no DMA is still landing when the buffers become the merge's regions
-#undef AP_BO
-#undef AP_K
-#undef AP_V
-
-  // Every wave's partial into LDS, region w = the wave: [D columns][33]
-  // (token j at j; a pitch of 33 keeps a column's 32 tokens and the other
-  // half-wave's columns on distinct banks), then m and l. Lane (h2, j),
-  // element 4 q + r of block db: column 32 db + 8 q + 4 h2 + r of token j.
-  // Then wave (gr, wq) merges columns [gr D/NG, (gr + 1) D/NG) of its 32
-  // tokens over the NG groups in group order, each half-wavefront half of
-  // them, and stores them. Region r is region r % RK of Ks0, Ks1 (r < 2 RK),
-  // else of Vs0, Vs1.
-  constexpr int TP = 33;
-  constexpr int WR = D * TP + 64;
-  constexpr int RK = NG * C::KST * 16 / (WR * 4);  // regions per K buffer
-  constexpr int RV = NG * C::VST * 16 / (WR * 4);  // regions per V buffer
-  static_assert(RK >= 1 && RV >= 1 && 2 * RK + 2 * RV >= 2 * NG, "every wave's partial fits in LDS");
-  auto region = [&](const int r) -> float* {
-    if (r < RK) return reinterpret_cast<float*>(&Ks0[0][0]) + r * WR;
-    if (r < 2 * RK) return reinterpret_cast<float*>(&Ks1[0][0]) + (r - RK) * WR;
-    if (r < 2 * RK + RV) return reinterpret_cast<float*>(&Vs0[0][0]) + (r - 2 * RK) * WR;
-    return reinterpret_cast<float*>(&Vs1[0][0]) + (r - 2 * RK - RV) * WR;
-  };
-  {
-    float* rw = region(wave);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) rw[(32 * db + 8 * (e >> 2) + 4 * h2 + (e & 3)) * TP + j] = o[db][e];
-    if (h2 == 0) {
-      rw[D * TP + j] = m;
-      rw[D * TP + 32 + j] = l;
-    }
-  }
-  __syncthreads();
-  if (row_ok) {
-    constexpr int CW = D / NG / 2;  // columns per lane
-    static_assert(CW % 4 == 0, "whole 4-column stores");
-    const float* rg[NG];
-    float mg[NG], M = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < NG; ++q) {
-      rg[q] = region(2 * q + wq);
-      mg[q] = rg[q][D * TP + j];
-      M = fmaxf(M, mg[q]);
-    }
-    float f[NG], L = 0.f;
-#pragma unroll
-    for (int q = 0; q < NG; ++q) {
-      f[q] = __builtin_amdgcn_exp2f(mg[q] - M);
-      L += f[q] * rg[q][D * TP + 32 + j];
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const int c0 = gr * (D / NG) + h2 * CW;
-#pragma unroll
-    for (int i = 0; i < CW; i += 4) {
-      float v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = c0 + i + r;
-        float acc = f[0] * rg[0][col * TP + j];
-#pragma unroll
-        for (int q = 1; q < NG; ++q) acc += f[q] * rg[q][col * TP + j];
-        v[r] = acc * inv;
+      // Prologue: K and V of steps 0 and 1 in flight, then step 0's scores; K of
+      // step 2 follows once step 0's K buffer is free. Every DMA issue is
+      // unconditional (the last ones have empty ranges): with conditional
+      // issues the compiler could not tell which buffer's DMA is the newest and
+      // would wait for all of them before a fragment read.
+      AP_K(Ks0, 0)
+      AP_V(Vs0, 0)
+      AP_K(Ks1, 1)
+      AP_V(Vs1, 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * C::NUV + C::NUK));  // K of step 0 has landed
+      __builtin_amdgcn_s_barrier();
+      const bool late = NG == 4 && gr >= 2;  // wave-uniform
+      if (late) __builtin_amdgcn_s_barrier();  // the half that groups 0 and 1 spend on step 0's scores
+      if (gr < wblk) scores(Ks0[gr], sa);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+      AP_K(Ks0, 2)
+      // Whole pairs of steps (an odd count gets one step that multiplies
+      // nothing), so that the loop's back edge always follows an odd step and the
+      // compiler knows which buffers' DMAs are the newer ones at its top.
+      const int npair = (nstep + 1) / 2;
+      for (int tp = 0; tp < npair; ++tp) {
+        step(Vs0, Ks1, 2 * tp);
+        step(Vs1, Ks0, 2 * tp + 1);
       }
-      store_bf16x4(out + c0 + i, v[0], v[1], v[2], v[3]);
-    }
-  }
+      if (!late) __builtin_amdgcn_s_barrier();  // the half that groups 2 and 3 spend on their last step
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __builtin_amdgcn_s_barrier();  // no DMA is still landing when the buffers become the merge's regions
+    #undef AP_BO
+    #undef AP_K
+    #undef AP_V
+
+      // Every wave's partial into LDS, region w = the wave: [D columns][33]
+      // (token j at j; a pitch of 33 keeps a column's 32 tokens and the other
+      // half-wave's columns on distinct banks), then m and l. Lane (h2, j),
+      // element 4 q + r of block db: column 32 db + 8 q + 4 h2 + r of token j.
+      // Then wave (gr, wq) merges columns [gr D/NG, (gr + 1) D/NG) of its 32
+      // tokens over the NG groups in group order, each half-wavefront half of
+      // them, and stores them. Region r is region r % RK of Ks0, Ks1 (r < 2 RK),
+      // else of Vs0, Vs1.
+      constexpr int TP = 33;
+      constexpr int WR = D * TP + 64;
+      constexpr int RK = NG * C::KST * 16 / (WR * 4);  // regions per K buffer
+      constexpr int RV = NG * C::VST * 16 / (WR * 4);  // regions per V buffer
+      static_assert(RK >= 1 && RV >= 1 && 2 * RK + 2 * RV >= 2 * NG, "every wave's partial fits in LDS");
+      auto region = [&](const int r) -> float* {
+        if (r < RK) return reinterpret_cast<float*>(&Ks0[0][0]) + r * WR;
+        if (r < 2 * RK) return reinterpret_cast<float*>(&Ks1[0][0]) + (r - RK) * WR;
+        if (r < 2 * RK + RV) return reinterpret_cast<float*>(&Vs0[0][0]) + (r - 2 * RK) * WR;
+        return reinterpret_cast<float*>(&Vs1[0][0]) + (r - 2 * RK - RV) * WR;
+      };
+      {
+        float* rw = region(wave);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) rw[(32 * db + 8 * (e >> 2) + 4 * h2 + (e & 3)) * TP + j] = o[db][e];
+        if (h2 == 0) {
+          rw[D * TP + j] = m;
+          rw[D * TP + 32 + j] = l;
+        }
+      }
+      __syncthreads();
+      if (row_ok) {
+        constexpr int CW = D / NG / 2;  // columns per lane
+        static_assert(CW % 4 == 0, "whole 4-column stores");
+        const float* rg[NG];
+        float mg[NG], M = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+          rg[q] = region(2 * q + wq);
+          mg[q] = rg[q][D * TP + j];
+          M = fmaxf(M, mg[q]);
+        }
+        float f[NG], L = 0.f;
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+          f[q] = __builtin_amdgcn_exp2f(mg[q] - M);
+          L += f[q] * rg[q][D * TP + 32 + j];
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const int c0 = gr * (D / NG) + h2 * CW;
+#pragma unroll
+        for (int i = 0; i < CW; i += 4) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int col = c0 + i + r;
+            float acc = f[0] * rg[0][col * TP + j];
+#pragma unroll
+            for (int q = 1; q < NG; ++q) acc += f[q] * rg[q][col * TP + j];
+            v[r] = acc * inv;
+          }
+          store_bf16x4(out + c0 + i, v[0], v[1], v[2], v[3]);
+        }
+      }
+    }  // kl > 0
+    __syncthreads();  // the next unit's DMA reuses the merge's LDS
+  }  // pass
 }
 
 template <int D>
@@ -840,11 +850,17 @@ hipError_t launch_attention_d(const AttnArgs& a, bool decode, hipStream_t s) {
     // the CUs' two slots at least twice, or once with short chains; otherwise
     // four groups (one workgroup per CU), which halves the longest chain.
     const int64_t units = (int64_t)nqb * a.nq * a.S;
-    const dim3 grid((unsigned)units);
-    if (units >= 1024 || (units >= 512 && nqb <= 16))
-      hipLaunchKernelGGL((attn_prefill_kernel<D, 2>), grid, dim3(256), 0, s, a, nqb);
-    else
-      hipLaunchKernelGGL((attn_prefill_kernel<D, 4>), grid, dim3(512), 0, s, a, nqb);
+    if (units >= 1024 || (units >= 512 && nqb <= 16)) {
+      hipLaunchKernelGGL((attn_prefill_kernel<D, 2>), dim3((unsigned)units), dim3(256), 0, s, a, nqb, (int)units, 0);
+    } else {
+      // Four groups run one workgroup per CU. When the units fill close to
+      // two rounds of the 256 CUs, workgroups take them in pairs (longest
+      // with shortest): one round, with no second wave of workgroup starts.
+      // 70B rank 0 at 4096 tokens: 67.7-68.2 against 68.7-69.1 us.
+      const int paired = units > 448 && units <= 512;
+      const dim3 grid(paired ? (unsigned)((units + 1) / 2) : (unsigned)units);
+      hipLaunchKernelGGL((attn_prefill_kernel<D, 4>), grid, dim3(512), 0, s, a, nqb, (int)units, paired);
+    }
   }
   return hipGetLastError();
 }
