@@ -181,3 +181,50 @@ def test_llama70b_ffn_tp8_rank_fp8(M):
     Href = oracle.gateup_swiglu_fp8(X, Wgu_r, pg)
     assert_parity(host_f64(Hh), oracle.bf16_to_f64(Href), "H")
     assert_parity(host_f64(P), oracle.row_linear_fp8(Href, Wd_r, pd), "P")
+
+
+def _random_cases8(n=18, seed=2025):
+    """Seeded random 8-bit shards (column, gate/up and row kinds, t in {1, 2,
+    4, 8}, random rank), K and N up to 2048, token counts on either side of
+    the decode / prefill boundary."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        kind = ("col", "gateup_col", "row")[c % 3]
+        t = int(rng.choice([1, 2, 4, 8]))
+        r = int(rng.integers(0, t))
+        wide = t * 8 * int(rng.integers(1, 1 + 2048 // (8 * t)))
+        other = 8 * int(rng.integers(1, 257))
+        if kind == "row":
+            K, N = wide, other
+        elif kind == "col":
+            K, N = other, wide
+        else:
+            K, N = other, 2 * (wide // 2 // (8 * t) * 8 * t or 8 * t)
+        M = int(rng.integers(1, 65)) if c % 2 else int(rng.integers(65, 600))
+        cases.append((kind, K, N, t, r, M))
+    return cases
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,M", _random_cases8())
+def test_random_shards8_against_oracle(kind, K, N, t, r, M):
+    """Random 8-bit shapes through the automatic path choice: every row at
+    decode sizes, the edges and one row per 256-token tile at prefill sizes."""
+    say("random shard8", kind, K, N, t, r, M)
+    rows = list(range(M)) if M <= 64 else sorted({0, 1, M // 2, M - 2, M - 1} | set(range(100, M, 256)))
+    X = si.normal_bf16(52, (M, K), 1.0)
+    W = si.normal_bf16(53, (K, N), 0.05)
+    d, p = plan8(kind, K, N, t, r)
+    Wp = tp.tp_shard_pack(d, dev(W))
+    if kind == "row":
+        Zr = X[:, p["rows"]]
+        got = host_f64(tp.tp_row_linear(d, dev(Zr), Wp))[rows]
+        ref = oracle.row_linear_fp8(np.ascontiguousarray(Zr[rows]), W, p)
+    else:
+        got = host_f64(tp.tp_col_linear(d, dev(X), Wp))[rows]
+        Xs = np.ascontiguousarray(X[rows])
+        if kind == "gateup_col":
+            ref = oracle.bf16_to_f64(oracle.gateup_swiglu_fp8(Xs, W, p))
+        else:
+            ref = oracle.bf16_to_f64(oracle.round_bf16(oracle.col_linear_fp8(Xs, W, p)))
+    assert_parity(got, ref, f"fp8 {kind} K={K} N={N} t={t} r={r} M={M}")

@@ -122,6 +122,50 @@ def test_row_small(M, path):
         assert_parity(got, ref, f"row M={M} K={K} N={N} t={t} r={r}")
 
 
+def _random_cases(n=36, seed=2024):
+    """Seeded random shards: column, gate/up and row kinds at t in {1, 2, 4,
+    8} on a random rank, K and N up to 2048 (multiples of 8 per shard), and
+    token counts on either side of the decode / prefill boundary."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        kind = ("col", "gateup_col", "row")[c % 3]
+        t = int(rng.choice([1, 2, 4, 8]))
+        r = int(rng.integers(0, t))
+        wide = t * 8 * int(rng.integers(1, 1 + 2048 // (8 * t)))
+        other = 8 * int(rng.integers(1, 257))
+        if kind == "row":
+            K, N = wide, other
+        elif kind == "col":
+            K, N = other, wide
+        else:
+            K, N = other, 2 * (wide // 2 // (8 * t) * 8 * t or 8 * t)
+        M = int(rng.integers(1, 65)) if c % 2 else int(rng.integers(65, 700))
+        cases.append((kind, K, N, t, r, M))
+    return cases
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,M", _random_cases())
+def test_random_shards_against_oracle(kind, K, N, t, r, M):
+    """Random shapes through the automatic path choice: every row at decode
+    sizes, the edges and one row per 256-token tile at prefill sizes."""
+    say("random shard", kind, K, N, t, r, M)
+    rows = list(range(M)) if M <= 64 else sorted({0, 1, M // 2, M - 2, M - 1} | set(range(100, M, 256)))
+    X = si.normal_bf16(50, (M, K), 1.0)
+    W = si.normal_bf16(51, (K, N), 0.05)
+    d, p = plan_both(kind, K, N, t, r)
+    Wp = tp.tp_shard_pack(d, dev(W))
+    if kind == "row":
+        Zr = X[:, p["rows"]]
+        got = host_f64(tp.tp_row_linear(d, dev(Zr), Wp))[rows]
+        ref = oracle.row_linear(np.ascontiguousarray(Zr[rows]), W, p)
+    else:
+        got = host_f64(tp.tp_col_linear(d, dev(X), Wp))[rows]
+        fn = oracle.gateup_swiglu if kind == "gateup_col" else oracle.col_linear_bf16
+        ref = oracle.bf16_to_f64(fn(np.ascontiguousarray(X[rows]), W, p))
+    assert_parity(got, ref, f"{kind} K={K} N={N} t={t} r={r} M={M}")
+
+
 # Grids of at least 256 workgroups of 256 x 256 run the big-tile prefill
 # kernel: ragged token count, ragged last k-step, odd and partial column tiles.
 # Grids of 256 + 16 tiles also run the half-height tail launch (including a
