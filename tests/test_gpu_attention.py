@@ -266,6 +266,40 @@ def test_decode_longer_chunks_for_large_batches(heads, t, r, S, L, chunk):
 # d = 128), in the benchmark's launch shapes; sampled rows.
 # ---------------------------------------------------------------------------
 
+def _random_attention_cases(n=16, seed=77):
+    """Seeded random calls: a head layout, 1 to 3 sequences in shuffled cache
+    slots, each with its own cache length, and new-token counts on both sides
+    of the decode / prefill choice."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        heads, t, r = LAYOUTS[int(rng.integers(0, len(LAYOUTS)))]
+        q_len = int(rng.choice([1, 2, 3, 5, 16, 17, 64, 100, 250]))
+        S = int(rng.integers(1, 4))
+        L_max = q_len + int(rng.integers(0, 1500))
+        kv_len = [int(rng.integers(q_len, L_max + 1)) for _ in range(S)]
+        n_slots = S + int(rng.integers(0, 3))
+        slot = [int(x) for x in rng.permutation(n_slots)[:S]]
+        cases.append((heads, t, r, q_len, kv_len, slot, n_slots, L_max))
+    return cases
+
+
+@pytest.mark.parametrize("heads,t,r,q_len,kv_len,slot,n_slots,L_max", _random_attention_cases())
+def test_random_calls_match_oracle(heads, t, r, q_len, kv_len, slot, n_slots, L_max):
+    """Append then attend, against the oracle: the caches bit-exact, the
+    output on every row (or 48 seeded rows of larger calls)."""
+    say("random attention", heads, t, r, q_len, kv_len, slot, n_slots, L_max)
+    c = Case(heads, t, r, q_len, kv_len, slot, n_slots, L_max, 900 + q_len + L_max % 97)
+    c.append()
+    A = host_bits(c.run())
+    np.testing.assert_array_equal(host_bits(c.Kd), c.Kh)
+    np.testing.assert_array_equal(host_bits(c.Vd), c.Vh)
+    M = len(kv_len) * q_len
+    rows = list(range(M)) if M <= 64 else sorted(int(x) for x in np.random.default_rng(M).choice(M, 48, replace=False))
+    assert_parity(oracle.bf16_to_f64(A[rows]), oracle.bf16_to_f64(c.ref(rows)),
+                  f"heads={heads} t={t} r={r} q_len={q_len} kv={kv_len}")
+
+
 def test_llama70b_tp8_decode_batch():
     """32 sequences, one new token each, 4096 cached positions."""
     say("70b decode 32 x 4096")
