@@ -105,6 +105,44 @@ def test_weight_grad_matches_oracle(kind, K, N, t, r, heads, M):
     assert_parity(got, oracle.grad_weight(A, dC, p), f"dW {kind} M={M}")
 
 
+def _random_backward_cases(n=18, seed=99):
+    """Seeded random forward shards (column, gate/up and row kinds, t in {1,
+    2, 4, 8}, random rank, K and N up to 2048) with token counts from 1 to
+    about 1500."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        kind = ("col", "gateup_col", "row")[c % 3]
+        t = int(rng.choice([1, 2, 4, 8]))
+        r = int(rng.integers(0, t))
+        wide = t * 8 * int(rng.integers(1, 1 + 2048 // (8 * t)))
+        other = 8 * int(rng.integers(1, 257))
+        if kind == "row":
+            K, N = wide, other
+        elif kind == "col":
+            K, N = other, wide
+        else:
+            K, N = other, 2 * (wide // 2 // (8 * t) * 8 * t or 8 * t)
+        M = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(65, 1500))]))
+        cases.append((kind, K, N, t, r, M))
+    return cases
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,M", _random_backward_cases())
+def test_random_shard_gradients_match_oracle(kind, K, N, t, r, M):
+    """Input gradient (the transposed shard through tp_row_linear) and weight
+    gradient of random shards, against the oracle."""
+    say("random backward", kind, K, N, t, r, M)
+    f, d, p, W, packed = _pack_dgrad(kind, K, N, t, r, None, 330 + M)
+    dC = si.normal_bf16(331 + M, (M, f.shard_n), 1.0)
+    A = si.normal_bf16(332 + M, (M, f.shard_k), 1.0)
+    dA = tp.tp_row_linear(d, dev(dC), packed)
+    assert_parity(host_f64(dA), oracle.grad_input(dC, W, p), f"dA {kind} K={K} N={N} t={t} r={r} M={M}")
+    dW = torch.full((f.shard_k, f.shard_n), float("nan"), dtype=torch.float32, device="cuda")
+    tp.tp_weight_grad(f, dev(A), dev(dC), dW=dW)
+    assert_parity(host_f64(dW), oracle.grad_weight(A, dC, p), f"dW {kind} K={K} N={N} t={t} r={r} M={M}")
+
+
 @pytest.mark.parametrize("M", [7, 100, 4097])
 def test_weight_grad_exact_integers_bit_exact(M):
     say("wgrad exact", M)
