@@ -166,6 +166,49 @@ def test_random_shards_against_oracle(kind, K, N, t, r, M):
     assert_parity(got, ref, f"{kind} K={K} N={N} t={t} r={r} M={M}")
 
 
+def _random_big_cases(n=10, seed=4096):
+    """Seeded random prefill shapes large enough for the big-tile GEMM (whole
+    rounds, a split last round, split K, half tiles), all three kinds."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        kind = ("col", "gateup_col", "row")[c % 3]
+        t = int(rng.choice([1, 2, 4]))
+        r = int(rng.integers(0, t))
+        M = int(rng.integers(2049, 8193))
+        wide = t * 8 * int(rng.integers(16, 1 + 12288 // (8 * t)))
+        other = 8 * int(rng.integers(4, 385))
+        if kind == "row":
+            K, N = wide // 4 // (8 * t) * 8 * t or 8 * t, other * 4
+        elif kind == "col":
+            K, N = other, wide
+        else:
+            K, N = other, 2 * (wide // 2 // (8 * t) * 8 * t or 8 * t)
+        cases.append((kind, K, N, t, r, M))
+    return cases
+
+
+@pytest.mark.parametrize("kind,K,N,t,r,M", _random_big_cases())
+def test_random_prefill_shapes_against_oracle(kind, K, N, t, r, M):
+    """Random big prefill shapes: the first and last rows and two rows of
+    every 256-token tile against the oracle."""
+    say("random prefill", kind, K, N, t, r, M)
+    rows = sorted({0, M - 1} | set(range(37, M, 256)) | set(range(200, M, 256)))
+    X = si.normal_bf16(54, (M, K), 1.0)
+    W = si.normal_bf16(55, (K, N), 0.05)
+    d, p = plan_both(kind, K, N, t, r)
+    Wp = tp.tp_shard_pack(d, dev(W))
+    if kind == "row":
+        Zr = X[:, p["rows"]]
+        got = host_f64(tp.tp_row_linear(d, dev(Zr), Wp))[rows]
+        ref = oracle.row_linear(np.ascontiguousarray(Zr[rows]), W, p)
+    else:
+        got = host_f64(tp.tp_col_linear(d, dev(X), Wp))[rows]
+        fn = oracle.gateup_swiglu if kind == "gateup_col" else oracle.col_linear_bf16
+        ref = oracle.bf16_to_f64(fn(np.ascontiguousarray(X[rows]), W, p))
+    assert_parity(got, ref, f"{kind} K={K} N={N} t={t} r={r} M={M}")
+
+
 # Grids of at least 256 workgroups of 256 x 256 run the big-tile prefill
 # kernel: ragged token count, ragged last k-step, odd and partial column tiles.
 # Grids of 256 + 16 tiles also run the half-height tail launch (including a
