@@ -2,9 +2,12 @@
 // matrix cores ("Tensor vs Pipeline Parallelism", "A worked communication
 // estimate": prompt compute is about 2 x parameters x tokens operations).
 //
-// Two kernels. gemm_big (256 x 256 tiles, 8 wavefronts, 32x32x16 MFMA,
-// stages landed in LDS by DMA) runs whenever the grid fills the GPU; gemm_kernel (128 x 128
-// tiles, 16x16x32 MFMA, register-staged) covers grids too small for that. On
+// Three kernels. gemm_big (256 x 256 tiles, 8 wavefronts, 32x32x16 MFMA,
+// stages landed in LDS by DMA) runs whenever the grid fills the GPU;
+// gemm_mid (128 x 256 tiles, three LDS stage buffers) runs prefills of up to
+// 512 tokens, where the weights stream from HBM and need more DMA lead, and
+// grids of big tiles that neither fill a round nor split K; gemm_kernel
+// (128 x 128 tiles, 16x16x32 MFMA, register-staged) covers the rest. On
 // gfx950 the 32x32x16 bf16 MFMA sustains about 1.5x the rate of the 16x16x32
 // one when fed from LDS.
 //
@@ -379,6 +382,175 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
   }
 }
 
+// gemm_mid: prefills of at most a few hundred tokens, where every weight byte
+// comes from HBM once and the big tile's one stage of DMA lead (about 1.2 us)
+// is shorter than the HBM latency under a full streaming load. 128-token x
+// 256-column tiles (gemm_big's half-height form, 48 KiB stages), three LDS
+// stage buffers instead of two: a stage's DMA goes out two stages before its
+// fragments are read. Token tiles of 128 rows, grouped as gemm_big groups its
+// tiles, so the token tiles of one weight column block share an XCD's L2.
+// The stage, fragment and epilogue layouts are gemm_big's with TB = 1.
+template <int EPI, bool SPLIT>
+__global__ __launch_bounds__(BIG_THREADS) void gemm_mid(LinearArgs a, int ntn, int ntm, int64_t kper, float* part) {
+  constexpr int ROWS = 128;
+  constexpr int XI = 2;                              // token DMA instructions per wave and stage
+  constexpr int STAGE_U4 = BIG_WCH * 64 + ROWS * 8;  // 48 KiB per stage
+  __shared__ uint4 L0[STAGE_U4], L1[STAGE_U4], L2[STAGE_U4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1;  // column half, token quarter
+
+  int bid = (int)blockIdx.x;
+  {
+    const int per = (int)gridDim.x / 8;
+    if (bid < per * 8) bid = (bid % 8) * per + bid / 8;
+  }
+  constexpr int GM = 8;
+  const int first_m = bid / (GM * ntn) * GM;
+  const int gsize = ntm - first_m < GM ? ntm - first_m : GM;
+  const int tm = first_m + (bid % (GM * ntn)) % gsize;
+  const int tn = (bid % (GM * ntn)) / gsize;
+  const int64_t nt0 = (int64_t)tn * BIG_T;
+  const int64_t m0 = (int64_t)tm * ROWS;
+  const int64_t ksteps = a.ksteps;
+  int64_t kcnt = ksteps;
+  if constexpr (SPLIT) {
+    const int64_t k0 = (int64_t)blockIdx.y * kper;
+    kcnt = ksteps - k0 < kper ? ksteps - k0 : kper;
+    a.W += k0 * 2 * kTileU4;
+    a.X += k0 * kTileK;
+    a.K = a.K - k0 * kTileK < kcnt * kTileK ? a.K - k0 * kTileK : kcnt * kTileK;
+    a.out = part + (int64_t)blockIdx.y * a.M * (a.ntiles * kTileN);
+    a.ldo = a.ntiles * kTileN;
+    a.out_n = a.ldo;
+  }
+  const int64_t nst = (kcnt + 1) / 2;
+
+  const int64_t wt = a.ntiles - nt0 < BIG_T ? a.ntiles - nt0 : BIG_T;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.W + nt0 * ksteps * kTileU4), (short)0, (int)(wt * ksteps * 1024), 0x00020000);
+  const int64_t rows = a.M - m0 < ROWS ? (a.M > m0 ? a.M - m0 : 0) : ROWS;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.X + m0 * a.ldx), (short)0, (int)(rows * a.ldx * 2), 0x00020000);
+
+  unsigned woff[4], xoff[XI], kx[XI];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = wave * 4 + j;
+    woff[j] = (unsigned)(tile_index(c >> 1, c & 1, ksteps) * 1024 + lane * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < XI; ++j) {
+    const int r = (wave * XI + j) * 8 + (lane >> 3);
+    const int o = (lane & 7) ^ ((r >> 1) & 7);
+    xoff[j] = (unsigned)(((int64_t)r * a.ldx + 8 * o) * 2);
+    kx[j] = a.K > 8 * o ? (unsigned)(a.K - 8 * o) : 0u;
+  }
+#define TP_ISSUE(LB, S)                                                                          \
+  {                                                                                              \
+    const unsigned s_ = (unsigned)(S);                                                           \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
+        rw, (lds_void_t*)&LB[(wave * 4 + j) * 64], 16,                                           \
+        2 * s_ + (j & 1) < (unsigned)kcnt ? woff[j] + s_ * 4096u : 0x80000000u, 0, 0, 0);        \
+    _Pragma("unroll") for (int j = 0; j < XI; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(     \
+        rx, (lds_void_t*)&LB[BIG_WCH * 64 + (wave * XI + j) * 64], 16,                           \
+        64u * s_ < kx[j] ? xoff[j] + s_ * 128u : 0x80000000u, 0, 0, 0);                          \
+  }
+  const int fh = lane >> 5, fj = lane & 31;
+  const int fa = (fj >> 4) * 128 + fh * 16 + (fj & 15);
+  const int swz = fh ^ ((fj >> 1) & 7);
+  const int fb = BIG_WCH * 64 + (wm * 32 + fj) * 8;
+  uint4 FA[4][4], FB[4];
+#define TP_READ(LB, KH)                                                                          \
+  _Pragma("unroll") for (int x = 0; x < 4; ++x)                                                  \
+      FA[KH][x] = LB[(wn * 4 + x) * 256 + ((KH) >> 1) * 64 + ((KH) & 1) * 32 + fa];              \
+  FB[KH] = LB[fb + ((2 * (KH)) ^ swz)];
+#define TP_MMA(KH) _Pragma("unroll") for (int x = 0; x < 4; ++x) acc[x] = mfma_32x32x16(FA[KH][x], FB[KH], acc[x]);
+#define TP_SB __builtin_amdgcn_sched_barrier(0);
+#define TP_INTERLEAVE                                             \
+  _Pragma("unroll") for (int q = 0; q < 4 + XI; ++q) {            \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* MFMA */ \
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* VMEM */ \
+  }
+#define TP_STAGE(LB)                                                                             \
+  TP_MMA(0) TP_INTERLEAVE TP_SB TP_READ(LB, 0) TP_SB TP_MMA(1) TP_SB TP_READ(LB, 1) TP_SB        \
+  TP_MMA(2) TP_SB TP_READ(LB, 2) TP_SB TP_MMA(3) TP_SB TP_READ(LB, 3)
+  // The next stage has landed (only the one after it may still be in flight),
+  // and every wave has finished reading the buffer that the new DMA refills.
+  constexpr int kWaitNext = 0x0F70 | (4 + XI);
+#define TP_SYNC()                                    \
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);            \
+  __builtin_amdgcn_s_waitcnt(kWaitNext);             \
+  __builtin_amdgcn_s_barrier();
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) acc[x] = f32x16_t{};
+
+  TP_ISSUE(L0, 0)
+  TP_ISSUE(L1, 1)
+  TP_ISSUE(L2, 2)
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (4 + XI)));  // stage 0 has landed
+  __builtin_amdgcn_s_barrier();
+  TP_READ(L0, 0) TP_READ(L0, 1) TP_READ(L0, 2) TP_READ(L0, 3)
+  // Distinct markers keep the prologue's reads and the loop's last reads
+  // from being merged into one block at the loop's head, where the wait
+  // insertion could no longer tell which buffer each pending DMA fills.
+  asm volatile(";; prologue reads");
+  // Whole groups of three stages; the stages past K are all-zero padding.
+  for (int64_t s = 0; s < nst; s += 3) {
+    TP_SYNC()
+    TP_ISSUE(L0, s + 3)
+    TP_STAGE(L1)
+    TP_SYNC()
+    TP_ISSUE(L1, s + 4)
+    TP_STAGE(L2)
+    TP_SYNC()
+    TP_ISSUE(L2, s + 5)
+    TP_STAGE(L0)
+    asm volatile(";; stage group end");
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#undef TP_ISSUE
+#undef TP_READ
+#undef TP_MMA
+#undef TP_SB
+#undef TP_INTERLEAVE
+#undef TP_STAGE
+#undef TP_SYNC
+
+  const int64_t m = m0 + wm * 32 + fj;
+  if (m >= a.M) return;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int64_t ntb = nt0 + wn * 8 + 2 * x;
+    const f32x16_t& v = acc[x];
+    if constexpr (EPI == kEpiSwiglu) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int64_t n = (ntb >> 1) * kTileN + 8 * q + 4 * fh;
+        if (ntb >= a.ntiles || n >= a.out_n) continue;
+        store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + n, swiglu(v[4 * q], v[4 * q + 8]),
+                     swiglu(v[4 * q + 1], v[4 * q + 9]), swiglu(v[4 * q + 2], v[4 * q + 10]),
+                     swiglu(v[4 * q + 3], v[4 * q + 11]));
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = ntb * kTileN + 8 * q + 4 * fh;
+        if (n >= a.out_n) continue;
+        if constexpr (EPI == kEpiBf16) {
+          store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + n, v[4 * q], v[4 * q + 1], v[4 * q + 2],
+                       v[4 * q + 3]);
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + m * a.ldo + n) =
+              make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
+      }
+    }
+  }
+}
+
 // How a prefill linear is launched. The big tile needs buffer offsets below
 // 2^31. When its tiles alone cannot fill the 256 CUs (one workgroup per CU),
 // K is split G ways, G = the whole number of tile sets that fit in one round
@@ -451,10 +623,49 @@ TailPlan plan_tail(int64_t M, int64_t ksteps, int64_t ntiles) {
   return t;
 }
 
+// When gemm_mid runs instead of gemm_big: prefills of at most 512 tokens
+// (every weight byte comes from HBM, and the big tile's single stage of DMA
+// lead stalls on it), and grids of 129-255 big tiles, which neither fill a
+// round nor split K (those would otherwise fall back to gemm_kernel). K is
+// split G ways (whole stages) when the 128-token tiles alone cannot fill the
+// GPU.
+constexpr int64_t kMidMaxM = 512;
+struct MidPlan {
+  bool use;
+  int G;
+  int64_t kper;
+};
+
+MidPlan plan_mid(int64_t M, int64_t ldx, int64_t ksteps, int64_t ntiles) {
+  MidPlan p{false, 1, ksteps};
+  if ((int64_t)128 * ldx * 2 >= (1LL << 31) || (int64_t)BIG_T * ksteps * 1024 >= (1LL << 31)) return p;
+  const int64_t ntn = (ntiles + BIG_T - 1) / BIG_T;
+  const int64_t big_tiles = ntn * ((M + BIG_MT * 16 - 1) / (BIG_MT * 16));
+  const bool small = M <= kMidMaxM;
+  const bool unfilled = big_tiles > 128 && big_tiles < 256 && ksteps >= 32;
+  if (!small && !unfilled) return p;
+  const int64_t tiles = ntn * ((M + 127) / 128);
+  int64_t G = 1;
+  if (tiles < 256) {
+    G = 256 / tiles;
+    if (G > ksteps / 16) G = ksteps / 16;
+    if (G < 1) G = 1;
+  }
+  if (tiles * G < 64) return p;  // too few workgroups either way: the other plans
+  p.use = true;
+  if (G >= 2) {
+    p.kper = ((ksteps + G - 1) / G + 1) / 2 * 2;
+    p.G = (int)((ksteps + p.kper - 1) / p.kper);
+  }
+  return p;
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t M, int64_t ldx, int64_t ksteps, int64_t ntiles) {
   if (M <= 0) return 0;
+  const MidPlan mp = plan_mid(M, ldx, ksteps, ntiles);
+  if (mp.use) return mp.G > 1 ? (size_t)mp.G * M * ntiles * kTileN * sizeof(float) : 0;
   const GemmPlan p = plan_gemm(M, ldx, ksteps, ntiles);
   if (!p.big) return 0;
   if (p.G > 1) return (size_t)p.G * M * ntiles * kTileN * sizeof(float);
@@ -465,6 +676,24 @@ size_t gemm_workspace_bytes(int64_t M, int64_t ldx, int64_t ksteps, int64_t ntil
 hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t s) {
   if (a.M <= 0 || a.ntiles == 0) return hipSuccess;
   const int64_t ntn = (a.ntiles + BIG_T - 1) / BIG_T, ntm = (a.M + BIG_MT * 16 - 1) / (BIG_MT * 16);
+  const MidPlan mp = plan_mid(a.M, a.ldx, a.ksteps, a.ntiles);
+  if (mp.use) {
+    const int64_t ntm128 = (a.M + 127) / 128;
+    const dim3 grid((unsigned)(ntn * ntm128), (unsigned)mp.G);
+    if (mp.G > 1) {
+      if (ws == nullptr) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_mid<kEpiF32, true>), grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm128, mp.kper, ws);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_split_fixup(a, epi, ws, mp.G, s);
+    }
+    switch (epi) {
+      case kEpiSwiglu: hipLaunchKernelGGL((gemm_mid<kEpiSwiglu, false>), grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm128, (int64_t)0, nullptr); break;
+      case kEpiBf16: hipLaunchKernelGGL((gemm_mid<kEpiBf16, false>), grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm128, (int64_t)0, nullptr); break;
+      case kEpiF32: hipLaunchKernelGGL((gemm_mid<kEpiF32, false>), grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm128, (int64_t)0, nullptr); break;
+    }
+    return hipGetLastError();
+  }
   const GemmPlan p = plan_gemm(a.M, a.ldx, a.ksteps, a.ntiles);
   if (p.big && p.G > 1) {
     if (ws == nullptr) return hipErrorInvalidValue;
