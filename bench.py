@@ -809,6 +809,47 @@ def config_405b_ffn_backward(timer):
                 peak=MFMA_BF16_PEAK_TFS, per_op=per)
 
 
+def config_8b_ffn_batches(timer):
+    """The Llama-3.1-8B feed-forward share at TP = 1 between decode and full
+    prefill: batches of 96 to 1024 tokens, gate/up + SwiGLU and down timed
+    apart on 4 rotating weight copies (1.4 GB), in GB/s of the algorithmic
+    bytes and TFLOP/s. Up to 512 tokens the products run the 128-token-tile
+    GEMM, beyond it the 256-token one."""
+    import torch
+    import tensor_transformer_linear_megatron_amd as tp
+    from seeded_inputs import workloads as wl
+    lib, VP, ref, stream = _abi()
+    c = wl.LLAMA8B
+    H, I = c["hidden"], c["inter"]
+    gu = tp.tp_shard_plan("gateup_col", H, 2 * I, 1, 0)
+    dn = tp.tp_shard_plan("row", I, H, 1, 0)
+    log("[bench] 8B feed-forward share: generating and packing 4 weight copies")
+    Wg, Wd = to_dev(wl.gateup(H, I, c["sigma"])), to_dev(wl.down(I, H, c["sigma"]))
+    packs = [(tp.tp_shard_pack(gu, Wg), tp.tp_shard_pack(dn, Wd)) for _ in range(4)]
+    del Wg, Wd
+    Ms = (96, 128, 256, 384, 512, 768, 1024)
+    X = to_dev(wl.activations(max(Ms), H))
+    res = []
+    for M in Ms:
+        Hs = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
+        P = torch.empty((M, H), dtype=torch.float32, device="cuda")
+        wsn = max(16, tp.tp_workspace_bytes(gu, M), tp.tp_workspace_bytes(dn, M))
+        ws = torch.empty(wsn, dtype=torch.uint8, device="cuda")
+        g_calls = [[(lib.tp_col_linear, (ref(gu), VP(X.data_ptr()), M, H, VP(gp.data_ptr()), VP(Hs.data_ptr()), I,
+                                         VP(ws.data_ptr()), wsn, stream))] for gp, _ in packs]
+        d_calls = [[(lib.tp_row_linear, (ref(dn), VP(Hs.data_ptr()), M, I, VP(dp.data_ptr()), VP(P.data_ptr()), H,
+                                         VP(ws.data_ptr()), wsn, stream))] for _, dp in packs]
+        ug = time_steps(timer, lambda i: _run(g_calls[i % 4]), 20)
+        ud = time_steps(timer, lambda i: _run(d_calls[i % 4]), 20)
+        gb, db, _ = decode_bytes(M, H, I)
+        fl_g, fl_d = 2 * M * H * 2 * I, 2 * M * I * H
+        res.append(dict(M=M, gateup_us=round(ug, 2), down_us=round(ud, 2), gateup_GBs=round(gb / ug / 1e3, 1),
+                        down_GBs=round(db / ud / 1e3, 1), gateup_TFs=round(fl_g / ug / 1e6, 1),
+                        down_TFs=round(fl_d / ud / 1e6, 1)))
+    return dict(config="llama3.1-8b FFN share, TP=1, batches of 96-1024 tokens", unit="GB/s and TFLOP/s",
+                batches=res)
+
+
 def config_405b_ffn_prefill(timer):
     """The prefill workload alone (rank 0 of the 405B feed-forward layer at
     TP = 8, 8192 tokens), without the CPU baseline: for profiler runs."""
@@ -819,7 +860,7 @@ CONFIGS = {"worked_tp2": config_worked_tp2, "70b_ffn_decode": config_70b_ffn_dec
            "70b_attention_prefill": config_70b_attention_prefill, "sequence_parallel": config_sequence_parallel,
            "405b_ffn_backward": config_405b_ffn_backward, "70b_attention_block": config_70b_attention_block}
 # run only with --config (the default line already carries the prefill workload)
-PROFILE_ONLY = {"405b_ffn_prefill": config_405b_ffn_prefill}
+PROFILE_ONLY = {"405b_ffn_prefill": config_405b_ffn_prefill, "8b_ffn_batches": config_8b_ffn_batches}
 
 
 def main():
