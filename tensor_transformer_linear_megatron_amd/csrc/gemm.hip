@@ -391,7 +391,8 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
 // tiles, so the token tiles of one weight column block share an XCD's L2.
 // The stage, fragment and epilogue layouts are gemm_big's with TB = 1.
 template <int EPI, bool SPLIT>
-__global__ __launch_bounds__(BIG_THREADS) void gemm_mid(LinearArgs a, int ntn, int ntm, int64_t kper, float* part) {
+__global__ __launch_bounds__(BIG_THREADS) void gemm_mid(LinearArgs a, int ntn, int ntm, int tail_base, int64_t kper,
+                                                         float* part) {
   constexpr int ROWS = 128;
   constexpr int XI = 2;                              // token DMA instructions per wave and stage
   constexpr int STAGE_U4 = BIG_WCH * 64 + ROWS * 8;  // 48 KiB per stage
@@ -400,8 +401,13 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_mid(LinearArgs a, int ntn, i
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;  // column half, token quarter
 
-  int bid = (int)blockIdx.x;
-  {
+  // tail_base < 0: 128-token tiles in gemm_big's grouped order (ntm counts
+  // 128-token tiles). tail_base >= 0: the halves of gemm_big's 256-token
+  // tiles tail_base + x / 2 (ntm counts 256-token tiles), for the last,
+  // partial round of a big-tile grid.
+  const bool tail = tail_base >= 0;
+  int bid = tail ? tail_base + (int)(blockIdx.x >> 1) : (int)blockIdx.x;
+  if (!tail) {
     const int per = (int)gridDim.x / 8;
     if (bid < per * 8) bid = (bid % 8) * per + bid / 8;
   }
@@ -411,7 +417,7 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_mid(LinearArgs a, int ntn, i
   const int tm = first_m + (bid % (GM * ntn)) % gsize;
   const int tn = (bid % (GM * ntn)) / gsize;
   const int64_t nt0 = (int64_t)tn * BIG_T;
-  const int64_t m0 = (int64_t)tm * ROWS;
+  const int64_t m0 = tail ? (int64_t)tm * (2 * ROWS) + (int64_t)(blockIdx.x & 1) * ROWS : (int64_t)tm * ROWS;
   const int64_t ksteps = a.ksteps;
   int64_t kcnt = ksteps;
   if constexpr (SPLIT) {
@@ -682,15 +688,15 @@ hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t
     const dim3 grid((unsigned)(ntn * ntm128), (unsigned)mp.G);
     if (mp.G > 1) {
       if (ws == nullptr) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_mid<kEpiF32, true>), grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm128, mp.kper, ws);
+      hipLaunchKernelGGL((gemm_mid<kEpiF32, true>), grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm128, -1, mp.kper, ws);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       return launch_split_fixup(a, epi, ws, mp.G, s);
     }
     switch (epi) {
-      case kEpiSwiglu: hipLaunchKernelGGL((gemm_mid<kEpiSwiglu, false>), grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm128, (int64_t)0, nullptr); break;
-      case kEpiBf16: hipLaunchKernelGGL((gemm_mid<kEpiBf16, false>), grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm128, (int64_t)0, nullptr); break;
-      case kEpiF32: hipLaunchKernelGGL((gemm_mid<kEpiF32, false>), grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm128, (int64_t)0, nullptr); break;
+      case kEpiSwiglu: hipLaunchKernelGGL((gemm_mid<kEpiSwiglu, false>), grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm128, -1, (int64_t)0, nullptr); break;
+      case kEpiBf16: hipLaunchKernelGGL((gemm_mid<kEpiBf16, false>), grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm128, -1, (int64_t)0, nullptr); break;
+      case kEpiF32: hipLaunchKernelGGL((gemm_mid<kEpiF32, false>), grid, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm128, -1, (int64_t)0, nullptr); break;
     }
     return hipGetLastError();
   }
@@ -739,11 +745,12 @@ hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t
       if (e != hipSuccess) return e;
       return launch_split_fixup(b, epi, ws, tp.G, s);
     }
+    // Otherwise as 128-token halves of its tiles, on gemm_mid's three stages.
     const dim3 g2((unsigned)(2 * left));
     switch (epi) {
-      case kEpiSwiglu: hipLaunchKernelGGL((gemm_big<kEpiSwiglu, 1, false>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full, 0, nullptr); break;
-      case kEpiBf16: hipLaunchKernelGGL((gemm_big<kEpiBf16, 1, false>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full, 0, nullptr); break;
-      case kEpiF32: hipLaunchKernelGGL((gemm_big<kEpiF32, 1, false>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full, 0, nullptr); break;
+      case kEpiSwiglu: hipLaunchKernelGGL((gemm_mid<kEpiSwiglu, false>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full, (int64_t)0, nullptr); break;
+      case kEpiBf16: hipLaunchKernelGGL((gemm_mid<kEpiBf16, false>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full, (int64_t)0, nullptr); break;
+      case kEpiF32: hipLaunchKernelGGL((gemm_mid<kEpiF32, false>), g2, dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int)full, (int64_t)0, nullptr); break;
     }
     return hipGetLastError();
   }
