@@ -200,15 +200,15 @@ constexpr int BIG_THREADS = 512;
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
-// TB = 2: 256 x 256 tiles, workgroup x takes tile x of the launch. TB = 1:
-// 128-token half tiles, workgroup x takes half x & 1 of tile tile_base +
-// x / 2 (the last, partial round of a grid, split so that it fills the GPU).
-template <int EPI, int TB, bool SPLIT>
-__global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, int ntm, int tile_base,
-                                                        int64_t kper, float* part) {
+// 256 x 256 tiles: workgroup x takes tile x of the launch (its 128-token
+// halves, for a grid's partial last round, run on gemm_mid). TB counts the
+// 128-token halves of the tile.
+template <int EPI, bool SPLIT>
+__global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, int ntm, int64_t kper, float* part) {
+  constexpr int TB = 2;
   constexpr int ROWS = 128 * TB;                       // tokens per workgroup
   constexpr int XI = 2 * TB;                           // token DMA instructions per wave and stage
-  constexpr int STAGE_U4 = BIG_WCH * 64 + ROWS * 8;    // 64 or 48 KiB per stage
+  constexpr int STAGE_U4 = BIG_WCH * 64 + ROWS * 8;    // 64 KiB per stage
   __shared__ uint4 L0[STAGE_U4], L1[STAGE_U4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -216,8 +216,8 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
 
   // Tile of this workgroup: ids that share an XCD (id mod 8) get consecutive
   // tiles, grouped 8 token tiles deep.
-  int bid = TB == 2 ? (int)blockIdx.x : tile_base + (int)(blockIdx.x >> 1);
-  if (TB == 2) {
+  int bid = (int)blockIdx.x;
+  {
     const int per = (int)gridDim.x / 8;
     if (bid < per * 8) bid = (bid % 8) * per + bid / 8;
   }
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
   const int tm = first_m + (bid % (GM * ntn)) % gsize;
   const int tn = (bid % (GM * ntn)) / gsize;
   const int64_t nt0 = (int64_t)tn * BIG_T;
-  const int64_t m0 = (int64_t)tm * (BIG_MT * 16) + (TB == 1 ? (int64_t)(blockIdx.x & 1) * ROWS : 0);
+  const int64_t m0 = (int64_t)tm * (BIG_MT * 16);
   // ksteps is the packed layout's pair stride; kcnt the k-steps this
   // workgroup multiplies. A split takes k-steps [y kper, y kper + kcnt) and
   // writes its fp32 sum to part[y] ([M x ntiles 16], split order y).
@@ -248,7 +248,6 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
   const int64_t wt = a.ntiles - nt0 < BIG_T ? a.ntiles - nt0 : BIG_T;
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.W + nt0 * ksteps * kTileU4), (short)0, (int)(wt * ksteps * 1024), 0x00020000);
-  // A second half tile can lie wholly past M: then no row is in range.
   const int64_t rows = a.M - m0 < ROWS ? (a.M > m0 ? a.M - m0 : 0) : ROWS;
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.X + m0 * a.ldx), (short)0, (int)(rows * a.ldx * 2), 0x00020000);
@@ -389,7 +388,7 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
 // stage buffers instead of two: a stage's DMA goes out two stages before its
 // fragments are read. Token tiles of 128 rows, grouped as gemm_big groups its
 // tiles, so the token tiles of one weight column block share an XCD's L2.
-// The stage, fragment and epilogue layouts are gemm_big's with TB = 1.
+// The stage, fragment and epilogue layouts are gemm_big's at half height.
 template <int EPI, bool SPLIT>
 __global__ __launch_bounds__(BIG_THREADS) void gemm_mid(LinearArgs a, int ntn, int ntm, int tail_base, int64_t kper,
                                                          float* part) {
@@ -590,7 +589,8 @@ GemmPlan plan_gemm(int64_t M, int64_t ldx, int64_t ksteps, int64_t ntiles) {
 // tiles (ids [full, nb) of gemm_big's grouped order) form a rectangle of
 // token tiles x column tiles, it runs as a sub-GEMM with K split G = 256 /
 // tiles ways (fp32 partials, then the split fix-up applies the epilogue), so
-// that whole 256 x 256 tiles fill the GPU; otherwise as 128-token half tiles.
+// that whole 256 x 256 tiles fill the GPU; otherwise as 128-token half tiles
+// on gemm_mid.
 struct TailPlan {
   bool split = false;
   int64_t m0 = 0, rows = 0, nt0 = 0, nt = 0;  // token rows and packed tiles of the sub-GEMM
@@ -703,8 +703,8 @@ hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t
   const GemmPlan p = plan_gemm(a.M, a.ldx, a.ksteps, a.ntiles);
   if (p.big && p.G > 1) {
     if (ws == nullptr) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_big<kEpiF32, 2, true>), dim3((unsigned)(ntn * ntm), (unsigned)p.G),
-                       dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0, p.kper, ws);
+    hipLaunchKernelGGL((gemm_big<kEpiF32, true>), dim3((unsigned)(ntn * ntm), (unsigned)p.G),
+                       dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, p.kper, ws);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_split_fixup(a, epi, ws, p.G, s);
@@ -720,9 +720,9 @@ hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t
     const TailPlan tp = plan_tail(a.M, a.ksteps, a.ntiles);
     if (tp.split && ws == nullptr) return hipErrorInvalidValue;
     switch (epi) {
-      case kEpiSwiglu: hipLaunchKernelGGL((gemm_big<kEpiSwiglu, 2, false>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0, 0, nullptr); break;
-      case kEpiBf16: hipLaunchKernelGGL((gemm_big<kEpiBf16, 2, false>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0, 0, nullptr); break;
-      case kEpiF32: hipLaunchKernelGGL((gemm_big<kEpiF32, 2, false>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, 0, 0, nullptr); break;
+      case kEpiSwiglu: hipLaunchKernelGGL((gemm_big<kEpiSwiglu, false>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int64_t)0, nullptr); break;
+      case kEpiBf16: hipLaunchKernelGGL((gemm_big<kEpiBf16, false>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int64_t)0, nullptr); break;
+      case kEpiF32: hipLaunchKernelGGL((gemm_big<kEpiF32, false>), dim3(n1), dim3(BIG_THREADS), 0, s, a, (int)ntn, (int)ntm, (int64_t)0, nullptr); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !split) return e;
@@ -739,8 +739,8 @@ hipError_t launch_gemm(const LinearArgs& a, Epilogue epi, float* ws, hipStream_t
       b.out_n = a.out_n - col0 < width ? a.out_n - col0 : width;
       if (a.wscale != nullptr) b.wscale = a.wscale + tp.nt0 * kTileN;
       const int64_t bn = (b.ntiles + BIG_T - 1) / BIG_T, bm = (b.M + BIG_MT * 16 - 1) / (BIG_MT * 16);
-      hipLaunchKernelGGL((gemm_big<kEpiF32, 2, true>), dim3((unsigned)(bn * bm), (unsigned)tp.G),
-                         dim3(BIG_THREADS), 0, s, b, (int)bn, (int)bm, 0, tp.kper, ws);
+      hipLaunchKernelGGL((gemm_big<kEpiF32, true>), dim3((unsigned)(bn * bm), (unsigned)tp.G),
+                         dim3(BIG_THREADS), 0, s, b, (int)bn, (int)bm, tp.kper, ws);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       return launch_split_fixup(b, epi, ws, tp.G, s);
