@@ -177,10 +177,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
 //    and so does the padding stage when the stage count is odd.
 //  * Workgroup ids are spread so that the 32 workgroups an XCD runs together
 //    cover 8 token tiles x 4 column tiles (shared through that XCD's L2).
-//  * Epilogue in registers: lane (h, j) owns token j of each 32-token block
-//    and, for q = 0..3, output columns 8q + 4h .. +3 of each 32-column block
+//  * Epilogue: lane (h, j) owns token j of each 32-token block and, for
+//    q = 0..3, output columns 8q + 4h .. +3 of each 32-column block
 //    (accumulator elements 4q .. 4q+3). For SwiGLU a 32-column block is one
-//    gate tile (q = 0, 1) and its up tile (q = 2, 3).
+//    gate tile (q = 0, 1) and its up tile (q = 2, 3). bf16 and SwiGLU
+//    results are stored straight from that layout. fp32 results go out
+//    through each wave's 16 KiB of the freed stage buffers as whole 128-byte
+//    lines (store_block_f32): against direct stores (32 rows x 32 bytes per
+//    instruction) that took the 405B down projection from 1.48-1.52 to
+//    1.43-1.47 ms and the 70B O slice from 84-89 to 80-81 us. Through LDS
+//    the bf16 outputs gained nothing and lost up to 1 % (every wave then
+//    waits for the slowest at the barrier).
 // ---------------------------------------------------------------------------
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -199,6 +206,37 @@ constexpr int BIG_THREADS = 512;
 // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
+
+// fp32 epilogue of one wavefront's 32-token x 128-column block: accumulators
+// v0..v3 (32-column blocks x = 0..3 in the 32x32x16 MFMA layout: lane (h, j)
+// holds token j, columns 8q + 4h .. +3 as elements 4q .. 4q+3), first token
+// row m_first, first packed tile nt_first. In that layout a row's 512 bytes
+// sit in two lanes, so a direct store writes 32 rows x 32 bytes per
+// instruction; the block is transposed in the wave's 16 KiB of LDS T
+// instead (16-byte piece P of row r at slot 32 r + (P ^ r)), and each store
+// instruction writes two rows x 512 contiguous bytes. The caller has made T
+// free for the wave.
+__device__ __forceinline__ void store_block_f32(const LinearArgs& a, const f32x16_t& v0, const f32x16_t& v1,
+                                                const f32x16_t& v2, const f32x16_t& v3, uint4* T, int lane,
+                                                int64_t m_first, int64_t nt_first) {
+  const int fh = lane >> 5, fj = lane & 31;
+  const f32x16_t* v[4] = {&v0, &v1, &v2, &v3};
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      T[fj * 32 + ((8 * x + 2 * q + fh) ^ fj)] =
+          make_uint4(__float_as_uint((*v[x])[4 * q]), __float_as_uint((*v[x])[4 * q + 1]),
+                     __float_as_uint((*v[x])[4 * q + 2]), __float_as_uint((*v[x])[4 * q + 3]));
+  const int64_t n = nt_first * kTileN + (lane & 31) * 4;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = 2 * k + (lane >> 5);
+    const uint4 w = T[r * 32 + ((lane & 31) ^ r)];
+    const int64_t m = m_first + r;
+    if (m < a.M && n < a.out_n) *reinterpret_cast<uint4*>(static_cast<float*>(a.out) + m * a.ldo + n) = w;
+  }
+}
 
 // 256 x 256 tiles: workgroup x takes tile x of the launch (its 128-token
 // halves, for a grid's partial last round, run on gemm_mid). TB counts the
@@ -345,6 +383,16 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
 #undef TP_STAGE
 #undef TP_SYNC
 
+  if constexpr (EPI == kEpiF32) {
+    // Once every wave is done with the stage buffers, each wave has 16 KiB of them.
+    __syncthreads();
+    uint4* T = wave < 4 ? &L0[wave * 1024] : &L1[(wave - 4) * 1024];
+#pragma unroll
+    for (int y = 0; y < TB; ++y)
+      store_block_f32(a, acc[0][y], acc[1][y], acc[2][y], acc[3][y], T, lane, m0 + (wm * TB + y) * 32,
+                      nt0 + wn * 8);
+    return;
+  }
 #pragma unroll
   for (int y = 0; y < TB; ++y) {
     const int64_t m = m0 + (wm * TB + y) * 32 + fj;
@@ -368,13 +416,8 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
           const int64_t n = ntb * kTileN + 8 * q + 4 * fh;
           if (n >= a.out_n) continue;
           const f32x16_t& v = acc[x][y];
-          if constexpr (EPI == kEpiBf16) {
-            store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + n, v[4 * q], v[4 * q + 1],
-                         v[4 * q + 2], v[4 * q + 3]);
-          } else {
-            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + m * a.ldo + n) =
-                make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-          }
+          store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + n, v[4 * q], v[4 * q + 1], v[4 * q + 2],
+                       v[4 * q + 3]);
         }
       }
     }
@@ -524,6 +567,12 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_mid(LinearArgs a, int ntn, i
 #undef TP_STAGE
 #undef TP_SYNC
 
+  if constexpr (EPI == kEpiF32) {
+    __syncthreads();
+    uint4* T = wave < 3 ? &L0[wave * 1024] : (wave < 6 ? &L1[(wave - 3) * 1024] : &L2[(wave - 6) * 1024]);
+    store_block_f32(a, acc[0], acc[1], acc[2], acc[3], T, lane, m0 + wm * 32, nt0 + wn * 8);
+    return;
+  }
   const int64_t m = m0 + wm * 32 + fj;
   if (m >= a.M) return;
 #pragma unroll
@@ -544,13 +593,8 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_mid(LinearArgs a, int ntn, i
       for (int q = 0; q < 4; ++q) {
         const int64_t n = ntb * kTileN + 8 * q + 4 * fh;
         if (n >= a.out_n) continue;
-        if constexpr (EPI == kEpiBf16) {
-          store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + n, v[4 * q], v[4 * q + 1], v[4 * q + 2],
-                       v[4 * q + 3]);
-        } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + m * a.ldo + n) =
-              make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-        }
+        store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + n, v[4 * q], v[4 * q + 1], v[4 * q + 2],
+                     v[4 * q + 3]);
       }
     }
   }
