@@ -179,15 +179,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
 //    cover 8 token tiles x 4 column tiles (shared through that XCD's L2).
 //  * Epilogue: lane (h, j) owns token j of each 32-token block and, for
 //    q = 0..3, output columns 8q + 4h .. +3 of each 32-column block
-//    (accumulator elements 4q .. 4q+3). For SwiGLU a 32-column block is one
-//    gate tile (q = 0, 1) and its up tile (q = 2, 3). bf16 and SwiGLU
-//    results are stored straight from that layout. fp32 results go out
-//    through each wave's 16 KiB of the freed stage buffers as whole 128-byte
-//    lines (store_block_f32): against direct stores (32 rows x 32 bytes per
-//    instruction) that took the 405B down projection from 1.48-1.52 to
-//    1.43-1.47 ms and the 70B O slice from 84-89 to 80-81 us. Through LDS
-//    the bf16 outputs gained nothing and lost up to 1 % (every wave then
-//    waits for the slowest at the barrier).
+//    (accumulator elements 4q .. 4q+3), so a direct store writes 32 rows x
+//    32 (fp32) or 16 (bf16) bytes per instruction. Each wave instead passes
+//    its results through its own 4 KiB of LDS beside the stage buffers and
+//    writes whole 128-byte lines, with no barrier (store_block_lines).
+//    Against direct stores: the 405B down projection 1.48-1.52 -> 1.43-1.45
+//    ms, the 70B O slice 84-89 -> 73-76 us; SwiGLU and bf16 outputs
+//    unchanged.
 // ---------------------------------------------------------------------------
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -238,6 +236,72 @@ __device__ __forceinline__ void store_block_f32(const LinearArgs& a, const f32x1
   }
 }
 
+// gemm_big's epilogue of one wave's 32-token x 128-column block (arguments
+// as for store_block_f32) through the wave's own 4 KiB E of LDS, beside the
+// stage buffers, so no wave waits for another: rows of 128 bytes, 16-byte
+// piece P of row r at slot 8 r + (P ^ ((r >> 1) & 7)), and each store
+// instruction writes 8 rows x 128 contiguous bytes. SwiGLU: the block's 64
+// output columns at once (a 32-column block is one gate tile, elements 0..7
+// of each 16, and its up tile, 8..15); fp32: one 32-column block at a time;
+// bf16: 64 columns (two blocks) at a time.
+template <int EPI>
+__device__ __forceinline__ void store_block_lines(const LinearArgs& a, const f32x16_t& v0, const f32x16_t& v1,
+                                                const f32x16_t& v2, const f32x16_t& v3, uint4* E, int lane,
+                                                int64_t m_first, int64_t nt_first) {
+  const int fh = lane >> 5, fj = lane & 31;
+  const f32x16_t* v[4] = {&v0, &v1, &v2, &v3};
+  const int sw = (fj >> 1) & 7;
+  const int rr = lane >> 3, p = lane & 7;
+  if constexpr (EPI == kEpiF32) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        E[fj * 8 + ((2 * q + fh) ^ sw)] =
+            make_uint4(__float_as_uint((*v[x])[4 * q]), __float_as_uint((*v[x])[4 * q + 1]),
+                       __float_as_uint((*v[x])[4 * q + 2]), __float_as_uint((*v[x])[4 * q + 3]));
+      const int64_t n = (nt_first + 2 * x) * kTileN + p * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 8 * k + rr;
+        const uint4 w = E[r * 8 + (p ^ ((r >> 1) & 7))];
+        const int64_t m = m_first + r;
+        if (m < a.M && n < a.out_n) *reinterpret_cast<uint4*>(static_cast<float*>(a.out) + m * a.ldo + n) = w;
+      }
+    }
+  } else {
+    uint2* E2 = reinterpret_cast<uint2*>(E);
+    constexpr int NPASS = EPI == kEpiSwiglu ? 1 : 2;  // 64 output columns per pass
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+#pragma unroll
+      for (int xx = 0; xx < 4 / NPASS; ++xx) {
+        const int x = ps * (4 / NPASS) + xx;
+        const f32x16_t& w = *v[x];
+        if constexpr (EPI == kEpiSwiglu) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            E2[(fj * 8 + ((2 * x + q) ^ sw)) * 2 + fh] =
+                bf16x4(swiglu(w[4 * q], w[4 * q + 8]), swiglu(w[4 * q + 1], w[4 * q + 9]),
+                       swiglu(w[4 * q + 2], w[4 * q + 10]), swiglu(w[4 * q + 3], w[4 * q + 11]));
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            E2[(fj * 8 + ((4 * xx + q) ^ sw)) * 2 + fh] = bf16x4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+        }
+      }
+      const int64_t n = (EPI == kEpiSwiglu ? (nt_first >> 1) * kTileN : (nt_first + 4 * ps) * kTileN) + p * 8;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 8 * k + rr;
+        const uint4 w = E[r * 8 + (p ^ ((r >> 1) & 7))];
+        const int64_t m = m_first + r;
+        if (m < a.M && n < a.out_n) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + m * a.ldo + n) = w;
+      }
+    }
+  }
+}
+
 // 256 x 256 tiles: workgroup x takes tile x of the launch (its 128-token
 // halves, for a grid's partial last round, run on gemm_mid). TB counts the
 // 128-token halves of the tile.
@@ -248,6 +312,7 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
   constexpr int XI = 2 * TB;                           // token DMA instructions per wave and stage
   constexpr int STAGE_U4 = BIG_WCH * 64 + ROWS * 8;    // 64 KiB per stage
   __shared__ uint4 L0[STAGE_U4], L1[STAGE_U4];
+  __shared__ uint4 EP[8 * 256];  // the epilogue's 4 KiB per wave
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;  // column half, token quarter
@@ -383,45 +448,10 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big(LinearArgs a, int ntn, i
 #undef TP_STAGE
 #undef TP_SYNC
 
-  if constexpr (EPI == kEpiF32) {
-    // Once every wave is done with the stage buffers, each wave has 16 KiB of them.
-    __syncthreads();
-    uint4* T = wave < 4 ? &L0[wave * 1024] : &L1[(wave - 4) * 1024];
 #pragma unroll
-    for (int y = 0; y < TB; ++y)
-      store_block_f32(a, acc[0][y], acc[1][y], acc[2][y], acc[3][y], T, lane, m0 + (wm * TB + y) * 32,
-                      nt0 + wn * 8);
-    return;
-  }
-#pragma unroll
-  for (int y = 0; y < TB; ++y) {
-    const int64_t m = m0 + (wm * TB + y) * 32 + fj;
-    if (m >= a.M) continue;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int64_t ntb = nt0 + wn * 8 + 2 * x;  // first packed tile of this 32-column block
-      if constexpr (EPI == kEpiSwiglu) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int64_t n = (ntb >> 1) * kTileN + 8 * q + 4 * fh;
-          if (ntb >= a.ntiles || n >= a.out_n) continue;
-          const f32x16_t& v = acc[x][y];
-          store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + n, swiglu(v[4 * q], v[4 * q + 8]),
-                       swiglu(v[4 * q + 1], v[4 * q + 9]), swiglu(v[4 * q + 2], v[4 * q + 10]),
-                       swiglu(v[4 * q + 3], v[4 * q + 11]));
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = ntb * kTileN + 8 * q + 4 * fh;
-          if (n >= a.out_n) continue;
-          const f32x16_t& v = acc[x][y];
-          store_bf16x4(static_cast<uint16_t*>(a.out) + m * a.ldo + n, v[4 * q], v[4 * q + 1], v[4 * q + 2],
-                       v[4 * q + 3]);
-        }
-      }
-    }
-  }
+  for (int y = 0; y < TB; ++y)
+    store_block_lines<EPI>(a, acc[0][y], acc[1][y], acc[2][y], acc[3][y], &EP[wave * 256], lane,
+                           m0 + (wm * TB + y) * 32, nt0 + wn * 8);
 }
 
 // gemm_mid: prefills of at most a few hundred tokens, where every weight byte

@@ -163,11 +163,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // the quotient is -0; for g -> +inf it is g.
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-__device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, float c, float d) {
+// Four values rounded to bf16 and packed in order.
+__device__ __forceinline__ uint2 bf16x4(float a, float b, float c, float d) {
   uint2 v;
   v.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
   v.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
-  *reinterpret_cast<uint2*>(p) = v;
+  return v;
+}
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(p) = bf16x4(a, b, c, d);
 }
 
 }  // namespace tpk
