@@ -533,6 +533,44 @@ def test_ffn_shard_is_col_then_row_and_ldy_slices():
     assert torch.all(full[:, 256:] == 5.0)
 
 
+# Prefill epilogues write 16-byte pieces of whole rows; an output width that
+# is a multiple of 8 but not of 16, 32 or 128 leaves a half-filled last tile
+# and a partly valid last piece of each wave's columns. Each case writes into
+# the top-left [M x out_n] of a larger buffer (wider rows and extra rows hold
+# a sentinel) through the big-tile kernel (whole rounds, the tail), the
+# 128-token kernel and split K.
+BOUNDS_CASES = [("col", 72, 1000, 16300), ("gateup_col", 72, 2 * 1000, 8200), ("row", 72, 1000, 16300),
+                ("col", 200, 1000, 300), ("gateup_col", 200, 2 * 1000, 300), ("row", 200, 1000, 300),
+                ("row", 4096, 1000, 1000), ("gateup_col", 4096, 2 * 1000, 1000)]
+
+
+@pytest.mark.parametrize("kind,K,N,M", BOUNDS_CASES)
+def test_prefill_outputs_stay_in_bounds(kind, K, N, M):
+    say("prefill bounds", kind, K, N, M)
+    X = si.normal_bf16(94, (M, K), 1.0)
+    W = si.normal_bf16(95, (K, N), 0.05)
+    d, p = plan_both(kind, K, N, 1, 0)
+    d = with_path(d, tp.TP_PATH_PREFILL)
+    Wp = tp.tp_shard_pack(d, dev(W))
+    wide, extra = d.out_n + 24, 5
+    rows = sorted({0, 1, 31, 32, M // 2, M - 33, M - 2, M - 1})
+    if kind == "row":
+        sentinel = 12345.0
+        full = torch.full((M + extra, wide), sentinel, dtype=torch.float32, device="cuda")
+        tp.tp_row_linear(d, dev(X), Wp, P=full[:M, :d.out_n])
+        ref = oracle.row_linear(np.ascontiguousarray(X[rows]), W, p)
+    else:
+        sentinel = 5.0
+        full = torch.full((M + extra, wide), sentinel, dtype=torch.bfloat16, device="cuda")
+        tp.tp_col_linear(d, dev(X), Wp, Y=full[:M, :d.out_n])
+        fn = oracle.gateup_swiglu if kind == "gateup_col" else oracle.col_linear_bf16
+        ref = oracle.bf16_to_f64(fn(np.ascontiguousarray(X[rows]), W, p))
+    torch.cuda.synchronize()
+    assert torch.all(full[:M, d.out_n:] == sentinel), "a write landed right of the output columns"
+    assert torch.all(full[M:] == sentinel), "a write landed below the last token row"
+    assert_parity(host_f64(full[:M, :d.out_n][rows]), ref, f"{kind} K={K} N={N} M={M}")
+
+
 # ---------------------------------------------------------------------------
 # The model-shaped workloads at full size.
 # ---------------------------------------------------------------------------
