@@ -11,9 +11,15 @@ outputs are overwritten by eager work, with synchronisations around it.
 - A decode step of the attention core: KV append, then chunked attention
   with the merge.
 - A prefill call of the attention core.
+- A prefill of one rank's feed-forward share: the 128-token kernel, and the
+  big-tile kernel with its tail and a split-K down projection with its fix-up.
 
 Every replay must reproduce the eager result bit for bit. That holds only if
 the calls make no host synchronisation, allocation or memset of their own.
+
+A last case queues split-K calls on two streams at once, each with its own
+workspace, and checks them against the same calls made one after another:
+the calls keep no state of their own between launches.
 """
 from __future__ import annotations
 
@@ -135,3 +141,56 @@ def test_attention_prefill_replays():
         tp.tp_attention(q, QKV, T, kl, sl, Kc, Vc, T + 37, A=A)
 
     _check_replays(step, [A], keep=[Kc, Vc])
+
+
+@pytest.mark.parametrize("M", [300, 4100])
+def test_ffn_prefill_step_replays(M):
+    """A prefill of one rank's feed-forward share: at 300 tokens the 128-token
+    kernel; at 4100 the big-tile gate/up GEMM (a whole round and its tail)
+    and the down GEMM with K split, its workspace and fix-up."""
+    say("graph ffn prefill", M)
+    K, inter = 512, 2048
+    X = dev(si.normal_bf16(730, (M, K), 1.0))
+    Wgu = dev(si.normal_bf16(731, (K, 2 * inter), 0.02))
+    Wd = dev(si.normal_bf16(732, (inter, K), 0.02))
+    gu = tp.tp_shard_plan("gateup_col", K, 2 * inter, 1, 0)
+    dn = tp.tp_shard_plan("row", inter, K, 1, 0)
+    Pgu, Pd = tp.tp_shard_pack(gu, Wgu), tp.tp_shard_pack(dn, Wd)
+    need = max(tp.tp_workspace_bytes(gu, M), tp.tp_workspace_bytes(dn, M))
+    if M == 4100:
+        assert need > 0  # the down projection splits K
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    H = torch.empty((M, inter), dtype=torch.bfloat16, device="cuda")
+    P = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        tp.tp_ffn_shard(gu, dn, X, Pgu, Pd, H=H, P=P, ws=ws)
+
+    _check_replays(step, [H, P])
+    assert torch.isfinite(P).all()
+
+
+def test_two_streams_do_not_interfere():
+    """Split-K calls (decode at 40 tokens, prefill at 1000) queued on two
+    streams at once, each with its own workspace, give the bits of the same
+    calls made one after another."""
+    say("two streams")
+    K, N = 4096, 1024
+    d = tp.tp_shard_plan("row", K, N, 1, 0)
+    Wp = tp.tp_shard_pack(d, dev(si.normal_bf16(740, (K, N), 0.02)))
+    cases = [(40, 741), (1000, 742), (40, 743), (1000, 744)]
+    Xs = [dev(si.normal_bf16(seed, (M, K), 1.0)) for M, seed in cases]
+    want = [_bits(tp.tp_row_linear(d, X, Wp)).clone() for X in Xs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [torch.empty(max(tp.tp_workspace_bytes(d, M), 16), dtype=torch.uint8, device="cuda") for M, _ in cases]
+    outs = [torch.empty((M, N), dtype=torch.float32, device="cuda") for M, _ in cases]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, X in enumerate(Xs):
+            with torch.cuda.stream(streams[i % 2]):
+                tp.tp_row_linear(d, X, Wp, P=outs[i], ws=wss[i], stream=streams[i % 2])
+        torch.cuda.synchronize()
+        for i, (o, w) in enumerate(zip(outs, want)):
+            assert torch.equal(_bits(o), w), f"round {rep}, call {i} differs from the sequential run"
