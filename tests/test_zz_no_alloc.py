@@ -2,7 +2,8 @@
 library's static device array instead of a caller workspace. Called through
 the C ABI and checked against tp_ffn_shard (same kernels, caller workspace)
 bit for bit, and against the oracle, on two calls in a row with the second
-smaller; a shape whose scratch exceeds the array is refused on the host."""
+smaller; a shape whose scratch exceeds the array is refused on the host; and
+captured into a HIP graph, whose replays give the eager call's bits."""
 from __future__ import annotations
 
 import ctypes
@@ -67,3 +68,38 @@ def test_noalloc_matches_ffn_shard_twice_second_smaller():
         Href = oracle.gateup_swiglu(X[:M], Wgu, pgu)
         assert_parity(host_f64(H), oracle.bf16_to_f64(Href), f"H M={M}")
         assert_parity(host_f64(P), oracle.row_linear(Href, Wd, pdn), f"P M={M}")
+
+
+@pytest.mark.gpu
+def test_noalloc_under_graph_capture():
+    """The callers it is for: captured once into a HIP graph (after one eager
+    call, which looks up the scratch array's address) and replayed three
+    times, with the outputs overwritten in between; every replay gives the
+    eager bits."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    K, I, M = 2048, 1024, 48
+    gu, dn = tp.tp_shard_plan("gateup_col", K, 2 * I, 1, 0), tp.tp_shard_plan("row", I, K, 1, 0)
+    assert 0 < max(tp.tp_workspace_bytes(gu, M), tp.tp_workspace_bytes(dn, M)) <= _lib.NOALLOC_SCRATCH_BYTES
+    Wgp = tp.tp_shard_pack(gu, dev(si.normal_bf16(95, (K, 2 * I), 0.02)))
+    Wdp = tp.tp_shard_pack(dn, dev(si.normal_bf16(96, (I, K), 0.02)))
+    X = dev(si.normal_bf16(97, (M, K), 1.0))
+    H = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
+    P = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    say(f"noalloc graph M={M} K={K} I={I}")
+    assert _noalloc(gu, dn, X, Wgp, Wdp, H, P) == _lib.TP_OK
+    torch.cuda.synchronize()
+    want_h, want_p = H.view(torch.int16).clone(), P.view(torch.int32).clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = _noalloc(gu, dn, X, Wgp, Wdp, H, P)
+    assert st == _lib.TP_OK, tp.tp_status_str(st)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        H.view(torch.int16).fill_(0x5A5A)
+        P.view(torch.int32).fill_(0x5A5A5A5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(H.view(torch.int16), want_h), f"replay {rep}: H differs from the eager call"
+        assert torch.equal(P.view(torch.int32), want_p), f"replay {rep}: P differs from the eager call"
