@@ -13,6 +13,8 @@ outputs are overwritten by eager work, with synchronisations around it.
 - A prefill call of the attention core.
 - A prefill of one rank's feed-forward share: the 128-token kernel, and the
   big-tile kernel with its tail and a split-K down projection with its fix-up.
+- The same share on 8-bit shards: streaming decode, split decode, and prefill
+  through the bf16 copy of the shard in the workspace.
 
 Every replay must reproduce the eager result bit for bit. That holds only if
 the calls make no host synchronisation, allocation or memset of their own.
@@ -194,3 +196,30 @@ def test_two_streams_do_not_interfere():
         torch.cuda.synchronize()
         for i, (o, w) in enumerate(zip(outs, want)):
             assert torch.equal(_bits(o), w), f"round {rep}, call {i} differs from the sequential run"
+
+
+@pytest.mark.parametrize("M", [8, 40, 300])
+def test_ffn_8bit_steps_replay(M):
+    """One rank's feed-forward share on 8-bit shards: the streaming decode
+    kernel (8 tokens), the split shared-token kernel with its fix-up (40),
+    and prefill through the bf16 copy in the workspace (300)."""
+    say("graph ffn 8-bit", M)
+    K, inter = 1024, 1536
+    X = dev(si.normal_bf16(750, (M, K), 1.0))
+    gu = tp.tp_shard_set_wformat(tp.tp_shard_plan("gateup_col", K, 2 * inter, 2, 1), "fp8_e4m3")
+    dn = tp.tp_shard_set_wformat(tp.tp_shard_plan("row", inter, K, 2, 1), "fp8_e4m3")
+    Pgu = tp.tp_shard_pack(gu, dev(si.normal_bf16(751, (K, 2 * inter), 0.02)))
+    Pd = tp.tp_shard_pack(dn, dev(si.normal_bf16(752, (inter, K), 0.02)))
+    need = max(tp.tp_workspace_bytes(gu, M), tp.tp_workspace_bytes(dn, M))
+    if M > 16:
+        assert need > 0  # split partials, or the prefill's bf16 copy of the shard
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    H = torch.empty((M, inter // 2), dtype=torch.bfloat16, device="cuda")
+    P = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        tp.tp_ffn_shard(gu, dn, X, Pgu, Pd, H=H, P=P, ws=ws)
+
+    _check_replays(step, [H, P])
+    assert torch.isfinite(P).all()
