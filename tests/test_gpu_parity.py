@@ -629,6 +629,22 @@ def test_llama8b_ffn_tp1_decode(llama8b, M):
     np.testing.assert_array_equal(host_f64(Y), host_f64(P))  # t = 1: the sum is the partial
 
 
+@pytest.mark.parametrize("M", [96, 384, 513, 768, 1024])
+def test_llama8b_ffn_tp1_batches(llama8b, M):
+    """The 8B share at the batch sizes between decode and full prefill (the
+    128-token kernel with split K up to 512 tokens; big tiles, a half-tile
+    tail and split K beyond): the first and last rows and two rows of every
+    128-token tile of H and P against the oracle."""
+    say("llama8b ffn batch", M)
+    w = llama8b
+    X = wl.activations(M, wl.LLAMA8B["hidden"])
+    H, P = tp.tp_ffn_shard(w["gu"], w["dn"], dev(X), w["gp"], w["dp"])
+    rows = sorted({0, M - 1} | set(range(5, M, 128)) | set(range(100, M, 128)))
+    Href, Pref = oracle.ffn_shard(np.ascontiguousarray(X[rows]), w["Wgu"], w["Wd"], w["pgu"], w["pdn"])
+    assert_parity(host_f64(H[rows]), oracle.bf16_to_f64(Href), f"H M={M}")
+    assert_parity(host_f64(P[rows]), Pref, f"P M={M}")
+
+
 @pytest.fixture(scope="module")
 def llama70b_ffn():
     c = wl.LLAMA70B
