@@ -685,6 +685,31 @@ def test_llama70b_ffn_tp8_all_ranks(llama70b_ffn, M):
     assert_parity(Y[rows], ref, "sum over 8 ranks vs unsharded FFN")
 
 
+@pytest.mark.parametrize("M", [1536, 2048])
+def test_llama70b_ffn_tp8_prefill_unfilled_grids(llama70b_ffn, M):
+    """70B shares of TP = 8 at 1536 and 2048 tokens, whose gate/up grids of
+    168 and 224 big tiles run on the 128-token kernel: rank 3's H and P and
+    the sum over all 8 ranks against the oracle on sampled rows."""
+    say("llama70b ffn tp8 prefill", M)
+    w = llama70b_ffn
+    X = wl.activations(M, wl.LLAMA70B["hidden"])
+    Xd = dev(X)
+    P = torch.empty((w["t"], M, 8192), dtype=torch.float32, device="cuda")
+    Hs = []
+    for r, rk in enumerate(w["ranks"]):
+        H, _ = tp.tp_ffn_shard(rk["gu"], rk["dn"], Xd, rk["gp"], rk["dp"], P=P[r])
+        if r == 3:
+            Hs.append(H)
+    Y = tp.tp_reduce_partials(P)
+    rows = sorted({0, M - 1} | set(range(7, M, 256)) | set(range(200, M, 256)))
+    rk = w["ranks"][3]
+    H3, P3 = oracle.ffn_shard(np.ascontiguousarray(X[rows]), w["Wgu"], w["Wd"], rk["pgu"], rk["pdn"])
+    assert_parity(host_f64(Hs[0][rows]), oracle.bf16_to_f64(H3), f"rank 3 H M={M}")
+    assert_parity(host_f64(P[3][rows]), P3, f"rank 3 partial M={M}")
+    ref = oracle.ffn_unsharded(np.ascontiguousarray(X[rows]), w["Wgu"], w["Wd"])
+    assert_parity(host_f64(Y[rows]), ref, f"sum over 8 ranks vs unsharded FFN M={M}")
+
+
 SAMPLE_ROWS_4096 = [0, 1, 15, 16, 127, 128, 129, 1000, 2047, 2048, 3071, 4094, 4095]
 
 
