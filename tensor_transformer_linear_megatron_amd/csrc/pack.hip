@@ -64,18 +64,30 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int64_t total_u4)
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Pass 1: one thread per packed column. e = the smallest integer with
-// amax <= 448 2^e: with amax = f 2^x, f in [0.5, 1) and 448 = 0.875 2^9,
-// e = x - 9 if f <= 0.875, else x - 8. Padding and all-zero columns get 2^0.
-__global__ __launch_bounds__(256) void pack8_scale_kernel(PackArgs a) {
-  const int64_t pc = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (pc >= a.ntiles * kTileN) return;
+// Pass 1: the largest |w| of each packed column over the shard's rows, then
+// its scale. A workgroup of kScaleWaves wavefronts takes 64 columns (lane =
+// column); wavefront w reads rows w, w + kScaleWaves, ..., and the maxima
+// meet in LDS (a maximum does not depend on the order). e = the smallest
+// integer with amax <= 448 2^e: with amax = f 2^x, f in [0.5, 1) and
+// 448 = 0.875 2^9, e = x - 9 if f <= 0.875, else x - 8. Padding and all-zero
+// columns get 2^0.
+constexpr int kScaleWaves = 16;
+
+__global__ __launch_bounds__(64 * kScaleWaves) void pack8_scale_kernel(PackArgs a) {
+  __shared__ float red[kScaleWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t pc = (int64_t)blockIdx.x * 64 + lane;
   int64_t wcol;
   float amax = 0.0f;
-  if (source_col(a, pc / kTileN, (int)(pc % kTileN), &wcol)) {
-    for (int64_t k = 0; k < a.shard_k; ++k)
+  if (pc < a.ntiles * kTileN && source_col(a, pc / kTileN, (int)(pc % kTileN), &wcol)) {
+#pragma unroll 4
+    for (int64_t k = w; k < a.shard_k; k += kScaleWaves)
       amax = fmaxf(amax, fabsf(bf16_bits_to_f32(a.W[(a.row_begin + k) * a.ldw + wcol])));
   }
+  red[w][lane] = amax;
+  __syncthreads();
+  if (w != 0 || pc >= a.ntiles * kTileN) return;
+  for (int j = 1; j < kScaleWaves; ++j) amax = fmaxf(amax, red[j][lane]);
   int e = 0;
   if (amax > 0.0f) {
     int x;
@@ -204,7 +216,7 @@ hipError_t launch_pack_dgrad(const PackArgs& a, hipStream_t s) {
 hipError_t launch_pack8(const PackArgs& a, hipStream_t s) {
   const int64_t cols = a.ntiles * kTileN;
   if (cols == 0) return hipSuccess;
-  hipLaunchKernelGGL(pack8_scale_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(pack8_scale_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(64 * kScaleWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = a.ksteps * a.ntiles * kTileU4;
