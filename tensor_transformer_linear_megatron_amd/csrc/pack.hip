@@ -189,10 +189,24 @@ __global__ __launch_bounds__(256) void pack_dgrad_kernel(PackArgs a, int64_t tot
   const int64_t ks = rem >> 1, nt = 2 * pair + (rem & 1);
   const int g = lane >> 4, i = lane & 15;
   const int64_t n = nt * kTileN + i;
+  const int64_t k0 = ks * kTileK + g * 8;  // the lane's 8 contraction indices k0 .. k0 + 7
+  // When the octet lies inside one column range, its 8 values are 8
+  // consecutive elements of forward row n: one 16-byte load if aligned.
+  if (n < a.shard_n && k0 + 8 <= a.shard_k) {
+    for (int r = 0; r < a.n_ranges; ++r) {
+      if (k0 >= a.dst[r] && k0 + 8 <= a.dst[r] + a.len[r]) {
+        const uint16_t* p = a.W + (a.row_begin + n) * a.ldw + a.src[r] + (k0 - a.dst[r]);
+        if (((uintptr_t)p & 15) == 0) {
+          a.out[c] = *reinterpret_cast<const uint4*>(p);
+          return;
+        }
+      }
+    }
+  }
   uint16_t v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int64_t k = ks * kTileK + g * 8 + e;
+    const int64_t k = k0 + e;
     int64_t wcol = -1;
     if (n < a.shard_n && k < a.shard_k) {
       for (int r = 0; r < a.n_ranges; ++r)
